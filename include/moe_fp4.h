@@ -1,0 +1,229 @@
+/*
+ * moe_fp4.h -- C ABI of the MI355X (gfx950) FP4 mixture-of-experts feed-forward layer.
+ *
+ * The layer is the MoE FFN component described on the MoE module page of the Rust
+ * inference engine (spark_model/layers/moe/mod.rs): a router GEMM, top-K expert
+ * selection (softmax; sigmoid with a per-expert correction bias; or a static
+ * token-to-expert hash table), per selected expert a gate+up projection with
+ * SiLU(gate)*up and a down projection, and a routing-weighted sum blended into
+ * the residual. Expert weights are 4-bit E2M1 in NVFP4 or MXFP4 storage (doc of
+ * MoeLayer.experts_scale_kind on that page).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers unless marked "host". The caller owns all memory;
+ *   the library never allocates device memory. Scratch space is the caller's
+ *   workspace (size from moe_workspace_size).
+ * - Every call is asynchronous on `stream`: it validates on the host, enqueues
+ *   kernels and returns. No call waits for the device, except
+ *   moe_get_device_error, which synchronises `stream` to read the error word.
+ *   Indices and weights stay on the device (module doc: no device-to-host sync).
+ * - bf16 tensors are passed as uint16_t bit patterns; every activation is
+ *   row-major [tokens, hidden].
+ * - Host validation is O(1) and happens before any launch; a failing call
+ *   enqueues nothing and returns a negative moe_status.
+ * - Data errors that only the device can see (an expert id outside [0, E), a
+ *   token id outside [0, vocab), a hash-table entry outside [0, E)) do not stop
+ *   the call: the offending slot is dropped (id -1, weight 0) and bits are set
+ *   in the workspace's device error word (moe_get_device_error).
+ * - Results are deterministic: identical inputs give bitwise identical outputs
+ *   (no floating-point atomics; fixed reduction orders).
+ * - Calls that share one workspace must be ordered on one stream.
+ */
+#ifndef MOE_FP4_H
+#define MOE_FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point (0 = success). */
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, bad dimension, misaligned pointer, bad mode */
+  MOE_ERR_UNSUPPORTED = -2, /* valid request outside this build's limits (sizes, path) */
+  MOE_ERR_WORKSPACE = -3,   /* workspace null or smaller than moe_workspace_size */
+  MOE_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+  MOE_ERR_FORMAT = -5       /* weight format tag unknown or inconsistent with its scales;
+                               never silently decoded as the other format (cf. the
+                               MoE module page, MoeLayer::e8m0_or: a format mismatch
+                               must be loud) */
+} moe_status;
+
+/* Device error word bits (moe_get_device_error). */
+enum {
+  MOE_DEVERR_EXPERT_ID = 1, /* an expert id outside [0, num_experts) reached dispatch */
+  MOE_DEVERR_TOKEN_ID = 2,  /* hash routing: a token id outside [0, vocab) */
+  MOE_DEVERR_TABLE = 4      /* hash routing: a tid2eid entry outside [0, num_experts) */
+};
+
+/* Expert weight storage formats (MoE module page, doc of MoeLayer.experts_scale_kind). */
+enum {
+  MOE_FMT_NVFP4 = 0, /* E2M1 codes + one FP8-E4M3 (OCP "FN") scale per 16 values along K
+                        + one f32 global scale per expert tensor: w = e2m1 * e4m3 * global */
+  MOE_FMT_MXFP4 = 1  /* E2M1 codes + one E8M0 scale per 32 values along K: w = e2m1 * 2^(s-127) */
+};
+
+/* Routing score (MoE module page: doc of correction_bias_dev; constructor page: top-K kernels). */
+enum {
+  MOE_SCORE_SOFTMAX = 0, /* key = logit; weight = softmax probability */
+  MOE_SCORE_SIGMOID = 1  /* key = fp32(sigmoid(logit)) + correction_bias (selection only);
+                            weight = sigmoid(logit) */
+};
+
+/* Expert selection (MoE module page: doc of tid2eid_dev). */
+enum {
+  MOE_SELECT_TOPK = 0, /* the top_k largest keys; ties go to the lower expert index */
+  MOE_SELECT_HASH = 1  /* ids = tid2eid[token_id][0..top_k); weights = score at those ids */
+};
+
+/* Expert-path choice (both paths compute the same function). */
+enum {
+  MOE_PATH_AUTO = 0,    /* decode when tokens*top_k/min(E, tokens*top_k) < 4 rows per expert */
+  MOE_PATH_DECODE = 1,  /* HBM-streaming GEMV kernels */
+  MOE_PATH_PREFILL = 2  /* expert-grouped MFMA GEMM kernels (needs hidden, inter % 64 == 0) */
+};
+
+/* Build limits (checked on the host). */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOP_K 32
+
+/* One projection of a group of experts, in storage form (host struct, device pointers).
+ *   packed       uint8 [experts, n, k/2]: byte j of a row holds code 2j in its low nibble
+ *                and code 2j+1 in its high nibble (K contiguous per output row n)
+ *   scales       uint8 [experts, n, k/16] E4M3 codes (NVFP4) or [experts, n, k/32] E8M0 (MXFP4)
+ *   global_scale f32 [experts] for NVFP4; must be NULL for MXFP4
+ *   gate/up: n = inter, k = hidden.  down: n = hidden, k = inter.
+ * packed and scales must be 16-byte aligned; k % 32 == 0. */
+typedef struct {
+  int32_t format;
+  const uint8_t* packed;
+  const uint8_t* scales;
+  const float* global_scale;
+  int32_t experts;
+  int32_t n;
+  int32_t k;
+} moe_fp4_weight;
+
+/* The three projections of an expert group (routed: experts = num_experts; shared: 1). */
+typedef struct {
+  moe_fp4_weight gate;
+  moe_fp4_weight up;
+  moe_fp4_weight down;
+} moe_expert_weights;
+
+/* Layer configuration (host struct). */
+typedef struct {
+  int32_t tokens;       /* T >= 0 (T == 0: the call returns MOE_OK and touches no pointer) */
+  int32_t hidden;       /* H, multiple of 32 */
+  int32_t num_experts;  /* E in [1, MOE_MAX_EXPERTS] */
+  int32_t top_k;        /* k in [1, min(E, MOE_MAX_TOP_K)] */
+  int32_t inter;        /* I, routed-expert intermediate size, multiple of 32 */
+  int32_t score_mode;   /* MOE_SCORE_* */
+  int32_t select_mode;  /* MOE_SELECT_* */
+  int32_t renormalize;  /* 1: divide the k weights by their sum */
+  float routed_scaling; /* multiplies the (renormalised) routed weights; 1.0 = none */
+  int32_t has_shared;   /* 1: one always-on shared expert with weight 1 */
+  int32_t shared_inter; /* intermediate size of the shared expert (multiple of 32) */
+  int32_t pre_norm;     /* 1: RMSNorm(x)*gamma feeds the experts; the router sees raw x
+                           (MoE module page, doc of MoeLayer.pre_expert_norm) */
+  float norm_eps;       /* RMSNorm epsilon */
+  int64_t vocab;        /* hash routing: rows of tid2eid */
+  int32_t path;         /* MOE_PATH_* */
+} moe_config;
+
+/* Human-readable name of a moe_status value (host; static string). */
+const char* moe_status_string(int status);
+
+/* Bytes of workspace that moe_route / moe_experts_forward / moe_layer_forward need for
+ * `cfg` (host; pure function of the config). One workspace serves all three calls. */
+int moe_workspace_size(const moe_config* cfg, size_t* bytes_out);
+
+/* Router + top-K selection (constructor page: router GEMM with fp32 output and the
+ * softmax / sigmoid-with-bias / hash top-K kernels).
+ *   x            bf16 [T, H] router input; may be NULL when logits_in is given
+ *   router_w     bf16 [E, H]; may be NULL when logits_in is given
+ *   logit_bias   f32 [E] added to every logit before scoring, or NULL
+ *   correction_bias f32 [E] (sigmoid only; selection key only), or NULL
+ *   token_ids    int32 [T] (hash only), tid2eid int64 [vocab, top_k] (hash only)
+ *   logits_in    f32 [T, E]: route from these logits instead of computing them, or NULL
+ *   logits_out   f32 [T, E] receives the logits, or NULL
+ *   topk_ids     int32 [T, top_k] out: best first (key descending, then index ascending);
+ *                -1 marks a slot dropped by a data error (hash routing)
+ *   topk_w       f32 [T, top_k] out: routing weights (0 for dropped slots)
+ * Logits are fp32(x . W_r^T + logit_bias), the dot product accumulated in fp64 and
+ * rounded once. */
+int moe_route(const moe_config* cfg, const uint16_t* x, const uint16_t* router_w,
+              const float* logit_bias, const float* correction_bias,
+              const int32_t* token_ids, const int64_t* tid2eid, const float* logits_in,
+              float* logits_out, int32_t* topk_ids, float* topk_w, void* workspace,
+              size_t workspace_bytes, hipStream_t stream);
+
+/* Experts + weighted-sum blend for given routing (module doc: gate+up, SiLU*up, down;
+ * weighted-sum blend into the residual).
+ *   x_experts  bf16 [T, H] expert input (already normalised if a pre-norm applies)
+ *   topk_ids   int32 [T, top_k], topk_w f32 [T, top_k] (ids outside [0, E) are dropped
+ *              and flagged MOE_DEVERR_EXPERT_ID)
+ *   routed     host struct of the routed experts (experts == E, gate/up n == inter)
+ *   shared     host struct of the shared expert (experts == 1), or NULL if !has_shared
+ *   residual   bf16 [T, H], or NULL for zero
+ *   out        bf16 [T, H]: bf16_rne(residual + sum_j w_j y_j + y_shared), fp32 sum in
+ *              slot order; may alias residual, must not alias x_experts */
+int moe_experts_forward(const moe_config* cfg, const uint16_t* x_experts,
+                        const int32_t* topk_ids, const float* topk_w,
+                        const moe_expert_weights* routed, const moe_expert_weights* shared,
+                        const uint16_t* residual, uint16_t* out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* The whole layer: [RMSNorm] -> router -> top-K -> experts -> blend.
+ *   norm_gamma bf16 [H] (pre_norm only)
+ *   dbg_logits f32 [T, E], dbg_ids int32 [T, top_k], dbg_w f32 [T, top_k]: optional
+ *              copies of the routing decisions (NULL to skip)
+ * Other arguments as in moe_route and moe_experts_forward. */
+int moe_layer_forward(const moe_config* cfg, const uint16_t* x, const uint16_t* norm_gamma,
+                      const uint16_t* router_w, const float* logit_bias,
+                      const float* correction_bias, const int32_t* token_ids,
+                      const int64_t* tid2eid, const moe_expert_weights* routed,
+                      const moe_expert_weights* shared, const uint16_t* residual,
+                      uint16_t* out, float* dbg_logits, int32_t* dbg_ids, float* dbg_w,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Test entry: decode expert `expert` of `w` to f32 [n, k] with the device routine of
+ * the chosen path (MOE_PATH_DECODE: E2M1 to bf16 then the block scale as an fp32
+ * factor; MOE_PATH_PREFILL: the bf16 MFMA operand), times the NVFP4 global scale.
+ * Every value is exact, so the result is bit-comparable with the format definition. */
+int moe_debug_dequant_fp4(const moe_fp4_weight* w, int32_t expert, int32_t path, float* out,
+                          hipStream_t stream);
+
+/* Profiling aid: stage boundaries of moe_layer_forward, in launch order. */
+enum {
+  MOE_STAGE_BEGIN = 0,        /* before the first kernel of the call */
+  MOE_STAGE_ROUTED = 1,       /* after RMSNorm (if any), router GEMM and top-K */
+  MOE_STAGE_DISPATCHED = 2,   /* after the dispatch build */
+  MOE_STAGE_GATE_UP = 3,      /* after the routed experts' gate+up (+SiLU*up) kernel */
+  MOE_STAGE_DOWN = 4,         /* after the routed experts' down kernel */
+  MOE_STAGE_SHARED = 5,       /* after the shared expert's two kernels (none: same as DOWN) */
+  MOE_STAGE_COMBINED = 6,     /* after the weighted-sum blend */
+  MOE_STAGE_COUNT = 7
+};
+
+/* Profiling aid (host): the NEXT moe_layer_forward call made on this host thread
+ * records events[i] (caller-created HIP events) on its stream at boundary i, for
+ * i < count, then forgets the array. Elapsed times between consecutive events are the
+ * stage durations on that stream. events == NULL cancels a pending request. */
+int moe_set_stage_events(hipEvent_t* events, int32_t count);
+
+/* Synchronise `stream`, then copy the device error word of `workspace` (MOE_DEVERR_*
+ * bits of the last moe_experts_forward / moe_layer_forward on it) to *host_err. */
+int moe_get_device_error(const void* workspace, size_t workspace_bytes, int32_t* host_err,
+                         hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FP4_H */

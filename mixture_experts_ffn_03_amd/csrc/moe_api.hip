@@ -1,0 +1,458 @@
+// Host side of the C ABI declared in include/moe_fp4.h: validation, workspace layout,
+// path choice and the launch sequence. Nothing here waits on the device except
+// moe_get_device_error.
+//
+// Validation follows the MoE constructor page (spark_model/layers/moe/init.rs):
+// top_k must lie in 1..=num_experts with num_experts > 0, and the routing kernels'
+// own capacity bounds are checked up front rather than overrun. Here those bounds
+// are this library's (MOE_MAX_EXPERTS, MOE_MAX_TOP_K), set by the top-K kernel's
+// register and LDS budget. A weight whose format tag does not match its scale
+// layout is an error, never a silent decode in the other format (MoE module page,
+// MoeLayer::e8m0_or).
+#include <cstring>
+
+#include "moe_fp4.h"
+#include "moe_internal.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+struct Layout {
+  size_t partial, logits, ids, w, errtok, xn, row_token, inv, tiles, ntiles, h, y, total;
+  int ks, hsplit;
+  int rows;        // R
+  int h_stride;
+  int tile_bound_dec, tile_bound_pre;
+};
+
+int tile_bound(int S, int E, int h) { return S / h + (S < E ? S : E) + 1; }
+
+// Prefill M-tile height from the mean rows per routed expert.
+int prefill_mt(const moe_config& c) {
+  const int S = c.tokens * c.top_k;
+  const int groups = S < c.num_experts ? S : c.num_experts;
+  const int rpe = groups > 0 ? S / groups : 0;
+  if (rpe < 48) return 32;
+  if (rpe < 96) return 64;
+  return 128;
+}
+
+Layout make_layout(const moe_config& c) {
+  Layout L{};
+  const int T = c.tokens, E = c.num_experts, K = c.top_k, H = c.hidden;
+  const int S = T * K;
+  L.rows = S + (c.has_shared ? T : 0);
+  const int nblk = ceil_div(E, kRouterTile) * ceil_div(T > 0 ? T : 1, kRouterTile);
+  int ks = ceil_div(512, nblk);
+  if (ks > H / 32) ks = H / 32;
+  if (ks < 1) ks = 1;
+  L.hsplit = ceil_div(ceil_div(H, ks), 32) * 32;
+  L.ks = ceil_div(H, L.hsplit);
+  int imax = c.inter;
+  if (c.has_shared && c.shared_inter > imax) imax = c.shared_inter;
+  L.h_stride = ceil_div(imax, 8) * 8;
+  L.tile_bound_dec = tile_bound(S, E, kDecodeTile);
+  L.tile_bound_pre = tile_bound(S, E, prefill_mt(c));
+  const int tb = L.tile_bound_dec > L.tile_bound_pre ? L.tile_bound_dec : L.tile_bound_pre;
+  size_t off = kAlign;  // header: device error word
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.partial = take((size_t)L.ks * T * E * sizeof(double));
+  L.logits = take((size_t)T * E * 4);
+  L.ids = take((size_t)S * 4);
+  L.w = take((size_t)S * 4);
+  L.errtok = take((size_t)T * 4);
+  L.xn = take(c.pre_norm ? (size_t)T * H * 2 : 0);
+  L.row_token = take((size_t)L.rows * 4);
+  L.inv = take((size_t)S * 4);
+  L.tiles = take((size_t)tb * sizeof(Tile));
+  L.ntiles = take(16);
+  L.h = take((size_t)L.rows * L.h_stride * 2);
+  L.y = take((size_t)L.rows * H * 4);
+  L.total = off;
+  return L;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_config(const moe_config* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->tokens < 0 || c->hidden <= 0 || c->hidden % 32 != 0) return MOE_ERR_INVALID_ARG;
+  if (c->num_experts <= 0 || c->top_k < 1 || c->top_k > c->num_experts) return MOE_ERR_INVALID_ARG;
+  if (c->num_experts > MOE_MAX_EXPERTS || c->top_k > MOE_MAX_TOP_K) return MOE_ERR_UNSUPPORTED;
+  if (c->inter <= 0 || c->inter % 32 != 0) return MOE_ERR_INVALID_ARG;
+  if (c->score_mode != MOE_SCORE_SOFTMAX && c->score_mode != MOE_SCORE_SIGMOID)
+    return MOE_ERR_INVALID_ARG;
+  if (c->select_mode != MOE_SELECT_TOPK && c->select_mode != MOE_SELECT_HASH)
+    return MOE_ERR_INVALID_ARG;
+  if (c->select_mode == MOE_SELECT_HASH && c->vocab <= 0) return MOE_ERR_INVALID_ARG;
+  if (c->has_shared && (c->shared_inter <= 0 || c->shared_inter % 32 != 0))
+    return MOE_ERR_INVALID_ARG;
+  if (c->path < MOE_PATH_AUTO || c->path > MOE_PATH_PREFILL) return MOE_ERR_INVALID_ARG;
+  if (!(c->routed_scaling == c->routed_scaling)) return MOE_ERR_INVALID_ARG;
+  if (c->pre_norm && !(c->norm_eps >= 0.f)) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)c->tokens * c->top_k > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_weight(const moe_fp4_weight& w, int experts, int n, int k) {
+  if (w.format != MOE_FMT_NVFP4 && w.format != MOE_FMT_MXFP4) return MOE_ERR_FORMAT;
+  if (w.format == MOE_FMT_NVFP4 && !w.global_scale) return MOE_ERR_FORMAT;
+  if (w.format == MOE_FMT_MXFP4 && w.global_scale) return MOE_ERR_FORMAT;
+  if (!w.packed || !w.scales) return MOE_ERR_INVALID_ARG;
+  if (w.experts != experts || w.n != n || w.k != k) return MOE_ERR_INVALID_ARG;
+  if (k % 32 != 0 || n <= 0) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w.packed) || !aligned16(w.scales)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int check_group(const moe_expert_weights* g, int experts, int H, int I) {
+  if (!g) return MOE_ERR_INVALID_ARG;
+  int r;
+  if ((r = check_weight(g->gate, experts, I, H)) != MOE_OK) return r;
+  if ((r = check_weight(g->up, experts, I, H)) != MOE_OK) return r;
+  if ((r = check_weight(g->down, experts, H, I)) != MOE_OK) return r;
+  if (g->gate.format != g->up.format) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+WeightDesc desc(const moe_fp4_weight& w) {
+  WeightDesc d;
+  d.packed = w.packed;
+  d.scales = w.scales;
+  d.global = w.global_scale;
+  d.fmt = w.format;
+  d.n = w.n;
+  d.k = w.k;
+  return d;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<uint8_t*>(ws) + off);
+}
+
+// Which expert path runs, or an error when a forced path cannot take the shapes.
+int choose_path(const moe_config& c, int* path) {
+  const bool pre_ok = c.hidden % 64 == 0 && c.inter % 64 == 0 &&
+                      (!c.has_shared || c.shared_inter % 64 == 0);
+  if (c.path == MOE_PATH_DECODE) { *path = MOE_PATH_DECODE; return MOE_OK; }
+  if (c.path == MOE_PATH_PREFILL) {
+    if (!pre_ok) return MOE_ERR_UNSUPPORTED;
+    *path = MOE_PATH_PREFILL;
+    return MOE_OK;
+  }
+  const int S = c.tokens * c.top_k;
+  const int groups = S < c.num_experts ? S : c.num_experts;
+  const bool many_rows = groups > 0 && S >= 4 * groups;
+  *path = (many_rows && pre_ok) ? MOE_PATH_PREFILL : MOE_PATH_DECODE;
+  return MOE_OK;
+}
+
+#define MOE_HIP(call)                          \
+  do {                                         \
+    if ((call) != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+// One-shot stage-event request of this host thread (moe_set_stage_events).
+thread_local hipEvent_t* t_stage_events = nullptr;
+thread_local int t_stage_count = 0;
+
+struct StageMarks {
+  hipEvent_t* ev = nullptr;
+  int n = 0;
+  hipStream_t s = nullptr;
+  hipError_t mark(int i) const {
+    return (ev && i < n) ? hipEventRecord(ev[i], s) : hipSuccess;
+  }
+};
+
+// Dispatch + experts + blend on an already-validated config.
+int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const int32_t* ids,
+                const float* w, const int32_t* err_tok, const moe_expert_weights* routed,
+                const moe_expert_weights* shared, const uint16_t* residual, uint16_t* out,
+                void* ws, hipStream_t s, const StageMarks& marks = StageMarks()) {
+  int path;
+  int r = choose_path(c, &path);
+  if (r != MOE_OK) return r;
+  const bool pre = path == MOE_PATH_PREFILL;
+  const int mt = pre ? prefill_mt(c) : kDecodeTile;
+
+  DispatchArgs d{};
+  d.ids = ids;
+  d.err_tok = err_tok;
+  d.row_token = at<int32_t>(ws, L.row_token);
+  d.inv = at<int32_t>(ws, L.inv);
+  d.tiles = at<Tile>(ws, L.tiles);
+  d.ntiles = at<int32_t>(ws, L.ntiles);
+  d.err_word = at<int32_t>(ws, 0);
+  d.T = c.tokens;
+  d.K = c.top_k;
+  d.E = c.num_experts;
+  d.shared_rows = c.has_shared ? c.tokens : 0;
+  d.tile_h = mt;
+  MOE_HIP(launch_dispatch(d, s));
+  MOE_HIP(marks.mark(MOE_STAGE_DISPATCHED));
+
+  ExpertGemmArgs a{};
+  a.x = xe;
+  a.row_token = d.row_token;
+  a.src.tiles = d.tiles;
+  a.src.ntiles = d.ntiles;
+  a.tile_bound = pre ? L.tile_bound_pre : L.tile_bound_dec;
+  a.gate = desc(routed->gate);
+  a.up = desc(routed->up);
+  a.down = desc(routed->down);
+  a.h = at<uint16_t>(ws, L.h);
+  a.h_stride = L.h_stride;
+  a.y = at<void>(ws, L.y);
+  a.T = c.tokens;
+  a.H = c.hidden;
+  a.I = c.inter;
+  if (pre) {
+    MOE_HIP(launch_prefill_gate_up(a, mt, s));
+    MOE_HIP(marks.mark(MOE_STAGE_GATE_UP));
+    MOE_HIP(launch_prefill_down(a, mt, s));
+  } else {
+    MOE_HIP(launch_decode_gate_up(a, s));
+    MOE_HIP(marks.mark(MOE_STAGE_GATE_UP));
+    MOE_HIP(launch_decode_down(a, s));
+  }
+  MOE_HIP(marks.mark(MOE_STAGE_DOWN));
+  if (c.has_shared) {
+    ExpertGemmArgs b = a;
+    b.src.tiles = nullptr;
+    b.src.ntiles = nullptr;
+    b.src.implicit_row0 = 0;
+    b.src.implicit_rows = c.tokens;
+    b.src.implicit_height = mt;
+    b.tile_bound = ceil_div(c.tokens, mt);
+    b.gate = desc(shared->gate);
+    b.up = desc(shared->up);
+    b.down = desc(shared->down);
+    b.I = c.shared_inter;
+    if (pre) {
+      MOE_HIP(launch_prefill_gate_up(b, mt, s));
+      MOE_HIP(launch_prefill_down(b, mt, s));
+    } else {
+      MOE_HIP(launch_decode_gate_up(b, s));
+      MOE_HIP(launch_decode_down(b, s));
+    }
+  }
+  MOE_HIP(marks.mark(MOE_STAGE_SHARED));
+  CombineArgs cb{};
+  cb.y = a.y;
+  cb.y_bf16 = pre ? 1 : 0;
+  cb.w = w;
+  cb.inv = d.inv;
+  cb.shared = c.has_shared;
+  cb.residual = residual;
+  cb.out = out;
+  cb.T = c.tokens;
+  cb.K = c.top_k;
+  cb.H = c.hidden;
+  MOE_HIP(launch_combine(cb, s));
+  MOE_HIP(marks.mark(MOE_STAGE_COMBINED));
+  return MOE_OK;
+}
+
+int check_ws(const Layout& L, const void* ws, size_t bytes) {
+  if (!ws || bytes < L.total || !aligned16(ws)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+int launch_route(const moe_config& c, const Layout& L, const uint16_t* x,
+                 const uint16_t* router_w, const float* logit_bias, const float* corr,
+                 const int32_t* token_ids, const int64_t* tid2eid, const float* logits_in,
+                 float* logits_out, int32_t* ids, float* w, void* ws, hipStream_t s) {
+  if (!logits_in)
+    MOE_HIP(launch_router_partial(x, router_w, at<double>(ws, L.partial), c.tokens,
+                                  c.num_experts, c.hidden, L.ks, L.hsplit, s));
+  TopkArgs t{};
+  t.partial = logits_in ? nullptr : at<double>(ws, L.partial);
+  t.ks = L.ks;
+  t.logits_in = logits_in;
+  t.logit_bias = logit_bias;
+  t.correction_bias = c.score_mode == MOE_SCORE_SIGMOID ? corr : nullptr;
+  t.token_ids = token_ids;
+  t.tid2eid = tid2eid;
+  t.vocab = c.vocab;
+  t.logits_out = logits_out;
+  t.ids = ids;
+  t.w = w;
+  t.err_tok = at<int32_t>(ws, L.errtok);
+  t.T = c.tokens;
+  t.E = c.num_experts;
+  t.K = c.top_k;
+  t.score = c.score_mode;
+  t.select = c.select_mode;
+  t.renorm = c.renormalize;
+  t.scaling = c.routed_scaling;
+  MOE_HIP(launch_topk(t, s));
+  return MOE_OK;
+}
+
+int check_route_ptrs(const moe_config& c, const uint16_t* x, const uint16_t* router_w,
+                     const int32_t* token_ids, const int64_t* tid2eid, const float* logits_in) {
+  if (!logits_in && (!x || !router_w)) return MOE_ERR_INVALID_ARG;
+  if (c.select_mode == MOE_SELECT_HASH && (!token_ids || !tid2eid)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: outside this build's limits";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime or launch failure";
+    case MOE_ERR_FORMAT: return "MOE_ERR_FORMAT: weight format tag inconsistent with its scales";
+    default: return "unknown moe_status";
+  }
+}
+
+int moe_workspace_size(const moe_config* cfg, size_t* bytes_out) {
+  int r = check_config(cfg);
+  if (r != MOE_OK) return r;
+  if (!bytes_out) return MOE_ERR_INVALID_ARG;
+  *bytes_out = make_layout(*cfg).total;
+  return MOE_OK;
+}
+
+int moe_route(const moe_config* cfg, const uint16_t* x, const uint16_t* router_w,
+              const float* logit_bias, const float* correction_bias, const int32_t* token_ids,
+              const int64_t* tid2eid, const float* logits_in, float* logits_out,
+              int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes,
+              hipStream_t stream) {
+  int r = check_config(cfg);
+  if (r != MOE_OK) return r;
+  const moe_config& c = *cfg;
+  if (c.tokens == 0) return MOE_OK;  // no-op: no pointer is touched
+  if ((r = check_route_ptrs(c, x, router_w, token_ids, tid2eid, logits_in)) != MOE_OK) return r;
+  if (!topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  const Layout L = make_layout(c);
+  if ((r = check_ws(L, workspace, workspace_bytes)) != MOE_OK) return r;
+  if (c.tokens == 0) return MOE_OK;
+  return launch_route(c, L, x, router_w, logit_bias, correction_bias, token_ids, tid2eid,
+                      logits_in, logits_out, topk_ids, topk_w, workspace, stream);
+}
+
+int moe_experts_forward(const moe_config* cfg, const uint16_t* x_experts,
+                        const int32_t* topk_ids, const float* topk_w,
+                        const moe_expert_weights* routed, const moe_expert_weights* shared,
+                        const uint16_t* residual, uint16_t* out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  int r = check_config(cfg);
+  if (r != MOE_OK) return r;
+  const moe_config& c = *cfg;
+  if (c.tokens == 0) return MOE_OK;  // no-op: no pointer is touched
+  if (!x_experts || !topk_ids || !topk_w || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_experts) || !aligned16(out) || (residual && !aligned16(residual)))
+    return MOE_ERR_INVALID_ARG;
+  if (out == x_experts) return MOE_ERR_INVALID_ARG;
+  if ((r = check_group(routed, c.num_experts, c.hidden, c.inter)) != MOE_OK) return r;
+  if (c.has_shared) {
+    if ((r = check_group(shared, 1, c.hidden, c.shared_inter)) != MOE_OK) return r;
+  }
+  int path;
+  if ((r = choose_path(c, &path)) != MOE_OK) return r;
+  const Layout L = make_layout(c);
+  if ((r = check_ws(L, workspace, workspace_bytes)) != MOE_OK) return r;
+  if (c.tokens == 0) return MOE_OK;
+  return run_experts(c, L, x_experts, topk_ids, topk_w, nullptr, routed,
+                     c.has_shared ? shared : nullptr, residual, out, workspace, stream);
+}
+
+int moe_layer_forward(const moe_config* cfg, const uint16_t* x, const uint16_t* norm_gamma,
+                      const uint16_t* router_w, const float* logit_bias,
+                      const float* correction_bias, const int32_t* token_ids,
+                      const int64_t* tid2eid, const moe_expert_weights* routed,
+                      const moe_expert_weights* shared, const uint16_t* residual,
+                      uint16_t* out, float* dbg_logits, int32_t* dbg_ids, float* dbg_w,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int r = check_config(cfg);
+  if (r != MOE_OK) return r;
+  const moe_config& c = *cfg;
+  if (c.tokens == 0) return MOE_OK;  // no-op: no pointer is touched
+  if (!x || !router_w || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(out) || (residual && !aligned16(residual)))
+    return MOE_ERR_INVALID_ARG;
+  if (out == x) return MOE_ERR_INVALID_ARG;
+  if (c.pre_norm && !norm_gamma) return MOE_ERR_INVALID_ARG;
+  if ((r = check_route_ptrs(c, x, router_w, token_ids, tid2eid, nullptr)) != MOE_OK) return r;
+  if ((r = check_group(routed, c.num_experts, c.hidden, c.inter)) != MOE_OK) return r;
+  if (c.has_shared) {
+    if ((r = check_group(shared, 1, c.hidden, c.shared_inter)) != MOE_OK) return r;
+  }
+  int path;
+  if ((r = choose_path(c, &path)) != MOE_OK) return r;
+  const Layout L = make_layout(c);
+  if ((r = check_ws(L, workspace, workspace_bytes)) != MOE_OK) return r;
+  if (c.tokens == 0) return MOE_OK;
+  StageMarks marks;
+  marks.ev = t_stage_events;
+  marks.n = t_stage_count;
+  marks.s = stream;
+  t_stage_events = nullptr;
+  t_stage_count = 0;
+  MOE_HIP(marks.mark(MOE_STAGE_BEGIN));
+  const uint16_t* xe = x;
+  if (c.pre_norm) {
+    uint16_t* xn = at<uint16_t>(workspace, L.xn);
+    MOE_HIP(launch_rmsnorm(x, norm_gamma, xn, c.tokens, c.hidden, c.norm_eps, stream));
+    xe = xn;
+  }
+  int32_t* ids = at<int32_t>(workspace, L.ids);
+  float* w = at<float>(workspace, L.w);
+  r = launch_route(c, L, x, router_w, logit_bias, correction_bias, token_ids, tid2eid, nullptr,
+                   dbg_logits, ids, w, workspace, stream);
+  if (r != MOE_OK) return r;
+  MOE_HIP(marks.mark(MOE_STAGE_ROUTED));
+  r = run_experts(c, L, xe, ids, w, at<int32_t>(workspace, L.errtok), routed,
+                  c.has_shared ? shared : nullptr, residual, out, workspace, stream, marks);
+  if (r != MOE_OK) return r;
+  const size_t slots = (size_t)c.tokens * c.top_k;
+  if (dbg_ids) MOE_HIP(hipMemcpyAsync(dbg_ids, ids, slots * 4, hipMemcpyDeviceToDevice, stream));
+  if (dbg_w) MOE_HIP(hipMemcpyAsync(dbg_w, w, slots * 4, hipMemcpyDeviceToDevice, stream));
+  return MOE_OK;
+}
+
+int moe_debug_dequant_fp4(const moe_fp4_weight* w, int32_t expert, int32_t path, float* out,
+                          hipStream_t stream) {
+  if (!w || !out) return MOE_ERR_INVALID_ARG;
+  int r = check_weight(*w, w->experts, w->n, w->k);
+  if (r != MOE_OK) return r;
+  if (expert < 0 || expert >= w->experts) return MOE_ERR_INVALID_ARG;
+  if (path != MOE_PATH_DECODE && path != MOE_PATH_PREFILL) return MOE_ERR_INVALID_ARG;
+  MOE_HIP(launch_debug_dequant(desc(*w), expert, path, out, stream));
+  return MOE_OK;
+}
+
+int moe_set_stage_events(hipEvent_t* events, int32_t count) {
+  if (events && count < 0) return MOE_ERR_INVALID_ARG;
+  t_stage_events = events;
+  t_stage_count = events ? count : 0;
+  return MOE_OK;
+}
+
+int moe_get_device_error(const void* workspace, size_t workspace_bytes, int32_t* host_err,
+                         hipStream_t stream) {
+  if (!workspace || workspace_bytes < kAlign || !host_err) return MOE_ERR_INVALID_ARG;
+  MOE_HIP(hipMemcpyAsync(host_err, workspace, 4, hipMemcpyDeviceToHost, stream));
+  MOE_HIP(hipStreamSynchronize(stream));
+  return MOE_OK;
+}
+
+}  // extern "C"

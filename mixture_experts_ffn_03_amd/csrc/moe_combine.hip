@@ -1,0 +1,76 @@
+// Weighted-sum blend into the residual (MoE constructor page: the weighted-sum blend and
+// residual-add kernels; the unpermute-and-reduce step of the grouped prefill path):
+//   out[t] = bf16_rne(residual[t] + sum_j w[t,j] * y[row(t,j)] + y_shared[t])
+// summed in fp32 in the fixed order j = 0..K-1, then the shared expert, then the residual.
+// Each thread produces 8 consecutive outputs with 128-bit stores.
+#include "moe_device.h"
+
+namespace moe {
+
+template <bool YBF16>
+__device__ __forceinline__ void load_y8(const void* y, size_t off, float (&v)[8]) {
+  if (YBF16) {
+    const uint4 q = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(y) + off);
+    const uint32_t d[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32(d[i] & 0xFFFFu);
+      v[2 * i + 1] = bf16_to_f32(d[i] >> 16);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(y) + off);
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+template <bool YBF16>
+__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+  const int t = blockIdx.y;
+  const int h0 = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (h0 >= a.H) return;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int j = 0; j < a.K; ++j) {
+    const int p = a.inv[(size_t)t * a.K + j];
+    if (p < 0) continue;
+    const float w = a.w[(size_t)t * a.K + j];
+    float v[8];
+    load_y8<YBF16>(a.y, (size_t)p * a.H + h0, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+  }
+  if (a.shared) {
+    float v[8];
+    load_y8<YBF16>(a.y, (size_t)t * a.H + h0, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += v[i];
+  }
+  if (a.residual) {
+    const uint4 q = *reinterpret_cast<const uint4*>(a.residual + (size_t)t * a.H + h0);
+    const uint32_t d[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += bf16_to_f32(d[i] & 0xFFFFu);
+      acc[2 * i + 1] += bf16_to_f32(d[i] >> 16);
+    }
+  }
+  uint4 o;
+  o.x = pack_bf16x2(acc[0], acc[1]);
+  o.y = pack_bf16x2(acc[2], acc[3]);
+  o.z = pack_bf16x2(acc[4], acc[5]);
+  o.w = pack_bf16x2(acc[6], acc[7]);
+  *reinterpret_cast<uint4*>(a.out + (size_t)t * a.H + h0) = o;
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  const dim3 grid((a.H / 8 + 255) / 256, a.T);
+  if (a.y_bf16) hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

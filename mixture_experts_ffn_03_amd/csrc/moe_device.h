@@ -1,0 +1,182 @@
+// Device helpers of the gfx950 MoE kernels: bf16 packing, FP4 block decoding and
+// wavefront (64-lane) reductions. Every kernel of the library includes this file;
+// nothing here is used on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (gfx950 converts natively; denormals kept).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---------------------------------------------------------------------------
+// Scale decoding. E4M3 here is the OCP "FN" variant (bias 7, max 448, NaN at
+// S.1111.111), which NVFP4 uses for its per-16 block scales; E8M0 is the MX
+// per-32 shared exponent 2^(s-127) with 0xFF = NaN.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t s = (b & 0x80u) << 24;
+  const uint32_t em = b & 0x7Fu;
+  if (em == 0x7Fu) return __uint_as_float(0x7FC00000u);
+  if (em < 8u) {  // subnormal: m * 2^-9
+    return __uint_as_float(s | __float_as_uint((float)em * 0.001953125f));
+  }
+  // normal: exponent e-7 -> e-7+127 = e+120; the 3 mantissa bits move to the top of 23
+  return __uint_as_float(s | ((em + (120u << 3)) << 20));
+}
+
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+  if (b == 0xFFu) return __uint_as_float(0x7FC00000u);
+  if (b == 0u) return __uint_as_float(0x00400000u);  // 2^-127 (fp32 denormal)
+  return __uint_as_float(b << 23);
+}
+
+// ---------------------------------------------------------------------------
+// E2M1 decoding with the gfx950 scaled converts. The instruction applies only the
+// exponent of its f32 scale operand (checked exhaustively against the format
+// definition by the dequant parity test), so it is exact for power-of-two scales
+// (E8M0 and 1.0) and an E4M3 block scale is applied as a separate fp32 factor.
+// ---------------------------------------------------------------------------
+
+// Byte `sel` of q (codes 2*sel, 2*sel+1; low nibble first) -> bf16 pair times 2^exp(scale).
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t q, float pow2_scale) {
+  bf16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, pow2_scale, SEL);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+template <int SEL>
+__device__ __forceinline__ f32x2_t fp4x2_to_f32x2(uint32_t q, float pow2_scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, pow2_scale, SEL);
+}
+
+// 8 codes (one dword) -> 4 bf16 pairs, exact values e2m1 * 2^exp(pow2_scale).
+__device__ __forceinline__ void fp4x8_to_bf16(uint32_t q, float pow2_scale, uint32_t out[4]) {
+  out[0] = fp4x2_to_bf16x2<0>(q, pow2_scale);
+  out[1] = fp4x2_to_bf16x2<1>(q, pow2_scale);
+  out[2] = fp4x2_to_bf16x2<2>(q, pow2_scale);
+  out[3] = fp4x2_to_bf16x2<3>(q, pow2_scale);
+}
+
+// 8 codes -> 4 bf16 pairs of e2m1 * s for an arbitrary fp32 factor s whose product with
+// every E2M1 value is representable in bf16 (true for every E4M3 value): decode to f32,
+// multiply (exact), convert (exact).
+__device__ __forceinline__ void fp4x8_to_bf16_scaled(uint32_t q, float s, uint32_t out[4]) {
+  f32x2_t a = fp4x2_to_f32x2<0>(q, 1.0f);
+  f32x2_t b = fp4x2_to_f32x2<1>(q, 1.0f);
+  f32x2_t c = fp4x2_to_f32x2<2>(q, 1.0f);
+  f32x2_t d = fp4x2_to_f32x2<3>(q, 1.0f);
+  out[0] = pack_bf16x2(a[0] * s, a[1] * s);
+  out[1] = pack_bf16x2(b[0] * s, b[1] * s);
+  out[2] = pack_bf16x2(c[0] * s, c[1] * s);
+  out[3] = pack_bf16x2(d[0] * s, d[1] * s);
+}
+
+// Scale operand of the scaled convert for an E8M0 code: 2^(b-127) as f32 bits
+// (b = 0 is the denormal 2^-127; b = 255 gives the f32 exponent field 255).
+__device__ __forceinline__ float e8m0_cvt_scale(uint32_t b) {
+  return __uint_as_float(b ? (b << 23) : 0x00400000u);
+}
+
+// The bf16 B operand of the grouped GEMM for 8 codes of one scale block: exact
+// e2m1 * scale for both formats (MXFP4 through the scaled convert, NVFP4 through fp32).
+template <int FMT>
+__device__ __forceinline__ void mfma_operand_fp4x8(uint32_t q, uint32_t sb, uint32_t out[4]) {
+  if (FMT == 1) fp4x8_to_bf16(q, e8m0_cvt_scale(sb), out);
+  else fp4x8_to_bf16_scaled(q, e4m3_to_f32(sb), out);
+}
+
+__device__ __forceinline__ void mfma_operand_fp4x8(int fmt, uint32_t q, uint32_t sb,
+                                                   uint32_t out[4]) {
+  if (fmt == 1) mfma_operand_fp4x8<1>(q, sb, out);
+  else mfma_operand_fp4x8<0>(q, sb, out);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront reductions (64 lanes).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_f(v, m);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor_f(v, m));
+  return v;
+}
+
+// Sum NV per-lane values over each aligned group of L lanes (L a power of two <= 64),
+// halving the value count at each of the first log2(NV) butterfly distances so that
+// no lane reduces every value. On return a lane holds NF = max(1, NV / L) complete
+// sums in v[0..NF); the value index of v[i] is reduced_index(lane, i).
+template <int NV, int L>
+__device__ __forceinline__ void group_reduce_transpose(float (&v)[NV], int lane) {
+  int n = NV;
+#pragma unroll
+  for (int d = L / 2; d >= 1; d >>= 1) {
+    if (n > 1) {
+      const bool upper = (lane & d) != 0;
+      const int h = n / 2;
+#pragma unroll
+      for (int i = 0; i < NV / 2; ++i) {
+        if (i < h) {
+          const float send = upper ? v[i] : v[i + h];
+          const float keep = upper ? v[i + h] : v[i];
+          v[i] = keep + shfl_xor_f(send, d);
+        }
+      }
+      n = h;
+    } else {
+      v[0] += shfl_xor_f(v[0], d);
+    }
+  }
+}
+
+// Value index held in v[i] after group_reduce_transpose<NV, L>.
+template <int NV, int L>
+__device__ __forceinline__ int reduced_index(int lane, int i) {
+  int idx = i, n = NV;
+#pragma unroll
+  for (int d = L / 2; d >= 1; d >>= 1) {
+    if (n > 1) {
+      n >>= 1;
+      if (lane & d) idx += n;
+    }
+  }
+  return idx;
+}
+
+}  // namespace moe

@@ -1,0 +1,114 @@
+// Internal interface between the host side of the library (moe_api.hip) and the
+// kernel translation units: argument structs and launcher declarations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// One projection of an expert group, with device pointers. Expert e's matrix is
+// packed + e * n * (k/2) bytes, scales + e * n * (k/blk) bytes (blk = 16 NVFP4, 32 MXFP4).
+struct WeightDesc {
+  const uint8_t* packed;
+  const uint8_t* scales;
+  const float* global;  // NVFP4 only
+  int32_t fmt;          // 0 NVFP4, 1 MXFP4
+  int32_t n;
+  int32_t k;
+};
+
+// A run of rows of one expert group in the expert-sorted row space.
+struct Tile {
+  int32_t group;
+  int32_t row0;
+  int32_t count;
+  int32_t pad;
+};
+
+// Where the rows a kernel processes come from: either the device tile list written by
+// the dispatch kernel, or an implicit list of fixed-height tiles over a known row range
+// (the shared expert, whose rows are [0, T) of the row space).
+struct TileSource {
+  const Tile* tiles;       // device list, or nullptr for the implicit list
+  const int32_t* ntiles;   // device count of the list
+  int32_t implicit_row0;   // implicit list: first row
+  int32_t implicit_rows;   // implicit list: number of rows
+  int32_t implicit_height; // implicit list: rows per tile
+};
+
+constexpr int kRouterTile = 32;
+constexpr int kMaxExperts = 1024;  // MOE_MAX_EXPERTS
+constexpr int kMaxTopK = 32;       // MOE_MAX_TOP_K
+constexpr int kDecodeTile = 4;     // rows (tokens) per decode tile
+
+hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, uint16_t* out, int T, int H,
+                          float eps, hipStream_t s);
+
+hipError_t launch_router_partial(const uint16_t* x, const uint16_t* w, double* partial, int T,
+                                 int E, int H, int ks, int hsplit, hipStream_t s);
+
+struct TopkArgs {
+  const double* partial;  // [ks, T, E] or nullptr when logits_in is used
+  int ks;
+  const float* logits_in;
+  const float* logit_bias;
+  const float* correction_bias;
+  const int32_t* token_ids;
+  const int64_t* tid2eid;
+  int64_t vocab;
+  float* logits_out;
+  int32_t* ids;
+  float* w;
+  int32_t* err_tok;
+  int T, E, K;
+  int score, select, renorm;
+  float scaling;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+struct DispatchArgs {
+  const int32_t* ids;     // [T, K]
+  const int32_t* err_tok; // [T] or nullptr
+  int32_t* row_token;     // [R]
+  int32_t* inv;           // [T*K]
+  Tile* tiles;
+  int32_t* ntiles;
+  int32_t* err_word;
+  int T, K, E, shared_rows, tile_h;
+};
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+
+struct ExpertGemmArgs {
+  const uint16_t* x;          // bf16 [T, H] expert input
+  const int32_t* row_token;   // [R]
+  TileSource src;
+  int tile_bound;             // grid rows (>= number of tiles)
+  WeightDesc gate, up, down;
+  uint16_t* h;                // bf16 [R, h_stride]
+  int h_stride;
+  void* y;                    // [R, H]: fp32 (decode) or bf16 (prefill)
+  int T, H, I;
+};
+hipError_t launch_decode_gate_up(const ExpertGemmArgs& a, hipStream_t s);
+hipError_t launch_decode_down(const ExpertGemmArgs& a, hipStream_t s);
+hipError_t launch_prefill_gate_up(const ExpertGemmArgs& a, int mt, hipStream_t s);
+hipError_t launch_prefill_down(const ExpertGemmArgs& a, int mt, hipStream_t s);
+
+struct CombineArgs {
+  const void* y;          // [R, H] fp32 or bf16
+  int y_bf16;
+  const float* w;         // [T, K]
+  const int32_t* inv;     // [T, K] row of slot (t, j) or -1
+  int shared;             // shared rows are [0, T)
+  const uint16_t* residual;
+  uint16_t* out;
+  int T, K, H;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+hipError_t launch_debug_dequant(const WeightDesc& w, int expert, int path, float* out,
+                                hipStream_t s);
+
+}  // namespace moe

@@ -15,7 +15,7 @@ a decision is taken on a value the method defines in fp32 (router logits and
 the sigmoid selection key), which are rounded to fp32 exactly as defined.
 
 Layer (for every token t, top-k slots j):
-    x_e      = RMSNorm(x)            if a pre-expert norm is configured, else x
+    x_e      = bf16(RMSNorm(x))      if a pre-expert norm is configured, else x
     logits   = fp32(x . W_r^T + logit_bias)               (router sees raw x)
     ids, w   = select(score(logits))                       (softmax | sigmoid+bias | hash)
     y_{t,j}  = W_d[e] . (SiLU(W_g[e] . x_e[t]) * (W_u[e] . x_e[t]))
@@ -329,13 +329,26 @@ def layer_forward(x, residual, router_w, routed: DequantCache, top_k: int, *,
         logits = router_logits(x, router_w, logit_bias)
     ids, w = route(logits, top_k, score, select, renormalize, correction_bias,
                    token_ids, tid2eid, routed_scaling)
-    xe = rms_norm(x, gamma, norm_eps) if gamma is not None else x
+    # the experts' input is a bf16 activation [T, H] (the boundary passes it as bf16), so
+    # the normalised input is rounded once to bf16 before the expert GEMMs
+    xe = bf16_round_f64(rms_norm(x, gamma, norm_eps)) if gamma is not None else x
     out = experts_forward(xe, ids, w, routed, residual, shared, rows)
     return out, logits, ids, w
 
 
+def bf16_round_f64(v: np.ndarray) -> np.ndarray:
+    """Round fp64 values directly to the nearest bf16 value (8 significant bits, ties to
+    even), returned as fp64. Normal range only (the activations here are far from the
+    bf16 subnormal range); zeros, infinities and NaN pass through."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)  # v = m * 2^e, 0.5 <= |m| < 1
+    r = np.ldexp(np.round(np.ldexp(m, 8)), e - 8)  # np.round: half to even
+    return np.where(np.isfinite(v) & (v != 0), r, v)
+
+
 def bf16_round(v: np.ndarray) -> np.ndarray:
-    """Round fp64/fp32 values to bf16 (nearest even), returned as fp32."""
+    """Round fp32 values to bf16 (nearest even), returned as fp32 (fp64 input is first
+    rounded to fp32)."""
     f = np.asarray(v, dtype=np.float32)
     u = f.view(np.uint32).astype(np.uint64)
     lsb = (u >> 16) & 1

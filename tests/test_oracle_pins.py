@@ -371,7 +371,8 @@ def test_pre_norm_feeds_experts_but_not_router():
     gamma = inp.gamma.float().numpy()
     out, logits, ids, w = O.layer_forward(x, r, rw, _cache(inp.routed), 2, gamma=gamma)
     assert np.array_equal(logits, O.router_logits(x, rw))
-    xn = torch.nn.functional.rms_norm(inp.x.double(), (64,), inp.gamma.double(), eps=1e-6).numpy()
+    xn = torch.nn.functional.rms_norm(inp.x.double(), (64,), inp.gamma.double(), eps=1e-6)
+    xn = xn.to(torch.bfloat16).double().numpy()  # the expert input is a bf16 activation
     want = O.experts_forward(xn, ids, w, _cache(inp.routed), r)
     assert np.allclose(out, want, rtol=1e-12, atol=1e-12)
 
@@ -392,6 +393,17 @@ def test_rows_subset_equals_full():
     sub, _, _, _ = O.layer_forward(x, r, rw, _cache(inp.routed), 2, shared=_cache(inp.shared),
                                    rows=np.array([4, 1]))
     assert np.allclose(sub, full[[4, 1]], rtol=1e-13, atol=1e-13)
+
+
+def test_bf16_round_f64_matches_torch_and_ties_to_even():
+    torch.manual_seed(13)
+    v = torch.randn(10000, dtype=torch.float64) * 10
+    got = O.bf16_round_f64(v.numpy())
+    assert np.array_equal(got, v.to(torch.bfloat16).double().numpy())
+    ties = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 6.0 + 2 ** -6])
+    assert O.bf16_round_f64(ties).tolist() == [1.0, 1.0 + 2 ** -6, -1.0, 6.0]
+    # a value just above a tie must round up even though fp32 rounding would land on it
+    assert O.bf16_round_f64(np.array([1.0 + 2 ** -8 + 2 ** -40]))[0] == 1.0 + 2 ** -7
 
 
 def test_bf16_round_ties_to_even():

@@ -1,0 +1,340 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X FP4 MoE feed-forward layer: one step = one moe_layer_forward
+(router, top-K, dispatch, experts, blend) over one batch of synthetic input.
+
+Prints ONE JSON line on stdout (logs go to stderr):
+  value      whole-job MoE-layer tokens/s (inputs resident in HBM before timing)
+  roofline   the dominant kernel's achieved GB/s (decode, HBM-bound) or TFLOP/s
+             (prefill, MFMA-bound) against the MI355X peak, its duration measured with
+             HIP events recorded on the kernel's own stream during the timed steps
+  cpu_baseline  the CPU oracle timed on the host on a bounded sample of the workload
+
+The default workload is the Qwen3-30B-A3B-like decode layer at 8 tokens; --workload
+selects the others. Steps cycle through several weight sets and input batches so
+that weights are streamed from HBM rather than re-read from the 256 MB Infinity Cache.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s; decode HBM GB/s & prefill MFMA TFLOP/s vs peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+DESCRIPTIONS = {
+    "tiny": "Tiny MoE layer: 4 tokens, hidden 256, 8 experts, top_k=2, softmax, inter 512, NVFP4",
+    "qwen3_decode_t1": "Decode, Qwen3-30B-A3B-like: 1 token, hidden 2048, 128 experts, top_k=8, "
+                       "softmax renormalised, inter 768, NVFP4",
+    "qwen3_decode_t8": "Decode, Qwen3-30B-A3B-like: 8 tokens, hidden 2048, 128 experts, top_k=8, "
+                       "softmax renormalised, inter 768, NVFP4",
+    "dsv3_decode_t32": "Decode, DeepSeek-V3-like: 32 tokens, hidden 7168, 256 experts, top_k=8, "
+                       "sigmoid + correction bias, 1 shared expert, inter 2048, NVFP4",
+    "prefill_zipf_t4096": "Prefill grouped GEMM: 4096 tokens, hidden 4096, 64 experts, top_k=6, "
+                          "softmax with Zipf(1.1) logit bias, inter 1408, MXFP4",
+    "hash_mxfp4_t512": "Hash-routed layer: 512 tokens, vocab 32768, hidden 4096, 256 experts, "
+                       "top_k=6, inter 2048, MXFP4 routed + NVFP4 shared expert, RMSNorm input",
+}
+# weight sets cycled per step: enough distinct weights that the touched experts do not
+# stay resident in the 256 MB Infinity Cache between steps
+WEIGHT_SETS = {"tiny": 1, "qwen3_decode_t1": 4, "qwen3_decode_t8": 4, "dsv3_decode_t32": 1,
+               "prefill_zipf_t4096": 2, "hash_mxfp4_t512": 1}
+# oracle sample: tokens of one batch evaluated by the CPU oracle for the baseline
+CPU_SAMPLE_TOKENS = {"tiny": 4, "qwen3_decode_t1": 1, "qwen3_decode_t8": 8,
+                     "dsv3_decode_t32": 2, "prefill_zipf_t4096": 8, "hash_mxfp4_t512": 8}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def bytes_per_elem(fmt):
+    return 0.5 + (1.0 / 16 if fmt == 0 else 1.0 / 32)
+
+
+class HipEvents:
+    """Raw HIP events through the runtime library torch already loaded."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a),
+                                        ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_ffn_03_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from rocprofv3 FETCH_SIZE/WRITE_SIZE counters
+    (profiles/traffic_<workload>.json), or None if absent or taken on other sources."""
+    p = os.path.join(PROFILE_DIR, f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    k = d.get("kernels", {}).get(kernel)
+    if not k or d.get("source_digest") != source_digest():
+        return None
+    return k.get("bytes_per_launch")
+
+
+def cpu_baseline(spec, inp, name, seconds):
+    import numpy as np
+    import oracle as O
+    from threadpoolctl import threadpool_info
+
+    n_rows = min(CPU_SAMPLE_TOKENS.get(name, 4), spec.tokens)
+    rows = np.arange(n_rows)
+
+    def host(ws):
+        parts = {}
+        for p in ("gate", "up", "down"):
+            w = getattr(ws, p)
+            parts[p] = (w.fmt, w.packed.cpu().numpy(), w.scales.cpu().numpy(),
+                        None if w.global_scale is None else w.global_scale.cpu().numpy())
+        return parts
+
+    f32 = lambda t: None if t is None else t.float().cpu().numpy()  # noqa: E731
+    routed = host(inp.routed)
+    shared = host(inp.shared) if inp.shared is not None else None
+    args = dict(score=spec.score, select=spec.select, renormalize=spec.renormalize,
+                logit_bias=f32(inp.logit_bias), correction_bias=f32(inp.correction_bias),
+                token_ids=None if inp.token_ids is None else inp.token_ids.cpu().numpy(),
+                tid2eid=None if inp.tid2eid is None else inp.tid2eid.cpu().numpy(),
+                gamma=f32(inp.gamma), norm_eps=spec.norm_eps)
+    x, res, rw = f32(inp.x), f32(inp.residual), f32(inp.router_w)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        cache = O.DequantCache(routed["gate"], routed["up"], routed["down"])
+        sc = O.DequantCache(shared["gate"], shared["up"], shared["down"]) if shared else None
+        O.layer_forward(x, res, rw, cache, spec.top_k, shared=sc, rows=rows, **args)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(done * n_rows / el, 4), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} oracle evaluation(s) of {n_rows} token(s) of one batch of the "
+                      f"same workload (numpy fp64, BLAS threads={threads}, {el:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen3_decode_t8", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--weight-sets", type=int, default=0, help="0 = workload default")
+    ap.add_argument("--batches", type=int, default=8)
+    ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+                  f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_synth as S
+    import mixture_experts_ffn_03_amd as M
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    M.load_library()
+    name = args.workload
+    spec = S.WORKLOADS[name]
+    dev = "cuda"
+    nsets = args.weight_sets or WEIGHT_SETS[name]
+    path = {"auto": M.PATH_AUTO, "decode": M.PATH_DECODE, "prefill": M.PATH_PREFILL}[args.path]
+
+    t_gen = time.perf_counter()
+    sets = [S.make_inputs(spec, device=dev, seed=spec.seed + 101 * i) for i in range(nsets)]
+    batches = [S.make_activations(spec, device=dev, seed=spec.seed + 7 + 31 * b)
+               for b in range(args.batches)]
+    torch.cuda.synchronize()
+    log(f"[bench] {name}: {nsets} weight set(s), {args.batches} input batches generated in "
+        f"{time.perf_counter() - t_gen:.1f} s")
+
+    T, H, E, K, I = spec.tokens, spec.hidden, spec.experts, spec.top_k, spec.inter
+    cfg = M.make_config(T, H, E, K, I, score_mode=spec.score, select_mode=spec.select,
+                        renormalize=spec.renormalize, has_shared=spec.shared,
+                        shared_inter=spec.shared_inter, pre_norm=spec.pre_norm,
+                        norm_eps=spec.norm_eps, vocab=spec.vocab, path=path)
+    ws = M.alloc_workspace(cfg, dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    routed = [M.expert_weights(s.routed) for s in sets]
+    shared = [M.expert_weights(s.shared) if s.shared is not None else None for s in sets]
+    ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+
+    def step(i, dbg=False):
+        s, b = sets[i % nsets], batches[i % args.batches]
+        M.layer_forward(cfg, b.x, s.router_w, routed[i % nsets], out, ws, norm_gamma=s.gamma,
+                        logit_bias=s.logit_bias, correction_bias=s.correction_bias,
+                        token_ids=b.token_ids, tid2eid=s.tid2eid, shared=shared[i % nsets],
+                        residual=b.residual, dbg_ids=ids if dbg else None)
+
+    # routing of every (weight set, batch) pair: unique experts touched per step
+    period = nsets * args.batches // __import__("math").gcd(nsets, args.batches)
+    uniq = []
+    for i in range(period):
+        step(i, dbg=True)
+        torch.cuda.synchronize()
+        uniq.append(S.count_unique_experts(ids, E))
+    if M.get_device_error(ws) != 0:
+        raise RuntimeError("device error word set during the benchmark's routing pass")
+
+    hip = HipEvents()
+    nst = M.STAGE_COUNT
+    # instrumented pass (untimed): every stage boundary, to find the dominant kernel
+    prof_steps = max(8, min(args.warmup, 64))
+    evs = [[hip.create() for _ in range(nst)] for _ in range(prof_steps)]
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    arrs = []
+    for i in range(prof_steps):
+        arr = (ctypes.c_void_p * nst)(*evs[i])
+        arrs.append(arr)
+        M.set_stage_events(arr, nst)
+        step(i)
+    torch.cuda.synchronize()
+    stage_ms = {}
+    for si in range(1, nst):
+        stage_ms[M.STAGE_NAMES[si]] = sum(hip.elapsed_ms(evs[i][si - 1], evs[i][si])
+                                         for i in range(prof_steps)) / prof_steps
+    for row in evs:
+        for e in row:
+            hip.destroy(e)
+    kernel_stage = max(("gate_up", "down"), key=lambda k: stage_ms[k])
+    ks = M.STAGE_NAMES.index(kernel_stage)
+
+    # timed steps: HIP events around the dominant kernel only (on the layer's stream)
+    kev = [(hip.create(), hip.create()) for _ in range(args.steps)]
+    karrs = []
+    for i in range(args.steps):
+        arr = (ctypes.c_void_p * nst)()
+        arr[ks - 1], arr[ks] = kev[i]
+        karrs.append(arr)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        M.set_stage_events(karrs[i], nst)
+        step(args.warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    kernel_ms = sum(hip.elapsed_ms(a, b) for a, b in kev) / args.steps
+    for a, b in kev:
+        hip.destroy(a)
+        hip.destroy(b)
+    if M.get_device_error(ws) != 0:
+        raise RuntimeError("device error word set during the timed steps")
+
+    S_rows = T * K
+    groups = min(E, S_rows)
+    pre_ok = H % 64 == 0 and I % 64 == 0 and (not spec.shared or spec.shared_inter % 64 == 0)
+    decode = (path == M.PATH_DECODE) or (path == M.PATH_AUTO and not (S_rows >= 4 * groups
+                                                                       and pre_ok))
+    u_mean = sum(uniq[(args.warmup + i) % period] for i in range(args.steps)) / args.steps
+    bpe = bytes_per_elem(spec.fmt)
+    # algorithmic work of the dominant kernel per launch: each touched expert's weights
+    # once, its input activations and its output rows; flops of the routed rows
+    if kernel_stage == "gate_up":
+        kbytes = u_mean * 2 * I * H * bpe + T * H * 2 + S_rows * I * 2
+        kflops = 2 * S_rows * H * 2 * I
+        unit_bytes = "2*I*H*b bytes per touched expert (b = 0.5625 NVFP4, 0.53125 MXFP4) + x in + h out"
+        unit_flops = "4*H*I flops per routed row"
+    else:
+        kbytes = u_mean * I * H * bpe + S_rows * I * 2 + S_rows * H * (4 if decode else 2)
+        kflops = 2 * S_rows * H * I
+        unit_bytes = "I*H*b bytes per touched expert + h in + y out"
+        unit_flops = "2*H*I flops per routed row"
+    ridge = BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if kflops / kbytes < ridge:
+        achieved = kbytes / (kernel_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        per_launch, unit_note = kbytes, unit_bytes
+    else:
+        achieved = kflops / (kernel_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4)}
+        per_launch, unit_note = kflops, unit_flops
+    kname = f"{'decode' if decode else 'prefill'}_{kernel_stage}"
+    roof["traffic"] = load_traffic(name, kname)
+    roof["kernel"] = kname
+    roof["kernel_ms"] = round(kernel_ms, 5)
+    roof["per_launch"] = per_launch
+    roof["per_unit"] = unit_note
+    roof["arith_intensity"] = round(kflops / kbytes, 1)
+
+    # whole-layer algorithmic work
+    shared_bytes = (3 * H * spec.shared_inter * bytes_per_elem(spec.shared_fmt)) if spec.shared else 0
+    layer_bytes = u_mean * 3 * H * I * bpe + shared_bytes + E * H * 2 + 3 * T * H * 2
+    layer_flops = T * K * 6 * H * I + (T * 6 * H * spec.shared_inter if spec.shared else 0) + 2 * T * H * E
+    tokens_per_s = T / (ms_per_step * 1e-3)
+
+    result = {
+        "metric": METRIC, "value": round(tokens_per_s, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "weights": "nvfp4" if spec.fmt == 0 else "mxfp4",
+        "data": "synthetic (seeded; random-init FP4 weights, N(0,1) bf16 activations)",
+        "config": {"workload": name, "description": DESCRIPTIONS[name], "tokens": T,
+                   "hidden": H, "experts": E, "top_k": K, "inter": I,
+                   "path": "decode" if decode else "prefill", "weight_sets": nsets,
+                   "input_batches": args.batches, "unique_experts_mean": round(u_mean, 2)},
+        "layer": {"GB_per_s": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                  "TFLOP_per_s": round(layer_flops / (ms_per_step * 1e-3) / 1e12, 2),
+                  "hbm_frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()}},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the CPU oracle for about {args.cpu_seconds:.0f} s")
+        result["cpu_baseline"] = cpu_baseline(spec, sets[0], name, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

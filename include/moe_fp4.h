@@ -213,8 +213,9 @@ enum {
 
 /* Profiling aid (host): the NEXT moe_layer_forward call made on this host thread
  * records events[i] (caller-created HIP events) on its stream at boundary i, for
- * i < count, then forgets the array. Elapsed times between consecutive events are the
- * stage durations on that stream. events == NULL cancels a pending request. */
+ * i < count (NULL entries are skipped), then forgets the array. Elapsed times between
+ * consecutive events are the stage durations on that stream. events == NULL cancels a
+ * pending request. */
 int moe_set_stage_events(hipEvent_t* events, int32_t count);
 
 /* Synchronise `stream`, then copy the device error word of `workspace` (MOE_DEVERR_*

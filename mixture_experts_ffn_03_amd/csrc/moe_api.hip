@@ -47,12 +47,9 @@ Layout make_layout(const moe_config& c) {
   const int T = c.tokens, E = c.num_experts, K = c.top_k, H = c.hidden;
   const int S = T * K;
   L.rows = S + (c.has_shared ? T : 0);
-  const int nblk = ceil_div(E, kRouterTile) * ceil_div(T > 0 ? T : 1, kRouterTile);
-  int ks = ceil_div(512, nblk);
-  if (ks > H / 32) ks = H / 32;
-  if (ks < 1) ks = 1;
-  L.hsplit = ceil_div(ceil_div(H, ks), 32) * 32;
-  L.ks = ceil_div(H, L.hsplit);
+  const RouterPlan rp = plan_router(T, E, H);
+  L.ks = rp.ks;
+  L.hsplit = rp.hsplit;
   int imax = c.inter;
   if (c.has_shared && c.shared_inter > imax) imax = c.shared_inter;
   L.h_stride = ceil_div(imax, 8) * 8;
@@ -171,7 +168,7 @@ struct StageMarks {
   int n = 0;
   hipStream_t s = nullptr;
   hipError_t mark(int i) const {
-    return (ev && i < n) ? hipEventRecord(ev[i], s) : hipSuccess;
+    return (ev && i < n && ev[i]) ? hipEventRecord(ev[i], s) : hipSuccess;
   }
 };
 

@@ -9,11 +9,14 @@
 // at most kDecodeTile tokens routed to one expert, so every weight byte of an active
 // expert is streamed from HBM once per tile whatever the batch. Each lane streams 16-byte
 // chunks (32 E2M1 codes) of a row with 128-bit loads; a group of LPR lanes covers one row
-// and a wave covers several rows, which keeps many independent loads in flight. The
-// block's scale bytes are staged once in LDS with 128-bit loads. Codes are decoded in
+// and a wave covers several rows, which keeps many independent loads in flight. Codes are decoded in
 // registers to exact bf16 with the gfx950 scaled convert (scale 1.0), dotted with the
 // bf16 activations by v_dot2_f32_bf16, and each 16- or 32-code block partial is
-// multiplied by its fp32 block scale. The per-row sums are reduced across the lane group
+// multiplied by its fp32 block scale. The scale bytes travel with the codes in the same
+// load round trip, and tile records carry their token ids, so a block waits on memory
+// twice: for its tile record, then for weights, scales and activations together. Rows
+// per pass shrink as tokens per tile grow, keeping register use within 256 VGPRs so that
+// 2 waves share each SIMD and hide HBM latency. The per-row sums are reduced across the lane group
 // by a transposing butterfly (no LDS), then gate/up pairs are combined into
 // SiLU(gate) * up (gate+up kernel) or written as the expert output (down kernel).
 #include "moe_device.h"
@@ -24,7 +27,8 @@ constexpr int kGateRowsPerWave = 8;   // gate rows (and as many up rows) per wav
 constexpr int kDownRowsPerWave = 16;  // down rows per wave
 constexpr int kDecWaves = 4;
 
-__device__ __forceinline__ bool resolve_tile(const TileSource& src, int idx, Tile& t) {
+__device__ __forceinline__ bool resolve_tile(const TileSource& src, const int32_t* row_token,
+                                             int idx, Tile& t) {
   if (src.tiles) {
     if (idx >= src.ntiles[0]) return false;
     t = src.tiles[idx];
@@ -36,25 +40,26 @@ __device__ __forceinline__ bool resolve_tile(const TileSource& src, int idx, Til
   t.row0 = src.implicit_row0 + r0;
   t.count = min(src.implicit_height, src.implicit_rows - r0);
   t.pad = 0;
+#pragma unroll
+  for (int q = 0; q < kTileTok; ++q) t.tok[q] = q < t.count ? row_token[t.row0 + q] : 0;
   return true;
 }
 
-// Stage `bytes` (multiple of 16, 16-byte aligned source) of scale bytes into LDS.
-__device__ __forceinline__ void stage16(uint8_t* dst, const uint8_t* src, int bytes) {
-  const uint4* s = reinterpret_cast<const uint4*>(src);
-  uint4* d = reinterpret_cast<uint4*>(dst);
-  for (int i = threadIdx.x; i < bytes / 16; i += blockDim.x) d[i] = s[i];
+// Scale bytes of one 32-code chunk: NVFP4 two E4M3 codes (16-code blocks), MXFP4 one E8M0.
+template <int FMT>
+__device__ __forceinline__ uint32_t load_chunk_scales(const uint8_t* row_scales, int c) {
+  if (FMT == 0) return *reinterpret_cast<const uint16_t*>(row_scales + 2 * c);
+  return row_scales[c];
 }
 
-// Dot of one 16-byte chunk (32 codes) with TT activation chunks; FMT 0 = NVFP4 (two
-// 16-code blocks, E4M3 scales), 1 = MXFP4 (one 32-code block, E8M0 scale).
+// Dot of one 16-byte chunk (32 codes) with TT activation chunks: codes are decoded to exact
+// bf16 (scale 1), dotted by v_dot2_f32_bf16, and each 16- or 32-code block partial is
+// multiplied by its fp32 block scale.
 template <int FMT, int TT>
-__device__ __forceinline__ void chunk_dot(const uint4& w, const uint8_t* sc,
+__device__ __forceinline__ void chunk_dot(const uint4& w, uint32_t sc,
                                           const uint32_t (&xv)[TT][16], float (&acc)[TT]) {
   const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
   if (FMT == 0) {
-    const float s0 = e4m3_to_f32(sc[0]);
-    const float s1 = e4m3_to_f32(sc[1]);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       float part[TT];
@@ -69,12 +74,11 @@ __device__ __forceinline__ void chunk_dot(const uint4& w, const uint8_t* sc,
 #pragma unroll
           for (int t = 0; t < TT; ++t) part[t] = dot2_bf16(b[j], xv[t][4 * d + j], part[t]);
       }
-      const float s = blk ? s1 : s0;
+      const float s = e4m3_to_f32((sc >> (8 * blk)) & 0xFFu);
 #pragma unroll
       for (int t = 0; t < TT; ++t) acc[t] = fmaf(part[t], s, acc[t]);
     }
   } else {
-    const float s = e8m0_to_f32(sc[0]);
     float part[TT];
 #pragma unroll
     for (int t = 0; t < TT; ++t) part[t] = 0.f;
@@ -87,6 +91,7 @@ __device__ __forceinline__ void chunk_dot(const uint4& w, const uint8_t* sc,
 #pragma unroll
         for (int t = 0; t < TT; ++t) part[t] = dot2_bf16(b[j], xv[t][4 * d + j], part[t]);
     }
+    const float s = e8m0_to_f32(sc);
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[t] = fmaf(part[t], s, acc[t]);
   }
@@ -111,181 +116,181 @@ __device__ __forceinline__ void load_act_chunk(const uint16_t* base, const int (
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
+// Rows per pass: enough for every lane group of the wave to own a row, and few enough
+// that weights, activations and sums fit 256 VGPRs (2 waves per SIMD, 8 per CU, each
+// with 16 row loads of 16 bytes per lane in flight: about 128 KB per CU).
+template <int TT, int LPR, int BASE>
+struct RowSet {
+  static constexpr int G = kWave / LPR;
+  static constexpr int R0 = TT == 4 ? BASE / 2 : BASE;
+  static constexpr int R = R0 > G ? R0 : G;
+};
+
 // ----------------------------------------------------------------------------- gate+up
 template <int FMT, int TT, int LPR>
-__device__ __forceinline__ void gate_up_body(const ExpertGemmArgs& a, const Tile& tile,
-                                             const uint8_t* s_sc, int sbytes) {
+__device__ __forceinline__ void gate_up_body(const ExpertGemmArgs& a, const Tile& tile) {
   constexpr int G = kWave / LPR;
-  constexpr int NI = kGateRowsPerWave / G;
+  constexpr int GR = RowSet<TT, LPR, kGateRowsPerWave>::R;  // gate rows per pass
+  constexpr int NI = GR / G;
   constexpr int NV = 2 * NI * TT;
+  static_assert(NV <= LPR, "one reduced value per lane expected");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int sub = lane % LPR, grp = lane / LPR;
   const int H = a.H, I = a.I;
   const int e = tile.group;
-  const int nblk = blockIdx.x * (kDecWaves * kGateRowsPerWave);
   const int nchunk = H / 32;
   const size_t row_bytes = (size_t)H / 2;
+  const int sbytes = H / (FMT == 0 ? 16 : 32);
   const uint8_t* gp = a.gate.packed + (size_t)e * I * row_bytes;
   const uint8_t* upp = a.up.packed + (size_t)e * I * row_bytes;
-  const int cb = FMT == 0 ? 2 : 1;  // scale bytes per chunk
+  const uint8_t* gs = a.gate.scales + (size_t)e * I * sbytes;
+  const uint8_t* us = a.up.scales + (size_t)e * I * sbytes;
+  const float gsg = FMT == 0 ? a.gate.global[e] : 1.0f;
+  const float gsu = FMT == 0 ? a.up.global[e] : 1.0f;
 
   int row[TT];
 #pragma unroll
-  for (int t = 0; t < TT; ++t) row[t] = a.row_token[tile.row0 + (t < tile.count ? t : 0)];
+  for (int t = 0; t < TT; ++t) row[t] = tile.tok[t < tile.count ? t : 0];
 
-  float acc[NV];
+  const int nwave0 = blockIdx.x * (kDecWaves * kGateRowsPerWave) + wave * kGateRowsPerWave;
+#pragma unroll 1
+  for (int r0 = 0; r0 < kGateRowsPerWave; r0 += GR) {
+    float acc[NV];
 #pragma unroll
-  for (int v = 0; v < NV; ++v) acc[v] = 0.f;
-
-  for (int c = sub; c < nchunk; c += LPR) {
-    uint4 wv[NI][2];
+    for (int v = 0; v < NV; ++v) acc[v] = 0.f;
+#pragma unroll 1
+    for (int c = sub; c < nchunk; c += LPR) {
+      uint4 wv[NI][2];
+      uint32_t sv[NI][2];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int nl = wave * kGateRowsPerWave + grp + G * i;  // row inside the block
-      const int n = nblk + nl;
-      if (n < I) {
-        wv[i][0] = *reinterpret_cast<const uint4*>(gp + (size_t)n * row_bytes + c * 16);
-        wv[i][1] = *reinterpret_cast<const uint4*>(upp + (size_t)n * row_bytes + c * 16);
-      } else {
-        wv[i][0] = make_uint4(0, 0, 0, 0);
-        wv[i][1] = make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < NI; ++i) {
+        const int n = nwave0 + r0 + grp + G * i;
+        if (n < I) {
+          wv[i][0] = *reinterpret_cast<const uint4*>(gp + (size_t)n * row_bytes + c * 16);
+          wv[i][1] = *reinterpret_cast<const uint4*>(upp + (size_t)n * row_bytes + c * 16);
+          sv[i][0] = load_chunk_scales<FMT>(gs + (size_t)n * sbytes, c);
+          sv[i][1] = load_chunk_scales<FMT>(us + (size_t)n * sbytes, c);
+        } else {
+          wv[i][0] = wv[i][1] = make_uint4(0, 0, 0, 0);
+          sv[i][0] = sv[i][1] = 0;
+        }
+      }
+      uint32_t xv[TT][16];
+      load_act_chunk<TT>(a.x, row, H, c, xv);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+#pragma unroll
+        for (int gu = 0; gu < 2; ++gu) {
+          float r[TT];
+#pragma unroll
+          for (int t = 0; t < TT; ++t) r[t] = 0.f;
+          chunk_dot<FMT, TT>(wv[i][gu], sv[i][gu], xv, r);
+#pragma unroll
+          for (int t = 0; t < TT; ++t) acc[((i * TT + t) << 1) | gu] += r[t];
+        }
       }
     }
-    uint32_t xv[TT][16];
-    load_act_chunk<TT>(a.x, row, H, c, xv);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int nl = wave * kGateRowsPerWave + grp + G * i;
-#pragma unroll
-      for (int gu = 0; gu < 2; ++gu) {
-        float r[TT];
-#pragma unroll
-        for (int t = 0; t < TT; ++t) r[t] = 0.f;
-        chunk_dot<FMT, TT>(wv[i][gu], s_sc + gu * (kDecWaves * kGateRowsPerWave) * sbytes +
-                                          nl * sbytes + c * cb, xv, r);
-#pragma unroll
-        for (int t = 0; t < TT; ++t) acc[((i * TT + t) << 1) | gu] += r[t];
+    group_reduce_transpose<NV, LPR>(acc, lane);
+    // each lane holds one complete sum; gate/up partners differ in the lane bit of the
+    // last halving step, duplicates in the bits below it
+    constexpr int kPair = LPR / NV;
+    const float other = shfl_xor_f(acc[0], kPair);
+    const int idx = reduced_index<NV, LPR>(lane, 0);
+    if ((idx & 1) == 0 && (sub & (kPair - 1)) == 0) {
+      const int q = idx >> 1, i = q / TT, t = q % TT;
+      const int n = nwave0 + r0 + grp + G * i;
+      if (t < tile.count && n < I) {
+        const float g = acc[0] * gsg, u = other * gsu;
+        a.h[(size_t)(tile.row0 + t) * a.h_stride + n] = f32_to_bf16(silu(g) * u);
       }
-    }
-  }
-
-  group_reduce_transpose<NV, LPR>(acc, lane);
-  // NV <= LPR here, so each lane holds one complete sum; gate/up partners differ in the
-  // lane bit of the last halving step, duplicates in the bits below it
-  static_assert(NV <= LPR, "one value per lane expected");
-  constexpr int kPair = LPR / NV;
-  const float other = shfl_xor_f(acc[0], kPair);
-  const int idx = reduced_index<NV, LPR>(lane, 0);
-  if ((idx & 1) == 0 && (sub & (kPair - 1)) == 0) {
-    const int q = idx >> 1, i = q / TT, t = q % TT;
-    const int n = nblk + wave * kGateRowsPerWave + grp + G * i;
-    if (t < tile.count && n < I) {
-      float g = acc[0], u = other;
-      if (FMT == 0) {
-        g *= a.gate.global[e];
-        u *= a.up.global[e];
-      }
-      a.h[(size_t)(tile.row0 + t) * a.h_stride + n] = f32_to_bf16(silu(g) * u);
     }
   }
 }
 
 template <int FMT, int LPR>
-__global__ __launch_bounds__(256) void k_dec_gate_up(ExpertGemmArgs a) {
-  extern __shared__ uint8_t s_sc[];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_dec_gate_up(ExpertGemmArgs a) {
   Tile tile;
-  if (!resolve_tile(a.src, blockIdx.y, tile)) return;
-  const int I = a.I, H = a.H;
-  const int sbytes = H / (FMT == 0 ? 16 : 32);
-  const int rows = kDecWaves * kGateRowsPerWave;
-  const int nblk = blockIdx.x * rows;
-  const int nrows = min(rows, I - nblk);
-  const size_t off = ((size_t)tile.group * I + nblk) * sbytes;
-  stage16(s_sc, a.gate.scales + off, nrows * sbytes);
-  stage16(s_sc + rows * sbytes, a.up.scales + off, nrows * sbytes);
-  __syncthreads();
-  if (tile.count == 1) gate_up_body<FMT, 1, LPR>(a, tile, s_sc, sbytes);
-  else if (tile.count == 2) gate_up_body<FMT, 2, LPR>(a, tile, s_sc, sbytes);
-  else gate_up_body<FMT, 4, LPR>(a, tile, s_sc, sbytes);
+  if (!resolve_tile(a.src, a.row_token, blockIdx.y, tile)) return;
+  if (tile.count == 1) gate_up_body<FMT, 1, LPR>(a, tile);
+  else if (tile.count == 2) gate_up_body<FMT, 2, LPR>(a, tile);
+  else gate_up_body<FMT, 4, LPR>(a, tile);
 }
 
 // ----------------------------------------------------------------------------- down
 template <int FMT, int TT, int LPR>
-__device__ __forceinline__ void down_body(const ExpertGemmArgs& a, const Tile& tile,
-                                          const uint8_t* s_sc, int sbytes) {
+__device__ __forceinline__ void down_body(const ExpertGemmArgs& a, const Tile& tile) {
   constexpr int G = kWave / LPR;
-  constexpr int NI = kDownRowsPerWave / G;
+  constexpr int DR = RowSet<TT, LPR, kDownRowsPerWave>::R;  // rows per pass
+  constexpr int NI = DR / G;
   constexpr int NV = NI * TT;
+  static_assert(NV <= LPR, "one reduced value per lane expected");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int sub = lane % LPR, grp = lane / LPR;
   const int H = a.H, I = a.I;
   const int e = tile.group;
-  const int nblk = blockIdx.x * (kDecWaves * kDownRowsPerWave);
   const int nchunk = I / 32;
   const size_t row_bytes = (size_t)I / 2;
+  const int sbytes = I / (FMT == 0 ? 16 : 32);
   const uint8_t* dp = a.down.packed + (size_t)e * H * row_bytes;
-  const int cb = FMT == 0 ? 2 : 1;
+  const uint8_t* ds = a.down.scales + (size_t)e * H * sbytes;
+  const float gsd = FMT == 0 ? a.down.global[e] : 1.0f;
 
   int row[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t) row[t] = tile.row0 + (t < tile.count ? t : 0);
 
-  float acc[NV];
+  const int nwave0 = blockIdx.x * (kDecWaves * kDownRowsPerWave) + wave * kDownRowsPerWave;
+#pragma unroll 1
+  for (int r0 = 0; r0 < kDownRowsPerWave; r0 += DR) {
+    float acc[NV];
 #pragma unroll
-  for (int v = 0; v < NV; ++v) acc[v] = 0.f;
-
-  for (int c = sub; c < nchunk; c += LPR) {
-    uint4 wv[NI];
+    for (int v = 0; v < NV; ++v) acc[v] = 0.f;
+#pragma unroll 1
+    for (int c = sub; c < nchunk; c += LPR) {
+      uint4 wv[NI];
+      uint32_t sv[NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int n = nblk + wave * kDownRowsPerWave + grp + G * i;
-      wv[i] = n < H ? *reinterpret_cast<const uint4*>(dp + (size_t)n * row_bytes + c * 16)
-                    : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < NI; ++i) {
+        const int n = nwave0 + r0 + grp + G * i;
+        if (n < H) {
+          wv[i] = *reinterpret_cast<const uint4*>(dp + (size_t)n * row_bytes + c * 16);
+          sv[i] = load_chunk_scales<FMT>(ds + (size_t)n * sbytes, c);
+        } else {
+          wv[i] = make_uint4(0, 0, 0, 0);
+          sv[i] = 0;
+        }
+      }
+      uint32_t xv[TT][16];
+      load_act_chunk<TT>(a.h, row, a.h_stride, c, xv);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        float r[TT];
+#pragma unroll
+        for (int t = 0; t < TT; ++t) r[t] = 0.f;
+        chunk_dot<FMT, TT>(wv[i], sv[i], xv, r);
+#pragma unroll
+        for (int t = 0; t < TT; ++t) acc[i * TT + t] += r[t];
+      }
     }
-    uint32_t xv[TT][16];
-    load_act_chunk<TT>(a.h, row, a.h_stride, c, xv);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int nl = wave * kDownRowsPerWave + grp + G * i;
-      float r[TT];
-#pragma unroll
-      for (int t = 0; t < TT; ++t) r[t] = 0.f;
-      chunk_dot<FMT, TT>(wv[i], s_sc + nl * sbytes + c * cb, xv, r);
-#pragma unroll
-      for (int t = 0; t < TT; ++t) acc[i * TT + t] += r[t];
-    }
-  }
-
-  group_reduce_transpose<NV, LPR>(acc, lane);
-  static_assert(NV <= LPR, "one value per lane expected");
-  constexpr int kDup = LPR / NV;
-  const int idx = reduced_index<NV, LPR>(lane, 0);
-  if ((sub & (kDup - 1)) == 0) {
-    const int i = idx / TT, t = idx % TT;
-    const int n = nblk + wave * kDownRowsPerWave + grp + G * i;
-    if (t < tile.count && n < H) {
-      float v = acc[0];
-      if (FMT == 0) v *= a.down.global[e];
-      reinterpret_cast<float*>(a.y)[(size_t)(tile.row0 + t) * H + n] = v;
+    group_reduce_transpose<NV, LPR>(acc, lane);
+    constexpr int kDup = LPR / NV;
+    const int idx = reduced_index<NV, LPR>(lane, 0);
+    if ((sub & (kDup - 1)) == 0) {
+      const int i = idx / TT, t = idx % TT;
+      const int n = nwave0 + r0 + grp + G * i;
+      if (t < tile.count && n < H)
+        reinterpret_cast<float*>(a.y)[(size_t)(tile.row0 + t) * H + n] = acc[0] * gsd;
     }
   }
 }
 
 template <int FMT, int LPR>
-__global__ __launch_bounds__(256) void k_dec_down(ExpertGemmArgs a) {
-  extern __shared__ uint8_t s_sc[];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_dec_down(ExpertGemmArgs a) {
   Tile tile;
-  if (!resolve_tile(a.src, blockIdx.y, tile)) return;
-  const int I = a.I, H = a.H;
-  const int sbytes = I / (FMT == 0 ? 16 : 32);
-  const int rows = kDecWaves * kDownRowsPerWave;
-  const int nblk = blockIdx.x * rows;
-  const int nrows = min(rows, H - nblk);
-  stage16(s_sc, a.down.scales + ((size_t)tile.group * H + nblk) * sbytes, nrows * sbytes);
-  __syncthreads();
-  if (tile.count == 1) down_body<FMT, 1, LPR>(a, tile, s_sc, sbytes);
-  else if (tile.count == 2) down_body<FMT, 2, LPR>(a, tile, s_sc, sbytes);
-  else down_body<FMT, 4, LPR>(a, tile, s_sc, sbytes);
+  if (!resolve_tile(a.src, a.row_token, blockIdx.y, tile)) return;
+  if (tile.count == 1) down_body<FMT, 1, LPR>(a, tile);
+  else if (tile.count == 2) down_body<FMT, 2, LPR>(a, tile);
+  else down_body<FMT, 4, LPR>(a, tile);
 }
 
 // Lanes per row for a row of `nchunk` 16-byte chunks: the widest group that divides the
@@ -298,40 +303,31 @@ static int pick_lpr(int nchunk) {
   return 8;
 }
 
-template <template <int, int> class K>
-struct Noop {};
-
-#define MOE_DISPATCH_LPR(KERNEL, FMT, LPR, GRID, SMEM, S, A)                               \
-  switch (LPR) {                                                                          \
-    case 64: hipLaunchKernelGGL((KERNEL<FMT, 64>), GRID, dim3(256), SMEM, S, A); break;   \
-    case 32: hipLaunchKernelGGL((KERNEL<FMT, 32>), GRID, dim3(256), SMEM, S, A); break;   \
-    case 16: hipLaunchKernelGGL((KERNEL<FMT, 16>), GRID, dim3(256), SMEM, S, A); break;   \
-    default: hipLaunchKernelGGL((KERNEL<FMT, 8>), GRID, dim3(256), SMEM, S, A); break;    \
+#define MOE_DISPATCH_LPR(KERNEL, FMT, LPR, GRID, S, A)                                  \
+  switch (LPR) {                                                                       \
+    case 64: hipLaunchKernelGGL((KERNEL<FMT, 64>), GRID, dim3(256), 0, S, A); break;   \
+    case 32: hipLaunchKernelGGL((KERNEL<FMT, 32>), GRID, dim3(256), 0, S, A); break;   \
+    case 16: hipLaunchKernelGGL((KERNEL<FMT, 16>), GRID, dim3(256), 0, S, A); break;   \
+    default: hipLaunchKernelGGL((KERNEL<FMT, 8>), GRID, dim3(256), 0, S, A); break;    \
   }
 
 hipError_t launch_decode_gate_up(const ExpertGemmArgs& a, hipStream_t s) {
   if (a.tile_bound <= 0) return hipSuccess;
-  const int fmt = a.gate.fmt;
   const int rows = kDecWaves * kGateRowsPerWave;
   const dim3 grid((a.I + rows - 1) / rows, a.tile_bound);
-  const int sbytes = a.H / (fmt == 0 ? 16 : 32);
-  const size_t smem = 2 * (size_t)rows * sbytes;
   const int lpr = pick_lpr(a.H / 32);
-  if (fmt == 0) { MOE_DISPATCH_LPR(k_dec_gate_up, 0, lpr, grid, smem, s, a); }
-  else { MOE_DISPATCH_LPR(k_dec_gate_up, 1, lpr, grid, smem, s, a); }
+  if (a.gate.fmt == 0) { MOE_DISPATCH_LPR(k_dec_gate_up, 0, lpr, grid, s, a); }
+  else { MOE_DISPATCH_LPR(k_dec_gate_up, 1, lpr, grid, s, a); }
   return hipGetLastError();
 }
 
 hipError_t launch_decode_down(const ExpertGemmArgs& a, hipStream_t s) {
   if (a.tile_bound <= 0) return hipSuccess;
-  const int fmt = a.down.fmt;
   const int rows = kDecWaves * kDownRowsPerWave;
   const dim3 grid((a.H + rows - 1) / rows, a.tile_bound);
-  const int sbytes = a.I / (fmt == 0 ? 16 : 32);
-  const size_t smem = (size_t)rows * sbytes;
   const int lpr = pick_lpr(a.I / 32);
-  if (fmt == 0) { MOE_DISPATCH_LPR(k_dec_down, 0, lpr, grid, smem, s, a); }
-  else { MOE_DISPATCH_LPR(k_dec_down, 1, lpr, grid, smem, s, a); }
+  if (a.down.fmt == 0) { MOE_DISPATCH_LPR(k_dec_down, 0, lpr, grid, s, a); }
+  else { MOE_DISPATCH_LPR(k_dec_down, 1, lpr, grid, s, a); }
   return hipGetLastError();
 }
 

@@ -141,28 +141,33 @@ __device__ __forceinline__ float wave_max(float v) {
 // Sum NV per-lane values over each aligned group of L lanes (L a power of two <= 64),
 // halving the value count at each of the first log2(NV) butterfly distances so that
 // no lane reduces every value. On return a lane holds NF = max(1, NV / L) complete
-// sums in v[0..NF); the value index of v[i] is reduced_index(lane, i).
-template <int NV, int L>
-__device__ __forceinline__ void group_reduce_transpose(float (&v)[NV], int lane) {
-  int n = NV;
+// sums in v[0..NF); the value index of v[i] is reduced_index(lane, i). The steps are
+// unrolled at compile time (a runtime index would push the array into scratch memory).
+template <int NV, int D, int N>
+struct GroupReduceStep {
+  static __device__ __forceinline__ void run(float (&v)[NV], int lane) {
+    if constexpr (D >= 1) {
+      if constexpr (N > 1) {
+        constexpr int H = N / 2;
+        const bool upper = (lane & D) != 0;
 #pragma unroll
-  for (int d = L / 2; d >= 1; d >>= 1) {
-    if (n > 1) {
-      const bool upper = (lane & d) != 0;
-      const int h = n / 2;
-#pragma unroll
-      for (int i = 0; i < NV / 2; ++i) {
-        if (i < h) {
-          const float send = upper ? v[i] : v[i + h];
-          const float keep = upper ? v[i + h] : v[i];
-          v[i] = keep + shfl_xor_f(send, d);
+        for (int i = 0; i < H; ++i) {
+          const float send = upper ? v[i] : v[i + H];
+          const float keep = upper ? v[i + H] : v[i];
+          v[i] = keep + shfl_xor_f(send, D);
         }
+        GroupReduceStep<NV, D / 2, H>::run(v, lane);
+      } else {
+        v[0] += shfl_xor_f(v[0], D);
+        GroupReduceStep<NV, D / 2, 1>::run(v, lane);
       }
-      n = h;
-    } else {
-      v[0] += shfl_xor_f(v[0], d);
     }
   }
+};
+
+template <int NV, int L>
+__device__ __forceinline__ void group_reduce_transpose(float (&v)[NV], int lane) {
+  GroupReduceStep<NV, L / 2, NV>::run(v, lane);
 }
 
 // Value index held in v[i] after group_reduce_transpose<NV, L>.

@@ -126,6 +126,7 @@ __global__ __launch_bounds__(kDispatchThreads) void k_dispatch(DispatchArgs a) {
   const int nt = (tid < E) ? (cnt + h - 1) / h : 0;
   int ntot = 0;
   const int toff = block_exclusive_scan(nt, s_tmp, &ntot);
+  __syncthreads();  // row_token of every routed row is written (read back below)
   if (tid < E) {
     for (int i = 0; i < nt; ++i) {
       Tile tl;
@@ -133,6 +134,9 @@ __global__ __launch_bounds__(kDispatchThreads) void k_dispatch(DispatchArgs a) {
       tl.row0 = s_off[tid] + i * h;
       tl.count = min(h, cnt - i * h);
       tl.pad = 0;
+#pragma unroll
+      for (int q = 0; q < kTileTok; ++q)
+        tl.tok[q] = (h <= kTileTok && q < tl.count) ? a.row_token[tl.row0 + q] : 0;
       a.tiles[toff + i] = tl;
     }
   }

@@ -19,12 +19,15 @@ struct WeightDesc {
   int32_t k;
 };
 
-// A run of rows of one expert group in the expert-sorted row space.
+// A run of rows of one expert group in the expert-sorted row space. Tiles of at most
+// kTileTok rows also carry the tokens of their rows (saves a dependent load in decode).
+constexpr int kTileTok = 4;
 struct Tile {
   int32_t group;
   int32_t row0;
   int32_t count;
   int32_t pad;
+  int32_t tok[kTileTok];
 };
 
 // Where the rows a kernel processes come from: either the device tile list written by
@@ -38,13 +41,21 @@ struct TileSource {
   int32_t implicit_height; // implicit list: rows per tile
 };
 
-constexpr int kRouterTile = 32;
 constexpr int kMaxExperts = 1024;  // MOE_MAX_EXPERTS
 constexpr int kMaxTopK = 32;       // MOE_MAX_TOP_K
 constexpr int kDecodeTile = 4;     // rows (tokens) per decode tile
 
 hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, uint16_t* out, int T, int H,
                           float eps, hipStream_t s);
+
+// Router GEMM split: few tokens use one block per expert row (ks = 1), many tokens a tiled
+// kernel with H split in ks slices of hsplit columns.
+constexpr int kRouterRowsMaxT = 64;
+constexpr int kRouterMaxSplit = 8;
+struct RouterPlan {
+  int ks, hsplit;
+};
+RouterPlan plan_router(int T, int E, int H);
 
 hipError_t launch_router_partial(const uint16_t* x, const uint16_t* w, double* partial, int T,
                                  int E, int H, int ks, int hsplit, hipStream_t s);

@@ -48,56 +48,163 @@ hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, uint16_t* ou
 }
 
 // ---------------------------------------------------------------------------
-// Router GEMM, fp64 partial sums. Block tile: 32 experts x 32 tokens over one slice of
-// H (grid.z splits H so that small-T decode still fills the chip). Each thread owns a
-// 2x2 block of outputs; operand tiles are staged in LDS as fp64.
-// partial[z][t][e] = sum_{h in slice z} x[t,h] * W_r[e,h].
+// Router GEMM, fp64 sums: partial[z][t][e] = sum_{h in slice z} x[t,h] * W_r[e,h].
+//
+// Few tokens (decode): one block per expert row. The block streams the row once with
+// 16-byte loads, and every thread dots its chunks with each token's activations; the
+// per-token sums are reduced across the block in a fixed order (one slice, z = 0).
+//
+// Many tokens (prefill): 64 tokens x 64 experts per block with a 4x4 fp64 register
+// block per thread over LDS tiles, H split in z so that the grid fills the chip.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_router_partial(const uint16_t* __restrict__ x,
-                                                        const uint16_t* __restrict__ w,
-                                                        double* __restrict__ partial, int T, int E,
-                                                        int H, int hsplit) {
-  __shared__ double xs[kRouterTile][kRouterTile + 1];
-  __shared__ double ws[kRouterTile][kRouterTile + 1];
-  const int tid = threadIdx.x;
-  const int e0 = blockIdx.x * kRouterTile, t0 = blockIdx.y * kRouterTile;
-  const int kb = blockIdx.z * hsplit;
-  const int ke = min(H, kb + hsplit);
-  const int tx = tid & 15, ty = tid >> 4;
-  double acc00 = 0.0, acc01 = 0.0, acc10 = 0.0, acc11 = 0.0;
-  for (int k0 = kb; k0 < ke; k0 += kRouterTile) {
-    for (int i = tid; i < kRouterTile * kRouterTile; i += 256) {
-      const int r = i >> 5, c = i & 31;
-      const int k = k0 + c;
-      const int t = t0 + r, e = e0 + r;
-      xs[r][c] = (t < T && k < ke) ? (double)bf16_to_f32(x[(size_t)t * H + k]) : 0.0;
-      ws[r][c] = (e < E && k < ke) ? (double)bf16_to_f32(w[(size_t)e * H + k]) : 0.0;
+constexpr int kRowTok = 8;  // tokens per pass of the row kernel
+
+__device__ __forceinline__ void bf16x8_to_f64(const uint4& v, double (&o)[8]) {
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = (double)bf16_to_f32(d[i] & 0xFFFFu);
+    o[2 * i + 1] = (double)bf16_to_f32(d[i] >> 16);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_router_rows(const uint16_t* __restrict__ x,
+                                                     const uint16_t* __restrict__ w,
+                                                     double* __restrict__ partial, int T, int E,
+                                                     int H) {
+  __shared__ double s_red[4][kRowTok];
+  const int e = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nchunk = H / 8;
+  const uint16_t* wrow = w + (size_t)e * H;
+  for (int t0 = 0; t0 < T; t0 += kRowTok) {
+    double acc[kRowTok];
+#pragma unroll
+    for (int t = 0; t < kRowTok; ++t) acc[t] = 0.0;
+    for (int c = threadIdx.x; c < nchunk; c += 256) {
+      double wv[8];
+      bf16x8_to_f64(*reinterpret_cast<const uint4*>(wrow + c * 8), wv);
+#pragma unroll
+      for (int t = 0; t < kRowTok; ++t) {
+        if (t0 + t < T) {
+          double xv[8];
+          bf16x8_to_f64(*reinterpret_cast<const uint4*>(x + (size_t)(t0 + t) * H + c * 8), xv);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[t] = fma(xv[i], wv[i], acc[t]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kRowTok; ++t) {
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) acc[t] += __shfl_xor(acc[t], m, kWave);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int t = 0; t < kRowTok; ++t) s_red[wave][t] = acc[t];
     }
     __syncthreads();
-#pragma unroll 8
-    for (int c = 0; c < kRouterTile; ++c) {
-      const double a0 = xs[ty][c], a1 = xs[ty + 16][c];
-      const double b0 = ws[tx][c], b1 = ws[tx + 16][c];
-      acc00 = fma(a0, b0, acc00);
-      acc01 = fma(a0, b1, acc01);
-      acc10 = fma(a1, b0, acc10);
-      acc11 = fma(a1, b1, acc11);
+    if (threadIdx.x < kRowTok && t0 + threadIdx.x < T) {
+      const int t = threadIdx.x;
+      partial[(size_t)(t0 + t) * E + e] = (s_red[0][t] + s_red[1][t]) + (s_red[2][t] + s_red[3][t]);
+    }
+    __syncthreads();
+  }
+}
+
+constexpr int kRt = 64;   // tokens per block tile
+constexpr int kRe = 64;   // experts per block tile
+constexpr int kRk = 16;   // K per LDS stage
+
+__global__ __launch_bounds__(256) void k_router_tiled(const uint16_t* __restrict__ x,
+                                                      const uint16_t* __restrict__ w,
+                                                      double* __restrict__ partial, int T, int E,
+                                                      int H, int hsplit) {
+  __shared__ __align__(16) double xs[kRk][kRt + 2];
+  __shared__ __align__(16) double ws[kRk][kRe + 2];
+  const int tid = threadIdx.x;
+  const int e0 = blockIdx.x * kRe, t0 = blockIdx.y * kRt;
+  const int kb = blockIdx.z * hsplit;
+  const int ke = min(H, kb + hsplit);
+  const int tx = tid & 15, ty = tid >> 4;  // experts 4*tx.., tokens 4*ty..
+  double acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+  // loader: threads 0..127 load x rows, 128..255 W rows; 16 k = two 16-byte pieces per row
+  const int lrow = (tid & 127) >> 1, lpiece = tid & 1;
+  const bool lx = tid < 128;
+  for (int k0 = kb; k0 < ke; k0 += kRk) {
+    double v[8];
+    const int k = k0 + lpiece * 8;
+    const int r = (lx ? t0 : e0) + lrow;
+    const int lim = lx ? T : E;
+    if (r < lim && k < ke) {
+      const uint16_t* src = (lx ? x : w) + (size_t)r * H + k;
+      bf16x8_to_f64(*reinterpret_cast<const uint4*>(src), v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.0;
+    }
+    double(*dst)[kRt + 2] = lx ? xs : ws;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[lpiece * 8 + i][lrow] = v[i];
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kRk; ++kk) {
+      double a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = xs[kk][ty * 4 + i];
+        b[i] = ws[kk][tx * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
     }
     __syncthreads();
   }
   double* p = partial + (size_t)blockIdx.z * T * E;
-  const int ta = t0 + ty, tb = t0 + ty + 16, ea = e0 + tx, eb = e0 + tx + 16;
-  if (ta < T && ea < E) p[(size_t)ta * E + ea] = acc00;
-  if (ta < T && eb < E) p[(size_t)ta * E + eb] = acc01;
-  if (tb < T && ea < E) p[(size_t)tb * E + ea] = acc10;
-  if (tb < T && eb < E) p[(size_t)tb * E + eb] = acc11;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + ty * 4 + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + tx * 4 + j;
+      if (e < E) p[(size_t)t * E + e] = acc[i][j];
+    }
+  }
+}
+
+RouterPlan plan_router(int T, int E, int H) {
+  RouterPlan r;
+  if (T <= kRouterRowsMaxT) {
+    r.ks = 1;
+    r.hsplit = H;
+    return r;
+  }
+  const int blocks = ((E + kRe - 1) / kRe) * ((T + kRt - 1) / kRt);
+  int ks = (256 + blocks - 1) / blocks;
+  if (ks > kRouterMaxSplit) ks = kRouterMaxSplit;
+  if (ks > H / 64) ks = H / 64;
+  if (ks < 1) ks = 1;
+  r.hsplit = ((H + ks - 1) / ks + kRk - 1) / kRk * kRk;
+  r.ks = (H + r.hsplit - 1) / r.hsplit;
+  return r;
 }
 
 hipError_t launch_router_partial(const uint16_t* x, const uint16_t* w, double* partial, int T,
                                  int E, int H, int ks, int hsplit, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  dim3 grid((E + kRouterTile - 1) / kRouterTile, (T + kRouterTile - 1) / kRouterTile, ks);
-  hipLaunchKernelGGL(k_router_partial, grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
+  if (T <= kRouterRowsMaxT) {
+    hipLaunchKernelGGL(k_router_rows, dim3(E), dim3(256), 0, s, x, w, partial, T, E, H);
+  } else {
+    dim3 grid((E + kRe - 1) / kRe, (T + kRt - 1) / kRt, ks);
+    hipLaunchKernelGGL(k_router_tiled, grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
+  }
   return hipGetLastError();
 }
 
@@ -147,8 +254,15 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
       if (a.logits_in) {
         l = a.logits_in[(size_t)t * E + e];
       } else {
+        // the split-K partials: independent loads first, then a fixed-order sum
+        double pz[kRouterMaxSplit];
+#pragma unroll
+        for (int z = 0; z < kRouterMaxSplit; ++z)
+          pz[z] = z < a.ks ? a.partial[((size_t)z * a.T + t) * E + e] : 0.0;
         double acc = 0.0;
-        for (int z = 0; z < a.ks; ++z) acc += a.partial[((size_t)z * a.T + t) * E + e];
+#pragma unroll
+        for (int z = 0; z < kRouterMaxSplit; ++z)
+          if (z < a.ks) acc += pz[z];
         if (a.logit_bias) acc += (double)a.logit_bias[e];
         l = (float)acc;
       }

@@ -303,6 +303,28 @@ def make_inputs(spec: LayerSpec, device="cpu", seed: Optional[int] = None,
                        routed=routed, shared=shared)
 
 
+@dataclasses.dataclass
+class Activations:
+    x: torch.Tensor                  # bf16 [T, H]
+    residual: torch.Tensor           # bf16 [T, H]
+    token_ids: Optional[torch.Tensor]  # int32 [T] (hash routing)
+
+
+def make_activations(spec: LayerSpec, device="cpu", seed: int = 0,
+                     tokens: Optional[int] = None) -> Activations:
+    """Another batch of layer activations (x, residual, token ids) with the workload's
+    distributions, drawn from its own seed; used to vary the input between benchmark steps."""
+    T = spec.tokens if tokens is None else tokens
+    g = _gen(device, seed)
+    x = torch.randn((T, spec.hidden), generator=g, device=device).to(torch.bfloat16)
+    residual = torch.randn((T, spec.hidden), generator=g, device=device).to(torch.bfloat16)
+    token_ids = None
+    if spec.select == HASH:
+        token_ids = torch.randint(0, spec.vocab, (T,), generator=g, device=device,
+                                  dtype=torch.int64).to(torch.int32)
+    return Activations(x, residual, token_ids)
+
+
 def random_codes_weight(g, device, experts: int, n: int, k: int, fmt: int,
                         scale_codes: Optional[torch.Tensor] = None) -> Fp4Weight:
     """A weight tensor with uniformly random codes and scales (edge-case tests).

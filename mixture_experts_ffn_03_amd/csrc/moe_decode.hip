@@ -74,7 +74,7 @@ __device__ __forceinline__ void chunk_dot(const uint4& w, uint32_t sc,
 #pragma unroll
           for (int t = 0; t < TT; ++t) part[t] = dot2_bf16(b[j], xv[t][4 * d + j], part[t]);
       }
-      const float s = e4m3_to_f32((sc >> (8 * blk)) & 0xFFu);
+      const float s = blk ? e4m3_byte_to_f32<1>(sc) : e4m3_byte_to_f32<0>(sc);
 #pragma unroll
       for (int t = 0; t < TT; ++t) acc[t] = fmaf(part[t], s, acc[t]);
     }

@@ -38,16 +38,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // S.1111.111), which NVFP4 uses for its per-16 block scales; E8M0 is the MX
 // per-32 shared exponent 2^(s-127) with 0xFF = NaN.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  const uint32_t s = (b & 0x80u) << 24;
-  const uint32_t em = b & 0x7Fu;
-  if (em == 0x7Fu) return __uint_as_float(0x7FC00000u);
-  if (em < 8u) {  // subnormal: m * 2^-9
-    return __uint_as_float(s | __float_as_uint((float)em * 0.001953125f));
-  }
-  // normal: exponent e-7 -> e-7+127 = e+120; the 3 mantissa bits move to the top of 23
-  return __uint_as_float(s | ((em + (120u << 3)) << 20));
+// gfx950's FP8 convert reads the OCP E4M3FN encoding (NaN only at S.1111.111, no inf);
+// the exhaustive dequant parity test checks every code against the format definition.
+template <int SEL>
+__device__ __forceinline__ float e4m3_byte_to_f32(uint32_t word) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)word, SEL);
 }
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) { return e4m3_byte_to_f32<0>(b); }
 
 __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
   if (b == 0xFFu) return __uint_as_float(0x7FC00000u);

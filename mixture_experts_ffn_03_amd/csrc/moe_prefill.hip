@@ -9,19 +9,21 @@
 // rows fused into the GEMM's A load (doc of moe_permute_tokens_k).
 //
 // Design (gfx950, v_mfma_f32_32x32x16_bf16):
-// * A block computes an MT x 256 output tile of one expert: MT gathered token rows and
-//   256 weight rows (gate+up kernel: 128 gate rows and the same 128 up rows, so SwiGLU
-//   runs in the epilogue on values that sit in the same lane and register).
-// * The 4 waves split N (64 weight rows each) and share the A tile, which is gathered
-//   from the activations by row_token and staged in LDS (rows padded by 16 bytes so the
-//   32 rows an MFMA operand reads fall in distinct banks).
+// * A block of 8 waves computes an MT-row tile of one expert: MT gathered token rows times
+//   COLS weight rows (gate+up kernel: COLS gate rows and the same COLS up rows, so SwiGLU
+//   runs in the epilogue on values that sit in the same lane and register). Waves form a
+//   WM x WN grid; each owns 32*RB rows and two 32-column blocks (64 fp32 accumulators
+//   per lane for RB = 2), which keeps 2 waves per SIMD resident.
+// * The waves share the A tile, gathered from the activations by row_token and staged in
+//   LDS (rows padded by 16 bytes so the 32 rows an MFMA operand reads fall in distinct
+//   banks), double-buffered so that each 128-wide K chunk needs a single barrier.
 // * Each lane reads its B fragment straight from HBM: 32 contiguous bytes (64 codes) of
 //   one weight row per 128-wide K chunk, so the weight stream needs no LDS. The MFMA K
 //   order is permuted inside a chunk (lane half h covers codes 64h..64h+63) and the A
 //   fragments are read from LDS with the same permutation.
 // * E2M1 codes become exact bf16 operands in registers (MXFP4: scaled convert by the
 //   E8M0 power of two; NVFP4: convert, times the E4M3 scale in fp32, pack).
-// * Global loads for chunk c+1 are issued before the MFMAs of chunk c.
+// * Global loads (A and B) for chunk c+1 are issued before the MFMAs of chunk c.
 // * Block ids are remapped so that each XCD (ids dispatched round-robin over the 8
 //   XCDs) walks a contiguous run of (row tile, column tile) work, which keeps an A
 //   tile and an expert's weight rows in that XCD's L2 while they are reused.
@@ -29,7 +31,6 @@
 
 namespace moe {
 
-constexpr int kPreCols = 256;      // weight rows per block tile
 constexpr int kKc = 128;           // K per chunk
 constexpr int kLdsRow = kKc * 2 + 16;  // bytes per LDS row of the A tile (padded)
 constexpr int kXcds = 8;
@@ -76,15 +77,12 @@ struct BFrag {
   uint32_t sc;
 };
 
+// Loads are unconditional: callers clamp rows and chunks to valid addresses (results for
+// clamped rows are discarded), so the compiler can count outstanding loads and wait only
+// for the ones a step consumes.
 template <int FMT, int KCH>
 __device__ __forceinline__ void load_b(const uint8_t* packed_row, const uint8_t* scale_row,
-                                       int k0, int half, bool valid, BFrag<FMT, KCH>& f) {
-  if (!valid) {
-#pragma unroll
-    for (int i = 0; i < KCH / 16; ++i) f.q[i] = 0;
-    f.sc = 0;
-    return;
-  }
+                                       int k0, int half, BFrag<FMT, KCH>& f) {
   const uint8_t* p = packed_row + k0 / 2 + half * (KCH / 4);
 #pragma unroll
   for (int i = 0; i < KCH / 64; ++i) {
@@ -115,50 +113,65 @@ __device__ __forceinline__ bf16x8_t b_operand(const uint32_t q, const uint32_t s
   return as_bf16x8(d);
 }
 
-// Gathered A rows of one chunk -> registers (each thread 16-byte pieces), then -> LDS.
-template <int MT, int KCH>
+// Gathered A rows of one chunk -> registers (16-byte pieces spread over the NT threads of
+// the block), then -> LDS.
+template <int MT, int KCH, int NT>
 struct AStage {
-  static constexpr int kPieces = MT * (KCH / 8);                  // 16-byte pieces
-  static constexpr int kPerThread = (kPieces + 255) / 256;
-  uint4 v[kPerThread];
+  static constexpr int kPieces = MT * (KCH / 8);
+  static constexpr int kPerThread = (kPieces + NT - 1) / NT;
+  // one vector value (not an array of structs) so it stays in registers across the loop
+  typedef uint32_t vec_t __attribute__((ext_vector_type(4 * kPerThread)));
+  vec_t v;
 };
 
-template <int MT, int KCH, bool GATEUP>
-__device__ __forceinline__ void load_a(const ExpertGemmArgs& a, const Tile& t, const int* s_tok,
-                                       int k0, AStage<MT, KCH>& st) {
+// Source rows of this thread's A pieces (fixed across chunks): gathered activation rows
+// (gate+up) or the expert's h rows (down); rows past the tile's count read row 0.
+template <int MT, int KCH, int NT, bool GATEUP>
+__device__ __forceinline__ void a_rows(const ExpertGemmArgs& a, const Tile& t, const int* s_tok,
+                                       const uint16_t* (&src)[AStage<MT, KCH, NT>::kPerThread]) {
   constexpr int kRowPieces = KCH / 8;
 #pragma unroll
-  for (int i = 0; i < AStage<MT, KCH>::kPerThread; ++i) {
-    const int p = threadIdx.x + 256 * i;
-    const int row = p / kRowPieces, c = p % kRowPieces;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (p < AStage<MT, KCH>::kPieces && row < t.count) {
-      const uint16_t* src = GATEUP ? a.x + (size_t)s_tok[row] * a.H
-                                   : a.h + (size_t)(t.row0 + row) * a.h_stride;
-      v = *reinterpret_cast<const uint4*>(src + k0 + c * 8);
-    }
-    st.v[i] = v;
+  for (int i = 0; i < AStage<MT, KCH, NT>::kPerThread; ++i) {
+    const int p = (threadIdx.x + NT * i) % AStage<MT, KCH, NT>::kPieces;  // spare threads repeat
+    int row = p / kRowPieces;
+    row = row < t.count ? row : 0;
+    src[i] = GATEUP ? a.x + (size_t)s_tok[row] * a.H : a.h + (size_t)(t.row0 + row) * a.h_stride;
+    src[i] += (p % kRowPieces) * 8;
   }
 }
 
-template <int MT, int KCH>
-__device__ __forceinline__ void store_a(uint8_t* s_a, const AStage<MT, KCH>& st) {
+template <int MT, int KCH, int NT>
+__device__ __forceinline__ void load_a(const uint16_t* const (&src)[AStage<MT, KCH, NT>::kPerThread],
+                                       int k0, AStage<MT, KCH, NT>& st) {
+#pragma unroll
+  for (int i = 0; i < AStage<MT, KCH, NT>::kPerThread; ++i) {
+    const uint4 x = *reinterpret_cast<const uint4*>(src[i] + k0);
+    st.v[4 * i + 0] = x.x;
+    st.v[4 * i + 1] = x.y;
+    st.v[4 * i + 2] = x.z;
+    st.v[4 * i + 3] = x.w;
+  }
+}
+
+template <int MT, int KCH, int NT>
+__device__ __forceinline__ void store_a(uint8_t* s_a, const AStage<MT, KCH, NT>& st) {
   constexpr int kRowPieces = KCH / 8;
 #pragma unroll
-  for (int i = 0; i < AStage<MT, KCH>::kPerThread; ++i) {
-    const int p = threadIdx.x + 256 * i;
-    if (p < AStage<MT, KCH>::kPieces) {
+  for (int i = 0; i < AStage<MT, KCH, NT>::kPerThread; ++i) {
+    const int p = threadIdx.x + NT * i;
+    if (AStage<MT, KCH, NT>::kPieces % NT == 0 || p < AStage<MT, KCH, NT>::kPieces) {
       const int row = p / kRowPieces, c = p % kRowPieces;
-      *reinterpret_cast<uint4*>(s_a + row * kLdsRow + c * 16) = st.v[i];
+      *reinterpret_cast<uint4*>(s_a + row * kLdsRow + c * 16) =
+          make_uint4(st.v[4 * i], st.v[4 * i + 1], st.v[4 * i + 2], st.v[4 * i + 3]);
     }
   }
 }
 
-// MFMAs of one chunk: RB row blocks x 2 column blocks x KCH/16 steps.
-template <int FMT, int MT, int KCH>
+// MFMAs of one chunk for one wave: RB row blocks x 2 column blocks x KCH/16 steps.
+// s_a points at the wave's first A row in LDS.
+template <int FMT, int RB, int KCH>
 __device__ __forceinline__ void mma_chunk(const uint8_t* s_a, const BFrag<FMT, KCH> (&bf)[2],
-                                          f32x16_t (&acc)[MT / 32][2], int lane) {
-  constexpr int RB = MT / 32;
+                                          f32x16_t (&acc)[RB][2], int lane) {
   const int half = lane >> 5, r = lane & 31;
 #pragma unroll
   for (int s = 0; s < KCH / 16; ++s) {
@@ -176,29 +189,47 @@ __device__ __forceinline__ void mma_chunk(const uint8_t* s_a, const BFrag<FMT, K
   }
 }
 
-template <int FMT, int MT, bool GATEUP>
-__global__ __launch_bounds__(256) void k_pre_gemm(ExpertGemmArgs a) {
-  constexpr int RB = MT / 32;
-  __shared__ __align__(16) uint8_t s_a[MT * kLdsRow];
-  __shared__ int s_tok[MT];
+// Block = 8 waves in a WM x WN grid; each wave owns RB 32-row blocks of the tile's rows and
+// two 32-column blocks of weight rows (gate+up: the same rows of gate and of up). Tile
+// height MT = 32 * RB * WM. The A tile is double-buffered in LDS: chunk c+1 is loaded into
+// registers while chunk c's MFMAs run and is written to the other buffer afterwards, so
+// each chunk needs one barrier.
+constexpr int kPreThreads = 512;
+constexpr int kPreWaves = kPreThreads / 64;
+
+template <int FMT, int RB, int WM, bool GATEUP>
+struct PreShape {
+  static constexpr int WN = kPreWaves / WM;
+  static constexpr int MT = 32 * RB * WM;
+  static constexpr int COLS = GATEUP ? WN * 32 : WN * 64;  // weight rows per matrix per block
+};
+
+template <int FMT, int RB, int WM, bool GATEUP>
+__global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
+  using Sh = PreShape<FMT, RB, WM, GATEUP>;
+  constexpr int MT = Sh::MT, WN = Sh::WN, COLS = Sh::COLS, NT = kPreThreads;
+  extern __shared__ __align__(16) uint8_t s_dyn[];
+  uint8_t* s_a0 = s_dyn;
+  uint8_t* s_a1 = s_dyn + MT * kLdsRow;
+  int* s_tok = reinterpret_cast<int*>(s_dyn + 2 * MT * kLdsRow);
 
   const int N = GATEUP ? a.I : a.H;   // rows of each weight matrix
   const int K = GATEUP ? a.H : a.I;
-  const int ncol_tiles = GATEUP ? (N + 127) / 128 : (N + kPreCols - 1) / kPreCols;
+  const int ncol_tiles = (N + COLS - 1) / COLS;
   Tile t;
   int ct;
   if (!pre_resolve(a, ncol_tiles, t, ct)) return;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave / WN, wn = wave % WN;
   const int half = lane >> 5, r = lane & 31;
   const int e = t.group;
-  // this wave's two 32-row column blocks
   int ncol[2];
   if (GATEUP) {
-    ncol[0] = ct * 128 + wave * 32;  // gate rows; column block 1 = the same up rows
+    ncol[0] = ct * COLS + wn * 32;  // gate rows; column block 1 = the same up rows
     ncol[1] = ncol[0];
   } else {
-    ncol[0] = ct * kPreCols + wave * 64;
+    ncol[0] = ct * COLS + wn * 64;
     ncol[1] = ncol[0] + 32;
   }
   const bool valid0 = ncol[0] < N, valid1 = ncol[1] < N;
@@ -206,14 +237,17 @@ __global__ __launch_bounds__(256) void k_pre_gemm(ExpertGemmArgs a) {
   const int sbytes = K / (FMT == 0 ? 16 : 32);
   const WeightDesc& w0 = GATEUP ? a.gate : a.down;
   const WeightDesc& w1 = GATEUP ? a.up : a.down;
-  const uint8_t* p0 = w0.packed + ((size_t)e * N + ncol[0] + r) * row_bytes;
-  const uint8_t* p1 = w1.packed + ((size_t)e * N + ncol[1] + r) * row_bytes;
-  const uint8_t* q0 = w0.scales + ((size_t)e * N + ncol[0] + r) * sbytes;
-  const uint8_t* q1 = w1.scales + ((size_t)e * N + ncol[1] + r) * sbytes;
+  // column blocks past N read row r of the expert instead (their results are not stored)
+  const size_t r0 = (size_t)e * N + (valid0 ? ncol[0] : 0) + r;
+  const size_t r1 = (size_t)e * N + (valid1 ? ncol[1] : 0) + r;
+  const uint8_t* p0 = w0.packed + r0 * row_bytes;
+  const uint8_t* p1 = w1.packed + r1 * row_bytes;
+  const uint8_t* q0 = w0.scales + r0 * sbytes;
+  const uint8_t* q1 = w1.scales + r1 * sbytes;
+  const int arow0 = wm * 32 * RB;  // first A row of this wave
 
   if (GATEUP) {
-    for (int i = threadIdx.x; i < MT; i += 256)
-      s_tok[i] = i < t.count ? a.row_token[t.row0 + i] : 0;
+    for (int i = threadIdx.x; i < MT; i += NT) s_tok[i] = i < t.count ? a.row_token[t.row0 + i] : 0;
     __syncthreads();
   }
 
@@ -226,36 +260,59 @@ __global__ __launch_bounds__(256) void k_pre_gemm(ExpertGemmArgs a) {
 
   const int nfull = K / kKc;
   if (nfull > 0) {
-    AStage<MT, kKc> st;
-    BFrag<FMT, kKc> cur[2], nxt[2];
-    load_a<MT, kKc, GATEUP>(a, t, s_tok, 0, st);
-    load_b<FMT, kKc>(p0, q0, 0, half, valid0, cur[0]);
-    load_b<FMT, kKc>(p1, q1, 0, half, valid1, cur[1]);
-    for (int c = 0; c < nfull; ++c) {
-      store_a<MT, kKc>(s_a, st);
-      __syncthreads();
-      if (c + 1 < nfull) {
-        const int k1 = (c + 1) * kKc;
-        load_a<MT, kKc, GATEUP>(a, t, s_tok, k1, st);
-        load_b<FMT, kKc>(p0, q0, k1, half, valid0, nxt[0]);
-        load_b<FMT, kKc>(p1, q1, k1, half, valid1, nxt[1]);
-      }
-      mma_chunk<FMT, MT, kKc>(s_a, cur, acc, lane);
-      __syncthreads();
-      cur[0] = nxt[0];
-      cur[1] = nxt[1];
-    }
-  }
-  if (K % kKc) {  // 64-code tail (K % 64 == 0)
-    const int k0 = nfull * kKc;
-    AStage<MT, 64> st;
-    BFrag<FMT, 64> tb[2];
-    load_a<MT, 64, GATEUP>(a, t, s_tok, k0, st);
-    load_b<FMT, 64>(p0, q0, k0, half, valid0, tb[0]);
-    load_b<FMT, 64>(p1, q1, k0, half, valid1, tb[1]);
-    store_a<MT, 64>(s_a, st);
+    // Pipeline: B fragments rotate through three register slots, A stages through LDS.
+    // Step c runs chunk c's MFMAs, writes A(c+1) (already in registers) to the other LDS
+    // buffer, then issues the loads of A(c+2) and B(c+3) before the step's barrier. The
+    // barrier keeps those loads ahead of the next steps, whose MFMAs hide their latency.
+    // Past the last chunk the loads re-read it (unconditional loads, unused data).
+    AStage<MT, kKc, NT> st;
+    const uint16_t* asrc[AStage<MT, kKc, NT>::kPerThread];
+    a_rows<MT, kKc, NT, GATEUP>(a, t, s_tok, asrc);
+    const int klast = (nfull - 1) * kKc;
+    BFrag<FMT, kKc> b0[2], b1[2], b2[2];
+    load_a<MT, kKc, NT>(asrc, 0, st);
+    load_b<FMT, kKc>(p0, q0, 0, half, b0[0]);
+    load_b<FMT, kKc>(p1, q1, 0, half, b0[1]);
+    load_b<FMT, kKc>(p0, q0, min(kKc, klast), half, b1[0]);
+    load_b<FMT, kKc>(p1, q1, min(kKc, klast), half, b1[1]);
+    load_b<FMT, kKc>(p0, q0, min(2 * kKc, klast), half, b2[0]);
+    load_b<FMT, kKc>(p1, q1, min(2 * kKc, klast), half, b2[1]);
+    store_a<MT, kKc, NT>(s_a0, st);
+    load_a<MT, kKc, NT>(asrc, min(kKc, klast), st);
     __syncthreads();
-    mma_chunk<FMT, MT, 64>(s_a, tb, acc, lane);
+    // A macro rather than a lambda: a captured register array would be demoted to scratch.
+#define MOE_PRE_STEP(C, CUR)                                                               \
+  {                                                                                       \
+    mma_chunk<FMT, RB, kKc>((((C) & 1) ? s_a1 : s_a0) + arow0 * kLdsRow, CUR, acc, lane); \
+    store_a<MT, kKc, NT>(((C) & 1) ? s_a0 : s_a1, st);                                    \
+    load_a<MT, kKc, NT>(asrc, min(((C) + 2) * kKc, klast), st);                           \
+    const int k3 = min(((C) + 3) * kKc, klast);                                           \
+    load_b<FMT, kKc>(p0, q0, k3, half, CUR[0]);                                           \
+    load_b<FMT, kKc>(p1, q1, k3, half, CUR[1]);                                           \
+    __syncthreads();                                                                      \
+  }
+    // unrolled by three so the three B slots rotate by renaming, not by register copies
+    // (a copy of a slot whose loads are in flight would wait for them)
+#pragma unroll 1
+    for (int c = 0; c < nfull; c += 3) {
+      MOE_PRE_STEP(c, b0);
+      if (c + 1 < nfull) MOE_PRE_STEP(c + 1, b1);
+      if (c + 2 < nfull) MOE_PRE_STEP(c + 2, b2);
+    }
+#undef MOE_PRE_STEP
+  }
+  if (K % kKc) {  // 64-code tail (K % 64 == 0); both buffers are free after the last barrier
+    const int k0 = nfull * kKc;
+    AStage<MT, 64, NT> st;
+    const uint16_t* asrc[AStage<MT, 64, NT>::kPerThread];
+    a_rows<MT, 64, NT, GATEUP>(a, t, s_tok, asrc);
+    BFrag<FMT, 64> tb[2];
+    load_a<MT, 64, NT>(asrc, k0, st);
+    load_b<FMT, 64>(p0, q0, k0, half, tb[0]);
+    load_b<FMT, 64>(p1, q1, k0, half, tb[1]);
+    store_a<MT, 64, NT>(s_a0, st);
+    __syncthreads();
+    mma_chunk<FMT, RB, 64>(s_a0 + arow0 * kLdsRow, tb, acc, lane);
   }
 
   // epilogue: lane holds column j = lane % 32 of each 32x32 block, rows 8*(v/4)+4*half+v%4
@@ -268,7 +325,7 @@ __global__ __launch_bounds__(256) void k_pre_gemm(ExpertGemmArgs a) {
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int i = rb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
+        const int i = arow0 + rb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
         if (i < t.count) {
           const float g = acc[rb][0][v] * gs_g;
           const float u = acc[rb][1][v] * gs_u;
@@ -288,7 +345,7 @@ __global__ __launch_bounds__(256) void k_pre_gemm(ExpertGemmArgs a) {
       for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int i = rb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
+          const int i = arow0 + rb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
           if (i < t.count) y[(size_t)(t.row0 + i) * a.H + n] = f32_to_bf16(acc[rb][cb][v] * gs);
         }
       }
@@ -296,25 +353,37 @@ __global__ __launch_bounds__(256) void k_pre_gemm(ExpertGemmArgs a) {
   }
 }
 
+template <int FMT, int RB, int WM, bool GATEUP>
+static hipError_t launch_pre_shape(const ExpertGemmArgs& a, hipStream_t s) {
+  using Sh = PreShape<FMT, RB, WM, GATEUP>;
+  const int N = GATEUP ? a.I : a.H;
+  const int ncol = (N + Sh::COLS - 1) / Sh::COLS;
+  const size_t smem = 2 * (size_t)Sh::MT * kLdsRow + Sh::MT * sizeof(int);
+  auto kern = k_pre_gemm<FMT, RB, WM, GATEUP>;
+  static bool attr_set = false;  // one attribute call per instantiation and process
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(ncol, a.tile_bound), dim3(kPreThreads), smem, s, a);
+  return hipGetLastError();
+}
+
+// Tile height MT -> (row blocks per wave, waves along M): 128 = 2 x 2, 64 = 2 x 1, 32 = 1 x 1.
 template <bool GATEUP>
 static hipError_t launch_pre(const ExpertGemmArgs& a, int mt, hipStream_t s) {
   if (a.tile_bound <= 0) return hipSuccess;
-  const int N = GATEUP ? a.I : a.H;
-  const int ncol = GATEUP ? (N + 127) / 128 : (N + kPreCols - 1) / kPreCols;
-  const dim3 grid(ncol, a.tile_bound), block(256);
   const int fmt = GATEUP ? a.gate.fmt : a.down.fmt;
-#define MOE_PRE(F, M) hipLaunchKernelGGL((k_pre_gemm<F, M, GATEUP>), grid, block, 0, s, a)
   if (fmt == 0) {
-    if (mt == 32) MOE_PRE(0, 32);
-    else if (mt == 64) MOE_PRE(0, 64);
-    else MOE_PRE(0, 128);
-  } else {
-    if (mt == 32) MOE_PRE(1, 32);
-    else if (mt == 64) MOE_PRE(1, 64);
-    else MOE_PRE(1, 128);
+    if (mt == 32) return launch_pre_shape<0, 1, 1, GATEUP>(a, s);
+    if (mt == 64) return launch_pre_shape<0, 2, 1, GATEUP>(a, s);
+    return launch_pre_shape<0, 2, 2, GATEUP>(a, s);
   }
-#undef MOE_PRE
-  return hipGetLastError();
+  if (mt == 32) return launch_pre_shape<1, 1, 1, GATEUP>(a, s);
+  if (mt == 64) return launch_pre_shape<1, 2, 1, GATEUP>(a, s);
+  return launch_pre_shape<1, 2, 2, GATEUP>(a, s);
 }
 
 hipError_t launch_prefill_gate_up(const ExpertGemmArgs& a, int mt, hipStream_t s) {

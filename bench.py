@@ -30,6 +30,7 @@ METRIC = "MoE-layer tokens/s; decode HBM GB/s & prefill MFMA TFLOP/s vs peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PROFILE_DIR = os.path.join(ROOT, "profiles")
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 
 DESCRIPTIONS = {
     "tiny": "Tiny MoE layer: 4 tokens, hidden 256, 8 experts, top_k=2, softmax, inter 512, NVFP4",
@@ -66,14 +67,17 @@ class HipEvents:
 
     def __init__(self):
         self.lib = ctypes.CDLL("libamdhip64.so")
-        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                     ctypes.c_uint]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
                                                  ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
     def create(self):
         ev = ctypes.c_void_p()
-        if self.lib.hipEventCreate(ctypes.byref(ev)) != 0:
+        # timing-only events: no system-scope fence (cache writeback/invalidate) when the
+        # event is recorded, which would otherwise be timed as part of the kernel
+        if self.lib.hipEventCreateWithFlags(ctypes.byref(ev), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
             raise RuntimeError("hipEventCreate failed")
         return ev.value
 
@@ -109,6 +113,111 @@ def load_traffic(workload, kernel):
     if not k or d.get("source_digest") != source_digest():
         return None
     return k.get("bytes_per_launch")
+
+
+def _rocprof_rows(d, suffix):
+    import csv
+    import glob
+    rows = []
+    for p in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+        with open(p) as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return rows
+
+
+def summarize_trace(d, command):
+    """Markdown table of a `rocprofv3 --kernel-trace --stats --output-format csv` run."""
+    rows = [r for r in _rocprof_rows(d, "kernel_stats.csv") if "moe::" in r["Name"]]
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    out = ["# rocprofv3 kernel statistics", "", "Command:", "", "    " + command, "",
+           "Library kernels only (the input generator's torch kernels are left out); every "
+           "call of the run is counted, warm-up and routing passes included.", "",
+           "| kernel | calls | avg us | min us | max us | share |",
+           "|---|---:|---:|---:|---:|---:|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"].split("(")[0]
+        out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                   f"{float(r['TotalDurationNs']) / total:.1%} |")
+    return "\n".join(out) + "\n"
+
+
+# the routed experts' kernels of one layer call, in launch order after the dispatch build
+_ROUTED_KERNELS = {"decode": ("k_dec_gate_up", "k_dec_down"),
+                   "prefill": ("k_pre_gemm", "k_pre_gemm")}
+
+
+def _dispatch_id(r):
+    return int(next(v for k, v in r.items() if k.lower() == "dispatch_id"))
+
+
+def _routed_counter(d, path):
+    """Mean counter value (KiB) per dispatch of the routed gate+up and down kernels: the
+    first two expert kernels after each k_dispatch (shared-expert launches come later)."""
+    rows = _rocprof_rows(d, "counter_collection.csv")
+    per = {}
+    for r in rows:  # one row per (dispatch, counter); sum over counter instances
+        k = _dispatch_id(r)
+        e = per.setdefault(k, [r["Kernel_Name"], 0.0])
+        e[1] += float(r["Counter_Value"])
+    want = _ROUTED_KERNELS[path]
+    got = {"gate_up": [], "down": []}
+    stage = None
+    for k in sorted(per):
+        name, v = per[k]
+        if "k_dispatch" in name:
+            stage = 0
+        elif stage is not None and stage < 2 and want[stage] in name:
+            got["gate_up" if stage == 0 else "down"].append(v)
+            stage += 1
+    return {s: (sum(v) / len(v), len(v)) for s, v in got.items() if v}
+
+
+def _copy_counter(d):
+    rows = _rocprof_rows(d, "counter_collection.csv")
+    per = {}
+    for r in rows:
+        k = _dispatch_id(r)
+        per[k] = per.get(k, 0.0) + float(r["Counter_Value"])
+    top = max(per.values())
+    vals = [v for v in per.values() if v >= 0.5 * top]  # the 1 GiB copies, not small ones
+    return sum(vals) / len(vals)
+
+
+def summarize_traffic(d, workload, path, commands):
+    """profiles/traffic_<workload>.json from four rocprofv3 --pmc runs under `d`:
+    fetch/ and write/ (FETCH_SIZE, WRITE_SIZE of bench.py on the workload) and
+    copy_fetch/, copy_write/ (the same counters on 1 GiB device copies). Each counter is
+    scaled so that the copy kernel reads as 1 GiB fetched and 1 GiB written."""
+    copy_bytes = float(1 << 30)
+    f_copy, w_copy = _copy_counter(os.path.join(d, "copy_fetch")), \
+        _copy_counter(os.path.join(d, "copy_write"))
+    f_scale = copy_bytes / (f_copy * 1024.0)
+    w_scale = copy_bytes / (w_copy * 1024.0)
+    fetch = _routed_counter(os.path.join(d, "fetch"), path)
+    write = _routed_counter(os.path.join(d, "write"), path)
+    kernels = {}
+    for s in ("gate_up", "down"):
+        if s in fetch and s in write:
+            fb = fetch[s][0] * 1024.0 * f_scale
+            wb = write[s][0] * 1024.0 * w_scale
+            kernels[f"{path}_{s}"] = {
+                "fetch_kib_raw": round(fetch[s][0], 1), "write_kib_raw": round(write[s][0], 1),
+                "dispatches": [fetch[s][1], write[s][1]],
+                "fetch_bytes": round(fb), "write_bytes": round(wb),
+                "bytes_per_launch": round(fb + wb)}
+    doc = {"workload": workload, "source_digest": source_digest(),
+           "copy_calibration": {"bytes": int(copy_bytes), "fetch_kib": f_copy,
+                                "write_kib": w_copy, "fetch_scale": round(f_scale, 4),
+                                "write_scale": round(w_scale, 4)},
+           "kernels": kernels, "commands": commands}
+    out = os.path.join(PROFILE_DIR, f"traffic_{workload}.json")
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    with open(out, "w") as f:
+        json.dump(doc, f, indent=1)
+    return out
 
 
 def cpu_baseline(spec, inp, name, seconds):
@@ -166,7 +275,22 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 8 device-to-device copies of 1 GiB (a copy kernel of known "
                          "size, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a kernel table of a rocprofv3 --stats csv output dir and exit")
+    ap.add_argument("--summarize-traffic", metavar="DIR",
+                    help="write the workload's HBM traffic file from rocprofv3 --pmc runs in "
+                         "DIR/{fetch,write,copy_fetch,copy_write} and exit")
+    ap.add_argument("--command", action="append", default=[],
+                    help="command line recorded in a summary (repeatable)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, " ; ".join(args.command)), end="")
+        return
+    if args.summarize_traffic:
+        path = "prefill" if args.workload in ("prefill_zipf_t4096", "hash_mxfp4_t512") \
+            else "decode"
+        print(summarize_traffic(args.summarize_traffic, args.workload, path, args.command))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

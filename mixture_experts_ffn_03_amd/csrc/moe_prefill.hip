@@ -9,21 +9,27 @@
 // rows fused into the GEMM's A load (doc of moe_permute_tokens_k).
 //
 // Design (gfx950, v_mfma_f32_32x32x16_bf16):
-// * A block of 8 waves computes an MT-row tile of one expert: MT gathered token rows times
-//   COLS weight rows (gate+up kernel: COLS gate rows and the same COLS up rows, so SwiGLU
-//   runs in the epilogue on values that sit in the same lane and register). Waves form a
-//   WM x WN grid; each owns 32*RB rows and two 32-column blocks (64 fp32 accumulators
-//   per lane for RB = 2), which keeps 2 waves per SIMD resident.
-// * The waves share the A tile, gathered from the activations by row_token and staged in
-//   LDS (rows padded by 16 bytes so the 32 rows an MFMA operand reads fall in distinct
-//   banks), double-buffered so that each 128-wide K chunk needs a single barrier.
-// * Each lane reads its B fragment straight from HBM: 32 contiguous bytes (64 codes) of
-//   one weight row per 128-wide K chunk, so the weight stream needs no LDS. The MFMA K
-//   order is permuted inside a chunk (lane half h covers codes 64h..64h+63) and the A
-//   fragments are read from LDS with the same permutation.
+// * A block of 4 waves (one per SIMD) computes an MT-row tile of one expert against
+//   BROWS weight rows. Each wave owns RB 32-row blocks and four 32-column blocks of
+//   weight rows (gate+up: two of gate and the same two of up, so SwiGLU runs in the
+//   epilogue on values held by the same lane), i.e. 4*RB independent accumulators.
+// * Both operands reach LDS by direct-to-LDS loads (global_load_lds_*: the activation
+//   rows gathered by row_token, the FP4 weight rows and their scale bytes) into a ring
+//   of three 128-wide K stages. Step c waits for stage c, synchronises the block once,
+//   issues stage c+2 into the slot freed by step c-1, then runs the MFMAs of stage c.
+//   Loads therefore have two steps to land, and no registers are spent on them.
+// * The loads and their waits are explicit: the compiler's counter tracking cannot tell
+//   a direct-to-LDS load apart from the LDS reads of other stages and would drain every
+//   load before each read. No other vector-memory load is issued in the main loop, so
+//   "at most one stage of loads in flight" means "this step's stage has landed".
+// * LDS rows are swizzled in 16-byte slots (A: slot = piece ^ (row & 15); B: slot =
+//   piece ^ ((row >> 1 ^ row >> 3) & 3)) so that the rows read by one MFMA operand load
+//   fall in distinct banks; the load side picks the source piece for its fixed slot.
+// * The MFMA K order is permuted inside a stage (lane half h covers codes 64h..64h+63),
+//   so each lane's B codes are 32 contiguous bytes of one weight row; A is read with the
+//   same permutation.
 // * E2M1 codes become exact bf16 operands in registers (MXFP4: scaled convert by the
 //   E8M0 power of two; NVFP4: convert, times the E4M3 scale in fp32, pack).
-// * Global loads (A and B) for chunk c+1 are issued before the MFMAs of chunk c.
 // * Block ids are remapped so that each XCD (ids dispatched round-robin over the 8
 //   XCDs) walks a contiguous run of (row tile, column tile) work, which keeps an A
 //   tile and an expert's weight rows in that XCD's L2 while they are reused.
@@ -31,14 +37,49 @@
 
 namespace moe {
 
-constexpr int kKc = 128;           // K per chunk
-constexpr int kLdsRow = kKc * 2 + 16;  // bytes per LDS row of the A tile (padded)
+constexpr int kKc = 128;  // K codes per stage
+constexpr int kStages = 3;
 constexpr int kXcds = 8;
+constexpr int kPreThreads = 256;
+constexpr int kPreWaves = kPreThreads / 64;
+constexpr int kCB = 4;  // 32-column blocks per wave
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint32_t (&d)[4]) {
   uint4 v = make_uint4(d[0], d[1], d[2], d[3]);
   return __builtin_bit_cast(bf16x8_t, v);
 }
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const lds_u8*)p;
+}
+
+// Direct-to-LDS loads: every lane reads SIZE bytes at its own global address; the wave
+// writes them to LDS at m0 + lane * SIZE (m0 = the wave-uniform base). Their wait is
+// issued by hand (wait_stage).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds_base), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(lds_base), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void dma2(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ushort %1, off"
+               :: "s"(lds_base), "v"(g) : "memory", "m0");
+}
+
+// Wait until at most N vector-memory loads of this wave are in flight and its LDS reads
+// have returned, then synchronise the block: every wave's loads of the stage have
+// landed, and every read of the slot about to be refilled is done.
+template <int N>
+__device__ __forceinline__ void wait_stage() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
+__device__ __forceinline__ int b_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
 // Resolve this block's (row tile, column tile), remapped per XCD; false = no work.
 __device__ __forceinline__ bool pre_resolve(const ExpertGemmArgs& a, int ncol_tiles, Tile& t,
@@ -68,42 +109,7 @@ __device__ __forceinline__ bool pre_resolve(const ExpertGemmArgs& a, int ncol_ti
   return true;
 }
 
-// B fragment of one 32-row column block for a chunk of KCH (128 or 64) codes: lane
-// (row j = lane % 32, half h = lane / 32) holds codes [KCH/2 * h, KCH/2 * (h + 1)) of
-// the chunk, i.e. KCH/16 dwords, plus their scale bytes.
-template <int FMT, int KCH>
-struct BFrag {
-  uint32_t q[KCH / 16];
-  uint32_t sc;
-};
-
-// Loads are unconditional: callers clamp rows and chunks to valid addresses (results for
-// clamped rows are discarded), so the compiler can count outstanding loads and wait only
-// for the ones a step consumes.
-template <int FMT, int KCH>
-__device__ __forceinline__ void load_b(const uint8_t* packed_row, const uint8_t* scale_row,
-                                       int k0, int half, BFrag<FMT, KCH>& f) {
-  const uint8_t* p = packed_row + k0 / 2 + half * (KCH / 4);
-#pragma unroll
-  for (int i = 0; i < KCH / 64; ++i) {
-    const uint4 v = reinterpret_cast<const uint4*>(p)[i];
-    f.q[4 * i + 0] = v.x;
-    f.q[4 * i + 1] = v.y;
-    f.q[4 * i + 2] = v.z;
-    f.q[4 * i + 3] = v.w;
-  }
-  // scale bytes of the lane's KCH/2 codes: NVFP4 KCH/32 bytes, MXFP4 KCH/64 bytes
-  if (FMT == 0) {
-    const uint8_t* s = scale_row + k0 / 16 + half * (KCH / 32);
-    f.sc = KCH == 128 ? *reinterpret_cast<const uint32_t*>(s)
-                      : (uint32_t)*reinterpret_cast<const uint16_t*>(s);
-  } else {
-    const uint8_t* s = scale_row + k0 / 32 + half * (KCH / 64);
-    f.sc = KCH == 128 ? (uint32_t)*reinterpret_cast<const uint16_t*>(s) : (uint32_t)s[0];
-  }
-}
-
-// Operand for MFMA step s (codes 8s..8s+7 of the lane's half chunk).
+// Operand for MFMA step s (codes 8s..8s+7 of the lane's codes of the stage).
 template <int FMT>
 __device__ __forceinline__ bf16x8_t b_operand(const uint32_t q, const uint32_t sc_word, int s) {
   const int blk = FMT == 0 ? s / 2 : s / 4;  // 16- or 32-code block inside the lane's codes
@@ -113,109 +119,49 @@ __device__ __forceinline__ bf16x8_t b_operand(const uint32_t q, const uint32_t s
   return as_bf16x8(d);
 }
 
-// Gathered A rows of one chunk -> registers (16-byte pieces spread over the NT threads of
-// the block), then -> LDS.
-template <int MT, int KCH, int NT>
-struct AStage {
-  static constexpr int kPieces = MT * (KCH / 8);
-  static constexpr int kPerThread = (kPieces + NT - 1) / NT;
-  // one vector value (not an array of structs) so it stays in registers across the loop
-  typedef uint32_t vec_t __attribute__((ext_vector_type(4 * kPerThread)));
-  vec_t v;
-};
-
-// Source rows of this thread's A pieces (fixed across chunks): gathered activation rows
-// (gate+up) or the expert's h rows (down); rows past the tile's count read row 0.
-template <int MT, int KCH, int NT, bool GATEUP>
-__device__ __forceinline__ void a_rows(const ExpertGemmArgs& a, const Tile& t, const int* s_tok,
-                                       const uint16_t* (&src)[AStage<MT, KCH, NT>::kPerThread]) {
-  constexpr int kRowPieces = KCH / 8;
-#pragma unroll
-  for (int i = 0; i < AStage<MT, KCH, NT>::kPerThread; ++i) {
-    const int p = (threadIdx.x + NT * i) % AStage<MT, KCH, NT>::kPieces;  // spare threads repeat
-    int row = p / kRowPieces;
-    row = row < t.count ? row : 0;
-    src[i] = GATEUP ? a.x + (size_t)s_tok[row] * a.H : a.h + (size_t)(t.row0 + row) * a.h_stride;
-    src[i] += (p % kRowPieces) * 8;
-  }
-}
-
-template <int MT, int KCH, int NT>
-__device__ __forceinline__ void load_a(const uint16_t* const (&src)[AStage<MT, KCH, NT>::kPerThread],
-                                       int k0, AStage<MT, KCH, NT>& st) {
-#pragma unroll
-  for (int i = 0; i < AStage<MT, KCH, NT>::kPerThread; ++i) {
-    const uint4 x = *reinterpret_cast<const uint4*>(src[i] + k0);
-    st.v[4 * i + 0] = x.x;
-    st.v[4 * i + 1] = x.y;
-    st.v[4 * i + 2] = x.z;
-    st.v[4 * i + 3] = x.w;
-  }
-}
-
-template <int MT, int KCH, int NT>
-__device__ __forceinline__ void store_a(uint8_t* s_a, const AStage<MT, KCH, NT>& st) {
-  constexpr int kRowPieces = KCH / 8;
-#pragma unroll
-  for (int i = 0; i < AStage<MT, KCH, NT>::kPerThread; ++i) {
-    const int p = threadIdx.x + NT * i;
-    if (AStage<MT, KCH, NT>::kPieces % NT == 0 || p < AStage<MT, KCH, NT>::kPieces) {
-      const int row = p / kRowPieces, c = p % kRowPieces;
-      *reinterpret_cast<uint4*>(s_a + row * kLdsRow + c * 16) =
-          make_uint4(st.v[4 * i], st.v[4 * i + 1], st.v[4 * i + 2], st.v[4 * i + 3]);
-    }
-  }
-}
-
-// MFMAs of one chunk for one wave: RB row blocks x 2 column blocks x KCH/16 steps.
-// s_a points at the wave's first A row in LDS.
-template <int FMT, int RB, int KCH>
-__device__ __forceinline__ void mma_chunk(const uint8_t* s_a, const BFrag<FMT, KCH> (&bf)[2],
-                                          f32x16_t (&acc)[RB][2], int lane) {
-  const int half = lane >> 5, r = lane & 31;
-#pragma unroll
-  for (int s = 0; s < KCH / 16; ++s) {
-    const bf16x8_t b0 = b_operand<FMT>(bf[0].q[s], bf[0].sc, s);
-    const bf16x8_t b1 = b_operand<FMT>(bf[1].q[s], bf[1].sc, s);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      // A[i][k] for the same permuted k: lane half h, step s -> chunk codes KCH/2*h + 8s
-      const uint4 av = *reinterpret_cast<const uint4*>(
-          s_a + (rb * 32 + r) * kLdsRow + (half * (KCH / 2) + 8 * s) * 2);
-      const bf16x8_t af = __builtin_bit_cast(bf16x8_t, av);
-      acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b0, acc[rb][0], 0, 0, 0);
-      acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b1, acc[rb][1], 0, 0, 0);
-    }
-  }
-}
-
-// Block = 8 waves in a WM x WN grid; each wave owns RB 32-row blocks of the tile's rows and
-// two 32-column blocks of weight rows (gate+up: the same rows of gate and of up). Tile
-// height MT = 32 * RB * WM. The A tile is double-buffered in LDS: chunk c+1 is loaded into
-// registers while chunk c's MFMAs run and is written to the other buffer afterwards, so
-// each chunk needs one barrier.
-constexpr int kPreThreads = 512;
-constexpr int kPreWaves = kPreThreads / 64;
-
+// Block = 4 waves in a WM x WN grid. Tile height MT = 32 * RB * WM; BROWS weight rows per
+// block (gate+up: BROWS/2 gate rows and the same BROWS/2 up rows; down: BROWS output
+// columns). A stage holds the A tile (MT rows x 256 bytes), the B tile (BROWS rows x 64
+// bytes) and its scales (BROWS rows x two 4-byte slots: NVFP4 4 bytes each, MXFP4 2 bytes
+// each; the 64-code tail uses the first slot).
 template <int FMT, int RB, int WM, bool GATEUP>
 struct PreShape {
   static constexpr int WN = kPreWaves / WM;
   static constexpr int MT = 32 * RB * WM;
-  static constexpr int COLS = GATEUP ? WN * 32 : WN * 64;  // weight rows per matrix per block
+  static constexpr int BROWS = 32 * kCB * WN;
+  static constexpr int NCOLS = GATEUP ? BROWS / 2 : BROWS;  // output columns per block
+  static constexpr int SROW = 8;  // LDS bytes per row of scales per stage (two 4-byte slots)
+  static constexpr int A_BYTES = MT * 256;
+  static constexpr int B_BYTES = BROWS * 64;
+  static constexpr int S_BYTES = BROWS * SROW;
+  static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+  static constexpr int NA = MT * 16 / kPreThreads;      // 16-byte loads per lane (A)
+  static constexpr int NB = BROWS * 4 / kPreThreads;    // 16-byte loads per lane (B)
+  // scale loads: 4 bytes (NVFP4) or 2 bytes (MXFP4, whose rows may be only 2-aligned) per
+  // lane, each landing in a 4-byte LDS slot (sub-dword direct-to-LDS loads keep a 4-byte
+  // lane stride)
+  static constexpr int SUNIT = FMT == 0 ? 4 : 2;
+  static constexpr int NS = S_BYTES / 4 / kPreThreads;  // scale loads per lane
+  static constexpr int NLOADS = NA + NB + NS;
+  static constexpr size_t SMEM = (size_t)kStages * STAGE + MT * sizeof(int);
+  static_assert(NA * kPreThreads == MT * 16 && NB * kPreThreads == BROWS * 4 &&
+                    NS * kPreThreads * 4 == S_BYTES,
+                "a stage must split evenly over the block");
+  static_assert(NLOADS <= 31, "two stages of loads must fit the wait counter");
+  static_assert(SMEM <= 160 * 1024, "three stages must fit the 160 KB of LDS");
 };
 
 template <int FMT, int RB, int WM, bool GATEUP>
 __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
   using Sh = PreShape<FMT, RB, WM, GATEUP>;
-  constexpr int MT = Sh::MT, WN = Sh::WN, COLS = Sh::COLS, NT = kPreThreads;
+  constexpr int WN = Sh::WN, BROWS = Sh::BROWS, NCOLS = Sh::NCOLS, MT = Sh::MT;
+  constexpr int NA = Sh::NA, NB = Sh::NB, NS = Sh::NS;
   extern __shared__ __align__(16) uint8_t s_dyn[];
-  uint8_t* s_a0 = s_dyn;
-  uint8_t* s_a1 = s_dyn + MT * kLdsRow;
-  int* s_tok = reinterpret_cast<int*>(s_dyn + 2 * MT * kLdsRow);
+  int* s_tok = reinterpret_cast<int*>(s_dyn + kStages * Sh::STAGE);
 
-  const int N = GATEUP ? a.I : a.H;   // rows of each weight matrix
+  const int N = GATEUP ? a.I : a.H;  // rows of each weight matrix
   const int K = GATEUP ? a.H : a.I;
-  const int ncol_tiles = (N + COLS - 1) / COLS;
+  const int ncol_tiles = (N + NCOLS - 1) / NCOLS;
   Tile t;
   int ct;
   if (!pre_resolve(a, ncol_tiles, t, ct)) return;
@@ -224,113 +170,211 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
   const int wm = wave / WN, wn = wave % WN;
   const int half = lane >> 5, r = lane & 31;
   const int e = t.group;
-  int ncol[2];
-  if (GATEUP) {
-    ncol[0] = ct * COLS + wn * 32;  // gate rows; column block 1 = the same up rows
-    ncol[1] = ncol[0];
-  } else {
-    ncol[0] = ct * COLS + wn * 64;
-    ncol[1] = ncol[0] + 32;
-  }
-  const bool valid0 = ncol[0] < N, valid1 = ncol[1] < N;
+  const int n0 = ct * NCOLS;
   const size_t row_bytes = (size_t)K / 2;
   const int sbytes = K / (FMT == 0 ? 16 : 32);
   const WeightDesc& w0 = GATEUP ? a.gate : a.down;
   const WeightDesc& w1 = GATEUP ? a.up : a.down;
-  // column blocks past N read row r of the expert instead (their results are not stored)
-  const size_t r0 = (size_t)e * N + (valid0 ? ncol[0] : 0) + r;
-  const size_t r1 = (size_t)e * N + (valid1 ? ncol[1] : 0) + r;
-  const uint8_t* p0 = w0.packed + r0 * row_bytes;
-  const uint8_t* p1 = w1.packed + r1 * row_bytes;
-  const uint8_t* q0 = w0.scales + r0 * sbytes;
-  const uint8_t* q1 = w1.scales + r1 * sbytes;
-  const int arow0 = wm * 32 * RB;  // first A row of this wave
 
-  if (GATEUP) {
-    for (int i = threadIdx.x; i < MT; i += NT) s_tok[i] = i < t.count ? a.row_token[t.row0 + i] : 0;
-    __syncthreads();
+  // source row of each A tile row: gathered token (gate+up) or h row (down); rows past
+  // the tile's count repeat its first row (results discarded)
+  for (int i = threadIdx.x; i < MT; i += kPreThreads) {
+    const int ii = i < t.count ? i : 0;
+    s_tok[i] = GATEUP ? a.row_token[t.row0 + ii] : t.row0 + ii;
   }
+  __syncthreads();
 
-  f32x16_t acc[RB][2];
+  // Source address of each load of this lane (fixed across stages, + the stage's K
+  // offset). The i-th load of a wave fills LDS slots (wave * n + i) * 64 + lane of its
+  // region; a slot holds the source piece that the swizzle assigns to it.
+  const uint16_t* asrc[NA];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    acc[rb][0] = f32x16_t{};
-    acc[rb][1] = f32x16_t{};
+  for (int i = 0; i < NA; ++i) {
+    const int slot = (wave * NA + i) * 64 + lane;
+    const int row = slot >> 4, piece = (slot & 15) ^ (row & 15);
+    const uint16_t* base = GATEUP ? a.x + (size_t)s_tok[row] * a.H
+                                  : a.h + (size_t)s_tok[row] * a.h_stride;
+    asrc[i] = base + piece * 8;
+  }
+  // weight row of B-tile row brow; rows past N read row 0 of the expert (not stored)
+  auto wrow = [&](int brow, const WeightDesc*& w) -> size_t {
+    int n;
+    if (GATEUP) {
+      w = brow < BROWS / 2 ? &w0 : &w1;
+      n = n0 + (brow < BROWS / 2 ? brow : brow - BROWS / 2);
+    } else {
+      w = &w0;
+      n = n0 + brow;
+    }
+    return (size_t)e * N + (n < N ? n : 0);
+  };
+  const uint8_t* bsrc[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int slot = (wave * NB + i) * 64 + lane;
+    const int brow = slot >> 2, piece = (slot & 3) ^ b_swz(brow);
+    const WeightDesc* w;
+    const size_t rw = wrow(brow, w);
+    bsrc[i] = w->packed + rw * row_bytes + piece * 16;
+  }
+  const uint8_t* ssrc[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int slot = (wave * NS + i) * 64 + lane;  // 4-byte LDS slots, two per row
+    const WeightDesc* w;
+    const size_t rw = wrow(slot >> 1, w);
+    ssrc[i] = w->scales + rw * sbytes + (slot & 1) * Sh::SUNIT;
   }
 
   const int nfull = K / kKc;
-  if (nfull > 0) {
-    // Pipeline: B fragments rotate through three register slots, A stages through LDS.
-    // Step c runs chunk c's MFMAs, writes A(c+1) (already in registers) to the other LDS
-    // buffer, then issues the loads of A(c+2) and B(c+3) before the step's barrier. The
-    // barrier keeps those loads ahead of the next steps, whose MFMAs hide their latency.
-    // Past the last chunk the loads re-read it (unconditional loads, unused data).
-    AStage<MT, kKc, NT> st;
-    const uint16_t* asrc[AStage<MT, kKc, NT>::kPerThread];
-    a_rows<MT, kKc, NT, GATEUP>(a, t, s_tok, asrc);
-    const int klast = (nfull - 1) * kKc;
-    BFrag<FMT, kKc> b0[2], b1[2], b2[2];
-    load_a<MT, kKc, NT>(asrc, 0, st);
-    load_b<FMT, kKc>(p0, q0, 0, half, b0[0]);
-    load_b<FMT, kKc>(p1, q1, 0, half, b0[1]);
-    load_b<FMT, kKc>(p0, q0, min(kKc, klast), half, b1[0]);
-    load_b<FMT, kKc>(p1, q1, min(kKc, klast), half, b1[1]);
-    load_b<FMT, kKc>(p0, q0, min(2 * kKc, klast), half, b2[0]);
-    load_b<FMT, kKc>(p1, q1, min(2 * kKc, klast), half, b2[1]);
-    store_a<MT, kKc, NT>(s_a0, st);
-    load_a<MT, kKc, NT>(asrc, min(kKc, klast), st);
-    __syncthreads();
-    // A macro rather than a lambda: a captured register array would be demoted to scratch.
-#define MOE_PRE_STEP(C, CUR)                                                               \
-  {                                                                                       \
-    mma_chunk<FMT, RB, kKc>((((C) & 1) ? s_a1 : s_a0) + arow0 * kLdsRow, CUR, acc, lane); \
-    store_a<MT, kKc, NT>(((C) & 1) ? s_a0 : s_a1, st);                                    \
-    load_a<MT, kKc, NT>(asrc, min(((C) + 2) * kKc, klast), st);                           \
-    const int k3 = min(((C) + 3) * kKc, klast);                                           \
-    load_b<FMT, kKc>(p0, q0, k3, half, CUR[0]);                                           \
-    load_b<FMT, kKc>(p1, q1, k3, half, CUR[1]);                                           \
-    __syncthreads();                                                                      \
-  }
-    // unrolled by three so the three B slots rotate by renaming, not by register copies
-    // (a copy of a slot whose loads are in flight would wait for them)
-#pragma unroll 1
-    for (int c = 0; c < nfull; c += 3) {
-      MOE_PRE_STEP(c, b0);
-      if (c + 1 < nfull) MOE_PRE_STEP(c + 1, b1);
-      if (c + 2 < nfull) MOE_PRE_STEP(c + 2, b2);
+  const int nch = nfull + (K % kKc ? 1 : 0);  // the last stage may be a 64-code tail
+
+  // Loads of stage c: always NLOADS per lane, so the wait count is a constant. In the
+  // 64-code tail, pieces past K re-read pieces below K (their slots are not read).
+  auto issue = [&](int c) {
+    const uint32_t abase = lds_addr(s_dyn + (c % kStages) * Sh::STAGE);
+    const uint32_t bbase = abase + Sh::A_BYTES, sbase = bbase + Sh::B_BYTES;
+    const int k0 = c * kKc;
+    const bool tail = c == nfull;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int slot0 = (wave * NA + i) * 64, slot = slot0 + lane, row = slot >> 4;
+      const int piece = (slot & 15) ^ (row & 15);
+      dma16(asrc[i] + k0 - (tail ? (piece & 8) * 8 : 0),
+            __builtin_amdgcn_readfirstlane(abase + slot0 * 16));
     }
-#undef MOE_PRE_STEP
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int slot0 = (wave * NB + i) * 64, slot = slot0 + lane;
+      const int piece = (slot & 3) ^ b_swz(slot >> 2);
+      dma16(bsrc[i] + k0 / 2 - (tail ? (piece & 2) * 16 : 0),
+            __builtin_amdgcn_readfirstlane(bbase + slot0 * 16));
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      // a row's second half re-reads its first in the tail (half as many scale bytes)
+      const int slot0 = (wave * NS + i) * 64;
+      const int back = tail ? ((slot0 + lane) & 1) * Sh::SUNIT : 0;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(sbase + slot0 * 4);
+      if (FMT == 0) {
+        dma4(ssrc[i] + k0 / 16 - back, dst);
+      } else {
+        dma2(ssrc[i] + k0 / 32 - back, dst);
+      }
+    }
+  };
+
+  f32x16_t acc[RB][kCB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) acc[rb][cb] = f32x16_t{};
+
+  // B-tile rows of this wave's column blocks
+  int brow0[kCB];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) {
+    brow0[cb] = GATEUP ? (cb >> 1) * (BROWS / 2) + wn * 64 + (cb & 1) * 32 : wn * 128 + cb * 32;
   }
-  if (K % kKc) {  // 64-code tail (K % 64 == 0); both buffers are free after the last barrier
-    const int k0 = nfull * kKc;
-    AStage<MT, 64, NT> st;
-    const uint16_t* asrc[AStage<MT, 64, NT>::kPerThread];
-    a_rows<MT, 64, NT, GATEUP>(a, t, s_tok, asrc);
-    BFrag<FMT, 64> tb[2];
-    load_a<MT, 64, NT>(asrc, k0, st);
-    load_b<FMT, 64>(p0, q0, k0, half, tb[0]);
-    load_b<FMT, 64>(p1, q1, k0, half, tb[1]);
-    store_a<MT, 64, NT>(s_a0, st);
-    __syncthreads();
-    mma_chunk<FMT, RB, 64>(s_a0 + arow0 * kLdsRow, tb, acc, lane);
+  const int arow = wm * 32 * RB + r;  // + rb * 32
+  const int bsw = b_swz(r);            // = b_swz(brow0[cb] + r): brow0 is a multiple of 32
+
+  issue(0);
+  if (nch > 1) issue(1);
+  // full stages; the tail stage (if any) follows the loop so that the accumulators have
+  // a single definition inside it
+#pragma unroll 1
+  for (int c = 0; c < nfull; ++c) {
+    if (c + 1 < nch) {
+      wait_stage<Sh::NLOADS>();
+    } else {
+      wait_stage<0>();
+    }
+    if (c + 2 < nch) issue(c + 2);
+    const uint8_t* sa = s_dyn + (c % kStages) * Sh::STAGE;
+    const uint8_t* sbq = sa + Sh::A_BYTES;
+    const uint8_t* ssc = sbq + Sh::B_BYTES;
+    uint32_t q[kCB][8], sc[kCB];
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      const uint8_t* row = sbq + (brow0[cb] + r) * 64;
+      const uint4 v0 = *reinterpret_cast<const uint4*>(row + (((2 * half) ^ bsw) << 4));
+      const uint4 v1 = *reinterpret_cast<const uint4*>(row + (((2 * half + 1) ^ bsw) << 4));
+      q[cb][0] = v0.x; q[cb][1] = v0.y; q[cb][2] = v0.z; q[cb][3] = v0.w;
+      q[cb][4] = v1.x; q[cb][5] = v1.y; q[cb][6] = v1.z; q[cb][7] = v1.w;
+      const int srow = brow0[cb] + r;
+      sc[cb] = FMT == 0 ? *reinterpret_cast<const uint32_t*>(ssc + srow * 8 + 4 * half)
+                        : (uint32_t)*reinterpret_cast<const uint16_t*>(ssc + srow * 8 + 4 * half);
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      bf16x8_t bo[kCB];
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb) bo[cb] = b_operand<FMT>(q[cb][s], sc[cb], s);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int row = arow + rb * 32;
+        const uint4 av =
+            *reinterpret_cast<const uint4*>(sa + row * 256 + (((8 * half + s) ^ (row & 15)) << 4));
+        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, av);
+#pragma unroll
+        for (int cb = 0; cb < kCB; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bo[cb], acc[rb][cb], 0, 0, 0);
+      }
+    }
+  }
+  if (nch > nfull) {
+    // 64-code tail: lane half h covers codes 32h..32h+31 in 4 steps
+    wait_stage<0>();
+    const uint8_t* sa = s_dyn + (nfull % kStages) * Sh::STAGE;
+    const uint8_t* sbq = sa + Sh::A_BYTES;
+    const uint8_t* ssc = sbq + Sh::B_BYTES;
+    uint32_t q[kCB][4], sc[kCB];
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      const int srow = brow0[cb] + r;
+      const uint4 v0 = *reinterpret_cast<const uint4*>(sbq + srow * 64 + ((half ^ bsw) << 4));
+      q[cb][0] = v0.x; q[cb][1] = v0.y; q[cb][2] = v0.z; q[cb][3] = v0.w;
+      sc[cb] = FMT == 0 ? (uint32_t)*reinterpret_cast<const uint16_t*>(ssc + srow * 8 + 2 * half)
+                        : (uint32_t)ssc[srow * 8 + half];
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8_t bo[kCB];
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb) bo[cb] = b_operand<FMT>(q[cb][s], sc[cb], s);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int row = arow + rb * 32;
+        const uint4 av =
+            *reinterpret_cast<const uint4*>(sa + row * 256 + (((4 * half + s) ^ (row & 15)) << 4));
+        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, av);
+#pragma unroll
+        for (int cb = 0; cb < kCB; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bo[cb], acc[rb][cb], 0, 0, 0);
+      }
+    }
   }
 
   // epilogue: lane holds column j = lane % 32 of each 32x32 block, rows 8*(v/4)+4*half+v%4
   if (GATEUP) {
-    if (!valid0) return;
     const float gs_g = FMT == 0 ? a.gate.global[e] : 1.0f;
     const float gs_u = FMT == 0 ? a.up.global[e] : 1.0f;
-    const int n = ncol[0] + r;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+    for (int cg = 0; cg < 2; ++cg) {
+      const int n = n0 + wn * 64 + cg * 32 + r;
+      if (n >= N) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int i = arow0 + rb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
-        if (i < t.count) {
-          const float g = acc[rb][0][v] * gs_g;
-          const float u = acc[rb][1][v] * gs_u;
-          const float hval = g / (1.0f + expf(-g)) * u;
-          a.h[(size_t)(t.row0 + i) * a.h_stride + n] = f32_to_bf16(hval);
+      for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int i = wm * 32 * RB + rb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
+          if (i < t.count) {
+            const float g = acc[rb][cg][v] * gs_g;
+            const float u = acc[rb][2 + cg][v] * gs_u;
+            const float hval = g / (1.0f + expf(-g)) * u;
+            a.h[(size_t)(t.row0 + i) * a.h_stride + n] = f32_to_bf16(hval);
+          }
         }
       }
     }
@@ -338,14 +382,14 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
     const float gs = FMT == 0 ? a.down.global[e] : 1.0f;
     uint16_t* y = reinterpret_cast<uint16_t*>(a.y);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      if (!(cb ? valid1 : valid0)) continue;
-      const int n = ncol[cb] + r;
+    for (int cb = 0; cb < kCB; ++cb) {
+      const int n = n0 + wn * 128 + cb * 32 + r;
+      if (n >= N) continue;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int i = arow0 + rb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
+          const int i = wm * 32 * RB + rb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
           if (i < t.count) y[(size_t)(t.row0 + i) * a.H + n] = f32_to_bf16(acc[rb][cb][v] * gs);
         }
       }
@@ -357,32 +401,31 @@ template <int FMT, int RB, int WM, bool GATEUP>
 static hipError_t launch_pre_shape(const ExpertGemmArgs& a, hipStream_t s) {
   using Sh = PreShape<FMT, RB, WM, GATEUP>;
   const int N = GATEUP ? a.I : a.H;
-  const int ncol = (N + Sh::COLS - 1) / Sh::COLS;
-  const size_t smem = 2 * (size_t)Sh::MT * kLdsRow + Sh::MT * sizeof(int);
+  const int ncol = (N + Sh::NCOLS - 1) / Sh::NCOLS;
   auto kern = k_pre_gemm<FMT, RB, WM, GATEUP>;
   static bool attr_set = false;  // one attribute call per instantiation and process
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::SMEM);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(ncol, a.tile_bound), dim3(kPreThreads), smem, s, a);
+  hipLaunchKernelGGL(kern, dim3(ncol, a.tile_bound), dim3(kPreThreads), Sh::SMEM, s, a);
   return hipGetLastError();
 }
 
-// Tile height MT -> (row blocks per wave, waves along M): 128 = 2 x 2, 64 = 2 x 1, 32 = 1 x 1.
+// Tile height MT -> (row blocks per wave, waves along M): 128 = 2 x 2, 64 = 1 x 2, 32 = 1 x 1.
 template <bool GATEUP>
 static hipError_t launch_pre(const ExpertGemmArgs& a, int mt, hipStream_t s) {
   if (a.tile_bound <= 0) return hipSuccess;
   const int fmt = GATEUP ? a.gate.fmt : a.down.fmt;
   if (fmt == 0) {
     if (mt == 32) return launch_pre_shape<0, 1, 1, GATEUP>(a, s);
-    if (mt == 64) return launch_pre_shape<0, 2, 1, GATEUP>(a, s);
+    if (mt == 64) return launch_pre_shape<0, 1, 2, GATEUP>(a, s);
     return launch_pre_shape<0, 2, 2, GATEUP>(a, s);
   }
   if (mt == 32) return launch_pre_shape<1, 1, 1, GATEUP>(a, s);
-  if (mt == 64) return launch_pre_shape<1, 2, 1, GATEUP>(a, s);
+  if (mt == 64) return launch_pre_shape<1, 1, 2, GATEUP>(a, s);
   return launch_pre_shape<1, 2, 2, GATEUP>(a, s);
 }
 

@@ -121,16 +121,21 @@ __device__ __forceinline__ bf16x8_t b_operand(const uint32_t q, const uint32_t s
 
 // Block = 4 waves in a WM x WN grid. Tile height MT = 32 * RB * WM; BROWS weight rows per
 // block (gate+up: BROWS/2 gate rows and the same BROWS/2 up rows; down: BROWS output
-// columns). A stage holds the A tile (MT rows x 256 bytes), the B tile (BROWS rows x 64
-// bytes) and its scales (BROWS rows x two 4-byte slots: NVFP4 4 bytes each, MXFP4 2 bytes
-// each; the 64-code tail uses the first slot).
-template <int FMT, int RB, int WM, bool GATEUP>
+// columns). A stage holds the A tile (MT rows x 256 bytes) and the B tile (BROWS rows x 64
+// bytes). Scales come one of two ways:
+// * SS = false: with each stage, BROWS rows x two 4-byte slots (NVFP4 4 bytes each, MXFP4
+//   2 bytes each; the 64-code tail uses the first slot). Each row's few bytes are a
+//   separate memory request.
+// * SS = true (scale rows a multiple of 16 bytes): 16 bytes per row at a time, covering
+//   SUPER stages (4 MXFP4, 2 NVFP4), into one of two super-stage slots; a quarter or half
+//   as many requests.
+template <int FMT, int RB, int WM, bool GATEUP, bool SS>
 struct PreShape {
   static constexpr int WN = kPreWaves / WM;
   static constexpr int MT = 32 * RB * WM;
   static constexpr int BROWS = 32 * kCB * WN;
   static constexpr int NCOLS = GATEUP ? BROWS / 2 : BROWS;  // output columns per block
-  static constexpr int SROW = 8;  // LDS bytes per row of scales per stage (two 4-byte slots)
+  static constexpr int SROW = SS ? 0 : 8;  // LDS bytes per row of scales per stage
   static constexpr int A_BYTES = MT * 256;
   static constexpr int B_BYTES = BROWS * 64;
   static constexpr int S_BYTES = BROWS * SROW;
@@ -143,21 +148,26 @@ struct PreShape {
   static constexpr int SUNIT = FMT == 0 ? 4 : 2;
   static constexpr int NS = S_BYTES / 4 / kPreThreads;  // scale loads per lane
   static constexpr int NLOADS = NA + NB + NS;
-  static constexpr size_t SMEM = (size_t)kStages * STAGE + MT * sizeof(int);
+  static constexpr int SUPER = FMT == 0 ? 2 : 4;              // stages per super-stage
+  static constexpr int NSS = SS ? BROWS / kPreThreads : 0;    // 16-byte loads per lane
+  static constexpr int SS_BYTES = SS ? 2 * BROWS * 16 : 0;   // two super-stage slots
+  static constexpr size_t SMEM = (size_t)kStages * STAGE + SS_BYTES + MT * sizeof(int);
   static_assert(NA * kPreThreads == MT * 16 && NB * kPreThreads == BROWS * 4 &&
                     NS * kPreThreads * 4 == S_BYTES,
                 "a stage must split evenly over the block");
-  static_assert(NLOADS <= 31, "two stages of loads must fit the wait counter");
+  static_assert(!SS || NSS * kPreThreads == BROWS, "one super-stage load per row");
+  static_assert(NLOADS + NSS <= 31, "two stages of loads must fit the wait counter");
   static_assert(SMEM <= 160 * 1024, "three stages must fit the 160 KB of LDS");
 };
 
-template <int FMT, int RB, int WM, bool GATEUP>
+template <int FMT, int RB, int WM, bool GATEUP, bool SS>
 __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
-  using Sh = PreShape<FMT, RB, WM, GATEUP>;
+  using Sh = PreShape<FMT, RB, WM, GATEUP, SS>;
   constexpr int WN = Sh::WN, BROWS = Sh::BROWS, NCOLS = Sh::NCOLS, MT = Sh::MT;
-  constexpr int NA = Sh::NA, NB = Sh::NB, NS = Sh::NS;
+  constexpr int NA = Sh::NA, NB = Sh::NB, NS = Sh::NS, NSS = Sh::NSS, SUPER = Sh::SUPER;
   extern __shared__ __align__(16) uint8_t s_dyn[];
-  int* s_tok = reinterpret_cast<int*>(s_dyn + kStages * Sh::STAGE);
+  uint8_t* s_ss = s_dyn + kStages * Sh::STAGE;  // super-stage scale slots (SS)
+  int* s_tok = reinterpret_cast<int*>(s_ss + Sh::SS_BYTES);
 
   const int N = GATEUP ? a.I : a.H;  // rows of each weight matrix
   const int K = GATEUP ? a.H : a.I;
@@ -217,13 +227,21 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
     const size_t rw = wrow(brow, w);
     bsrc[i] = w->packed + rw * row_bytes + piece * 16;
   }
-  const uint8_t* ssrc[NS];
+  const uint8_t* ssrc[NS > 0 ? NS : 1];
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
     const int slot = (wave * NS + i) * 64 + lane;  // 4-byte LDS slots, two per row
     const WeightDesc* w;
     const size_t rw = wrow(slot >> 1, w);
     ssrc[i] = w->scales + rw * sbytes + (slot & 1) * Sh::SUNIT;
+  }
+
+  const uint8_t* sssrc[NSS > 0 ? NSS : 1];
+#pragma unroll
+  for (int i = 0; i < NSS; ++i) {
+    const WeightDesc* w;
+    const size_t rw = wrow((wave * NSS + i) * 64 + lane, w);  // one lane per row
+    sssrc[i] = w->scales + rw * sbytes;
   }
 
   const int nfull = K / kKc;
@@ -236,6 +254,15 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
     const uint32_t bbase = abase + Sh::A_BYTES, sbase = bbase + Sh::B_BYTES;
     const int k0 = c * kKc;
     const bool tail = c == nfull;
+    if (SS && c % SUPER == 0) {
+      const int j = c / SUPER;
+      const uint32_t ssbase = lds_addr(s_ss + (j & 1) * BROWS * 16);
+#pragma unroll
+      for (int i = 0; i < NSS; ++i) {
+        const int slot0 = (wave * NSS + i) * 64;
+        dma16(sssrc[i] + 16 * j, __builtin_amdgcn_readfirstlane(ssbase + slot0 * 16));
+      }
+    }
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int slot0 = (wave * NA + i) * 64, slot = slot0 + lane, row = slot >> 4;
@@ -285,10 +312,13 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
   // a single definition inside it
 #pragma unroll 1
   for (int c = 0; c < nfull; ++c) {
-    if (c + 1 < nch) {
-      wait_stage<Sh::NLOADS>();
-    } else {
+    // in flight: the loads of stage c+1 (with a super-stage of scales if it starts one)
+    if (c + 1 >= nch) {
       wait_stage<0>();
+    } else if (SS && (c + 1) % SUPER == 0) {
+      wait_stage<Sh::NLOADS + NSS>();
+    } else {
+      wait_stage<Sh::NLOADS>();
     }
     if (c + 2 < nch) issue(c + 2);
     const uint8_t* sa = s_dyn + (c % kStages) * Sh::STAGE;
@@ -303,8 +333,14 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
       q[cb][0] = v0.x; q[cb][1] = v0.y; q[cb][2] = v0.z; q[cb][3] = v0.w;
       q[cb][4] = v1.x; q[cb][5] = v1.y; q[cb][6] = v1.z; q[cb][7] = v1.w;
       const int srow = brow0[cb] + r;
-      sc[cb] = FMT == 0 ? *reinterpret_cast<const uint32_t*>(ssc + srow * 8 + 4 * half)
-                        : (uint32_t)*reinterpret_cast<const uint16_t*>(ssc + srow * 8 + 4 * half);
+      if (SS) {
+        const uint8_t* sp = s_ss + ((c / SUPER) & 1) * BROWS * 16 + srow * 16;
+        sc[cb] = FMT == 0 ? *reinterpret_cast<const uint32_t*>(sp + (c & 1) * 8 + 4 * half)
+                          : (uint32_t)*reinterpret_cast<const uint16_t*>(sp + (c & 3) * 4 + 2 * half);
+      } else {
+        sc[cb] = FMT == 0 ? *reinterpret_cast<const uint32_t*>(ssc + srow * 8 + 4 * half)
+                          : (uint32_t)*reinterpret_cast<const uint16_t*>(ssc + srow * 8 + 4 * half);
+      }
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -397,12 +433,12 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
   }
 }
 
-template <int FMT, int RB, int WM, bool GATEUP>
-static hipError_t launch_pre_shape(const ExpertGemmArgs& a, hipStream_t s) {
-  using Sh = PreShape<FMT, RB, WM, GATEUP>;
+template <int FMT, int RB, int WM, bool GATEUP, bool SS>
+static hipError_t launch_pre_ss(const ExpertGemmArgs& a, hipStream_t s) {
+  using Sh = PreShape<FMT, RB, WM, GATEUP, SS>;
   const int N = GATEUP ? a.I : a.H;
   const int ncol = (N + Sh::NCOLS - 1) / Sh::NCOLS;
-  auto kern = k_pre_gemm<FMT, RB, WM, GATEUP>;
+  auto kern = k_pre_gemm<FMT, RB, WM, GATEUP, SS>;
   static bool attr_set = false;  // one attribute call per instantiation and process
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -412,6 +448,15 @@ static hipError_t launch_pre_shape(const ExpertGemmArgs& a, hipStream_t s) {
   }
   hipLaunchKernelGGL(kern, dim3(ncol, a.tile_bound), dim3(kPreThreads), Sh::SMEM, s, a);
   return hipGetLastError();
+}
+
+// Super-staged scales when each scale row is a whole number of 16-byte pieces.
+template <int FMT, int RB, int WM, bool GATEUP>
+static hipError_t launch_pre_shape(const ExpertGemmArgs& a, hipStream_t s) {
+  const int K = GATEUP ? a.H : a.I;
+  const int sbytes = K / (FMT == 0 ? 16 : 32);
+  if (sbytes % 16 == 0) return launch_pre_ss<FMT, RB, WM, GATEUP, true>(a, s);
+  return launch_pre_ss<FMT, RB, WM, GATEUP, false>(a, s);
 }
 
 // Tile height MT -> (row blocks per wave, waves along M): 128 = 2 x 2, 64 = 1 x 2, 32 = 1 x 1.

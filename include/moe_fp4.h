@@ -202,7 +202,9 @@ int moe_debug_dequant_fp4(const moe_fp4_weight* w, int32_t expert, int32_t path,
 /* Profiling aid: stage boundaries of moe_layer_forward, in launch order. */
 enum {
   MOE_STAGE_BEGIN = 0,        /* before the first kernel of the call */
-  MOE_STAGE_ROUTED = 1,       /* after RMSNorm (if any), router GEMM and top-K */
+  MOE_STAGE_ROUTED = 1,       /* after RMSNorm (if any), the router GEMM and the top-K; with
+                                 few tokens the top-K runs fused with the dispatch build
+                                 and is counted in the next stage */
   MOE_STAGE_DISPATCHED = 2,   /* after the dispatch build */
   MOE_STAGE_GATE_UP = 3,      /* after the routed experts' gate+up (+SiLU*up) kernel */
   MOE_STAGE_DOWN = 4,         /* after the routed experts' down kernel */

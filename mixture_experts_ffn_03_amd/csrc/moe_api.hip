@@ -172,17 +172,10 @@ struct StageMarks {
   }
 };
 
-// Dispatch + experts + blend on an already-validated config.
-int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const int32_t* ids,
-                const float* w, const int32_t* err_tok, const moe_expert_weights* routed,
-                const moe_expert_weights* shared, const uint16_t* residual, uint16_t* out,
-                void* ws, hipStream_t s, const StageMarks& marks = StageMarks()) {
-  int path;
-  int r = choose_path(c, &path);
-  if (r != MOE_OK) return r;
-  const bool pre = path == MOE_PATH_PREFILL;
-  const int mt = pre ? prefill_mt(c) : kDecodeTile;
-
+DispatchArgs make_dispatch_args(const moe_config& c, const Layout& L, const int32_t* ids,
+                                const int32_t* err_tok, void* ws) {
+  int path = MOE_PATH_DECODE;
+  choose_path(c, &path);
   DispatchArgs d{};
   d.ids = ids;
   d.err_tok = err_tok;
@@ -195,8 +188,24 @@ int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const 
   d.K = c.top_k;
   d.E = c.num_experts;
   d.shared_rows = c.has_shared ? c.tokens : 0;
-  d.tile_h = mt;
-  MOE_HIP(launch_dispatch(d, s));
+  d.tile_h = path == MOE_PATH_PREFILL ? prefill_mt(c) : kDecodeTile;
+  return d;
+}
+
+// Dispatch (unless the caller already built it) + experts + blend on a validated config.
+int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const int32_t* ids,
+                const float* w, const int32_t* err_tok, const moe_expert_weights* routed,
+                const moe_expert_weights* shared, const uint16_t* residual, uint16_t* out,
+                void* ws, hipStream_t s, const StageMarks& marks = StageMarks(),
+                bool dispatched = false) {
+  int path;
+  int r = choose_path(c, &path);
+  if (r != MOE_OK) return r;
+  const bool pre = path == MOE_PATH_PREFILL;
+  const int mt = pre ? prefill_mt(c) : kDecodeTile;
+
+  const DispatchArgs d = make_dispatch_args(c, L, ids, err_tok, ws);
+  if (!dispatched) MOE_HIP(launch_dispatch(d, s));
   MOE_HIP(marks.mark(MOE_STAGE_DISPATCHED));
 
   ExpertGemmArgs a{};
@@ -266,13 +275,10 @@ int check_ws(const Layout& L, const void* ws, size_t bytes) {
   return MOE_OK;
 }
 
-int launch_route(const moe_config& c, const Layout& L, const uint16_t* x,
-                 const uint16_t* router_w, const float* logit_bias, const float* corr,
-                 const int32_t* token_ids, const int64_t* tid2eid, const float* logits_in,
-                 float* logits_out, int32_t* ids, float* w, void* ws, hipStream_t s) {
-  if (!logits_in)
-    MOE_HIP(launch_router_partial(x, router_w, at<double>(ws, L.partial), c.tokens,
-                                  c.num_experts, c.hidden, L.ks, L.hsplit, s));
+TopkArgs make_topk_args(const moe_config& c, const Layout& L, const float* logit_bias,
+                        const float* corr, const int32_t* token_ids, const int64_t* tid2eid,
+                        const float* logits_in, float* logits_out, int32_t* ids, float* w,
+                        void* ws) {
   TopkArgs t{};
   t.partial = logits_in ? nullptr : at<double>(ws, L.partial);
   t.ks = L.ks;
@@ -293,7 +299,31 @@ int launch_route(const moe_config& c, const Layout& L, const uint16_t* x,
   t.select = c.select_mode;
   t.renorm = c.renormalize;
   t.scaling = c.routed_scaling;
+  return t;
+}
+
+// Router GEMM (unless logits_in) + top-K. With fuse_dispatch and few tokens, the top-K
+// runs fused with the dispatch build and *dispatched is set; the stage mark ROUTED is
+// then recorded between the router GEMM and that kernel.
+int launch_route(const moe_config& c, const Layout& L, const uint16_t* x,
+                 const uint16_t* router_w, const float* logit_bias, const float* corr,
+                 const int32_t* token_ids, const int64_t* tid2eid, const float* logits_in,
+                 float* logits_out, int32_t* ids, float* w, void* ws, hipStream_t s,
+                 const StageMarks* marks = nullptr, bool* dispatched = nullptr) {
+  if (!logits_in)
+    MOE_HIP(launch_router_partial(x, router_w, at<double>(ws, L.partial), c.tokens,
+                                  c.num_experts, c.hidden, L.ks, L.hsplit, s));
+  const TopkArgs t = make_topk_args(c, L, logit_bias, corr, token_ids, tid2eid, logits_in,
+                                    logits_out, ids, w, ws);
+  if (dispatched && fused_topk_dispatch_fits(c.tokens, c.num_experts, c.top_k)) {
+    if (marks) MOE_HIP(marks->mark(MOE_STAGE_ROUTED));
+    const DispatchArgs d = make_dispatch_args(c, L, ids, t.err_tok, ws);
+    MOE_HIP(launch_topk_dispatch(t, d, s));
+    *dispatched = true;
+    return MOE_OK;
+  }
   MOE_HIP(launch_topk(t, s));
+  if (marks) MOE_HIP(marks->mark(MOE_STAGE_ROUTED));
   return MOE_OK;
 }
 
@@ -413,12 +443,13 @@ int moe_layer_forward(const moe_config* cfg, const uint16_t* x, const uint16_t* 
   }
   int32_t* ids = at<int32_t>(workspace, L.ids);
   float* w = at<float>(workspace, L.w);
+  bool dispatched = false;
   r = launch_route(c, L, x, router_w, logit_bias, correction_bias, token_ids, tid2eid, nullptr,
-                   dbg_logits, ids, w, workspace, stream);
+                   dbg_logits, ids, w, workspace, stream, &marks, &dispatched);
   if (r != MOE_OK) return r;
-  MOE_HIP(marks.mark(MOE_STAGE_ROUTED));
   r = run_experts(c, L, xe, ids, w, at<int32_t>(workspace, L.errtok), routed,
-                  c.has_shared ? shared : nullptr, residual, out, workspace, stream, marks);
+                  c.has_shared ? shared : nullptr, residual, out, workspace, stream, marks,
+                  dispatched);
   if (r != MOE_OK) return r;
   const size_t slots = (size_t)c.tokens * c.top_k;
   if (dbg_ids) MOE_HIP(hipMemcpyAsync(dbg_ids, ids, slots * 4, hipMemcpyDeviceToDevice, stream));

@@ -48,10 +48,11 @@ constexpr int kDecodeTile = 4;     // rows (tokens) per decode tile
 hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, uint16_t* out, int T, int H,
                           float eps, hipStream_t s);
 
-// Router GEMM split: few tokens use one block per expert row (ks = 1), many tokens a tiled
-// kernel with H split in ks slices of hsplit columns.
-constexpr int kRouterRowsMaxT = 64;
-constexpr int kRouterMaxSplit = 8;
+// Router GEMM split: H is summed in ks slices of hsplit columns (fp64 partials, added in
+// slice order by the top-K kernel); few tokens use the fp64-MFMA kernel, many tokens a
+// tiled fp64 kernel.
+constexpr int kRouterSmallMaxT = 64;  // tokens up to which the MFMA router runs
+constexpr int kRouterMaxSplit = 8;    // H slices of the router sum
 struct RouterPlan {
   int ks, hsplit;
 };
@@ -90,6 +91,13 @@ struct DispatchArgs {
   int T, K, E, shared_rows, tile_h;
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+
+// Top-K and dispatch fused in one block (few tokens: decode).
+constexpr int kFusedMaxTokens = 16;  // one block: beyond this, separate kernels are faster
+constexpr int kFusedMaxExperts = 256;
+constexpr int kFusedMaxSlots = 1024;
+bool fused_topk_dispatch_fits(int T, int E, int K);
+hipError_t launch_topk_dispatch(const TopkArgs& ta, const DispatchArgs& da, hipStream_t s);
 
 struct ExpertGemmArgs {
   const uint16_t* x;          // bf16 [T, H] expert input

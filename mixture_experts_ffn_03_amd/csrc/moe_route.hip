@@ -10,7 +10,7 @@
 // but vanishingly rare cases, whatever the summation order. That makes the expert choice
 // reproducible against any exact evaluation, which a plain fp32 accumulation (order-
 // dependent in the last bit) cannot promise at near-ties.
-#include "moe_device.h"
+#include "moe_select.h"
 
 namespace moe {
 
@@ -50,15 +50,15 @@ hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, uint16_t* ou
 // ---------------------------------------------------------------------------
 // Router GEMM, fp64 sums: partial[z][t][e] = sum_{h in slice z} x[t,h] * W_r[e,h].
 //
-// Few tokens (decode): one block per expert row. The block streams the row once with
-// 16-byte loads, and every thread dots its chunks with each token's activations; the
-// per-token sums are reduced across the block in a fixed order (one slice, z = 0).
+// Few tokens (decode, T <= 64): fp64 matrix cores. A block computes 16 experts x all
+// tokens (up to four 16-token fragments) over one H slice with v_mfma_f64_16x16x4_f64 on
+// exactly widened bf16 operands; its four waves take interleaved 32-wide K chunks and
+// are summed in a fixed order at the end. H is split over blocks so the grid fills the
+// chip (z = slice).
 //
 // Many tokens (prefill): 64 tokens x 64 experts per block with a 4x4 fp64 register
 // block per thread over LDS tiles, H split in z so that the grid fills the chip.
 // ---------------------------------------------------------------------------
-constexpr int kRowTok = 8;  // tokens per pass of the row kernel
-
 __device__ __forceinline__ void bf16x8_to_f64(const uint4& v, double (&o)[8]) {
   const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -68,47 +68,67 @@ __device__ __forceinline__ void bf16x8_to_f64(const uint4& v, double (&o)[8]) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_router_rows(const uint16_t* __restrict__ x,
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+// MF 16-token fragments. MFMA operand layout (16x16x4 f64): lane l holds A[l % 16][l / 16]
+// and B[l / 16][l % 16]; the result D[l / 16 + 4 v][l % 16] sits in element v. The
+// K index of (lane quad q, step s) inside a 32-wide chunk is 8q + s for both operands.
+template <int MF>
+__global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict__ x,
                                                      const uint16_t* __restrict__ w,
                                                      double* __restrict__ partial, int T, int E,
-                                                     int H) {
-  __shared__ double s_red[4][kRowTok];
-  const int e = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nchunk = H / 8;
-  const uint16_t* wrow = w + (size_t)e * H;
-  for (int t0 = 0; t0 < T; t0 += kRowTok) {
-    double acc[kRowTok];
+                                                     int H, int hsplit) {
+  __shared__ f64x4_t s_red[3][MF][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int idx = lane & 15, q = lane >> 4;
+  const int e0 = blockIdx.x * 16;
+  const int kb = blockIdx.z * hsplit;
+  const int ke = min(H, kb + hsplit);
+  const int eload = e0 + idx < E ? e0 + idx : 0;  // rows past E: results not stored
+  const uint16_t* wrow = w + (size_t)eload * H + 8 * q;
+  const uint16_t* xrow[MF];
+  bool tv[MF];
 #pragma unroll
-    for (int t = 0; t < kRowTok; ++t) acc[t] = 0.0;
-    for (int c = threadIdx.x; c < nchunk; c += 256) {
-      double wv[8];
-      bf16x8_to_f64(*reinterpret_cast<const uint4*>(wrow + c * 8), wv);
+  for (int m = 0; m < MF; ++m) {
+    const int t = m * 16 + idx;
+    tv[m] = t < T;
+    xrow[m] = x + (size_t)(tv[m] ? t : 0) * H + 8 * q;
+  }
+  f64x4_t acc[MF];
 #pragma unroll
-      for (int t = 0; t < kRowTok; ++t) {
-        if (t0 + t < T) {
-          double xv[8];
-          bf16x8_to_f64(*reinterpret_cast<const uint4*>(x + (size_t)(t0 + t) * H + c * 8), xv);
+  for (int m = 0; m < MF; ++m) acc[m] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  for (int k0 = kb + 32 * wave; k0 < ke; k0 += 128) {
+    double wd[8];
+    bf16x8_to_f64(*reinterpret_cast<const uint4*>(wrow + k0), wd);
+    double xd[MF][8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[t] = fma(xv[i], wv[i], acc[t]);
-        }
-      }
+    for (int m = 0; m < MF; ++m) {
+      const uint4 v = tv[m] ? *reinterpret_cast<const uint4*>(xrow[m] + k0) : make_uint4(0, 0, 0, 0);
+      bf16x8_to_f64(v, xd[m]);
     }
 #pragma unroll
-    for (int t = 0; t < kRowTok; ++t) {
+    for (int st = 0; st < 8; ++st)
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) acc[t] += __shfl_xor(acc[t], m, kWave);
-    }
-    if (lane == 0) {
+      for (int m = 0; m < MF; ++m)
+        acc[m] = __builtin_amdgcn_mfma_f64_16x16x4f64(xd[m][st], wd[st], acc[m], 0, 0, 0);
+  }
+  if (wave > 0) {
 #pragma unroll
-      for (int t = 0; t < kRowTok; ++t) s_red[wave][t] = acc[t];
+    for (int m = 0; m < MF; ++m) s_red[wave - 1][m][lane] = acc[m];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int e = e0 + idx;
+  if (e >= E) return;
+  double* p = partial + (size_t)blockIdx.z * T * E;
+#pragma unroll
+  for (int m = 0; m < MF; ++m) {
+    const f64x4_t sum = ((acc[m] + s_red[0][m][lane]) + s_red[1][m][lane]) + s_red[2][m][lane];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int t = m * 16 + q + 4 * v;
+      if (t < T) p[(size_t)t * E + e] = sum[v];
     }
-    __syncthreads();
-    if (threadIdx.x < kRowTok && t0 + threadIdx.x < T) {
-      const int t = threadIdx.x;
-      partial[(size_t)(t0 + t) * E + e] = (s_red[0][t] + s_red[1][t]) + (s_red[2][t] + s_red[3][t]);
-    }
-    __syncthreads();
   }
 }
 
@@ -181,17 +201,18 @@ __global__ __launch_bounds__(256) void k_router_tiled(const uint16_t* __restrict
 
 RouterPlan plan_router(int T, int E, int H) {
   RouterPlan r;
-  if (T <= kRouterRowsMaxT) {
-    r.ks = 1;
-    r.hsplit = H;
-    return r;
+  int ks;
+  if (T <= kRouterSmallMaxT) {
+    const int blocks = (E + 15) / 16;
+    ks = min((256 + blocks - 1) / blocks, min(kRouterMaxSplit, H / 32));
+    ks = max(ks, 1);
+    r.hsplit = ((H + ks - 1) / ks + 31) / 32 * 32;  // whole 32-wide chunks
+  } else {
+    const int blocks = ((E + kRe - 1) / kRe) * ((T + kRt - 1) / kRt);
+    ks = min((256 + blocks - 1) / blocks, min(kRouterMaxSplit, H / 64));
+    ks = max(ks, 1);
+    r.hsplit = ((H + ks - 1) / ks + kRk - 1) / kRk * kRk;
   }
-  const int blocks = ((E + kRe - 1) / kRe) * ((T + kRt - 1) / kRt);
-  int ks = (256 + blocks - 1) / blocks;
-  if (ks > kRouterMaxSplit) ks = kRouterMaxSplit;
-  if (ks > H / 64) ks = H / 64;
-  if (ks < 1) ks = 1;
-  r.hsplit = ((H + ks - 1) / ks + kRk - 1) / kRk * kRk;
   r.ks = (H + r.hsplit - 1) / r.hsplit;
   return r;
 }
@@ -199,8 +220,13 @@ RouterPlan plan_router(int T, int E, int H) {
 hipError_t launch_router_partial(const uint16_t* x, const uint16_t* w, double* partial, int T,
                                  int E, int H, int ks, int hsplit, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (T <= kRouterRowsMaxT) {
-    hipLaunchKernelGGL(k_router_rows, dim3(E), dim3(256), 0, s, x, w, partial, T, E, H);
+  if (T <= kRouterSmallMaxT) {
+    const dim3 grid((E + 15) / 16, 1, ks);
+    const int mf = (T + 15) / 16;
+    if (mf == 1) hipLaunchKernelGGL(k_router_mfma<1>, grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
+    else if (mf == 2) hipLaunchKernelGGL(k_router_mfma<2>, grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
+    else if (mf == 3) hipLaunchKernelGGL(k_router_mfma<3>, grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
+    else hipLaunchKernelGGL(k_router_mfma<4>, grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
   } else {
     dim3 grid((E + kRe - 1) / kRe, (T + kRt - 1) / kRt, ks);
     hipLaunchKernelGGL(k_router_tiled, grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
@@ -209,28 +235,8 @@ hipError_t launch_router_partial(const uint16_t* x, const uint16_t* w, double* p
 }
 
 // ---------------------------------------------------------------------------
-// Scores + top-K: one wavefront per token, the token's keys spread over the 64 lanes
-// (NPL per lane). Selection is k rounds of a wave-wide arg-max on a 64-bit composite
-// (order-preserving key bits << 32 | ~index): the largest key wins, equal keys go to
-// the lower expert index, -0 == +0, and NaN ranks below -inf.
+// Scores + top-K: one wavefront per token (topk_token), kTopkWaves tokens per block.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t ordered_key(float f) {
-  if (f != f) return 0u;                         // NaN: below everything
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;                  // -0 == +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ uint64_t composite(float key, int idx) {
-  return ((uint64_t)ordered_key(key) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
-}
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, m, kWave);
-  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 constexpr int kTopkWaves = 4;
 
 template <int NPL>
@@ -238,122 +244,10 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
   __shared__ float s_logit[kTopkWaves][kMaxExperts];
   __shared__ int s_id[kTopkWaves][kMaxTopK];
   __shared__ float s_w[kTopkWaves][kMaxTopK];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int t = blockIdx.x * kTopkWaves + wave;
   if (t >= a.T) return;  // whole wavefronts exit together
-  const int E = a.E, K = a.K;
-
-  float lg[NPL];
-  float key[NPL];
-  uint32_t taken = 0;
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const int e = lane + kWave * i;
-    float l = -__builtin_inff();
-    if (e < E) {
-      if (a.logits_in) {
-        l = a.logits_in[(size_t)t * E + e];
-      } else {
-        // the split-K partials: independent loads first, then a fixed-order sum
-        double pz[kRouterMaxSplit];
-#pragma unroll
-        for (int z = 0; z < kRouterMaxSplit; ++z)
-          pz[z] = z < a.ks ? a.partial[((size_t)z * a.T + t) * E + e] : 0.0;
-        double acc = 0.0;
-#pragma unroll
-        for (int z = 0; z < kRouterMaxSplit; ++z)
-          if (z < a.ks) acc += pz[z];
-        if (a.logit_bias) acc += (double)a.logit_bias[e];
-        l = (float)acc;
-      }
-      if (a.logits_out) a.logits_out[(size_t)t * E + e] = l;
-      s_logit[wave][e] = l;
-    } else {
-      taken |= 1u << i;  // padding is never selectable
-    }
-    lg[i] = l;
-    float k = l;
-    if (a.score == 1) {  // sigmoid: key = fp32(sigmoid) + correction bias (fp32 add)
-      const float sg = (float)(1.0 / (1.0 + exp(-(double)l)));
-      k = a.correction_bias && e < E ? sg + a.correction_bias[e] : sg;
-    }
-    key[i] = k;
-  }
-
-  // softmax normaliser over all experts (fp32): m = max, S = sum exp(l - m)
-  float m = -__builtin_inff(), S = 0.f;
-  if (a.score == 0) {
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) m = fmaxf(m, lg[i]);
-    m = wave_max(m);
-#pragma unroll
-    for (int i = 0; i < NPL; ++i)
-      if (lane + kWave * i < E) S += expf(lg[i] - m);
-    S = wave_sum(S);
-  }
-  __builtin_amdgcn_wave_barrier();
-
-  int err = 0;
-  if (a.select == 0) {
-    for (int j = 0; j < K; ++j) {
-      uint64_t best = 0;
-      bool have = false;
-#pragma unroll
-      for (int i = 0; i < NPL; ++i) {
-        if (!(taken & (1u << i))) {
-          const uint64_t c = composite(key[i], lane + kWave * i);
-          if (!have || c > best) { best = c; have = true; }
-        }
-      }
-      uint64_t g = best;
-#pragma unroll
-      for (int msk = 32; msk >= 1; msk >>= 1) {
-        const uint64_t o = shfl_xor_u64(g, msk);
-        g = o > g ? o : g;
-      }
-      const int idx = (int)(0xFFFFFFFFu - (uint32_t)g);
-      if ((idx & 63) == lane) taken |= 1u << (idx >> 6);
-      if (lane == 0) s_id[wave][j] = idx;
-    }
-  } else {  // hash routing: ids from the static table, no selection
-    const int64_t tok = a.token_ids[t];
-    const bool tok_ok = tok >= 0 && tok < a.vocab;
-    if (!tok_ok) err |= 2;
-    if (lane == 0) {
-      for (int j = 0; j < K; ++j) {
-        int id = -1;
-        if (tok_ok) {
-          const int64_t e = a.tid2eid[tok * K + j];
-          if (e >= 0 && e < E) id = (int)e;
-          else err |= 4;
-        }
-        s_id[wave][j] = id;
-      }
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-
-  if (lane == 0) {
-    float sum = 0.f;
-    for (int j = 0; j < K; ++j) {
-      const int id = s_id[wave][j];
-      float wj = 0.f;
-      if (id >= 0) {
-        const float l = s_logit[wave][id];
-        wj = a.score == 0 ? expf(l - m) / S : (float)(1.0 / (1.0 + exp(-(double)l)));
-      }
-      s_w[wave][j] = wj;
-      sum += wj;
-    }
-    for (int j = 0; j < K; ++j) {
-      float wj = s_w[wave][j];
-      if (a.renorm) wj = sum > 0.f ? wj / sum : 0.f;
-      a.w[(size_t)t * K + j] = wj * a.scaling;
-      a.ids[(size_t)t * K + j] = s_id[wave][j];
-    }
-    if (a.err_tok) a.err_tok[t] = err;
-  }
+  topk_token<NPL>(a, t, s_logit[wave], s_id[wave], s_w[wave], nullptr, nullptr);
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {

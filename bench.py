@@ -141,6 +141,24 @@ def summarize_trace(d, command):
         out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                    f"{float(r['TotalDurationNs']) / total:.1%} |")
+    # the routed experts' launches alone (a kernel symbol may also serve the shared expert)
+    trace = [r for r in _rocprof_rows(d, "kernel_trace.csv") if "moe::" in r["Kernel_Name"]]
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dur = {"gate_up": [], "down": []}
+    stage = None
+    for r in trace:
+        name = r["Kernel_Name"]
+        if "k_dispatch" in name:
+            stage = 0
+        elif stage is not None and stage < 2 and ("k_dec_" in name or "k_pre_gemm" in name):
+            dur["gate_up" if stage == 0 else "down"].append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            stage += 1
+    out += ["", "Routed experts' launches only (the first two expert kernels after each dispatch "
+            "build):", "", "| stage | launches | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
+    for k, v in dur.items():
+        if v:
+            out.append(f"| {k} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
     return "\n".join(out) + "\n"
 
 

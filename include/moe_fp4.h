@@ -83,14 +83,17 @@ enum {
 
 /* Expert-path choice (both paths compute the same function). */
 enum {
-  MOE_PATH_AUTO = 0,    /* decode when tokens*top_k/min(E, tokens*top_k) < 4 rows per expert */
-  MOE_PATH_DECODE = 1,  /* HBM-streaming GEMV kernels */
+  MOE_PATH_AUTO = 0,    /* decode when tokens*top_k/min(E, tokens*top_k) < 4 rows per expert
+                           (and the decode limit below holds), else prefill */
+  MOE_PATH_DECODE = 1,  /* HBM-streaming GEMV kernels (needs 4 * max(hidden, inter,
+                           shared_inter) * 2 bytes <= MOE_DECODE_MAX_LDS) */
   MOE_PATH_PREFILL = 2  /* expert-grouped MFMA GEMM kernels (needs hidden, inter % 64 == 0) */
 };
 
 /* Build limits (checked on the host). */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOP_K 32
+#define MOE_DECODE_MAX_LDS (160 * 1024) /* decode stages 4 activation rows per tile in LDS */
 
 /* One projection of a group of experts, in storage form (host struct, device pointers).
  *   packed       uint8 [experts, n, k/2]: byte j of a row holds code 2j in its low nibble

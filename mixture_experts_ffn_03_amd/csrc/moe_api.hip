@@ -141,7 +141,15 @@ T* at(void* ws, size_t off) {
 int choose_path(const moe_config& c, int* path) {
   const bool pre_ok = c.hidden % 64 == 0 && c.inter % 64 == 0 &&
                       (!c.has_shared || c.shared_inter % 64 == 0);
-  if (c.path == MOE_PATH_DECODE) { *path = MOE_PATH_DECODE; return MOE_OK; }
+  // decode stages a tile's activation rows in LDS: kTileTok rows of K bf16 in 160 KB
+  int kmax = c.hidden > c.inter ? c.hidden : c.inter;
+  if (c.has_shared && c.shared_inter > kmax) kmax = c.shared_inter;
+  const bool dec_ok = (long long)kTileTok * kmax * 2 <= kDecodeMaxLds;
+  if (c.path == MOE_PATH_DECODE) {
+    if (!dec_ok) return MOE_ERR_UNSUPPORTED;
+    *path = MOE_PATH_DECODE;
+    return MOE_OK;
+  }
   if (c.path == MOE_PATH_PREFILL) {
     if (!pre_ok) return MOE_ERR_UNSUPPORTED;
     *path = MOE_PATH_PREFILL;
@@ -150,7 +158,12 @@ int choose_path(const moe_config& c, int* path) {
   const int S = c.tokens * c.top_k;
   const int groups = S < c.num_experts ? S : c.num_experts;
   const bool many_rows = groups > 0 && S >= 4 * groups;
-  *path = (many_rows && pre_ok) ? MOE_PATH_PREFILL : MOE_PATH_DECODE;
+  if ((many_rows || !dec_ok) && pre_ok) {
+    *path = MOE_PATH_PREFILL;
+    return MOE_OK;
+  }
+  if (!dec_ok) return MOE_ERR_UNSUPPORTED;
+  *path = MOE_PATH_DECODE;
   return MOE_OK;
 }
 

@@ -7,24 +7,25 @@
 //
 // Design (gfx950): the grid is (block of output rows, expert tile); one tile is a run of
 // at most kDecodeTile tokens routed to one expert, so every weight byte of an active
-// expert is streamed from HBM once per tile whatever the batch. Each lane streams 16-byte
-// chunks (32 E2M1 codes) of a row with 128-bit loads; a group of LPR lanes covers one row
-// and a wave covers several rows, which keeps many independent loads in flight. Codes are decoded in
-// registers to exact bf16 with the gfx950 scaled convert (scale 1.0), dotted with the
-// bf16 activations by v_dot2_f32_bf16, and each 16- or 32-code block partial is
-// multiplied by its fp32 block scale. The scale bytes travel with the codes in the same
-// load round trip, and tile records carry their token ids, so a block waits on memory
-// twice: for its tile record, then for weights, scales and activations together. Rows
-// per pass shrink as tokens per tile grow, keeping register use within 256 VGPRs so that
-// 2 waves share each SIMD and hide HBM latency. The per-row sums are reduced across the lane group
-// by a transposing butterfly (no LDS), then gate/up pairs are combined into
-// SiLU(gate) * up (gate+up kernel) or written as the expert output (down kernel).
+// expert is streamed from HBM once per tile whatever the batch. The tile's activation rows
+// are first copied to LDS (bf16), so the streaming loop issues weight loads only. Each
+// lane streams 16-byte chunks (32 E2M1 codes) of a row with 128-bit loads; a group of LPR
+// lanes covers one row and a wave covers several rows per pass. The loop over (pass,
+// chunk) is software-pipelined: the loads of the next step are in flight while the codes
+// of the current one are decoded in registers to exact bf16 with the gfx950 scaled
+// convert (scale 1.0), dotted with the activations by v_dot2_f32_bf16, and each 16- or
+// 32-code block partial is multiplied by its fp32 block scale. The per-row sums of a pass
+// are reduced across the lane group by a transposing butterfly (no LDS), then gate/up
+// pairs are combined into SiLU(gate) * up (gate+up kernel) or written as the expert
+// output (down kernel). Rows per pass shrink as tokens per tile grow, keeping register
+// use within 256 VGPRs so that 2 waves share each SIMD; rows per wave (passes) grow when
+// the grid would otherwise run several short rounds of blocks.
 #include "moe_device.h"
 
 namespace moe {
 
-constexpr int kGateRowsPerWave = 8;   // gate rows (and as many up rows) per wave
-constexpr int kDownRowsPerWave = 16;  // down rows per wave
+constexpr int kGateRowsPerPass = 8;   // gate rows (and as many up rows) per wave pass
+constexpr int kDownRowsPerPass = 16;  // down rows per wave pass
 constexpr int kDecWaves = 4;
 
 __device__ __forceinline__ bool resolve_tile(const TileSource& src, const int32_t* row_token,
@@ -97,12 +98,13 @@ __device__ __forceinline__ void chunk_dot(const uint4& w, uint32_t sc,
   }
 }
 
+// Chunk c (32 codes) of the TT activation rows staged in LDS ([TT][K] bf16).
 template <int TT>
-__device__ __forceinline__ void load_act_chunk(const uint16_t* base, const int (&row)[TT],
-                                               int stride, int c, uint32_t (&xv)[TT][16]) {
+__device__ __forceinline__ void lds_act_chunk(const uint16_t* s_x, int K, int c,
+                                              uint32_t (&xv)[TT][16]) {
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
-    const uint4* p = reinterpret_cast<const uint4*>(base + (size_t)row[t] * stride + c * 32);
+    const uint4* p = reinterpret_cast<const uint4*>(s_x + (size_t)t * K + c * 32);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint4 v = p[q];
@@ -114,11 +116,43 @@ __device__ __forceinline__ void load_act_chunk(const uint16_t* base, const int (
   }
 }
 
+// Chunk c (32 codes) of the TT activation rows read straight from memory (rows[t] of src).
+template <int TT>
+__device__ __forceinline__ void global_act_chunk(const uint16_t* src, size_t stride,
+                                                 const int (&rows)[TT], int c,
+                                                 uint32_t (&xv)[TT][16]) {
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    const uint4* p = reinterpret_cast<const uint4*>(src + (size_t)rows[t] * stride + c * 32);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = p[q];
+      xv[t][4 * q + 0] = v.x;
+      xv[t][4 * q + 1] = v.y;
+      xv[t][4 * q + 2] = v.z;
+      xv[t][4 * q + 3] = v.w;
+    }
+  }
+}
+
+// Copy the tile's activation rows (src rows rows[t], t < TT) into LDS [TT][K].
+template <int TT>
+__device__ __forceinline__ void stage_activations(const uint16_t* src, size_t stride,
+                                                  const int (&rows)[TT], int K, uint16_t* s_x) {
+  const int pieces = K / 8;  // 16-byte pieces per row
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    const uint4* g = reinterpret_cast<const uint4*>(src + (size_t)rows[t] * stride);
+    uint4* l = reinterpret_cast<uint4*>(s_x + (size_t)t * K);
+    for (int c = threadIdx.x; c < pieces; c += blockDim.x) l[c] = g[c];
+  }
+  __syncthreads();
+}
+
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // Rows per pass: enough for every lane group of the wave to own a row, and few enough
-// that weights, activations and sums fit 256 VGPRs (2 waves per SIMD, 8 per CU, each
-// with 16 row loads of 16 bytes per lane in flight: about 128 KB per CU).
+// that two steps of weights, the activations and the sums fit 256 VGPRs (2 waves per SIMD).
 template <int TT, int LPR, int BASE>
 struct RowSet {
   static constexpr int G = kWave / LPR;
@@ -126,11 +160,48 @@ struct RowSet {
   static constexpr int R = R0 > G ? R0 : G;
 };
 
+// One pipeline step's weights: NI rows x M matrices (gate+up: 2, down: 1).
+template <int NI, int M>
+struct WStep {
+  uint4 w[NI][M];
+  uint32_t s[NI][M];
+};
+
+// Weight rows of one pipeline matrix set: packed codes and scales of up to two matrices
+// (gate+up: 2, down: 1), passed by value so that nothing lives in memory.
+struct WSrc {
+  const uint8_t* p0;
+  const uint8_t* p1;
+  const uint8_t* s0;
+  const uint8_t* s1;
+};
+
+// Loads of step `it` (pass it / nci, chunk-slot it % nci) of this lane; every address is
+// clamped to a valid row and chunk (out-of-range results are discarded).
+template <int FMT, int NI, int M, int G, int GR>
+__device__ __forceinline__ void load_step(const WSrc src, size_t row_bytes, int sbytes,
+                                          int n_base, int nmax, int sub, int lpr, int nci,
+                                          int nchunk, int it, WStep<NI, M>& st) {
+  const int pass = it / nci, ci = it - pass * nci;
+  const int c = min(sub + ci * lpr, nchunk - 1);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int n = min(n_base + pass * GR + G * i, nmax);
+    st.w[i][0] = *reinterpret_cast<const uint4*>(src.p0 + (size_t)n * row_bytes + c * 16);
+    st.s[i][0] = load_chunk_scales<FMT>(src.s0 + (size_t)n * sbytes, c);
+    if (M > 1) {
+      st.w[i][M - 1] = *reinterpret_cast<const uint4*>(src.p1 + (size_t)n * row_bytes + c * 16);
+      st.s[i][M - 1] = load_chunk_scales<FMT>(src.s1 + (size_t)n * sbytes, c);
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------- gate+up
-template <int FMT, int TT, int LPR>
-__device__ __forceinline__ void gate_up_body(const ExpertGemmArgs& a, const Tile& tile) {
+template <int FMT, int TT, int LPR, bool STAGED>
+__device__ __forceinline__ void gate_up_body(const ExpertGemmArgs& a, const Tile& tile, int rpw,
+                                             uint16_t* s_x) {
   constexpr int G = kWave / LPR;
-  constexpr int GR = RowSet<TT, LPR, kGateRowsPerWave>::R;  // gate rows per pass
+  constexpr int GR = RowSet<TT, LPR, kGateRowsPerPass>::R;  // gate rows per pass
   constexpr int NI = GR / G;
   constexpr int NV = 2 * NI * TT;
   static_assert(NV <= LPR, "one reduced value per lane expected");
@@ -141,42 +212,36 @@ __device__ __forceinline__ void gate_up_body(const ExpertGemmArgs& a, const Tile
   const int nchunk = H / 32;
   const size_t row_bytes = (size_t)H / 2;
   const int sbytes = H / (FMT == 0 ? 16 : 32);
-  const uint8_t* gp = a.gate.packed + (size_t)e * I * row_bytes;
-  const uint8_t* upp = a.up.packed + (size_t)e * I * row_bytes;
-  const uint8_t* gs = a.gate.scales + (size_t)e * I * sbytes;
-  const uint8_t* us = a.up.scales + (size_t)e * I * sbytes;
+  const WSrc src{a.gate.packed + (size_t)e * I * row_bytes, a.up.packed + (size_t)e * I * row_bytes,
+                 a.gate.scales + (size_t)e * I * sbytes, a.up.scales + (size_t)e * I * sbytes};
   const float gsg = FMT == 0 ? a.gate.global[e] : 1.0f;
   const float gsu = FMT == 0 ? a.up.global[e] : 1.0f;
 
-  int row[TT];
+  const int nwave0 = blockIdx.x * (kDecWaves * rpw) + wave * rpw;
+  const int nci = (nchunk + LPR - 1) / LPR;
+  const int total = (rpw / GR) * nci;
+  // the first weights are requested before the activations are staged (two round trips
+  // in parallel instead of in sequence)
+  WStep<NI, 2> s0, s1;
+  const int nbase = nwave0 + grp;
+  load_step<FMT, NI, 2, G, GR>(src, row_bytes, sbytes, nbase, I - 1, sub, LPR, nci, nchunk, 0, s0);
+  int rows[TT];
 #pragma unroll
-  for (int t = 0; t < TT; ++t) row[t] = tile.tok[t < tile.count ? t : 0];
+  for (int t = 0; t < TT; ++t) rows[t] = t < tile.count ? tile.tok[t] : tile.tok[0];
+  // (a single step per wave has nothing to overlap: it reads the activations directly)
+  if (STAGED) stage_activations<TT>(a.x, (size_t)H, rows, H, s_x);
+  float acc[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) acc[v] = 0.f;
 
-  const int nwave0 = blockIdx.x * (kDecWaves * kGateRowsPerWave) + wave * kGateRowsPerWave;
-#pragma unroll 1
-  for (int r0 = 0; r0 < kGateRowsPerWave; r0 += GR) {
-    float acc[NV];
-#pragma unroll
-    for (int v = 0; v < NV; ++v) acc[v] = 0.f;
-#pragma unroll 1
-    for (int c = sub; c < nchunk; c += LPR) {
-      uint4 wv[NI][2];
-      uint32_t sv[NI][2];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int n = nwave0 + r0 + grp + G * i;
-        if (n < I) {
-          wv[i][0] = *reinterpret_cast<const uint4*>(gp + (size_t)n * row_bytes + c * 16);
-          wv[i][1] = *reinterpret_cast<const uint4*>(upp + (size_t)n * row_bytes + c * 16);
-          sv[i][0] = load_chunk_scales<FMT>(gs + (size_t)n * sbytes, c);
-          sv[i][1] = load_chunk_scales<FMT>(us + (size_t)n * sbytes, c);
-        } else {
-          wv[i][0] = wv[i][1] = make_uint4(0, 0, 0, 0);
-          sv[i][0] = sv[i][1] = 0;
-        }
-      }
+  // consume step it: dot products, and at the end of a pass the reduction and the store
+  auto consume = [&](int it, const WStep<NI, 2>& st) {
+    const int pass = it / nci, ci = it - pass * nci;
+    const int c = sub + ci * LPR;
+    if (c < nchunk) {
       uint32_t xv[TT][16];
-      load_act_chunk<TT>(a.x, row, H, c, xv);
+      if (STAGED) lds_act_chunk<TT>(s_x, H, c, xv);
+      else global_act_chunk<TT>(a.x, (size_t)H, rows, c, xv);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
 #pragma unroll
@@ -184,43 +249,75 @@ __device__ __forceinline__ void gate_up_body(const ExpertGemmArgs& a, const Tile
           float r[TT];
 #pragma unroll
           for (int t = 0; t < TT; ++t) r[t] = 0.f;
-          chunk_dot<FMT, TT>(wv[i][gu], sv[i][gu], xv, r);
+          chunk_dot<FMT, TT>(st.w[i][gu], st.s[i][gu], xv, r);
 #pragma unroll
           for (int t = 0; t < TT; ++t) acc[((i * TT + t) << 1) | gu] += r[t];
         }
       }
     }
-    group_reduce_transpose<NV, LPR>(acc, lane);
-    // each lane holds one complete sum; gate/up partners differ in the lane bit of the
-    // last halving step, duplicates in the bits below it
-    constexpr int kPair = LPR / NV;
-    const float other = shfl_xor_f(acc[0], kPair);
-    const int idx = reduced_index<NV, LPR>(lane, 0);
-    if ((idx & 1) == 0 && (sub & (kPair - 1)) == 0) {
-      const int q = idx >> 1, i = q / TT, t = q % TT;
-      const int n = nwave0 + r0 + grp + G * i;
-      if (t < tile.count && n < I) {
-        const float g = acc[0] * gsg, u = other * gsu;
-        a.h[(size_t)(tile.row0 + t) * a.h_stride + n] = f32_to_bf16(silu(g) * u);
+    if (ci == nci - 1) {
+      group_reduce_transpose<NV, LPR>(acc, lane);
+      // each lane holds one complete sum; gate/up partners differ in the lane bit of the
+      // last halving step, duplicates in the bits below it
+      constexpr int kPair = LPR / NV;
+      const float other = shfl_xor_f(acc[0], kPair);
+      const int idx = reduced_index<NV, LPR>(lane, 0);
+      if ((idx & 1) == 0 && (sub & (kPair - 1)) == 0) {
+        const int q = idx >> 1, i = q / TT, t = q % TT;
+        const int n = nwave0 + pass * GR + grp + G * i;
+        if (t < tile.count && n < I) {
+          const float g = acc[0] * gsg, u = other * gsu;
+          a.h[(size_t)(tile.row0 + t) * a.h_stride + n] = f32_to_bf16(silu(g) * u);
+        }
       }
+#pragma unroll
+      for (int v = 0; v < NV; ++v) acc[v] = 0.f;
     }
+  };
+
+  if (!STAGED) {  // one step
+    consume(0, s0);
+    return;
+  }
+  // two register sets renamed by a 2-step unroll (a copy of a set in flight would wait)
+#pragma unroll 1
+  for (int it = 0; it < total; it += 2) {
+    load_step<FMT, NI, 2, G, GR>(src, row_bytes, sbytes, nbase, I - 1, sub, LPR, nci, nchunk,
+                                 min(it + 1, total - 1), s1);
+    consume(it, s0);
+    if (it + 1 >= total) break;
+    load_step<FMT, NI, 2, G, GR>(src, row_bytes, sbytes, nbase, I - 1, sub, LPR, nci, nchunk,
+                                 min(it + 2, total - 1), s0);
+    consume(it + 1, s1);
   }
 }
 
 template <int FMT, int LPR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_dec_gate_up(ExpertGemmArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_dec_gate_up(ExpertGemmArgs a, int rpw) {
+  extern __shared__ __align__(16) uint16_t s_x[];
   Tile tile;
   if (!resolve_tile(a.src, a.row_token, blockIdx.y, tile)) return;
-  if (tile.count == 1) gate_up_body<FMT, 1, LPR>(a, tile);
-  else if (tile.count == 2) gate_up_body<FMT, 2, LPR>(a, tile);
-  else gate_up_body<FMT, 4, LPR>(a, tile);
+  if (blockIdx.x * kDecWaves * rpw >= a.I) return;
+  // one step per wave (one pass, one chunk per lane and row): no staging, no pipeline
+  const bool one = rpw == kGateRowsPerPass && a.H / 32 <= LPR;
+  if (tile.count == 1) {
+    if (one) gate_up_body<FMT, 1, LPR, false>(a, tile, rpw, s_x);
+    else gate_up_body<FMT, 1, LPR, true>(a, tile, rpw, s_x);
+  } else if (tile.count == 2) {
+    if (one) gate_up_body<FMT, 2, LPR, false>(a, tile, rpw, s_x);
+    else gate_up_body<FMT, 2, LPR, true>(a, tile, rpw, s_x);
+  } else {
+    // four tokens halve the rows per pass: two steps, pipelined
+    gate_up_body<FMT, 4, LPR, true>(a, tile, rpw, s_x);
+  }
 }
 
 // ----------------------------------------------------------------------------- down
-template <int FMT, int TT, int LPR>
-__device__ __forceinline__ void down_body(const ExpertGemmArgs& a, const Tile& tile) {
+template <int FMT, int TT, int LPR, bool STAGED>
+__device__ __forceinline__ void down_body(const ExpertGemmArgs& a, const Tile& tile, int rpw,
+                                          uint16_t* s_x) {
   constexpr int G = kWave / LPR;
-  constexpr int DR = RowSet<TT, LPR, kDownRowsPerWave>::R;  // rows per pass
+  constexpr int DR = RowSet<TT, LPR, kDownRowsPerPass>::R;  // rows per pass
   constexpr int NI = DR / G;
   constexpr int NV = NI * TT;
   static_assert(NV <= LPR, "one reduced value per lane expected");
@@ -231,66 +328,88 @@ __device__ __forceinline__ void down_body(const ExpertGemmArgs& a, const Tile& t
   const int nchunk = I / 32;
   const size_t row_bytes = (size_t)I / 2;
   const int sbytes = I / (FMT == 0 ? 16 : 32);
-  const uint8_t* dp = a.down.packed + (size_t)e * H * row_bytes;
-  const uint8_t* ds = a.down.scales + (size_t)e * H * sbytes;
+  const WSrc src{a.down.packed + (size_t)e * H * row_bytes, nullptr,
+                 a.down.scales + (size_t)e * H * sbytes, nullptr};
   const float gsd = FMT == 0 ? a.down.global[e] : 1.0f;
 
-  int row[TT];
+  const int nwave0 = blockIdx.x * (kDecWaves * rpw) + wave * rpw;
+  const int nci = (nchunk + LPR - 1) / LPR;
+  const int total = (rpw / DR) * nci;
+  WStep<NI, 1> s0, s1;
+  const int nbase = nwave0 + grp;
+  load_step<FMT, NI, 1, G, DR>(src, row_bytes, sbytes, nbase, H - 1, sub, LPR, nci, nchunk, 0, s0);
+  int rows[TT];
 #pragma unroll
-  for (int t = 0; t < TT; ++t) row[t] = tile.row0 + (t < tile.count ? t : 0);
+  for (int t = 0; t < TT; ++t) rows[t] = tile.row0 + (t < tile.count ? t : 0);
+  if (STAGED) stage_activations<TT>(a.h, (size_t)a.h_stride, rows, I, s_x);
+  float acc[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) acc[v] = 0.f;
 
-  const int nwave0 = blockIdx.x * (kDecWaves * kDownRowsPerWave) + wave * kDownRowsPerWave;
-#pragma unroll 1
-  for (int r0 = 0; r0 < kDownRowsPerWave; r0 += DR) {
-    float acc[NV];
-#pragma unroll
-    for (int v = 0; v < NV; ++v) acc[v] = 0.f;
-#pragma unroll 1
-    for (int c = sub; c < nchunk; c += LPR) {
-      uint4 wv[NI];
-      uint32_t sv[NI];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int n = nwave0 + r0 + grp + G * i;
-        if (n < H) {
-          wv[i] = *reinterpret_cast<const uint4*>(dp + (size_t)n * row_bytes + c * 16);
-          sv[i] = load_chunk_scales<FMT>(ds + (size_t)n * sbytes, c);
-        } else {
-          wv[i] = make_uint4(0, 0, 0, 0);
-          sv[i] = 0;
-        }
-      }
+  auto consume = [&](int it, const WStep<NI, 1>& st) {
+    const int pass = it / nci, ci = it - pass * nci;
+    const int c = sub + ci * LPR;
+    if (c < nchunk) {
       uint32_t xv[TT][16];
-      load_act_chunk<TT>(a.h, row, a.h_stride, c, xv);
+      if (STAGED) lds_act_chunk<TT>(s_x, I, c, xv);
+      else global_act_chunk<TT>(a.h, (size_t)a.h_stride, rows, c, xv);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         float r[TT];
 #pragma unroll
         for (int t = 0; t < TT; ++t) r[t] = 0.f;
-        chunk_dot<FMT, TT>(wv[i], sv[i], xv, r);
+        chunk_dot<FMT, TT>(st.w[i][0], st.s[i][0], xv, r);
 #pragma unroll
         for (int t = 0; t < TT; ++t) acc[i * TT + t] += r[t];
       }
     }
-    group_reduce_transpose<NV, LPR>(acc, lane);
-    constexpr int kDup = LPR / NV;
-    const int idx = reduced_index<NV, LPR>(lane, 0);
-    if ((sub & (kDup - 1)) == 0) {
-      const int i = idx / TT, t = idx % TT;
-      const int n = nwave0 + r0 + grp + G * i;
-      if (t < tile.count && n < H)
-        reinterpret_cast<float*>(a.y)[(size_t)(tile.row0 + t) * H + n] = acc[0] * gsd;
+    if (ci == nci - 1) {
+      group_reduce_transpose<NV, LPR>(acc, lane);
+      constexpr int kDup = LPR / NV;
+      const int idx = reduced_index<NV, LPR>(lane, 0);
+      if ((sub & (kDup - 1)) == 0) {
+        const int i = idx / TT, t = idx % TT;
+        const int n = nwave0 + pass * DR + grp + G * i;
+        if (t < tile.count && n < H)
+          reinterpret_cast<float*>(a.y)[(size_t)(tile.row0 + t) * H + n] = acc[0] * gsd;
+      }
+#pragma unroll
+      for (int v = 0; v < NV; ++v) acc[v] = 0.f;
     }
+  };
+
+  if (!STAGED) {  // one step
+    consume(0, s0);
+    return;
+  }
+#pragma unroll 1
+  for (int it = 0; it < total; it += 2) {
+    load_step<FMT, NI, 1, G, DR>(src, row_bytes, sbytes, nbase, H - 1, sub, LPR, nci, nchunk,
+                                 min(it + 1, total - 1), s1);
+    consume(it, s0);
+    if (it + 1 >= total) break;
+    load_step<FMT, NI, 1, G, DR>(src, row_bytes, sbytes, nbase, H - 1, sub, LPR, nci, nchunk,
+                                 min(it + 2, total - 1), s0);
+    consume(it + 1, s1);
   }
 }
 
 template <int FMT, int LPR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_dec_down(ExpertGemmArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_dec_down(ExpertGemmArgs a, int rpw) {
+  extern __shared__ __align__(16) uint16_t s_x[];
   Tile tile;
   if (!resolve_tile(a.src, a.row_token, blockIdx.y, tile)) return;
-  if (tile.count == 1) down_body<FMT, 1, LPR>(a, tile);
-  else if (tile.count == 2) down_body<FMT, 2, LPR>(a, tile);
-  else down_body<FMT, 4, LPR>(a, tile);
+  if (blockIdx.x * kDecWaves * rpw >= a.H) return;
+  const bool one = rpw == kDownRowsPerPass && a.I / 32 <= LPR;
+  if (tile.count == 1) {
+    if (one) down_body<FMT, 1, LPR, false>(a, tile, rpw, s_x);
+    else down_body<FMT, 1, LPR, true>(a, tile, rpw, s_x);
+  } else if (tile.count == 2) {
+    if (one) down_body<FMT, 2, LPR, false>(a, tile, rpw, s_x);
+    else down_body<FMT, 2, LPR, true>(a, tile, rpw, s_x);
+  } else {
+    down_body<FMT, 4, LPR, true>(a, tile, rpw, s_x);
+  }
 }
 
 // Lanes per row for a row of `nchunk` 16-byte chunks: the widest group that divides the
@@ -303,31 +422,68 @@ static int pick_lpr(int nchunk) {
   return 8;
 }
 
-#define MOE_DISPATCH_LPR(KERNEL, FMT, LPR, GRID, S, A)                                  \
-  switch (LPR) {                                                                       \
-    case 64: hipLaunchKernelGGL((KERNEL<FMT, 64>), GRID, dim3(256), 0, S, A); break;   \
-    case 32: hipLaunchKernelGGL((KERNEL<FMT, 32>), GRID, dim3(256), 0, S, A); break;   \
-    case 16: hipLaunchKernelGGL((KERNEL<FMT, 16>), GRID, dim3(256), 0, S, A); break;   \
-    default: hipLaunchKernelGGL((KERNEL<FMT, 8>), GRID, dim3(256), 0, S, A); break;    \
+// Rows per wave: one pass per wave unless the grid would run several short rounds of
+// blocks (few tiles): then up to four passes, pipelined inside the wave.
+#ifndef MOE_DEC_PASS_DIV
+#define MOE_DEC_PASS_DIV 3000
+#endif
+static int pick_rows_per_wave(int base, int n, int tile_bound) {
+  const int blocks1 = ((n + kDecWaves * base - 1) / (kDecWaves * base)) * tile_bound;
+  int m = blocks1 / MOE_DEC_PASS_DIV;
+  m = m < 1 ? 1 : (m > 4 ? 4 : m);
+  return base * m;
+}
+
+// LDS for the staged activations: kTileTok rows of K bf16 (beyond 64 KB the kernel's
+// limit is raised once per instantiation; the host caps K so that it fits 160 KB).
+static hipError_t raise_lds(const void* kern, size_t smem, bool& done) {
+  if (smem <= 65536 || done) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e == hipSuccess) done = true;
+  return e;
+}
+
+template <int FMT, int LPR>
+static void launch_gu(const ExpertGemmArgs& a, int rpw, hipStream_t s) {
+  const dim3 grid((a.I + kDecWaves * rpw - 1) / (kDecWaves * rpw), a.tile_bound);
+  const size_t smem = (size_t)kTileTok * a.H * sizeof(uint16_t);
+  static bool raised = false;
+  if (raise_lds(reinterpret_cast<const void*>(k_dec_gate_up<FMT, LPR>), smem, raised) != hipSuccess) return;
+  hipLaunchKernelGGL((k_dec_gate_up<FMT, LPR>), grid, dim3(256), smem, s, a, rpw);
+}
+
+template <int FMT, int LPR>
+static void launch_dn(const ExpertGemmArgs& a, int rpw, hipStream_t s) {
+  const dim3 grid((a.H + kDecWaves * rpw - 1) / (kDecWaves * rpw), a.tile_bound);
+  const size_t smem = (size_t)kTileTok * a.I * sizeof(uint16_t);
+  static bool raised = false;
+  if (raise_lds(reinterpret_cast<const void*>(k_dec_down<FMT, LPR>), smem, raised) != hipSuccess) return;
+  hipLaunchKernelGGL((k_dec_down<FMT, LPR>), grid, dim3(256), smem, s, a, rpw);
+}
+
+#define MOE_DISPATCH_LPR(LAUNCH, FMT, LPR, A, RPW, S)     \
+  switch (LPR) {                                          \
+    case 64: LAUNCH<FMT, 64>(A, RPW, S); break;           \
+    case 32: LAUNCH<FMT, 32>(A, RPW, S); break;           \
+    case 16: LAUNCH<FMT, 16>(A, RPW, S); break;           \
+    default: LAUNCH<FMT, 8>(A, RPW, S); break;            \
   }
 
 hipError_t launch_decode_gate_up(const ExpertGemmArgs& a, hipStream_t s) {
   if (a.tile_bound <= 0) return hipSuccess;
-  const int rows = kDecWaves * kGateRowsPerWave;
-  const dim3 grid((a.I + rows - 1) / rows, a.tile_bound);
+  const int rpw = pick_rows_per_wave(kGateRowsPerPass, a.I, a.tile_bound);
   const int lpr = pick_lpr(a.H / 32);
-  if (a.gate.fmt == 0) { MOE_DISPATCH_LPR(k_dec_gate_up, 0, lpr, grid, s, a); }
-  else { MOE_DISPATCH_LPR(k_dec_gate_up, 1, lpr, grid, s, a); }
+  if (a.gate.fmt == 0) { MOE_DISPATCH_LPR(launch_gu, 0, lpr, a, rpw, s); }
+  else { MOE_DISPATCH_LPR(launch_gu, 1, lpr, a, rpw, s); }
   return hipGetLastError();
 }
 
 hipError_t launch_decode_down(const ExpertGemmArgs& a, hipStream_t s) {
   if (a.tile_bound <= 0) return hipSuccess;
-  const int rows = kDecWaves * kDownRowsPerWave;
-  const dim3 grid((a.H + rows - 1) / rows, a.tile_bound);
+  const int rpw = pick_rows_per_wave(kDownRowsPerPass, a.H, a.tile_bound);
   const int lpr = pick_lpr(a.I / 32);
-  if (a.down.fmt == 0) { MOE_DISPATCH_LPR(k_dec_down, 0, lpr, grid, s, a); }
-  else { MOE_DISPATCH_LPR(k_dec_down, 1, lpr, grid, s, a); }
+  if (a.down.fmt == 0) { MOE_DISPATCH_LPR(launch_dn, 0, lpr, a, rpw, s); }
+  else { MOE_DISPATCH_LPR(launch_dn, 1, lpr, a, rpw, s); }
   return hipGetLastError();
 }
 

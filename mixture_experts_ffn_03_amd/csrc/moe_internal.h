@@ -44,6 +44,7 @@ struct TileSource {
 constexpr int kMaxExperts = 1024;  // MOE_MAX_EXPERTS
 constexpr int kMaxTopK = 32;       // MOE_MAX_TOP_K
 constexpr int kDecodeTile = 4;     // rows (tokens) per decode tile
+constexpr int kDecodeMaxLds = 160 * 1024;  // staged activations of a decode tile
 
 hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, uint16_t* out, int T, int H,
                           float eps, hipStream_t s);

@@ -70,9 +70,13 @@ enum {
 
 /* Routing score (MoE module page: doc of correction_bias_dev; constructor page: top-K kernels). */
 enum {
-  MOE_SCORE_SOFTMAX = 0, /* key = logit; weight = softmax probability */
-  MOE_SCORE_SIGMOID = 1  /* key = fp32(sigmoid(logit)) + correction_bias (selection only);
-                            weight = sigmoid(logit) */
+  MOE_SCORE_SOFTMAX = 0,       /* key = logit; weight = softmax probability */
+  MOE_SCORE_SIGMOID = 1,       /* key = fp32(sigmoid(logit)) + correction_bias (selection only);
+                                  weight = sigmoid(logit) */
+  MOE_SCORE_SQRT_SOFTPLUS = 2  /* key = fp32(sqrt(softplus(logit))) + correction_bias
+                                  (selection only); weight = sqrt(softplus(logit)) (the
+                                  DeepSeek-V4 sqrtsoftplus top-K kernels of the constructor
+                                  page); the score is evaluated in fp64, rounded once */
 };
 
 /* Expert selection (MoE module page: doc of tid2eid_dev). */

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe_fp4.so")
 
 MOE_OK = 0
 FMT_NVFP4, FMT_MXFP4 = 0, 1
-SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
+SCORE_SOFTMAX, SCORE_SIGMOID, SCORE_SQRT_SOFTPLUS = 0, 1, 2
 SELECT_TOPK, SELECT_HASH = 0, 1
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 DEVERR_EXPERT_ID, DEVERR_TOKEN_ID, DEVERR_TABLE = 1, 2, 4

@@ -86,7 +86,8 @@ int check_config(const moe_config* c) {
   if (c->num_experts <= 0 || c->top_k < 1 || c->top_k > c->num_experts) return MOE_ERR_INVALID_ARG;
   if (c->num_experts > MOE_MAX_EXPERTS || c->top_k > MOE_MAX_TOP_K) return MOE_ERR_UNSUPPORTED;
   if (c->inter <= 0 || c->inter % 32 != 0) return MOE_ERR_INVALID_ARG;
-  if (c->score_mode != MOE_SCORE_SOFTMAX && c->score_mode != MOE_SCORE_SIGMOID)
+  if (c->score_mode != MOE_SCORE_SOFTMAX && c->score_mode != MOE_SCORE_SIGMOID &&
+      c->score_mode != MOE_SCORE_SQRT_SOFTPLUS)
     return MOE_ERR_INVALID_ARG;
   if (c->select_mode != MOE_SELECT_TOPK && c->select_mode != MOE_SELECT_HASH)
     return MOE_ERR_INVALID_ARG;
@@ -297,7 +298,7 @@ TopkArgs make_topk_args(const moe_config& c, const Layout& L, const float* logit
   t.ks = L.ks;
   t.logits_in = logits_in;
   t.logit_bias = logit_bias;
-  t.correction_bias = c.score_mode == MOE_SCORE_SIGMOID ? corr : nullptr;
+  t.correction_bias = c.score_mode != MOE_SCORE_SOFTMAX ? corr : nullptr;
   t.token_ids = token_ids;
   t.tid2eid = tid2eid;
   t.vocab = c.vocab;

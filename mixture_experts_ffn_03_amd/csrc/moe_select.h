@@ -52,6 +52,17 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return max_u64(max_u64(r[0], r[1]), max_u64(r[2], r[3]));
 }
 
+// Per-expert score of the sigmoid (1) and sqrt-softplus (2) modes, in fp64: rounded once
+// to fp32 by the caller, it is the correctly rounded value in all but rare cases, so the
+// selection is reproducible on any platform. softplus(l) = ln(1 + e^l) is evaluated as
+// l + log1p(e^-l) for l > 0 and log1p(e^l) otherwise (no overflow).
+__device__ __forceinline__ double score_f64(int score, float logit) {
+  const double l = (double)logit;
+  if (score == 1) return 1.0 / (1.0 + exp(-l));
+  const double sp = l > 0.0 ? l + log1p(exp(-l)) : log1p(exp(l));
+  return sqrt(sp);
+}
+
 // ---------------------------------------------------------------------------
 // Scores + top-K of token t by one wavefront, its E keys spread over the 64 lanes (NPL
 // per lane). Selection is k rounds of a wave-wide arg-max on the composite. s_logit
@@ -111,8 +122,8 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, int t, float* s_lo
       lg[i] = -__builtin_inff();  // padding: never selectable, no softmax mass
     }
     float k = lg[i];
-    if (a.score == 1) {  // sigmoid: key = fp32(sigmoid) + correction bias (fp32 add)
-      const float sg = (float)(1.0 / (1.0 + exp(-(double)lg[i])));
+    if (a.score != 0) {  // sigmoid / sqrt-softplus: key = fp32(score) + correction bias
+      const float sg = (float)score_f64(a.score, lg[i]);
       k = a.correction_bias ? sg + cbias[i] : sg;
     }
     key[i] = k;
@@ -169,7 +180,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, int t, float* s_lo
   float wj = 0.f;
   if (lane < K && my_id >= 0) {
     const float l = s_logit[my_id];
-    wj = a.score == 0 ? expf(l - m) / S : (float)(1.0 / (1.0 + exp(-(double)l)));
+    wj = a.score == 0 ? expf(l - m) / S : (float)score_f64(a.score, l);
   }
   if (a.renorm) {
     const float sum = wave_sum(wj);

@@ -38,6 +38,7 @@ MXFP4 = 1
 
 SOFTMAX = 0
 SIGMOID = 1
+SQRT_SOFTPLUS = 2
 
 TOPK = 0
 HASH = 1

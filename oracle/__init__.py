@@ -17,7 +17,7 @@ the sigmoid selection key), which are rounded to fp32 exactly as defined.
 Layer (for every token t, top-k slots j):
     x_e      = bf16(RMSNorm(x))      if a pre-expert norm is configured, else x
     logits   = fp32(x . W_r^T + logit_bias)               (router sees raw x)
-    ids, w   = select(score(logits))                       (softmax | sigmoid+bias | hash)
+    ids, w   = select(score(logits))    (softmax | sigmoid+bias | sqrt-softplus+bias | hash)
     y_{t,j}  = W_d[e] . (SiLU(W_g[e] . x_e[t]) * (W_u[e] . x_e[t]))
     out[t]   = residual[t] + sum_j w[t,j] * y_{t,j} + y_shared[t]
 
@@ -35,6 +35,7 @@ NVFP4 = 0
 MXFP4 = 1
 SOFTMAX = 0
 SIGMOID = 1
+SQRT_SOFTPLUS = 2
 TOPK = 0
 HASH = 1
 
@@ -187,6 +188,37 @@ def sigmoid_key(logits: np.ndarray, correction_bias: Optional[np.ndarray]) -> np
     return (s + np.asarray(correction_bias, dtype=np.float32)).astype(np.float32)
 
 
+def sqrt_softplus(logits: np.ndarray) -> np.ndarray:
+    """sqrt(softplus(l)) = sqrt(ln(1 + e^l)) in fp64 (softplus via logaddexp, no overflow).
+
+    The sqrt-softplus routing score of the constructor page (the DeepSeek-V4 top-K
+    kernels moe_topk_sqrtsoftplus / _batched) and of the MoE module page (field docs of
+    the sqrtsoftplus routing kernels).
+    """
+    return np.sqrt(np.logaddexp(0.0, np.asarray(logits, dtype=np.float64)))
+
+
+def sqrt_softplus_key(logits: np.ndarray, correction_bias: Optional[np.ndarray]) -> np.ndarray:
+    """Selection key of sqrt-softplus routing: fp32(sqrt(softplus(l))) + bias, the
+    addition in fp32 (the score evaluated in fp64 and rounded once, as for sigmoid)."""
+    s = sqrt_softplus(logits).astype(np.float32)
+    if correction_bias is None:
+        return s
+    return (s + np.asarray(correction_bias, dtype=np.float32)).astype(np.float32)
+
+
+def scores(logits: np.ndarray, score: int) -> np.ndarray:
+    """The routing weight of every expert before selection, fp64."""
+    l = np.asarray(logits, dtype=np.float32)
+    if score == SOFTMAX:
+        return softmax(l)
+    if score == SIGMOID:
+        return 1.0 / (1.0 + np.exp(-l.astype(np.float64)))
+    if score == SQRT_SOFTPLUS:
+        return sqrt_softplus(l)
+    raise ValueError(f"unknown score mode {score}")
+
+
 def route(logits: np.ndarray, top_k: int, score: int = SOFTMAX, select: int = TOPK,
           renormalize: bool = False, correction_bias: Optional[np.ndarray] = None,
           token_ids: Optional[np.ndarray] = None, tid2eid: Optional[np.ndarray] = None,
@@ -197,9 +229,12 @@ def route(logits: np.ndarray, top_k: int, score: int = SOFTMAX, select: int = TO
     sigmoid: key = sigmoid(logit) + correction bias (selection only),
              weight = unbiased sigmoid (MoE module page: doc of correction_bias_dev,
              "DeepSeek-V3 / MiniMax-M2 style").
+    sqrt-softplus: key = sqrt(softplus(logit)) + correction bias (selection only),
+             weight = unbiased sqrt(softplus(logit)) (the DeepSeek-V4 routing kernels of
+             the constructor page; the bias handled as for sigmoid).
     hash:    ids = tid2eid[token] (MoE module page: doc of tid2eid_dev), weight =
-             softmax probability at those ids; an out-of-range token id or table
-             entry gives id -1 and weight 0.
+             the score (softmax probability, sigmoid or sqrt-softplus) at those ids;
+             an out-of-range token id or table entry gives id -1 and weight 0.
     Optional renormalisation divides the chosen weights by their sum; the routed
     scaling factor multiplies them afterwards.
     """
@@ -209,8 +244,7 @@ def route(logits: np.ndarray, top_k: int, score: int = SOFTMAX, select: int = TO
         if tid2eid is None or token_ids is None:
             raise ValueError("hash routing needs token_ids and tid2eid")
         tid2eid = np.asarray(tid2eid)
-        p = softmax(logits) if score == SOFTMAX else \
-            1.0 / (1.0 + np.exp(-logits.astype(np.float64)))
+        p = scores(logits, score)
         ids = np.full((t, top_k), -1, dtype=np.int32)
         w = np.zeros((t, top_k), dtype=np.float64)
         for i in range(t):
@@ -226,10 +260,10 @@ def route(logits: np.ndarray, top_k: int, score: int = SOFTMAX, select: int = TO
         ids = select_topk(logits, top_k)
         p = softmax(logits)
         w = np.take_along_axis(p, ids.astype(np.int64), axis=1)
-    elif score == SIGMOID:
-        ids = select_topk(sigmoid_key(logits, correction_bias), top_k)
-        s = 1.0 / (1.0 + np.exp(-logits.astype(np.float64)))
-        w = np.take_along_axis(s, ids.astype(np.int64), axis=1)
+    elif score in (SIGMOID, SQRT_SOFTPLUS):
+        key = sigmoid_key if score == SIGMOID else sqrt_softplus_key
+        ids = select_topk(key(logits, correction_bias), top_k)
+        w = np.take_along_axis(scores(logits, score), ids.astype(np.int64), axis=1)
     else:
         raise ValueError(f"unknown score mode {score}")
     if renormalize:

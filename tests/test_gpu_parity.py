@@ -103,6 +103,8 @@ ROUTING_CASES = {
     "softmax_e64_k6": dict(E=64, K=6, score=S.SOFTMAX, renorm=False),
     "softmax_e1024_k32": dict(E=1024, K=32, score=S.SOFTMAX, renorm=True),
     "sigmoid_e32_k32": dict(E=32, K=32, score=S.SIGMOID, renorm=False),
+    "sqrtsp_bias_e256_k8": dict(E=256, K=8, score=S.SQRT_SOFTPLUS, renorm=True, corr=True),
+    "sqrtsp_e64_k6": dict(E=64, K=6, score=S.SQRT_SOFTPLUS, renorm=False),
 }
 
 
@@ -143,7 +145,8 @@ def test_route_nan_logits_rank_last():
     assert np.array_equal(ids, O.route(logits.numpy(), K)[0])
 
 
-def test_hash_routing_and_bad_ids():
+@pytest.mark.parametrize("score", [S.SOFTMAX, S.SIGMOID, S.SQRT_SOFTPLUS])
+def test_hash_routing_and_bad_ids(score):
     T, E, K, V = 9, 16, 3, 50
     g = torch.Generator().manual_seed(4)
     logits = torch.randn((T, E), generator=g)
@@ -154,9 +157,10 @@ def test_hash_routing_and_bad_ids():
     tok[2] = 7
     tok[3] = V + 1        # bad token id
     tok[4] = 8
-    cfg = M.make_config(T, 256, E, K, 256, select_mode=M.SELECT_HASH, renormalize=True, vocab=V)
+    cfg = M.make_config(T, 256, E, K, 256, score_mode=score, select_mode=M.SELECT_HASH,
+                        renormalize=True, vocab=V)
     ids, w, _ = _route_gpu(cfg, logits=logits.to(DEV), token_ids=tok.to(DEV), tid2eid=table.to(DEV))
-    oid, ow = O.route(logits.numpy(), K, O.SOFTMAX, O.HASH, True, token_ids=tok.numpy(),
+    oid, ow = O.route(logits.numpy(), K, score, O.HASH, True, token_ids=tok.numpy(),
                       tid2eid=table.numpy())
     assert np.array_equal(ids, oid)
     assert np.allclose(w, ow, rtol=W_RTOL, atol=1e-7)
@@ -197,6 +201,12 @@ SMALL = {
                           inter=192),
     "hash_mini": S.scaled(S.WORKLOADS["hash_mxfp4_t512"], tokens=77, hidden=512, experts=32,
                           inter=256, shared_inter=128, vocab=1000),
+    # sqrt-softplus scoring (with the correction bias; and weighting a hash layer)
+    "sqrtsp_mini": S.scaled(S.WORKLOADS["dsv3_decode_t32"], tokens=13, hidden=1024, experts=64,
+                            inter=256, shared_inter=192, score=S.SQRT_SOFTPLUS),
+    "hash_sqrtsp_mini": S.scaled(S.WORKLOADS["hash_mxfp4_t512"], tokens=40, hidden=512,
+                                 experts=32, inter=256, shared_inter=128, vocab=1000,
+                                 score=S.SQRT_SOFTPLUS),
 }
 
 

@@ -237,6 +237,44 @@ def test_zero_bias_sigmoid_ranks_like_softmax():
     assert np.array_equal(a, b)
 
 
+def test_sqrt_softplus_score_closed_forms():
+    # softplus(0) = ln 2; softplus(l) - softplus(-l) = l; exp(softplus(l)) - 1 = exp(l)
+    assert O.sqrt_softplus(np.array([0.0]))[0] == math.sqrt(math.log(2.0))
+    l = np.linspace(-30.0, 30.0, 121)
+    s_pos, s_neg = O.sqrt_softplus(l), O.sqrt_softplus(-l)
+    assert np.allclose(s_pos ** 2 - s_neg ** 2, l, rtol=0, atol=1e-13)
+    mid = np.linspace(-8.0, 8.0, 33)
+    assert np.allclose(np.expm1(O.sqrt_softplus(mid) ** 2), np.exp(mid), rtol=1e-13)
+    # no overflow far out: sqrt(softplus(l)) -> sqrt(l) for large l, -> exp(l / 2) for very negative l
+    big = O.sqrt_softplus(np.array([1000.0, -1000.0]))
+    assert big[0] == math.sqrt(1000.0) and big[1] == 0.0
+    assert np.all(np.diff(O.sqrt_softplus(np.linspace(-50, 50, 1001))) > 0)  # monotone
+
+
+def test_sqrt_softplus_routing():
+    torch.manual_seed(10)
+    logits = torch.randn(40, 256).numpy().astype(np.float32)
+    # monotone in the logit: with no bias it ranks like softmax
+    a, _ = O.route(logits, 8, O.SOFTMAX)
+    b, w = O.route(logits, 8, O.SQRT_SOFTPLUS, correction_bias=np.zeros(256, np.float32))
+    assert np.array_equal(a, b)
+    # the bias moves selection, not the weights (the unbiased score at the chosen ids)
+    bias = (torch.rand(256) * 0.2 - 0.1).numpy().astype(np.float32)
+    ids, w = O.route(logits, 8, O.SQRT_SOFTPLUS, correction_bias=bias)
+    sp = torch.sqrt(torch.nn.functional.softplus(torch.from_numpy(logits).double())).numpy()
+    assert np.allclose(w, np.take_along_axis(sp, ids.astype(np.int64), 1), rtol=1e-14)
+    key = (torch.from_numpy(sp).float() + torch.from_numpy(bias)).numpy()
+    assert np.array_equal(ids, torch.topk(torch.from_numpy(key), 8, dim=1).indices.numpy())
+    # hash layers weighted by it: the table's ids, renormalised sqrt-softplus weights
+    tok = np.arange(40, dtype=np.int32)
+    table = np.tile(np.arange(6, dtype=np.int64), (40, 1)) * 7
+    hid, hw = O.route(logits, 6, O.SQRT_SOFTPLUS, O.HASH, renormalize=True, token_ids=tok,
+                      tid2eid=table)
+    assert np.array_equal(hid, table.astype(np.int32))
+    want = sp[:, ::7][:, :6]
+    assert np.allclose(hw, want / want.sum(1, keepdims=True), rtol=1e-14)
+
+
 def test_hash_with_softmax_ids_reproduces_softmax_routing():
     torch.manual_seed(9)
     t, e, k, v = 6, 16, 3, 40

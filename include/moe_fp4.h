@@ -22,8 +22,8 @@
  *   row-major [tokens, hidden].
  * - Host validation is O(1) and happens before any launch; a failing call
  *   enqueues nothing and returns a negative moe_status.
- * - Data errors that only the device can see (an expert id outside [0, E), a
- *   token id outside [0, vocab), a hash-table entry outside [0, E)) do not stop
+ * - Data errors that only the device can see (an expert id outside [0, E + Z), a
+ *   token id outside [0, vocab), a hash-table entry outside [0, E + Z)) do not stop
  *   the call: the offending slot is dropped (id -1, weight 0) and bits are set
  *   in the workspace's device error word (moe_get_device_error).
  * - Results are deterministic: identical inputs give bitwise identical outputs
@@ -73,10 +73,14 @@ enum {
   MOE_SCORE_SOFTMAX = 0,       /* key = logit; weight = softmax probability */
   MOE_SCORE_SIGMOID = 1,       /* key = fp32(sigmoid(logit)) + correction_bias (selection only);
                                   weight = sigmoid(logit) */
-  MOE_SCORE_SQRT_SOFTPLUS = 2  /* key = fp32(sqrt(softplus(logit))) + correction_bias
+  MOE_SCORE_SQRT_SOFTPLUS = 2, /* key = fp32(sqrt(softplus(logit))) + correction_bias
                                   (selection only); weight = sqrt(softplus(logit)) (the
                                   DeepSeek-V4 sqrtsoftplus top-K kernels of the constructor
                                   page); the score is evaluated in fp64, rounded once */
+  MOE_SCORE_SOFTMAX_BIAS = 3   /* key = fp32(softmax probability) + correction_bias (selection
+                                  only); weight = the probability (the LongCat softmax+bias
+                                  top-K kernels of the constructor page); the probabilities
+                                  are evaluated in fp64, rounded once */
 };
 
 /* Expert selection (MoE module page: doc of tid2eid_dev). */
@@ -141,6 +145,13 @@ typedef struct {
   float norm_eps;       /* RMSNorm epsilon */
   int64_t vocab;        /* hash routing: rows of tid2eid */
   int32_t path;         /* MOE_PATH_* */
+  int32_t zero_experts; /* Z >= 0 zero-computation experts (constructor page: the LongCat
+                           router logit width num_experts + zero_expert_num and its
+                           zero-expert add kernel). The router then has E + Z outputs
+                           (router_w [E + Z, H]; logit_bias, correction_bias, logits
+                           [.., E + Z]) and a slot whose id is in [E, E + Z) adds
+                           weight * expert input (identity) instead of running an expert.
+                           E + Z <= MOE_MAX_EXPERTS, top_k <= E + Z. */
 } moe_config;
 
 /* Human-readable name of a moe_status value (host; static string). */
@@ -153,12 +164,14 @@ int moe_workspace_size(const moe_config* cfg, size_t* bytes_out);
 /* Router + top-K selection (constructor page: router GEMM with fp32 output and the
  * softmax / sigmoid-with-bias / hash top-K kernels).
  *   x            bf16 [T, H] router input; may be NULL when logits_in is given
- *   router_w     bf16 [E, H]; may be NULL when logits_in is given
- *   logit_bias   f32 [E] added to every logit before scoring, or NULL
- *   correction_bias f32 [E] (sigmoid only; selection key only), or NULL
+ *   (E + Z router outputs: Z = cfg->zero_experts, usually 0)
+ *   router_w     bf16 [E + Z, H]; may be NULL when logits_in is given
+ *   logit_bias   f32 [E + Z] added to every logit before scoring, or NULL
+ *   correction_bias f32 [E + Z] (sigmoid, sqrt-softplus, softmax+bias; selection key
+ *                only), or NULL
  *   token_ids    int32 [T] (hash only), tid2eid int64 [vocab, top_k] (hash only)
- *   logits_in    f32 [T, E]: route from these logits instead of computing them, or NULL
- *   logits_out   f32 [T, E] receives the logits, or NULL
+ *   logits_in    f32 [T, E + Z]: route from these logits instead of computing them, or NULL
+ *   logits_out   f32 [T, E + Z] receives the logits, or NULL
  *   topk_ids     int32 [T, top_k] out: best first (key descending, then index ascending);
  *                -1 marks a slot dropped by a data error (hash routing)
  *   topk_w       f32 [T, top_k] out: routing weights (0 for dropped slots)
@@ -173,8 +186,9 @@ int moe_route(const moe_config* cfg, const uint16_t* x, const uint16_t* router_w
 /* Experts + weighted-sum blend for given routing (module doc: gate+up, SiLU*up, down;
  * weighted-sum blend into the residual).
  *   x_experts  bf16 [T, H] expert input (already normalised if a pre-norm applies)
- *   topk_ids   int32 [T, top_k], topk_w f32 [T, top_k] (ids outside [0, E) are dropped
- *              and flagged MOE_DEVERR_EXPERT_ID)
+ *   topk_ids   int32 [T, top_k], topk_w f32 [T, top_k]: ids in [E, E + Z) are zero-
+ *              computation experts (y = x_experts row); ids outside [0, E + Z) are dropped
+ *              and flagged MOE_DEVERR_EXPERT_ID
  *   routed     host struct of the routed experts (experts == E, gate/up n == inter)
  *   shared     host struct of the shared expert (experts == 1), or NULL if !has_shared
  *   residual   bf16 [T, H], or NULL for zero
@@ -188,7 +202,7 @@ int moe_experts_forward(const moe_config* cfg, const uint16_t* x_experts,
 
 /* The whole layer: [RMSNorm] -> router -> top-K -> experts -> blend.
  *   norm_gamma bf16 [H] (pre_norm only)
- *   dbg_logits f32 [T, E], dbg_ids int32 [T, top_k], dbg_w f32 [T, top_k]: optional
+ *   dbg_logits f32 [T, E + Z], dbg_ids int32 [T, top_k], dbg_w f32 [T, top_k]: optional
  *              copies of the routing decisions (NULL to skip)
  * Other arguments as in moe_route and moe_experts_forward. */
 int moe_layer_forward(const moe_config* cfg, const uint16_t* x, const uint16_t* norm_gamma,

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe_fp4.so")
 
 MOE_OK = 0
 FMT_NVFP4, FMT_MXFP4 = 0, 1
-SCORE_SOFTMAX, SCORE_SIGMOID, SCORE_SQRT_SOFTPLUS = 0, 1, 2
+SCORE_SOFTMAX, SCORE_SIGMOID, SCORE_SQRT_SOFTPLUS, SCORE_SOFTMAX_BIAS = 0, 1, 2, 3
 SELECT_TOPK, SELECT_HASH = 0, 1
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 DEVERR_EXPERT_ID, DEVERR_TOKEN_ID, DEVERR_TABLE = 1, 2, 4
@@ -42,7 +42,7 @@ class MoeConfig(ctypes.Structure):
                 ("routed_scaling", ctypes.c_float), ("has_shared", ctypes.c_int32),
                 ("shared_inter", ctypes.c_int32), ("pre_norm", ctypes.c_int32),
                 ("norm_eps", ctypes.c_float), ("vocab", ctypes.c_int64),
-                ("path", ctypes.c_int32)]
+                ("path", ctypes.c_int32), ("zero_experts", ctypes.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -118,10 +118,11 @@ def _stream(stream=None):
 def make_config(tokens, hidden, num_experts, top_k, inter, score_mode=SCORE_SOFTMAX,
                 select_mode=SELECT_TOPK, renormalize=False, routed_scaling=1.0,
                 has_shared=False, shared_inter=0, pre_norm=False, norm_eps=1e-6, vocab=0,
-                path=PATH_AUTO) -> MoeConfig:
+                path=PATH_AUTO, zero_experts=0) -> MoeConfig:
     return MoeConfig(tokens, hidden, num_experts, top_k, inter, score_mode, select_mode,
                      int(bool(renormalize)), float(routed_scaling), int(bool(has_shared)),
-                     shared_inter, int(bool(pre_norm)), float(norm_eps), int(vocab), path)
+                     shared_inter, int(bool(pre_norm)), float(norm_eps), int(vocab), path,
+                     int(zero_experts))
 
 
 def fp4_weight(w) -> MoeFp4Weight:

@@ -45,9 +45,10 @@ int prefill_mt(const moe_config& c) {
 Layout make_layout(const moe_config& c) {
   Layout L{};
   const int T = c.tokens, E = c.num_experts, K = c.top_k, H = c.hidden;
+  const int NE = E + c.zero_experts;  // router outputs
   const int S = T * K;
   L.rows = S + (c.has_shared ? T : 0);
-  const RouterPlan rp = plan_router(T, E, H);
+  const RouterPlan rp = plan_router(T, NE, H);
   L.ks = rp.ks;
   L.hsplit = rp.hsplit;
   int imax = c.inter;
@@ -62,8 +63,8 @@ Layout make_layout(const moe_config& c) {
     off = align_up(off + bytes);
     return o;
   };
-  L.partial = take((size_t)L.ks * T * E * sizeof(double));
-  L.logits = take((size_t)T * E * 4);
+  L.partial = take((size_t)L.ks * T * NE * sizeof(double));
+  L.logits = take((size_t)T * NE * 4);
   L.ids = take((size_t)S * 4);
   L.w = take((size_t)S * 4);
   L.errtok = take((size_t)T * 4);
@@ -83,11 +84,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int check_config(const moe_config* c) {
   if (!c) return MOE_ERR_INVALID_ARG;
   if (c->tokens < 0 || c->hidden <= 0 || c->hidden % 32 != 0) return MOE_ERR_INVALID_ARG;
-  if (c->num_experts <= 0 || c->top_k < 1 || c->top_k > c->num_experts) return MOE_ERR_INVALID_ARG;
-  if (c->num_experts > MOE_MAX_EXPERTS || c->top_k > MOE_MAX_TOP_K) return MOE_ERR_UNSUPPORTED;
+  if (c->num_experts <= 0 || c->zero_experts < 0) return MOE_ERR_INVALID_ARG;
+  const int64_t ntot = (int64_t)c->num_experts + c->zero_experts;  // router outputs
+  if (c->top_k < 1 || c->top_k > ntot) return MOE_ERR_INVALID_ARG;
+  if (ntot > MOE_MAX_EXPERTS || c->top_k > MOE_MAX_TOP_K) return MOE_ERR_UNSUPPORTED;
   if (c->inter <= 0 || c->inter % 32 != 0) return MOE_ERR_INVALID_ARG;
   if (c->score_mode != MOE_SCORE_SOFTMAX && c->score_mode != MOE_SCORE_SIGMOID &&
-      c->score_mode != MOE_SCORE_SQRT_SOFTPLUS)
+      c->score_mode != MOE_SCORE_SQRT_SOFTPLUS && c->score_mode != MOE_SCORE_SOFTMAX_BIAS)
     return MOE_ERR_INVALID_ARG;
   if (c->select_mode != MOE_SELECT_TOPK && c->select_mode != MOE_SELECT_HASH)
     return MOE_ERR_INVALID_ARG;
@@ -201,6 +204,7 @@ DispatchArgs make_dispatch_args(const moe_config& c, const Layout& L, const int3
   d.T = c.tokens;
   d.K = c.top_k;
   d.E = c.num_experts;
+  d.zero = c.zero_experts;
   d.shared_rows = c.has_shared ? c.tokens : 0;
   d.tile_h = path == MOE_PATH_PREFILL ? prefill_mt(c) : kDecodeTile;
   return d;
@@ -271,6 +275,7 @@ int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const 
   CombineArgs cb{};
   cb.y = a.y;
   cb.y_bf16 = pre ? 1 : 0;
+  cb.xe = xe;
   cb.w = w;
   cb.inv = d.inv;
   cb.shared = c.has_shared;
@@ -307,7 +312,7 @@ TopkArgs make_topk_args(const moe_config& c, const Layout& L, const float* logit
   t.w = w;
   t.err_tok = at<int32_t>(ws, L.errtok);
   t.T = c.tokens;
-  t.E = c.num_experts;
+  t.E = c.num_experts + c.zero_experts;  // selection runs over the zero experts too
   t.K = c.top_k;
   t.score = c.score_mode;
   t.select = c.select_mode;
@@ -326,10 +331,10 @@ int launch_route(const moe_config& c, const Layout& L, const uint16_t* x,
                  const StageMarks* marks = nullptr, bool* dispatched = nullptr) {
   if (!logits_in)
     MOE_HIP(launch_router_partial(x, router_w, at<double>(ws, L.partial), c.tokens,
-                                  c.num_experts, c.hidden, L.ks, L.hsplit, s));
+                                  c.num_experts + c.zero_experts, c.hidden, L.ks, L.hsplit, s));
   const TopkArgs t = make_topk_args(c, L, logit_bias, corr, token_ids, tid2eid, logits_in,
                                     logits_out, ids, w, ws);
-  if (dispatched && fused_topk_dispatch_fits(c.tokens, c.num_experts, c.top_k)) {
+  if (dispatched && fused_topk_dispatch_fits(c.tokens, c.num_experts + c.zero_experts, c.top_k)) {
     if (marks) MOE_HIP(marks->mark(MOE_STAGE_ROUTED));
     const DispatchArgs d = make_dispatch_args(c, L, ids, t.err_tok, ws);
     MOE_HIP(launch_topk_dispatch(t, d, s));

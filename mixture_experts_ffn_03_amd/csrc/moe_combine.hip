@@ -1,7 +1,9 @@
 // Weighted-sum blend into the residual (MoE constructor page: the weighted-sum blend and
-// residual-add kernels; the unpermute-and-reduce step of the grouped prefill path):
+// residual-add kernels; the unpermute-and-reduce step of the grouped prefill path; the
+// zero-expert add kernel):
 //   out[t] = bf16_rne(residual[t] + sum_j w[t,j] * y[row(t,j)] + y_shared[t])
 // summed in fp32 in the fixed order j = 0..K-1, then the shared expert, then the residual.
+// A zero-computation expert's y is the expert input x_e[t] itself.
 // Each thread produces 8 consecutive outputs with 128-bit stores.
 #include "moe_device.h"
 
@@ -35,10 +37,14 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   for (int j = 0; j < a.K; ++j) {
     const int p = a.inv[(size_t)t * a.K + j];
-    if (p < 0) continue;
+    if (p < 0 && p != -2) continue;
     const float w = a.w[(size_t)t * a.K + j];
     float v[8];
-    load_y8<YBF16>(a.y, (size_t)p * a.H + h0, v);
+    if (p >= 0) {
+      load_y8<YBF16>(a.y, (size_t)p * a.H + h0, v);
+    } else {  // zero expert: identity of the expert input
+      load_y8<true>(a.xe, (size_t)t * a.H + h0, v);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
   }

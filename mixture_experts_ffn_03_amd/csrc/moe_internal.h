@@ -90,6 +90,7 @@ struct DispatchArgs {
   int32_t* ntiles;
   int32_t* err_word;
   int T, K, E, shared_rows, tile_h;
+  int zero;               // ids in [E, E + zero): zero-computation experts (inv = -2)
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
 
@@ -120,7 +121,8 @@ struct CombineArgs {
   const void* y;          // [R, H] fp32 or bf16
   int y_bf16;
   const float* w;         // [T, K]
-  const int32_t* inv;     // [T, K] row of slot (t, j) or -1
+  const int32_t* inv;     // [T, K] row of slot (t, j), -1 (dropped) or -2 (zero expert)
+  const uint16_t* xe;     // [T, H] expert input (the identity of a zero expert)
   int shared;             // shared rows are [0, T)
   const uint16_t* residual;
   uint16_t* out;

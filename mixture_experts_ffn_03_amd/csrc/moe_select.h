@@ -122,23 +122,38 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, int t, float* s_lo
       lg[i] = -__builtin_inff();  // padding: never selectable, no softmax mass
     }
     float k = lg[i];
-    if (a.score != 0) {  // sigmoid / sqrt-softplus: key = fp32(score) + correction bias
+    if (a.score == 1 || a.score == 2) {  // sigmoid / sqrt-softplus: fp32(score) + bias
       const float sg = (float)score_f64(a.score, lg[i]);
       k = a.correction_bias ? sg + cbias[i] : sg;
     }
     key[i] = k;
   }
 
-  // softmax normaliser over all experts (fp32): m = max, S = sum exp(l - m)
+  // softmax normaliser over all experts: m = max, S = sum exp(l - m) (fp32; fp64 for the
+  // softmax+bias key, whose probability is rounded once)
   float m = -__builtin_inff(), S = 0.f;
-  if (a.score == 0) {
+  double S64 = 0.0;
+  if (a.score == 0 || a.score == 3) {
 #pragma unroll
     for (int i = 0; i < NPL; ++i) m = fmaxf(m, lg[i]);
     m = wave_max(m);
+  }
+  if (a.score == 0) {
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
       if (lane + kWave * i < E) S += expf(lg[i] - m);
     S = wave_sum(S);
+  } else if (a.score == 3) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (lane + kWave * i < E) S64 += exp((double)lg[i] - (double)m);
+#pragma unroll
+    for (int msk = 32; msk >= 1; msk >>= 1) S64 += __shfl_xor(S64, msk, kWave);
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const float p = (float)(exp((double)lg[i] - (double)m) / S64);
+      key[i] = a.correction_bias ? p + cbias[i] : p;
+    }
   }
 
   int err = 0;
@@ -180,7 +195,9 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, int t, float* s_lo
   float wj = 0.f;
   if (lane < K && my_id >= 0) {
     const float l = s_logit[my_id];
-    wj = a.score == 0 ? expf(l - m) / S : (float)score_f64(a.score, l);
+    wj = a.score == 0   ? expf(l - m) / S
+         : a.score == 3 ? (float)(exp((double)l - (double)m) / S64)
+                        : (float)score_f64(a.score, l);
   }
   if (a.renorm) {
     const float sum = wave_sum(wj);
@@ -203,7 +220,8 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, int t, float* s_lo
 // Row space: when a shared expert is present its T rows come first (row t = token t),
 // then the routed groups in expert order, each group's rows in (token, slot) order.
 // Outputs: row_token[p] (token whose input feeds row p), inv[t*K + j] (row of slot
-// (t, j), or -1 if its id is outside [0, E)), the tile list ((expert, first row, row
+// (t, j); -2 for a zero-computation expert, id in [E, E + zero); -1 for any other id
+// outside [0, E)), the tile list ((expert, first row, row
 // count) runs of at most tile_h rows), ntiles and the call's error word. ids / err_tok
 // may point to global or LDS memory; s_wbase holds NW x EMAX ints.
 // ---------------------------------------------------------------------------
@@ -257,7 +275,7 @@ __device__ void dispatch_body(const DispatchArgs& a, const int32_t* ids, const i
     if (s < se) {
       const int e = ids[s];
       if (e >= 0 && e < E) atomicAdd(&s_wbase[wave][e], 1);
-      else if (!(err_tok && e == -1)) err |= 1;
+      else if (!(err_tok && e == -1) && !(e >= E && e < E + a.zero)) err |= 1;
     }
   }
   if (err_tok)
@@ -303,7 +321,7 @@ __device__ void dispatch_body(const DispatchArgs& a, const int32_t* ids, const i
       a.inv[s] = pos;
       if (rank == cntm - 1) s_wbase[wave][e] = base + cntm;
     } else if (in) {
-      a.inv[s] = -1;
+      a.inv[s] = (e >= E && e < E + a.zero) ? -2 : -1;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();

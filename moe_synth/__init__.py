@@ -39,6 +39,7 @@ MXFP4 = 1
 SOFTMAX = 0
 SIGMOID = 1
 SQRT_SOFTPLUS = 2
+SOFTMAX_BIAS = 3
 
 TOPK = 0
 HASH = 1
@@ -66,6 +67,7 @@ class LayerSpec:
     vocab: int = 0
     zipf_bias: float = 0.0          # exponent of the Zipf logit bias, 0 = none
     correction_bias: bool = False    # U(-0.1, 0.1) per-expert bias (sigmoid routing)
+    zero_experts: int = 0            # zero-computation experts (router outputs E + Z)
     seed: int = 1000
 
 
@@ -282,11 +284,12 @@ def make_inputs(spec: LayerSpec, device="cpu", seed: Optional[int] = None,
 
     x = torch.randn((T, H), generator=ga, device=device).to(torch.bfloat16)
     residual = torch.randn((T, H), generator=ga, device=device).to(torch.bfloat16)
-    router_w = _normal(gw, (E, H), 0.02, device).to(torch.bfloat16)
-    logit_bias = zipf_logit_bias(gw, E, spec.zipf_bias, device) if spec.zipf_bias > 0 else None
+    NE = E + spec.zero_experts  # router outputs
+    router_w = _normal(gw, (NE, H), 0.02, device).to(torch.bfloat16)
+    logit_bias = zipf_logit_bias(gw, NE, spec.zipf_bias, device) if spec.zipf_bias > 0 else None
     corr = None
     if spec.correction_bias:
-        corr = (torch.rand((E,), generator=gw, device=device) * 0.2 - 0.1).to(torch.float32)
+        corr = (torch.rand((NE,), generator=gw, device=device) * 0.2 - 0.1).to(torch.float32)
     routed = _expert_set(gw, device, E, H, I, spec.fmt)
     shared = _expert_set(gw, device, 1, H, spec.shared_inter, spec.shared_fmt) if spec.shared else None
     gamma = None

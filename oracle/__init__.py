@@ -17,8 +17,10 @@ the sigmoid selection key), which are rounded to fp32 exactly as defined.
 Layer (for every token t, top-k slots j):
     x_e      = bf16(RMSNorm(x))      if a pre-expert norm is configured, else x
     logits   = fp32(x . W_r^T + logit_bias)               (router sees raw x)
-    ids, w   = select(score(logits))    (softmax | sigmoid+bias | sqrt-softplus+bias | hash)
+    ids, w   = select(score(logits))    (softmax | sigmoid+bias | sqrt-softplus+bias |
+                                         softmax+bias | hash)
     y_{t,j}  = W_d[e] . (SiLU(W_g[e] . x_e[t]) * (W_u[e] . x_e[t]))
+               (or x_e[t] for a zero-computation expert, ids E..E+Z-1)
     out[t]   = residual[t] + sum_j w[t,j] * y_{t,j} + y_shared[t]
 
 Every function below cites the passage it follows. Readings of points the
@@ -36,6 +38,7 @@ MXFP4 = 1
 SOFTMAX = 0
 SIGMOID = 1
 SQRT_SOFTPLUS = 2
+SOFTMAX_BIAS = 3
 TOPK = 0
 HASH = 1
 
@@ -216,7 +219,18 @@ def scores(logits: np.ndarray, score: int) -> np.ndarray:
         return 1.0 / (1.0 + np.exp(-l.astype(np.float64)))
     if score == SQRT_SOFTPLUS:
         return sqrt_softplus(l)
+    if score == SOFTMAX_BIAS:
+        return softmax(l)
     raise ValueError(f"unknown score mode {score}")
+
+
+def softmax_bias_key(logits: np.ndarray, correction_bias: Optional[np.ndarray]) -> np.ndarray:
+    """Selection key of softmax+bias routing: fp32(softmax probability) + bias, the
+    addition in fp32 (the probability evaluated in fp64 and rounded once)."""
+    s = softmax(logits).astype(np.float32)
+    if correction_bias is None:
+        return s
+    return (s + np.asarray(correction_bias, dtype=np.float32)).astype(np.float32)
 
 
 def route(logits: np.ndarray, top_k: int, score: int = SOFTMAX, select: int = TOPK,
@@ -232,6 +246,9 @@ def route(logits: np.ndarray, top_k: int, score: int = SOFTMAX, select: int = TO
     sqrt-softplus: key = sqrt(softplus(logit)) + correction bias (selection only),
              weight = unbiased sqrt(softplus(logit)) (the DeepSeek-V4 routing kernels of
              the constructor page; the bias handled as for sigmoid).
+    softmax+bias: key = softmax probability + correction bias (selection only), weight
+             = the probability (the LongCat softmax+bias top-K kernels of the
+             constructor page; their logit width num_experts + zero_expert_num).
     hash:    ids = tid2eid[token] (MoE module page: doc of tid2eid_dev), weight =
              the score (softmax probability, sigmoid or sqrt-softplus) at those ids;
              an out-of-range token id or table entry gives id -1 and weight 0.
@@ -260,8 +277,9 @@ def route(logits: np.ndarray, top_k: int, score: int = SOFTMAX, select: int = TO
         ids = select_topk(logits, top_k)
         p = softmax(logits)
         w = np.take_along_axis(p, ids.astype(np.int64), axis=1)
-    elif score in (SIGMOID, SQRT_SOFTPLUS):
-        key = sigmoid_key if score == SIGMOID else sqrt_softplus_key
+    elif score in (SIGMOID, SQRT_SOFTPLUS, SOFTMAX_BIAS):
+        key = {SIGMOID: sigmoid_key, SQRT_SOFTPLUS: sqrt_softplus_key,
+               SOFTMAX_BIAS: softmax_bias_key}[score]
         ids = select_topk(key(logits, correction_bias), top_k)
         w = np.take_along_axis(scores(logits, score), ids.astype(np.int64), axis=1)
     else:
@@ -313,11 +331,15 @@ class DequantCache:
 
 def experts_forward(xe: np.ndarray, ids: np.ndarray, w: np.ndarray, routed: DequantCache,
                     residual: np.ndarray, shared: Optional[DequantCache] = None,
-                    rows: Optional[np.ndarray] = None) -> np.ndarray:
+                    rows: Optional[np.ndarray] = None,
+                    num_experts: Optional[int] = None) -> np.ndarray:
     """out[t] = residual[t] + sum_j w[t,j] y_{t,j} + y_shared[t] in fp64, for tokens ``rows``.
 
     The sum runs over slots j in order, then the shared expert (weight 1, own
     format, same normalised input), then the residual. Slots with id -1 are skipped.
+    With ``num_experts`` = E given, ids E and above are zero-computation experts: their
+    y is the expert input itself (the constructor page's zero-expert add kernel, which
+    folds their weights into one identity contribution per token).
     """
     xe = np.asarray(xe, dtype=np.float64)
     t_all = xe.shape[0]
@@ -331,6 +353,10 @@ def experts_forward(xe: np.ndarray, ids: np.ndarray, w: np.ndarray, routed: Dequ
             if e >= 0:
                 by_expert.setdefault(e, []).append((ri, t, j))
     contrib = np.zeros((len(rows), ids.shape[1], xe.shape[1]), dtype=np.float64)
+    if num_experts is not None:
+        for e in [e for e in by_expert if e >= num_experts]:
+            for ri, t, j in by_expert.pop(e):
+                contrib[ri, j] = w[t, j] * xe[t]
     for e in sorted(by_expert):
         wg, wu, wd = routed.get(e)
         lst = by_expert[e]
@@ -352,11 +378,12 @@ def layer_forward(x, residual, router_w, routed: DequantCache, top_k: int, *,
                   score=SOFTMAX, select=TOPK, renormalize=False, logit_bias=None,
                   correction_bias=None, token_ids=None, tid2eid=None, gamma=None,
                   norm_eps=1e-6, shared: Optional[DequantCache] = None,
-                  routed_scaling=1.0, rows=None, logits=None):
+                  routed_scaling=1.0, rows=None, logits=None, zero_experts=0):
     """Whole layer -> (out fp64 [len(rows), H], logits fp32, ids, w).
 
     ``logits`` may be given to route from fixed fp32 logits (used by the
-    routing-parity checks); otherwise they are computed from x.
+    routing-parity checks); otherwise they are computed from x. With zero_experts = Z
+    the router has E + Z outputs and its last Z experts are zero-computation experts.
     """
     x = np.asarray(x, dtype=np.float64)
     if logits is None:
@@ -366,7 +393,8 @@ def layer_forward(x, residual, router_w, routed: DequantCache, top_k: int, *,
     # the experts' input is a bf16 activation [T, H] (the boundary passes it as bf16), so
     # the normalised input is rounded once to bf16 before the expert GEMMs
     xe = bf16_round_f64(rms_norm(x, gamma, norm_eps)) if gamma is not None else x
-    out = experts_forward(xe, ids, w, routed, residual, shared, rows)
+    num_experts = np.asarray(logits).shape[1] - zero_experts if zero_experts else None
+    out = experts_forward(xe, ids, w, routed, residual, shared, rows, num_experts)
     return out, logits, ids, w
 
 

@@ -22,7 +22,7 @@ def config_for(inp: S.LayerInputs, path=M.PATH_AUTO) -> M.MoeConfig:
     return M.make_config(s.tokens, s.hidden, s.experts, s.top_k, s.inter, score_mode=s.score,
                          select_mode=s.select, renormalize=s.renormalize, has_shared=s.shared,
                          shared_inter=s.shared_inter, pre_norm=s.pre_norm, norm_eps=s.norm_eps,
-                         vocab=s.vocab, path=path)
+                         vocab=s.vocab, path=path, zero_experts=s.zero_experts)
 
 
 class LazyHost:
@@ -55,7 +55,7 @@ def run_layer(inp: S.LayerInputs, path=M.PATH_AUTO, residual=True, stream=None):
     dev = inp.x.device
     ws = M.alloc_workspace(cfg, dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    logits = torch.empty((T, E + inp.spec.zero_experts), dtype=torch.float32, device=dev)
     ids = torch.empty((T, K), dtype=torch.int32, device=dev)
     w = torch.empty((T, K), dtype=torch.float32, device=dev)
     M.layer_forward(cfg, inp.x, inp.router_w, M.expert_weights(inp.routed), out, ws,
@@ -78,7 +78,8 @@ def oracle_layer(inp: S.LayerInputs, rows=None, residual=True):
         token_ids=None if inp.token_ids is None else inp.token_ids.cpu().numpy(),
         tid2eid=None if inp.tid2eid is None else inp.tid2eid.cpu().numpy(),
         gamma=f32(inp.gamma), norm_eps=s.norm_eps,
-        shared=oracle_cache(inp.shared) if inp.shared is not None else None, rows=rows)
+        shared=oracle_cache(inp.shared) if inp.shared is not None else None, rows=rows,
+        zero_experts=s.zero_experts)
 
 
 def bf16_half_ulp(v: np.ndarray) -> np.ndarray:

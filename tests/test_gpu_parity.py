@@ -105,6 +105,7 @@ ROUTING_CASES = {
     "sigmoid_e32_k32": dict(E=32, K=32, score=S.SIGMOID, renorm=False),
     "sqrtsp_bias_e256_k8": dict(E=256, K=8, score=S.SQRT_SOFTPLUS, renorm=True, corr=True),
     "sqrtsp_e64_k6": dict(E=64, K=6, score=S.SQRT_SOFTPLUS, renorm=False),
+    "softmax_bias_e96_k8": dict(E=96, K=8, score=S.SOFTMAX_BIAS, renorm=False, corr=True),
 }
 
 
@@ -207,6 +208,11 @@ SMALL = {
     "hash_sqrtsp_mini": S.scaled(S.WORKLOADS["hash_mxfp4_t512"], tokens=40, hidden=512,
                                  experts=32, inter=256, shared_inter=128, vocab=1000,
                                  score=S.SQRT_SOFTPLUS),
+    # softmax+bias routing over 48 + 16 zero-computation experts (identity contributions)
+    "zero_experts_mini": S.LayerSpec(name="zero_experts_mini", tokens=23, hidden=512,
+                                     experts=48, top_k=8, inter=256, fmt=S.NVFP4,
+                                     score=S.SOFTMAX_BIAS, renormalize=False,
+                                     correction_bias=True, zero_experts=16, seed=1077),
 }
 
 

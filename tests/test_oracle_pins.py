@@ -275,6 +275,45 @@ def test_sqrt_softplus_routing():
     assert np.allclose(hw, want / want.sum(1, keepdims=True), rtol=1e-14)
 
 
+def test_softmax_bias_routing():
+    torch.manual_seed(12)
+    logits = torch.randn(30, 96).numpy().astype(np.float32)
+    # the probability is monotone in the logit: with no bias it ranks like softmax
+    a, wa = O.route(logits, 6, O.SOFTMAX)
+    b, wb = O.route(logits, 6, O.SOFTMAX_BIAS, correction_bias=np.zeros(96, np.float32))
+    assert np.array_equal(a, b) and np.allclose(wa, wb, rtol=0, atol=0)
+    # with a bias: selection on fp32(p) + bias, weights the unbiased probabilities
+    bias = (torch.rand(96) * 0.02 - 0.01).numpy().astype(np.float32)
+    ids, w = O.route(logits, 6, O.SOFTMAX_BIAS, correction_bias=bias)
+    p = torch.softmax(torch.from_numpy(logits).double(), dim=1)
+    key = (p.float() + torch.from_numpy(bias)).numpy()
+    assert np.array_equal(ids, torch.topk(torch.from_numpy(key), 6, dim=1).indices.numpy())
+    assert np.allclose(w, np.take_along_axis(p.numpy(), ids.astype(np.int64), 1), rtol=1e-14)
+
+
+def test_zero_experts_add_the_expert_input():
+    inp = _small_layer(seed=21, t=4, h=64, e=4, k=2, i=32)
+    x = inp.x.double().numpy()
+    res = inp.residual.double().numpy()
+    rw = inp.router_w.float().numpy()
+    z = 3  # router outputs 4 + 3; the last three are zero-computation experts
+    rw_z = np.concatenate([rw, np.zeros((z, rw.shape[1]), np.float32)])
+    # logits that select only zero experts: the output is residual + (sum of weights) * x
+    lz = np.full((4, 7), -5.0, np.float32)
+    lz[:, 4:] = [1.0, 2.0, 3.0]
+    out, _, ids, w = O.layer_forward(x, res, rw_z, _cache(inp.routed), 2, renormalize=True,
+                                     logits=lz, zero_experts=z)
+    assert np.all(ids >= 4)
+    assert np.allclose(out, res + x, rtol=0, atol=1e-12)
+    # logits that never select a zero expert: the layer of the E real experts
+    ln = np.concatenate([torch.randn(4, 4).numpy().astype(np.float32),
+                         np.full((4, z), -np.inf, np.float32)], axis=1)
+    o1, _, i1, w1 = O.layer_forward(x, res, rw_z, _cache(inp.routed), 2, logits=ln,
+                                    zero_experts=z)
+    o0, _, i0, w0 = O.layer_forward(x, res, rw, _cache(inp.routed), 2, logits=ln[:, :4])
+    assert np.array_equal(i1, i0) and np.allclose(o1, o0, rtol=0, atol=0)
+
+
 def test_hash_with_softmax_ids_reproduces_softmax_routing():
     torch.manual_seed(9)
     t, e, k, v = 6, 16, 3, 40

@@ -40,9 +40,6 @@ namespace moe {
 constexpr int kKc = 128;  // K codes per stage
 constexpr int kStages = 3;
 constexpr int kXcds = 8;
-constexpr int kPreThreads = 256;
-constexpr int kPreWaves = kPreThreads / 64;
-constexpr int kCB = 4;  // 32-column blocks per wave
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -129,40 +126,44 @@ __device__ __forceinline__ bf16x8_t b_operand(const uint32_t q, const uint32_t s
 // * SS = true (scale rows a multiple of 16 bytes): 16 bytes per row at a time, covering
 //   SUPER stages (4 MXFP4, 2 NVFP4), into one of two super-stage slots; a quarter or half
 //   as many requests.
-template <int FMT, int RB, int WM, bool GATEUP, bool SS>
+template <int FMT, int RB, int WM, int NW, int CB, bool GATEUP, bool SS>
 struct PreShape {
-  static constexpr int WN = kPreWaves / WM;
+  static constexpr int NT = NW * 64;  // threads per block
+  static constexpr int WN = NW / WM;
   static constexpr int MT = 32 * RB * WM;
-  static constexpr int BROWS = 32 * kCB * WN;
+  static constexpr int BROWS = 32 * CB * WN;
   static constexpr int NCOLS = GATEUP ? BROWS / 2 : BROWS;  // output columns per block
   static constexpr int SROW = SS ? 0 : 8;  // LDS bytes per row of scales per stage
   static constexpr int A_BYTES = MT * 256;
   static constexpr int B_BYTES = BROWS * 64;
   static constexpr int S_BYTES = BROWS * SROW;
   static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-  static constexpr int NA = MT * 16 / kPreThreads;      // 16-byte loads per lane (A)
-  static constexpr int NB = BROWS * 4 / kPreThreads;    // 16-byte loads per lane (B)
+  static constexpr int NA = MT * 16 / NT;      // 16-byte loads per lane (A)
+  static constexpr int NB = BROWS * 4 / NT;    // 16-byte loads per lane (B)
   // scale loads: 4 bytes (NVFP4) or 2 bytes (MXFP4, whose rows may be only 2-aligned) per
   // lane, each landing in a 4-byte LDS slot (sub-dword direct-to-LDS loads keep a 4-byte
   // lane stride)
   static constexpr int SUNIT = FMT == 0 ? 4 : 2;
-  static constexpr int NS = S_BYTES / 4 / kPreThreads;  // scale loads per lane
+  static constexpr int NS = S_BYTES / 4 / NT;  // scale loads per lane
   static constexpr int NLOADS = NA + NB + NS;
   static constexpr int SUPER = FMT == 0 ? 2 : 4;              // stages per super-stage
-  static constexpr int NSS = SS ? BROWS / kPreThreads : 0;    // 16-byte loads per lane
+  // super-stage scale loads: one lane per row, issued by the first SS_WAVES waves
+  static constexpr int SS_WAVES = SS ? (BROWS / 64 < NW ? BROWS / 64 : NW) : 0;
+  static constexpr int NSS = SS ? BROWS / (SS_WAVES * 64) : 0;  // per lane of those waves
   static constexpr int SS_BYTES = SS ? 2 * BROWS * 16 : 0;   // two super-stage slots
   static constexpr size_t SMEM = (size_t)kStages * STAGE + SS_BYTES + MT * sizeof(int);
-  static_assert(NA * kPreThreads == MT * 16 && NB * kPreThreads == BROWS * 4 &&
-                    NS * kPreThreads * 4 == S_BYTES,
+  static_assert(NA * NT == MT * 16 && NB * NT == BROWS * 4 && NS * NT * 4 == S_BYTES,
                 "a stage must split evenly over the block");
-  static_assert(!SS || NSS * kPreThreads == BROWS, "one super-stage load per row");
+  static_assert(!SS || NSS * SS_WAVES * 64 == BROWS, "one super-stage load per row");
+  static_assert(CB % 2 == 0 || !GATEUP, "gate+up pairs column blocks");
   static_assert(NLOADS + NSS <= 31, "two stages of loads must fit the wait counter");
   static_assert(SMEM <= 160 * 1024, "three stages must fit the 160 KB of LDS");
 };
 
-template <int FMT, int RB, int WM, bool GATEUP, bool SS>
-__global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
-  using Sh = PreShape<FMT, RB, WM, GATEUP, SS>;
+template <int FMT, int RB, int WM, int NW, int CB, bool GATEUP, bool SS>
+__global__ __launch_bounds__(NW * 64) void k_pre_gemm(ExpertGemmArgs a) {
+  using Sh = PreShape<FMT, RB, WM, NW, CB, GATEUP, SS>;
+  constexpr int NT = Sh::NT;
   constexpr int WN = Sh::WN, BROWS = Sh::BROWS, NCOLS = Sh::NCOLS, MT = Sh::MT;
   constexpr int NA = Sh::NA, NB = Sh::NB, NS = Sh::NS, NSS = Sh::NSS, SUPER = Sh::SUPER;
   extern __shared__ __align__(16) uint8_t s_dyn[];
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
 
   // source row of each A tile row: gathered token (gate+up) or h row (down); rows past
   // the tile's count repeat its first row (results discarded)
-  for (int i = threadIdx.x; i < MT; i += kPreThreads) {
+  for (int i = threadIdx.x; i < MT; i += NT) {
     const int ii = i < t.count ? i : 0;
     s_tok[i] = GATEUP ? a.row_token[t.row0 + ii] : t.row0 + ii;
   }
@@ -240,7 +241,8 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
 #pragma unroll
   for (int i = 0; i < NSS; ++i) {
     const WeightDesc* w;
-    const size_t rw = wrow((wave * NSS + i) * 64 + lane, w);  // one lane per row
+    const int row = (wave * NSS + i) * 64 + lane;  // one lane per row (waves < SS_WAVES)
+    const size_t rw = wrow(row < BROWS ? row : 0, w);
     sssrc[i] = w->scales + rw * sbytes;
   }
 
@@ -254,7 +256,7 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
     const uint32_t bbase = abase + Sh::A_BYTES, sbase = bbase + Sh::B_BYTES;
     const int k0 = c * kKc;
     const bool tail = c == nfull;
-    if (SS && c % SUPER == 0) {
+    if (SS && c % SUPER == 0 && wave < Sh::SS_WAVES) {
       const int j = c / SUPER;
       const uint32_t ssbase = lds_addr(s_ss + (j & 1) * BROWS * 16);
 #pragma unroll
@@ -291,17 +293,20 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
     }
   };
 
-  f32x16_t acc[RB][kCB];
+  f32x16_t acc[RB][CB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) acc[rb][cb] = f32x16_t{};
+    for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x16_t{};
 
   // B-tile rows of this wave's column blocks
-  int brow0[kCB];
+  // (gate+up: column blocks 0..CB/2-1 are gate rows, CB/2.. the same rows of up)
+  constexpr int CH = GATEUP ? CB / 2 : CB;
+  int brow0[CB];
 #pragma unroll
-  for (int cb = 0; cb < kCB; ++cb) {
-    brow0[cb] = GATEUP ? (cb >> 1) * (BROWS / 2) + wn * 64 + (cb & 1) * 32 : wn * 128 + cb * 32;
+  for (int cb = 0; cb < CB; ++cb) {
+    brow0[cb] = GATEUP ? (cb / CH) * (BROWS / 2) + wn * CH * 32 + (cb % CH) * 32
+                       : wn * CB * 32 + cb * 32;
   }
   const int arow = wm * 32 * RB + r;  // + rb * 32
   const int bsw = b_swz(r);            // = b_swz(brow0[cb] + r): brow0 is a multiple of 32
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
     // in flight: the loads of stage c+1 (with a super-stage of scales if it starts one)
     if (c + 1 >= nch) {
       wait_stage<0>();
-    } else if (SS && (c + 1) % SUPER == 0) {
+    } else if (SS && (c + 1) % SUPER == 0 && wave < Sh::SS_WAVES) {
       wait_stage<Sh::NLOADS + NSS>();
     } else {
       wait_stage<Sh::NLOADS>();
@@ -324,9 +329,9 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
     const uint8_t* sa = s_dyn + (c % kStages) * Sh::STAGE;
     const uint8_t* sbq = sa + Sh::A_BYTES;
     const uint8_t* ssc = sbq + Sh::B_BYTES;
-    uint32_t q[kCB][8], sc[kCB];
+    uint32_t q[CB][8], sc[CB];
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
+    for (int cb = 0; cb < CB; ++cb) {
       const uint8_t* row = sbq + (brow0[cb] + r) * 64;
       const uint4 v0 = *reinterpret_cast<const uint4*>(row + (((2 * half) ^ bsw) << 4));
       const uint4 v1 = *reinterpret_cast<const uint4*>(row + (((2 * half + 1) ^ bsw) << 4));
@@ -344,9 +349,9 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      bf16x8_t bo[kCB];
+      bf16x8_t bo[CB];
 #pragma unroll
-      for (int cb = 0; cb < kCB; ++cb) bo[cb] = b_operand<FMT>(q[cb][s], sc[cb], s);
+      for (int cb = 0; cb < CB; ++cb) bo[cb] = b_operand<FMT>(q[cb][s], sc[cb], s);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const int row = arow + rb * 32;
@@ -354,7 +359,7 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
             *reinterpret_cast<const uint4*>(sa + row * 256 + (((8 * half + s) ^ (row & 15)) << 4));
         const bf16x8_t af = __builtin_bit_cast(bf16x8_t, av);
 #pragma unroll
-        for (int cb = 0; cb < kCB; ++cb)
+        for (int cb = 0; cb < CB; ++cb)
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bo[cb], acc[rb][cb], 0, 0, 0);
       }
     }
@@ -365,9 +370,9 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
     const uint8_t* sa = s_dyn + (nfull % kStages) * Sh::STAGE;
     const uint8_t* sbq = sa + Sh::A_BYTES;
     const uint8_t* ssc = sbq + Sh::B_BYTES;
-    uint32_t q[kCB][4], sc[kCB];
+    uint32_t q[CB][4], sc[CB];
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
+    for (int cb = 0; cb < CB; ++cb) {
       const int srow = brow0[cb] + r;
       const uint4 v0 = *reinterpret_cast<const uint4*>(sbq + srow * 64 + ((half ^ bsw) << 4));
       q[cb][0] = v0.x; q[cb][1] = v0.y; q[cb][2] = v0.z; q[cb][3] = v0.w;
@@ -376,9 +381,9 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      bf16x8_t bo[kCB];
+      bf16x8_t bo[CB];
 #pragma unroll
-      for (int cb = 0; cb < kCB; ++cb) bo[cb] = b_operand<FMT>(q[cb][s], sc[cb], s);
+      for (int cb = 0; cb < CB; ++cb) bo[cb] = b_operand<FMT>(q[cb][s], sc[cb], s);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const int row = arow + rb * 32;
@@ -386,7 +391,7 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
             *reinterpret_cast<const uint4*>(sa + row * 256 + (((4 * half + s) ^ (row & 15)) << 4));
         const bf16x8_t af = __builtin_bit_cast(bf16x8_t, av);
 #pragma unroll
-        for (int cb = 0; cb < kCB; ++cb)
+        for (int cb = 0; cb < CB; ++cb)
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bo[cb], acc[rb][cb], 0, 0, 0);
       }
     }
@@ -397,8 +402,8 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
     const float gs_g = FMT == 0 ? a.gate.global[e] : 1.0f;
     const float gs_u = FMT == 0 ? a.up.global[e] : 1.0f;
 #pragma unroll
-    for (int cg = 0; cg < 2; ++cg) {
-      const int n = n0 + wn * 64 + cg * 32 + r;
+    for (int cg = 0; cg < CH; ++cg) {
+      const int n = n0 + wn * CH * 32 + cg * 32 + r;
       if (n >= N) continue;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -407,7 +412,7 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
           const int i = wm * 32 * RB + rb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
           if (i < t.count) {
             const float g = acc[rb][cg][v] * gs_g;
-            const float u = acc[rb][2 + cg][v] * gs_u;
+            const float u = acc[rb][CH + cg][v] * gs_u;
             const float hval = g / (1.0f + expf(-g)) * u;
             a.h[(size_t)(t.row0 + i) * a.h_stride + n] = f32_to_bf16(hval);
           }
@@ -418,8 +423,8 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
     const float gs = FMT == 0 ? a.down.global[e] : 1.0f;
     uint16_t* y = reinterpret_cast<uint16_t*>(a.y);
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
-      const int n = n0 + wn * 128 + cb * 32 + r;
+    for (int cb = 0; cb < CB; ++cb) {
+      const int n = n0 + wn * CB * 32 + cb * 32 + r;
       if (n >= N) continue;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -433,12 +438,12 @@ __global__ __launch_bounds__(kPreThreads) void k_pre_gemm(ExpertGemmArgs a) {
   }
 }
 
-template <int FMT, int RB, int WM, bool GATEUP, bool SS>
+template <int FMT, int RB, int WM, int NW, int CB, bool GATEUP, bool SS>
 static hipError_t launch_pre_ss(const ExpertGemmArgs& a, hipStream_t s) {
-  using Sh = PreShape<FMT, RB, WM, GATEUP, SS>;
+  using Sh = PreShape<FMT, RB, WM, NW, CB, GATEUP, SS>;
   const int N = GATEUP ? a.I : a.H;
   const int ncol = (N + Sh::NCOLS - 1) / Sh::NCOLS;
-  auto kern = k_pre_gemm<FMT, RB, WM, GATEUP, SS>;
+  auto kern = k_pre_gemm<FMT, RB, WM, NW, CB, GATEUP, SS>;
   static bool attr_set = false;  // one attribute call per instantiation and process
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -446,32 +451,38 @@ static hipError_t launch_pre_ss(const ExpertGemmArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(ncol, a.tile_bound), dim3(kPreThreads), Sh::SMEM, s, a);
+  hipLaunchKernelGGL(kern, dim3(ncol, a.tile_bound), dim3(Sh::NT), Sh::SMEM, s, a);
   return hipGetLastError();
 }
 
 // Super-staged scales when each scale row is a whole number of 16-byte pieces.
-template <int FMT, int RB, int WM, bool GATEUP>
+template <int FMT, int RB, int WM, int NW, int CB, bool GATEUP>
 static hipError_t launch_pre_shape(const ExpertGemmArgs& a, hipStream_t s) {
   const int K = GATEUP ? a.H : a.I;
   const int sbytes = K / (FMT == 0 ? 16 : 32);
-  if (sbytes % 16 == 0) return launch_pre_ss<FMT, RB, WM, GATEUP, true>(a, s);
-  return launch_pre_ss<FMT, RB, WM, GATEUP, false>(a, s);
+  if (sbytes % 16 == 0) return launch_pre_ss<FMT, RB, WM, NW, CB, GATEUP, true>(a, s);
+  return launch_pre_ss<FMT, RB, WM, NW, CB, GATEUP, false>(a, s);
 }
 
-// Tile height MT -> (row blocks per wave, waves along M): 128 = 2 x 2, 64 = 1 x 2, 32 = 1 x 1.
+// Tile height MT -> block shape (row blocks per wave RB, waves along M WM, waves NW,
+// column blocks per wave CB): 128 = RB 2 x WM 2 with 8 waves of 2 column blocks (two waves
+// per SIMD), 64 = 1 x 2 (4 waves of 4), 32 = 1 x 1 (4 waves of 4).
+#ifndef MOE_PRE_NW128
+#define MOE_PRE_NW128 8
+#endif
 template <bool GATEUP>
 static hipError_t launch_pre(const ExpertGemmArgs& a, int mt, hipStream_t s) {
   if (a.tile_bound <= 0) return hipSuccess;
   const int fmt = GATEUP ? a.gate.fmt : a.down.fmt;
+  constexpr int NW = MOE_PRE_NW128, CB = 16 / NW;
   if (fmt == 0) {
-    if (mt == 32) return launch_pre_shape<0, 1, 1, GATEUP>(a, s);
-    if (mt == 64) return launch_pre_shape<0, 1, 2, GATEUP>(a, s);
-    return launch_pre_shape<0, 2, 2, GATEUP>(a, s);
+    if (mt == 32) return launch_pre_shape<0, 1, 1, 4, 4, GATEUP>(a, s);
+    if (mt == 64) return launch_pre_shape<0, 1, 2, 4, 4, GATEUP>(a, s);
+    return launch_pre_shape<0, 2, 2, NW, CB, GATEUP>(a, s);
   }
-  if (mt == 32) return launch_pre_shape<1, 1, 1, GATEUP>(a, s);
-  if (mt == 64) return launch_pre_shape<1, 1, 2, GATEUP>(a, s);
-  return launch_pre_shape<1, 2, 2, GATEUP>(a, s);
+  if (mt == 32) return launch_pre_shape<1, 1, 1, 4, 4, GATEUP>(a, s);
+  if (mt == 64) return launch_pre_shape<1, 1, 2, 4, 4, GATEUP>(a, s);
+  return launch_pre_shape<1, 2, 2, NW, CB, GATEUP>(a, s);
 }
 
 hipError_t launch_prefill_gate_up(const ExpertGemmArgs& a, int mt, hipStream_t s) {

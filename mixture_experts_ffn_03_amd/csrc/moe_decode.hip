@@ -149,8 +149,6 @@ __device__ __forceinline__ void stage_activations(const uint16_t* src, size_t st
   __syncthreads();
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
-
 // Rows per pass: enough for every lane group of the wave to own a row, and few enough
 // that two steps of weights, the activations and the sums fit 256 VGPRs (2 waves per SIMD).
 template <int TT, int LPR, int BASE>

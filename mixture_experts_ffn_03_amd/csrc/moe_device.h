@@ -26,6 +26,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
+// SiLU(g) = g * sigmoid(g) = g / (1 + e^-g) from the hardware base-2 exponential and
+// reciprocal (about 1 ulp each; the product is rounded to bf16 next). Large -g gives
+// e^-g = inf and a zero result; large g gives g.
+__device__ __forceinline__ float silu(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2_t v;
   v[0] = (__bf16)lo;

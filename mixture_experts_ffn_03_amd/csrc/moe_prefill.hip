@@ -33,6 +33,8 @@
 // * Block ids are remapped so that each XCD (ids dispatched round-robin over the 8
 //   XCDs) walks a contiguous run of (row tile, column tile) work, which keeps an A
 //   tile and an expert's weight rows in that XCD's L2 while they are reused.
+#include <type_traits>
+
 #include "moe_device.h"
 
 namespace moe {
@@ -311,33 +313,37 @@ __global__ __launch_bounds__(NW * 64) void k_pre_gemm(ExpertGemmArgs a) {
   const int arow = wm * 32 * RB + r;  // + rb * 32
   const int bsw = b_swz(r);            // = b_swz(brow0[cb] + r): brow0 is a multiple of 32
 
-  issue(0);
-  if (nch > 1) issue(1);
-  // full stages; the tail stage (if any) follows the loop so that the accumulators have
-  // a single definition inside it
-#pragma unroll 1
-  for (int c = 0; c < nfull; ++c) {
-    // in flight: the loads of stage c+1 (with a super-stage of scales if it starts one)
-    if (c + 1 >= nch) {
-      wait_stage<0>();
-    } else if (SS && (c + 1) % SUPER == 0 && wave < Sh::SS_WAVES) {
-      wait_stage<Sh::NLOADS + NSS>();
-    } else {
-      wait_stage<Sh::NLOADS>();
-    }
-    if (c + 2 < nch) issue(c + 2);
+  // row blocks of this wave that hold rows of the tile: a partly filled tile skips the
+  // MFMAs of its empty 32-row blocks (the other waves of the same SIMD then run alone)
+  int nrb = (t.count - wm * 32 * RB + 31) / 32;
+  nrb = nrb < 0 ? 0 : (nrb > RB ? RB : nrb);
+
+  // MFMAs of one stage for the first NR row blocks (STEPS = 8, or 4 in the 64-code tail
+  // where lane half h covers codes 32h..32h+31)
+  auto stage_mma = [&](auto nr_c, auto steps_c, int c) {
+    constexpr int NR = decltype(nr_c)::value, STEPS = decltype(steps_c)::value;
+    if constexpr (NR == 0) return;
+    const bool tail = STEPS == 4;
     const uint8_t* sa = s_dyn + (c % kStages) * Sh::STAGE;
     const uint8_t* sbq = sa + Sh::A_BYTES;
     const uint8_t* ssc = sbq + Sh::B_BYTES;
     uint32_t q[CB][8], sc[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      const uint8_t* row = sbq + (brow0[cb] + r) * 64;
+      const int srow = brow0[cb] + r;
+      const uint8_t* row = sbq + srow * 64;
+      if (tail) {
+        const uint4 v0 = *reinterpret_cast<const uint4*>(row + ((half ^ bsw) << 4));
+        q[cb][0] = v0.x; q[cb][1] = v0.y; q[cb][2] = v0.z; q[cb][3] = v0.w;
+        q[cb][4] = q[cb][5] = q[cb][6] = q[cb][7] = 0;
+        sc[cb] = FMT == 0 ? (uint32_t)*reinterpret_cast<const uint16_t*>(ssc + srow * 8 + 2 * half)
+                          : (uint32_t)ssc[srow * 8 + half];
+        continue;
+      }
       const uint4 v0 = *reinterpret_cast<const uint4*>(row + (((2 * half) ^ bsw) << 4));
       const uint4 v1 = *reinterpret_cast<const uint4*>(row + (((2 * half + 1) ^ bsw) << 4));
       q[cb][0] = v0.x; q[cb][1] = v0.y; q[cb][2] = v0.z; q[cb][3] = v0.w;
       q[cb][4] = v1.x; q[cb][5] = v1.y; q[cb][6] = v1.z; q[cb][7] = v1.w;
-      const int srow = brow0[cb] + r;
       if (SS) {
         const uint8_t* sp = s_ss + ((c / SUPER) & 1) * BROWS * 16 + srow * 16;
         sc[cb] = FMT == 0 ? *reinterpret_cast<const uint32_t*>(sp + (c & 1) * 8 + 4 * half)
@@ -347,54 +353,62 @@ __global__ __launch_bounds__(NW * 64) void k_pre_gemm(ExpertGemmArgs a) {
                           : (uint32_t)*reinterpret_cast<const uint16_t*>(ssc + srow * 8 + 4 * half);
       }
     }
+    // every A operand of the stage is read up front, in the order of use, so that LDS
+    // latency overlaps the MFMAs instead of stalling each step (LDS reads return in order)
+    uint4 av[NR > 0 ? NR : 1][STEPS];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < STEPS; ++s) {
+#pragma unroll
+      for (int rb = 0; rb < NR; ++rb) {
+        const int row = arow + rb * 32;
+        const int piece = tail ? 4 * half + s : 8 * half + s;
+        av[rb][s] = *reinterpret_cast<const uint4*>(sa + row * 256 + ((piece ^ (row & 15)) << 4));
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads in the order they are used
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
       bf16x8_t bo[CB];
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) bo[cb] = b_operand<FMT>(q[cb][s], sc[cb], s);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int row = arow + rb * 32;
-        const uint4 av =
-            *reinterpret_cast<const uint4*>(sa + row * 256 + (((8 * half + s) ^ (row & 15)) << 4));
-        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, av);
+      for (int rb = 0; rb < NR; ++rb) {
+        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, av[rb][s]);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bo[cb], acc[rb][cb], 0, 0, 0);
       }
     }
-  }
-  if (nch > nfull) {
-    // 64-code tail: lane half h covers codes 32h..32h+31 in 4 steps
-    wait_stage<0>();
-    const uint8_t* sa = s_dyn + (nfull % kStages) * Sh::STAGE;
-    const uint8_t* sbq = sa + Sh::A_BYTES;
-    const uint8_t* ssc = sbq + Sh::B_BYTES;
-    uint32_t q[CB][4], sc[CB];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int srow = brow0[cb] + r;
-      const uint4 v0 = *reinterpret_cast<const uint4*>(sbq + srow * 64 + ((half ^ bsw) << 4));
-      q[cb][0] = v0.x; q[cb][1] = v0.y; q[cb][2] = v0.z; q[cb][3] = v0.w;
-      sc[cb] = FMT == 0 ? (uint32_t)*reinterpret_cast<const uint16_t*>(ssc + srow * 8 + 2 * half)
-                        : (uint32_t)ssc[srow * 8 + half];
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8_t bo[CB];
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) bo[cb] = b_operand<FMT>(q[cb][s], sc[cb], s);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int row = arow + rb * 32;
-        const uint4 av =
-            *reinterpret_cast<const uint4*>(sa + row * 256 + (((4 * half + s) ^ (row & 15)) << 4));
-        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, av);
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bo[cb], acc[rb][cb], 0, 0, 0);
+  };
+  issue(0);
+  if (nch > 1) issue(1);
+  // full stages, then the 64-code tail stage (if any) after the loop, so that the
+  // accumulators have a single definition inside the loop
+  auto kloop = [&](auto nr_c) {
+#pragma unroll 1
+    for (int c = 0; c < nfull; ++c) {
+      // in flight: the loads of stage c+1 (with a super-stage of scales if it starts one)
+      if (c + 1 >= nch) {
+        wait_stage<0>();
+      } else if (SS && (c + 1) % SUPER == 0 && wave < Sh::SS_WAVES) {
+        wait_stage<Sh::NLOADS + NSS>();
+      } else {
+        wait_stage<Sh::NLOADS>();
       }
+      if (c + 2 < nch) issue(c + 2);
+      stage_mma(nr_c, std::integral_constant<int, 8>{}, c);
     }
+    if (nch > nfull) {
+      wait_stage<0>();
+      stage_mma(nr_c, std::integral_constant<int, 4>{}, nfull);
+    }
+  };
+  if (nrb >= RB) {
+    kloop(std::integral_constant<int, RB>{});
+  } else if (nrb == 1) {
+    kloop(std::integral_constant<int, 1>{});
+  } else {
+    kloop(std::integral_constant<int, 0>{});
   }
 
   // epilogue: lane holds column j = lane % 32 of each 32x32 block, rows 8*(v/4)+4*half+v%4
@@ -413,7 +427,7 @@ __global__ __launch_bounds__(NW * 64) void k_pre_gemm(ExpertGemmArgs a) {
           if (i < t.count) {
             const float g = acc[rb][cg][v] * gs_g;
             const float u = acc[rb][CH + cg][v] * gs_u;
-            const float hval = g / (1.0f + expf(-g)) * u;
+            const float hval = silu(g) * u;
             a.h[(size_t)(t.row0 + i) * a.h_stride + n] = f32_to_bf16(hval);
           }
         }

@@ -263,6 +263,33 @@ def test_deterministic_and_in_place(path):
     assert torch.equal(res, a)
 
 
+@pytest.mark.parametrize("fmt", [S.NVFP4, S.MXFP4])
+def test_prefill_partly_filled_tiles(fmt):
+    """Expert row counts around the 32-row blocks of a 128-row prefill tile (1, 32, 33,
+    64, 65, 96, 97, 127 rows in an expert's last tile, and an expert with no rows), so that
+    the waves of a tile skip none, some or all of their row blocks."""
+    counts = [129, 32, 33, 64, 65, 97, 127, 349, 0]  # 896 rows over 9 experts: 128-row tiles
+    T, k = sum(counts) // 2, 2
+    spec = S.LayerSpec(name="partial_tiles", tokens=T, hidden=512, experts=len(counts),
+                       top_k=k, inter=192, fmt=fmt, seed=1090 + fmt)
+    inp = S.make_inputs(spec, device=DEV)
+    labels = np.repeat(np.arange(len(counts)), counts)
+    oids = np.stack([labels[:T], labels[T:]], axis=1).astype(np.int32)  # distinct per token
+    assert (oids[:, 0] != oids[:, 1]).all()
+    rng = np.random.default_rng(7)
+    ow = rng.uniform(0.1, 1.0, size=(T, k)).astype(np.float32)
+    cfg = config_for(inp, M.PATH_PREFILL)
+    ws = M.alloc_workspace(cfg, DEV)
+    out = torch.empty_like(inp.x)
+    M.experts_forward(cfg, inp.x, torch.from_numpy(oids).to(DEV), torch.from_numpy(ow).to(DEV),
+                      M.expert_weights(inp.routed), None, inp.residual, out, ws)
+    _sync()
+    assert M.get_device_error(ws) == 0
+    want = O.experts_forward(f32(inp.x), oids, ow.astype(np.float64),
+                             oracle_cache(inp.routed), f32(inp.residual))
+    assert_layer_close(out.float().cpu().numpy(), want, f32(inp.residual), "partial-tiles")
+
+
 def spec_e(inp):
     return inp.spec.experts
 

@@ -15,18 +15,21 @@
 //   epilogue on values held by the same lane), i.e. 4*RB independent accumulators.
 // * Both operands reach LDS by direct-to-LDS loads (global_load_lds_*: the activation
 //   rows gathered by row_token, the FP4 weight rows and their scale bytes) into a ring
-//   of three 128-wide K stages. Step c waits for stage c, synchronises the block once,
+//   of three 64-wide K stages. Step c waits for stage c, synchronises the block once,
 //   issues stage c+2 into the slot freed by step c-1, then runs the MFMAs of stage c.
 //   Loads therefore have two steps to land, and no registers are spent on them.
+// * A block takes at most 80 KB of LDS, so two blocks run on each CU; their barriers
+//   and LDS waits fall at different times, and each fills the other's MFMA gaps.
 // * The loads and their waits are explicit: the compiler's counter tracking cannot tell
 //   a direct-to-LDS load apart from the LDS reads of other stages and would drain every
 //   load before each read. No other vector-memory load is issued in the main loop, so
 //   "at most one stage of loads in flight" means "this step's stage has landed".
-// * LDS rows are swizzled in 16-byte slots (A: slot = piece ^ (row & 15); B: slot =
-//   piece ^ ((row >> 1 ^ row >> 3) & 3)) so that the rows read by one MFMA operand load
-//   fall in distinct banks; the load side picks the source piece for its fixed slot.
-// * The MFMA K order is permuted inside a stage (lane half h covers codes 64h..64h+63),
-//   so each lane's B codes are 32 contiguous bytes of one weight row; A is read with the
+// * LDS rows are swizzled in 16-byte slots (A: slot = piece ^ (row & 7); B: slot =
+//   piece ^ ((row >> 2) & 1)) so that the 8 rows served per LDS cycle by one MFMA
+//   operand read fall in distinct banks; the load side picks the source piece for its
+//   fixed slot.
+// * The MFMA K order is permuted inside a stage (lane half h covers codes 32h..32h+31),
+//   so each lane's B codes are 16 contiguous bytes of one weight row; A is read with the
 //   same permutation.
 // * E2M1 codes become exact bf16 operands in registers (MXFP4: scaled convert by the
 //   E8M0 power of two; NVFP4: convert, times the E4M3 scale in fp32, pack).
@@ -39,7 +42,6 @@
 
 namespace moe {
 
-constexpr int kKc = 128;  // K codes per stage
 constexpr int kStages = 3;
 constexpr int kXcds = 8;
 
@@ -78,7 +80,20 @@ __device__ __forceinline__ void wait_stage() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
-__device__ __forceinline__ int b_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// B-row swizzle for PB 16-byte pieces per row (2: rows r and r+4 of 8 consecutive rows
+// take opposite pieces; 4: rows spread over the four pieces within 8 rows)
+template <int PB>
+__device__ __forceinline__ int b_swz(int row) {
+  return PB == 2 ? (row >> 2) & 1 : ((row >> 1) ^ (row >> 3)) & 3;
+}
+
+// Little-endian load of W (1, 2 or 4) scale bytes from LDS.
+template <int W>
+__device__ __forceinline__ uint32_t lds_scale(const uint8_t* p) {
+  if (W == 4) return *reinterpret_cast<const uint32_t*>(p);
+  if (W == 2) return *reinterpret_cast<const uint16_t*>(p);
+  return *p;
+}
 
 // Resolve this block's (row tile, column tile), remapped per XCD; false = no work.
 __device__ __forceinline__ bool pre_resolve(const ExpertGemmArgs& a, int ncol_tiles, Tile& t,
@@ -118,62 +133,75 @@ __device__ __forceinline__ bf16x8_t b_operand(const uint32_t q, const uint32_t s
   return as_bf16x8(d);
 }
 
-// Block = 4 waves in a WM x WN grid. Tile height MT = 32 * RB * WM; BROWS weight rows per
-// block (gate+up: BROWS/2 gate rows and the same BROWS/2 up rows; down: BROWS output
-// columns). A stage holds the A tile (MT rows x 256 bytes) and the B tile (BROWS rows x 64
-// bytes). Scales come one of two ways:
-// * SS = false: with each stage, BROWS rows x two 4-byte slots (NVFP4 4 bytes each, MXFP4
-//   2 bytes each; the 64-code tail uses the first slot). Each row's few bytes are a
-//   separate memory request.
+// Block = 4 waves (one per SIMD) in a WM x WN grid. Tile height MT = 32 * RB * WM;
+// BROWS weight rows per block (gate+up: BROWS/2 gate rows and the same BROWS/2 up rows;
+// down: BROWS output columns). A stage holds KC (64 or 128) codes of K: the A tile (MT
+// rows x 2*KC bytes of bf16) and the B tile (BROWS rows x KC/2 bytes of E2M1 codes).
+// Scales come one of two ways:
+// * SS = false: with each stage, per weight row one 4-byte LDS slot per 64 codes holding
+//   their scale bytes (NVFP4 four, MXFP4 two), loaded as one dword or one ushort.
 // * SS = true (scale rows a multiple of 16 bytes): 16 bytes per row at a time, covering
-//   SUPER stages (4 MXFP4, 2 NVFP4), into one of two super-stage slots; a quarter or half
-//   as many requests.
-template <int FMT, int RB, int WM, int NW, int CB, bool GATEUP, bool SS>
+//   SUPER stages (256 codes NVFP4, 512 MXFP4), into one of two super-stage slots.
+// With KC = 64 a block takes at most 80 KB of LDS, so two blocks share a CU: the waves of
+// one fill the SIMDs while the other waits at its barrier or on LDS. KC = 128 (one block
+// per CU) reads each weight row in 64-byte pieces, which suits the HBM-bound short tiles.
+template <int FMT, int KC, int RB, int WM, int CB, bool GATEUP, bool SS>
 struct PreShape {
+  static constexpr int NW = 4;
   static constexpr int NT = NW * 64;  // threads per block
   static constexpr int WN = NW / WM;
   static constexpr int MT = 32 * RB * WM;
   static constexpr int BROWS = 32 * CB * WN;
   static constexpr int NCOLS = GATEUP ? BROWS / 2 : BROWS;  // output columns per block
-  static constexpr int SROW = SS ? 0 : 8;  // LDS bytes per row of scales per stage
-  static constexpr int A_BYTES = MT * 256;
-  static constexpr int B_BYTES = BROWS * 64;
+  static constexpr int STEPS = KC / 16;  // MFMA steps per stage (lane half: KC/2 codes)
+  static constexpr int PA = KC / 8;      // 16-byte pieces per A row per stage
+  static constexpr int PB = KC / 32;     // 16-byte pieces per B row per stage
+  static constexpr int A_ROW = 16 * PA;
+  static constexpr int B_ROW = 16 * PB;
+  static constexpr int SLOTS = KC / 64;                      // scale slots per row (SS off)
+  static constexpr int SROW = SS ? 0 : 4 * SLOTS;            // scale bytes per row per stage
+  static constexpr int SW = FMT == 0 ? KC / 32 : KC / 64;    // scale bytes per lane half
+  static constexpr int A_BYTES = MT * A_ROW;
+  static constexpr int B_BYTES = BROWS * B_ROW;
   static constexpr int S_BYTES = BROWS * SROW;
   static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-  static constexpr int NA = MT * 16 / NT;      // 16-byte loads per lane (A)
-  static constexpr int NB = BROWS * 4 / NT;    // 16-byte loads per lane (B)
-  // scale loads: 4 bytes (NVFP4) or 2 bytes (MXFP4, whose rows may be only 2-aligned) per
-  // lane, each landing in a 4-byte LDS slot (sub-dword direct-to-LDS loads keep a 4-byte
-  // lane stride)
-  static constexpr int SUNIT = FMT == 0 ? 4 : 2;
-  static constexpr int NS = S_BYTES / 4 / NT;  // scale loads per lane
+  static constexpr int NA = MT * PA / NT;        // 16-byte loads per lane (A)
+  static constexpr int NB = BROWS * PB / NT;     // 16-byte loads per lane (B)
+  static constexpr int NS = S_BYTES / 4 / NT;    // scale loads per lane (one per slot)
   static constexpr int NLOADS = NA + NB + NS;
-  static constexpr int SUPER = FMT == 0 ? 2 : 4;              // stages per super-stage
+  static constexpr int SUPER = (FMT == 0 ? 256 : 512) / KC;  // stages per 16 scale bytes
   // super-stage scale loads: one lane per row, issued by the first SS_WAVES waves
   static constexpr int SS_WAVES = SS ? (BROWS / 64 < NW ? BROWS / 64 : NW) : 0;
   static constexpr int NSS = SS ? BROWS / (SS_WAVES * 64) : 0;  // per lane of those waves
-  static constexpr int SS_BYTES = SS ? 2 * BROWS * 16 : 0;   // two super-stage slots
-  static constexpr size_t SMEM = (size_t)kStages * STAGE + SS_BYTES + MT * sizeof(int);
-  static_assert(NA * NT == MT * 16 && NB * NT == BROWS * 4 && NS * NT * 4 == S_BYTES,
+  static constexpr int SS_BYTES = SS ? 2 * BROWS * 16 : 0;       // two super-stage slots
+  static constexpr size_t SMEM = (size_t)kStages * STAGE + SS_BYTES;
+  static constexpr int BLOCKS_PER_CU = KC == 64 ? 2 : 1;
+  static_assert(KC == 64 || KC == 128, "stage width");
+  static_assert(NA * NT == MT * PA && NB * NT == BROWS * PB && NS * NT * 4 == S_BYTES,
                 "a stage must split evenly over the block");
   static_assert(!SS || NSS * SS_WAVES * 64 == BROWS, "one super-stage load per row");
   static_assert(CB % 2 == 0 || !GATEUP, "gate+up pairs column blocks");
   static_assert(NLOADS + NSS <= 31, "two stages of loads must fit the wait counter");
-  static_assert(SMEM <= 160 * 1024, "three stages must fit the 160 KB of LDS");
+  static_assert(MT * (int)sizeof(int) <= STAGE, "the row map borrows the third stage slot");
+  static_assert(SMEM * BLOCKS_PER_CU <= 160 * 1024, "the blocks of a CU must fit its LDS");
 };
 
-template <int FMT, int RB, int WM, int NW, int CB, bool GATEUP, bool SS>
-__global__ __launch_bounds__(NW * 64) void k_pre_gemm(ExpertGemmArgs a) {
-  using Sh = PreShape<FMT, RB, WM, NW, CB, GATEUP, SS>;
+template <int FMT, int KC, int RB, int WM, int CB, bool GATEUP, bool SS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KC == 64 ? 2 : 1, 2)))
+void k_pre_gemm(ExpertGemmArgs a) {
+  using Sh = PreShape<FMT, KC, RB, WM, CB, GATEUP, SS>;
   constexpr int NT = Sh::NT;
   constexpr int WN = Sh::WN, BROWS = Sh::BROWS, NCOLS = Sh::NCOLS, MT = Sh::MT;
   constexpr int NA = Sh::NA, NB = Sh::NB, NS = Sh::NS, NSS = Sh::NSS, SUPER = Sh::SUPER;
+  constexpr int PA = Sh::PA, PB = Sh::PB, STEPS = Sh::STEPS, SLOTS = Sh::SLOTS;
   extern __shared__ __align__(16) uint8_t s_dyn[];
   uint8_t* s_ss = s_dyn + kStages * Sh::STAGE;  // super-stage scale slots (SS)
-  int* s_tok = reinterpret_cast<int*>(s_ss + Sh::SS_BYTES);
+  // source row of each A tile row; lives in the third stage slot, which the first load
+  // into it (stage 2, issued after the first barrier of the main loop) overwrites
+  int* s_tok = reinterpret_cast<int*>(s_dyn + 2 * Sh::STAGE);
 
   const int N = GATEUP ? a.I : a.H;  // rows of each weight matrix
-  const int K = GATEUP ? a.H : a.I;
+  const int K = GATEUP ? a.H : a.I;  // a multiple of KC
   const int ncol_tiles = (N + NCOLS - 1) / NCOLS;
   Tile t;
   int ct;
@@ -189,8 +217,8 @@ __global__ __launch_bounds__(NW * 64) void k_pre_gemm(ExpertGemmArgs a) {
   const WeightDesc& w0 = GATEUP ? a.gate : a.down;
   const WeightDesc& w1 = GATEUP ? a.up : a.down;
 
-  // source row of each A tile row: gathered token (gate+up) or h row (down); rows past
-  // the tile's count repeat its first row (results discarded)
+  // gathered token (gate+up) or h row (down); rows past the tile's count repeat its
+  // first row (results discarded)
   for (int i = threadIdx.x; i < MT; i += NT) {
     const int ii = i < t.count ? i : 0;
     s_tok[i] = GATEUP ? a.row_token[t.row0 + ii] : t.row0 + ii;
@@ -200,11 +228,12 @@ __global__ __launch_bounds__(NW * 64) void k_pre_gemm(ExpertGemmArgs a) {
   // Source address of each load of this lane (fixed across stages, + the stage's K
   // offset). The i-th load of a wave fills LDS slots (wave * n + i) * 64 + lane of its
   // region; a slot holds the source piece that the swizzle assigns to it.
+  // A: PA pieces of 16 bytes per row, slot = piece ^ (row & (PA - 1)).
   const uint16_t* asrc[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int slot = (wave * NA + i) * 64 + lane;
-    const int row = slot >> 4, piece = (slot & 15) ^ (row & 15);
+    const int row = slot / PA, piece = (slot % PA) ^ (row & (PA - 1));
     const uint16_t* base = GATEUP ? a.x + (size_t)s_tok[row] * a.H
                                   : a.h + (size_t)s_tok[row] * a.h_stride;
     asrc[i] = base + piece * 8;
@@ -221,11 +250,12 @@ __global__ __launch_bounds__(NW * 64) void k_pre_gemm(ExpertGemmArgs a) {
     }
     return (size_t)e * N + (n < N ? n : 0);
   };
+  // B: PB pieces of 16 bytes per row, slot = piece ^ b_swz(row)
   const uint8_t* bsrc[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int slot = (wave * NB + i) * 64 + lane;
-    const int brow = slot >> 2, piece = (slot & 3) ^ b_swz(brow);
+    const int brow = slot / PB, piece = (slot % PB) ^ b_swz<PB>(brow);
     const WeightDesc* w;
     const size_t rw = wrow(brow, w);
     bsrc[i] = w->packed + rw * row_bytes + piece * 16;
@@ -233,12 +263,11 @@ __global__ __launch_bounds__(NW * 64) void k_pre_gemm(ExpertGemmArgs a) {
   const uint8_t* ssrc[NS > 0 ? NS : 1];
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
-    const int slot = (wave * NS + i) * 64 + lane;  // 4-byte LDS slots, two per row
     const WeightDesc* w;
-    const size_t rw = wrow(slot >> 1, w);
-    ssrc[i] = w->scales + rw * sbytes + (slot & 1) * Sh::SUNIT;
+    const int slot = (wave * NS + i) * 64 + lane;  // 4-byte slot u of its row: 64 codes
+    const size_t rw = wrow(slot / SLOTS, w);
+    ssrc[i] = w->scales + rw * sbytes + (slot % SLOTS) * (FMT == 0 ? 4 : 2);
   }
-
   const uint8_t* sssrc[NSS > 0 ? NSS : 1];
 #pragma unroll
   for (int i = 0; i < NSS; ++i) {
@@ -248,16 +277,13 @@ __global__ __launch_bounds__(NW * 64) void k_pre_gemm(ExpertGemmArgs a) {
     sssrc[i] = w->scales + rw * sbytes;
   }
 
-  const int nfull = K / kKc;
-  const int nch = nfull + (K % kKc ? 1 : 0);  // the last stage may be a 64-code tail
+  const int nch = K / KC;
 
-  // Loads of stage c: always NLOADS per lane, so the wait count is a constant. In the
-  // 64-code tail, pieces past K re-read pieces below K (their slots are not read).
+  // Loads of stage c: always NLOADS per lane, so the wait count is a constant.
   auto issue = [&](int c) {
     const uint32_t abase = lds_addr(s_dyn + (c % kStages) * Sh::STAGE);
     const uint32_t bbase = abase + Sh::A_BYTES, sbase = bbase + Sh::B_BYTES;
-    const int k0 = c * kKc;
-    const bool tail = c == nfull;
+    const int k0 = c * KC;
     if (SS && c % SUPER == 0 && wave < Sh::SS_WAVES) {
       const int j = c / SUPER;
       const uint32_t ssbase = lds_addr(s_ss + (j & 1) * BROWS * 16);
@@ -269,28 +295,22 @@ __global__ __launch_bounds__(NW * 64) void k_pre_gemm(ExpertGemmArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      const int slot0 = (wave * NA + i) * 64, slot = slot0 + lane, row = slot >> 4;
-      const int piece = (slot & 15) ^ (row & 15);
-      dma16(asrc[i] + k0 - (tail ? (piece & 8) * 8 : 0),
-            __builtin_amdgcn_readfirstlane(abase + slot0 * 16));
+      const int slot0 = (wave * NA + i) * 64;
+      dma16(asrc[i] + k0, __builtin_amdgcn_readfirstlane(abase + slot0 * 16));
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int slot0 = (wave * NB + i) * 64, slot = slot0 + lane;
-      const int piece = (slot & 3) ^ b_swz(slot >> 2);
-      dma16(bsrc[i] + k0 / 2 - (tail ? (piece & 2) * 16 : 0),
-            __builtin_amdgcn_readfirstlane(bbase + slot0 * 16));
+      const int slot0 = (wave * NB + i) * 64;
+      dma16(bsrc[i] + k0 / 2, __builtin_amdgcn_readfirstlane(bbase + slot0 * 16));
     }
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      // a row's second half re-reads its first in the tail (half as many scale bytes)
       const int slot0 = (wave * NS + i) * 64;
-      const int back = tail ? ((slot0 + lane) & 1) * Sh::SUNIT : 0;
       const uint32_t dst = __builtin_amdgcn_readfirstlane(sbase + slot0 * 4);
       if (FMT == 0) {
-        dma4(ssrc[i] + k0 / 16 - back, dst);
+        dma4(ssrc[i] + k0 / 16, dst);
       } else {
-        dma2(ssrc[i] + k0 / 32 - back, dst);
+        dma2(ssrc[i] + k0 / 32, dst);
       }
     }
   };
@@ -311,47 +331,37 @@ __global__ __launch_bounds__(NW * 64) void k_pre_gemm(ExpertGemmArgs a) {
                        : wn * CB * 32 + cb * 32;
   }
   const int arow = wm * 32 * RB + r;  // + rb * 32
-  const int bsw = b_swz(r);            // = b_swz(brow0[cb] + r): brow0 is a multiple of 32
+  const int bsw = b_swz<PB>(r);        // = b_swz(brow0[cb] + r): brow0 is a multiple of 32
 
   // row blocks of this wave that hold rows of the tile: a partly filled tile skips the
-  // MFMAs of its empty 32-row blocks (the other waves of the same SIMD then run alone)
+  // MFMAs of its empty 32-row blocks
   int nrb = (t.count - wm * 32 * RB + 31) / 32;
   nrb = nrb < 0 ? 0 : (nrb > RB ? RB : nrb);
 
-  // MFMAs of one stage for the first NR row blocks (STEPS = 8, or 4 in the 64-code tail
-  // where lane half h covers codes 32h..32h+31)
-  auto stage_mma = [&](auto nr_c, auto steps_c, int c) {
-    constexpr int NR = decltype(nr_c)::value, STEPS = decltype(steps_c)::value;
+  // MFMAs of stage c for the first NR row blocks: STEPS steps of K 16, lane half h
+  // covering codes (KC/2)h..(KC/2)h+KC/2-1 of the stage (8 per step)
+  auto stage_mma = [&](auto nr_c, int c) {
+    constexpr int NR = decltype(nr_c)::value;
     if constexpr (NR == 0) return;
-    const bool tail = STEPS == 4;
     const uint8_t* sa = s_dyn + (c % kStages) * Sh::STAGE;
     const uint8_t* sbq = sa + Sh::A_BYTES;
     const uint8_t* ssc = sbq + Sh::B_BYTES;
-    uint32_t q[CB][8], sc[CB];
+    uint32_t q[CB][STEPS], sc[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const int srow = brow0[cb] + r;
-      const uint8_t* row = sbq + srow * 64;
-      if (tail) {
-        const uint4 v0 = *reinterpret_cast<const uint4*>(row + ((half ^ bsw) << 4));
-        q[cb][0] = v0.x; q[cb][1] = v0.y; q[cb][2] = v0.z; q[cb][3] = v0.w;
-        q[cb][4] = q[cb][5] = q[cb][6] = q[cb][7] = 0;
-        sc[cb] = FMT == 0 ? (uint32_t)*reinterpret_cast<const uint16_t*>(ssc + srow * 8 + 2 * half)
-                          : (uint32_t)ssc[srow * 8 + half];
-        continue;
+#pragma unroll
+      for (int j = 0; j < PB / 2; ++j) {
+        const int piece = (PB / 2) * half + j;
+        const uint4 v = *reinterpret_cast<const uint4*>(sbq + srow * Sh::B_ROW + ((piece ^ bsw) << 4));
+        q[cb][4 * j] = v.x; q[cb][4 * j + 1] = v.y; q[cb][4 * j + 2] = v.z; q[cb][4 * j + 3] = v.w;
       }
-      const uint4 v0 = *reinterpret_cast<const uint4*>(row + (((2 * half) ^ bsw) << 4));
-      const uint4 v1 = *reinterpret_cast<const uint4*>(row + (((2 * half + 1) ^ bsw) << 4));
-      q[cb][0] = v0.x; q[cb][1] = v0.y; q[cb][2] = v0.z; q[cb][3] = v0.w;
-      q[cb][4] = v1.x; q[cb][5] = v1.y; q[cb][6] = v1.z; q[cb][7] = v1.w;
-      if (SS) {
-        const uint8_t* sp = s_ss + ((c / SUPER) & 1) * BROWS * 16 + srow * 16;
-        sc[cb] = FMT == 0 ? *reinterpret_cast<const uint32_t*>(sp + (c & 1) * 8 + 4 * half)
-                          : (uint32_t)*reinterpret_cast<const uint16_t*>(sp + (c & 3) * 4 + 2 * half);
-      } else {
-        sc[cb] = FMT == 0 ? *reinterpret_cast<const uint32_t*>(ssc + srow * 8 + 4 * half)
-                          : (uint32_t)*reinterpret_cast<const uint16_t*>(ssc + srow * 8 + 4 * half);
-      }
+      // this lane's scale bytes of the stage (blocks of its codes: NVFP4 KC/32, MXFP4 KC/64)
+      const uint8_t* sp =
+          SS ? s_ss + ((c / SUPER) & 1) * BROWS * 16 + srow * 16 + (c % SUPER) * 2 * Sh::SW +
+                   half * Sh::SW
+             : ssc + srow * Sh::SROW + (SLOTS == 2 ? 4 * half : half * Sh::SW);
+      sc[cb] = lds_scale<Sh::SW>(sp);
     }
     // every A operand of the stage is read up front, in the order of use, so that LDS
     // latency overlaps the MFMAs instead of stalling each step (LDS reads return in order)
@@ -361,8 +371,8 @@ __global__ __launch_bounds__(NW * 64) void k_pre_gemm(ExpertGemmArgs a) {
 #pragma unroll
       for (int rb = 0; rb < NR; ++rb) {
         const int row = arow + rb * 32;
-        const int piece = tail ? 4 * half + s : 8 * half + s;
-        av[rb][s] = *reinterpret_cast<const uint4*>(sa + row * 256 + ((piece ^ (row & 15)) << 4));
+        av[rb][s] = *reinterpret_cast<const uint4*>(
+            sa + row * Sh::A_ROW + (((STEPS * half + s) ^ (row & (PA - 1))) << 4));
         __builtin_amdgcn_sched_barrier(0);  // keep the reads in the order they are used
       }
     }
@@ -380,13 +390,12 @@ __global__ __launch_bounds__(NW * 64) void k_pre_gemm(ExpertGemmArgs a) {
       }
     }
   };
+
   issue(0);
   if (nch > 1) issue(1);
-  // full stages, then the 64-code tail stage (if any) after the loop, so that the
-  // accumulators have a single definition inside the loop
   auto kloop = [&](auto nr_c) {
 #pragma unroll 1
-    for (int c = 0; c < nfull; ++c) {
+    for (int c = 0; c < nch; ++c) {
       // in flight: the loads of stage c+1 (with a super-stage of scales if it starts one)
       if (c + 1 >= nch) {
         wait_stage<0>();
@@ -396,11 +405,7 @@ __global__ __launch_bounds__(NW * 64) void k_pre_gemm(ExpertGemmArgs a) {
         wait_stage<Sh::NLOADS>();
       }
       if (c + 2 < nch) issue(c + 2);
-      stage_mma(nr_c, std::integral_constant<int, 8>{}, c);
-    }
-    if (nch > nfull) {
-      wait_stage<0>();
-      stage_mma(nr_c, std::integral_constant<int, 4>{}, nfull);
+      stage_mma(nr_c, c);
     }
   };
   if (nrb >= RB) {
@@ -452,12 +457,12 @@ __global__ __launch_bounds__(NW * 64) void k_pre_gemm(ExpertGemmArgs a) {
   }
 }
 
-template <int FMT, int RB, int WM, int NW, int CB, bool GATEUP, bool SS>
+template <int FMT, int KC, int RB, int WM, int CB, bool GATEUP, bool SS>
 static hipError_t launch_pre_ss(const ExpertGemmArgs& a, hipStream_t s) {
-  using Sh = PreShape<FMT, RB, WM, NW, CB, GATEUP, SS>;
+  using Sh = PreShape<FMT, KC, RB, WM, CB, GATEUP, SS>;
   const int N = GATEUP ? a.I : a.H;
   const int ncol = (N + Sh::NCOLS - 1) / Sh::NCOLS;
-  auto kern = k_pre_gemm<FMT, RB, WM, NW, CB, GATEUP, SS>;
+  auto kern = k_pre_gemm<FMT, KC, RB, WM, CB, GATEUP, SS>;
   static bool attr_set = false;  // one attribute call per instantiation and process
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -470,33 +475,38 @@ static hipError_t launch_pre_ss(const ExpertGemmArgs& a, hipStream_t s) {
 }
 
 // Super-staged scales when each scale row is a whole number of 16-byte pieces.
-template <int FMT, int RB, int WM, int NW, int CB, bool GATEUP>
+template <int FMT, int KC, int RB, int WM, int CB, bool GATEUP>
 static hipError_t launch_pre_shape(const ExpertGemmArgs& a, hipStream_t s) {
   const int K = GATEUP ? a.H : a.I;
+  if (K % KC != 0) return hipErrorInvalidValue;
   const int sbytes = K / (FMT == 0 ? 16 : 32);
-  if (sbytes % 16 == 0) return launch_pre_ss<FMT, RB, WM, NW, CB, GATEUP, true>(a, s);
-  return launch_pre_ss<FMT, RB, WM, NW, CB, GATEUP, false>(a, s);
+  if (sbytes % 16 == 0) return launch_pre_ss<FMT, KC, RB, WM, CB, GATEUP, true>(a, s);
+  return launch_pre_ss<FMT, KC, RB, WM, CB, GATEUP, false>(a, s);
 }
 
-// Tile height MT -> block shape (row blocks per wave RB, waves along M WM, waves NW,
-// column blocks per wave CB): 128 = RB 2 x WM 2 with 8 waves of 2 column blocks (two waves
-// per SIMD), 64 = 1 x 2 (4 waves of 4), 32 = 1 x 1 (4 waves of 4).
-#ifndef MOE_PRE_NW128
-#define MOE_PRE_NW128 8
-#endif
+// Tile height MT -> stage width KC and block shape (row blocks per wave RB, waves along M
+// WM, column blocks per wave CB): 128 = 64-code stages, 2 x 2 x 4 (128 x 256 weight
+// rows); 64 = 64-code stages, 1 x 2 x 4 (64 x 256); 32 = 128-code stages, 1 x 1 x 4
+// (32 x 512). K that is not a multiple of 128 takes 64-code stages at height 32 too.
 template <bool GATEUP>
 static hipError_t launch_pre(const ExpertGemmArgs& a, int mt, hipStream_t s) {
   if (a.tile_bound <= 0) return hipSuccess;
   const int fmt = GATEUP ? a.gate.fmt : a.down.fmt;
-  constexpr int NW = MOE_PRE_NW128, CB = 16 / NW;
+  const int K = GATEUP ? a.H : a.I;
   if (fmt == 0) {
-    if (mt == 32) return launch_pre_shape<0, 1, 1, 4, 4, GATEUP>(a, s);
-    if (mt == 64) return launch_pre_shape<0, 1, 2, 4, 4, GATEUP>(a, s);
-    return launch_pre_shape<0, 2, 2, NW, CB, GATEUP>(a, s);
+    if (mt == 32) {
+      return K % 128 == 0 ? launch_pre_shape<0, 128, 1, 1, 4, GATEUP>(a, s)
+                          : launch_pre_shape<0, 64, 1, 1, 4, GATEUP>(a, s);
+    }
+    if (mt == 64) return launch_pre_shape<0, 64, 1, 2, 4, GATEUP>(a, s);
+    return launch_pre_shape<0, 64, 2, 2, 4, GATEUP>(a, s);
   }
-  if (mt == 32) return launch_pre_shape<1, 1, 1, 4, 4, GATEUP>(a, s);
-  if (mt == 64) return launch_pre_shape<1, 1, 2, 4, 4, GATEUP>(a, s);
-  return launch_pre_shape<1, 2, 2, NW, CB, GATEUP>(a, s);
+  if (mt == 32) {
+    return K % 128 == 0 ? launch_pre_shape<1, 128, 1, 1, 4, GATEUP>(a, s)
+                        : launch_pre_shape<1, 64, 1, 1, 4, GATEUP>(a, s);
+  }
+  if (mt == 64) return launch_pre_shape<1, 64, 1, 2, 4, GATEUP>(a, s);
+  return launch_pre_shape<1, 64, 2, 2, 4, GATEUP>(a, s);
 }
 
 hipError_t launch_prefill_gate_up(const ExpertGemmArgs& a, int mt, hipStream_t s) {

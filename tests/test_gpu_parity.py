@@ -208,6 +208,9 @@ SMALL = {
     "hash_sqrtsp_mini": S.scaled(S.WORKLOADS["hash_mxfp4_t512"], tokens=40, hidden=512,
                                  experts=32, inter=256, shared_inter=128, vocab=1000,
                                  score=S.SQRT_SOFTPLUS),
+    # K a multiple of 64 but not of 128 at 32-row prefill tiles (64-code stages)
+    "oddk_mini": S.LayerSpec(name="oddk_mini", tokens=9, hidden=320, experts=16, top_k=4,
+                             inter=192, fmt=S.MXFP4, seed=1078),
     # softmax+bias routing over 48 + 16 zero-computation experts (identity contributions)
     "zero_experts_mini": S.LayerSpec(name="zero_experts_mini", tokens=23, hidden=512,
                                      experts=48, top_k=8, inter=256, fmt=S.NVFP4,

@@ -49,11 +49,9 @@ constexpr int kDecodeMaxLds = 160 * 1024;  // staged activations of a decode til
 hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, uint16_t* out, int T, int H,
                           float eps, hipStream_t s);
 
-// Router GEMM split: H is summed in ks slices of hsplit columns (fp64 partials, added in
-// slice order by the top-K kernel); few tokens use the fp64-MFMA kernel, many tokens a
-// tiled fp64 kernel.
-constexpr int kRouterSmallMaxT = 64;  // tokens up to which the MFMA router runs
-constexpr int kRouterMaxSplit = 8;    // H slices of the router sum
+// Router GEMM split: H is summed in ks slices of hsplit columns (fp64 partials from the
+// fp64-MFMA kernel, added in slice order by the top-K kernel).
+constexpr int kRouterMaxSplit = 8;  // H slices of the router sum
 struct RouterPlan {
   int ks, hsplit;
 };

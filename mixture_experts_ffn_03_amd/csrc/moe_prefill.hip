@@ -24,10 +24,9 @@
 //   a direct-to-LDS load apart from the LDS reads of other stages and would drain every
 //   load before each read. No other vector-memory load is issued in the main loop, so
 //   "at most one stage of loads in flight" means "this step's stage has landed".
-// * LDS rows are swizzled in 16-byte slots (A: slot = piece ^ (row & 7); B: slot =
-//   piece ^ ((row >> 2) & 1)) so that the 8 rows served per LDS cycle by one MFMA
-//   operand read fall in distinct banks; the load side picks the source piece for its
-//   fixed slot.
+// * LDS rows are swizzled in 16-byte slots (a_swz, b_swz) so that the rows served per
+//   LDS cycle by one MFMA operand read fall in distinct banks; the load side picks the
+//   source piece for its fixed slot.
 // * The MFMA K order is permuted inside a stage (lane half h covers codes 32h..32h+31),
 //   so each lane's B codes are 16 contiguous bytes of one weight row; A is read with the
 //   same permutation.
@@ -42,7 +41,6 @@
 
 namespace moe {
 
-constexpr int kStages = 3;
 constexpr int kXcds = 8;
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -80,11 +78,35 @@ __device__ __forceinline__ void wait_stage() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
-// B-row swizzle for PB 16-byte pieces per row (2: rows r and r+4 of 8 consecutive rows
-// take opposite pieces; 4: rows spread over the four pieces within 8 rows)
+// wait_stage with R (0..3) stages of NL loads still in flight, one of which (ss) also
+// carries NSS super-stage scale loads
+template <int NL, int NSS>
+__device__ __forceinline__ void wait_inflight(int r, bool ss) {
+  if (r <= 0) {
+    wait_stage<0>();
+  } else if (r == 1) {
+    if (ss) wait_stage<NL + NSS>(); else wait_stage<NL>();
+  } else if (r == 2) {
+    if (ss) wait_stage<2 * NL + NSS>(); else wait_stage<2 * NL>();
+  } else {
+    if (ss) wait_stage<3 * NL + NSS>(); else wait_stage<3 * NL>();
+  }
+}
+
+// Row swizzles of the 16-byte pieces in LDS. An MFMA operand read (ds_read_b128) has
+// lane r read row r; every 16 consecutive lanes (one LDS cycle of 256 bytes), and every
+// 8 of them, must land on distinct 16-byte bank groups. A rows of 8 pieces (128 bytes)
+// XOR the piece with a permutation of row bits 0..3 that is distinct over any 8
+// consecutive rows and over the 8 rows of each parity within 16; rows of 16 pieces use
+// row bits 0..3 directly. B rows of 2 pieces (32 bytes) flip the piece by row bit 2 xor
+// bit 3; of 4 pieces (64 bytes) by ((row >> 1) ^ (row >> 3)) & 3.
+template <int PA>
+__device__ __forceinline__ int a_swz(int row) {
+  return PA == 16 ? row & 15 : ((row >> 1) ^ ((row & 1) << 2)) & 7;
+}
 template <int PB>
 __device__ __forceinline__ int b_swz(int row) {
-  return PB == 2 ? (row >> 2) & 1 : ((row >> 1) ^ (row >> 3)) & 3;
+  return PB == 2 ? ((row >> 2) ^ (row >> 3)) & 1 : ((row >> 1) ^ (row >> 3)) & 3;
 }
 
 // Little-endian load of W (1, 2 or 4) scale bytes from LDS.
@@ -133,7 +155,7 @@ __device__ __forceinline__ bf16x8_t b_operand(const uint32_t q, const uint32_t s
   return as_bf16x8(d);
 }
 
-// Block = 4 waves (one per SIMD) in a WM x WN grid. Tile height MT = 32 * RB * WM;
+// Block = 4 waves (one per SIMD) in a WM x WN grid, with a ring of NSTG stage slots. Tile height MT = 32 * RB * WM;
 // BROWS weight rows per block (gate+up: BROWS/2 gate rows and the same BROWS/2 up rows;
 // down: BROWS output columns). A stage holds KC (64 or 128) codes of K: the A tile (MT
 // rows x 2*KC bytes of bf16) and the B tile (BROWS rows x KC/2 bytes of E2M1 codes).
@@ -145,7 +167,7 @@ __device__ __forceinline__ bf16x8_t b_operand(const uint32_t q, const uint32_t s
 // With KC = 64 a block takes at most 80 KB of LDS, so two blocks share a CU: the waves of
 // one fill the SIMDs while the other waits at its barrier or on LDS. KC = 128 (one block
 // per CU) reads each weight row in 64-byte pieces, which suits the HBM-bound short tiles.
-template <int FMT, int KC, int RB, int WM, int CB, bool GATEUP, bool SS>
+template <int FMT, int KC, int NSTG, int RB, int WM, int CB, bool GATEUP, bool SS>
 struct PreShape {
   static constexpr int NW = 4;
   static constexpr int NT = NW * 64;  // threads per block
@@ -174,31 +196,39 @@ struct PreShape {
   static constexpr int SS_WAVES = SS ? (BROWS / 64 < NW ? BROWS / 64 : NW) : 0;
   static constexpr int NSS = SS ? BROWS / (SS_WAVES * 64) : 0;  // per lane of those waves
   static constexpr int SS_BYTES = SS ? 2 * BROWS * 16 : 0;       // two super-stage slots
-  static constexpr size_t SMEM = (size_t)kStages * STAGE + SS_BYTES;
-  static constexpr int BLOCKS_PER_CU = KC == 64 ? 2 : 1;
+  static constexpr int LEAD = NSTG - 1;  // stages in flight ahead of the one computed
+  static constexpr size_t SMEM = (size_t)NSTG * STAGE + SS_BYTES;
+  static constexpr int BLOCKS_PER_CU = SMEM <= 80 * 1024 ? 2 : 1;
   static_assert(KC == 64 || KC == 128, "stage width");
   static_assert(NA * NT == MT * PA && NB * NT == BROWS * PB && NS * NT * 4 == S_BYTES,
                 "a stage must split evenly over the block");
   static_assert(!SS || NSS * SS_WAVES * 64 == BROWS, "one super-stage load per row");
   static_assert(CB % 2 == 0 || !GATEUP, "gate+up pairs column blocks");
-  static_assert(NLOADS + NSS <= 31, "two stages of loads must fit the wait counter");
-  static_assert(MT * (int)sizeof(int) <= STAGE, "the row map borrows the third stage slot");
+  static_assert(NSTG >= 2 && NSTG <= 5, "ring depth");
+  static_assert(LEAD <= SUPER, "a super-stage slot is refilled only after its last read");
+  static_assert((LEAD - 1) * NLOADS + NSS <= 63, "the loads in flight must fit the wait counter");
+  static_assert(MT * (int)sizeof(int) <= STAGE, "the row map borrows the last stage slot");
   static_assert(SMEM * BLOCKS_PER_CU <= 160 * 1024, "the blocks of a CU must fit its LDS");
 };
 
-template <int FMT, int KC, int RB, int WM, int CB, bool GATEUP, bool SS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KC == 64 ? 2 : 1, 2)))
+// waves per SIMD the register allocation must allow: two when two blocks share a CU
+template <int FMT, int KC, int NSTG, int RB, int WM, int CB, bool GATEUP, bool SS>
+constexpr int kPreWaves = PreShape<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS>::BLOCKS_PER_CU;
+
+template <int FMT, int KC, int NSTG, int RB, int WM, int CB, bool GATEUP, bool SS>
+__global__ __launch_bounds__(256) __attribute__((
+    amdgpu_waves_per_eu(kPreWaves<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS>, 2)))
 void k_pre_gemm(ExpertGemmArgs a) {
-  using Sh = PreShape<FMT, KC, RB, WM, CB, GATEUP, SS>;
+  using Sh = PreShape<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS>;
   constexpr int NT = Sh::NT;
   constexpr int WN = Sh::WN, BROWS = Sh::BROWS, NCOLS = Sh::NCOLS, MT = Sh::MT;
   constexpr int NA = Sh::NA, NB = Sh::NB, NS = Sh::NS, NSS = Sh::NSS, SUPER = Sh::SUPER;
   constexpr int PA = Sh::PA, PB = Sh::PB, STEPS = Sh::STEPS, SLOTS = Sh::SLOTS;
   extern __shared__ __align__(16) uint8_t s_dyn[];
-  uint8_t* s_ss = s_dyn + kStages * Sh::STAGE;  // super-stage scale slots (SS)
-  // source row of each A tile row; lives in the third stage slot, which the first load
-  // into it (stage 2, issued after the first barrier of the main loop) overwrites
-  int* s_tok = reinterpret_cast<int*>(s_dyn + 2 * Sh::STAGE);
+  uint8_t* s_ss = s_dyn + NSTG * Sh::STAGE;  // super-stage scale slots (SS)
+  // source row of each A tile row; lives in the last stage slot, which the first load
+  // into it (stage LEAD, issued after the first barrier of the main loop) overwrites
+  int* s_tok = reinterpret_cast<int*>(s_dyn + Sh::LEAD * Sh::STAGE);
 
   const int N = GATEUP ? a.I : a.H;  // rows of each weight matrix
   const int K = GATEUP ? a.H : a.I;  // a multiple of KC
@@ -228,12 +258,12 @@ void k_pre_gemm(ExpertGemmArgs a) {
   // Source address of each load of this lane (fixed across stages, + the stage's K
   // offset). The i-th load of a wave fills LDS slots (wave * n + i) * 64 + lane of its
   // region; a slot holds the source piece that the swizzle assigns to it.
-  // A: PA pieces of 16 bytes per row, slot = piece ^ (row & (PA - 1)).
+  // A: PA pieces of 16 bytes per row, slot = piece ^ a_swz(row).
   const uint16_t* asrc[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int slot = (wave * NA + i) * 64 + lane;
-    const int row = slot / PA, piece = (slot % PA) ^ (row & (PA - 1));
+    const int row = slot / PA, piece = (slot % PA) ^ a_swz<PA>(row);
     const uint16_t* base = GATEUP ? a.x + (size_t)s_tok[row] * a.H
                                   : a.h + (size_t)s_tok[row] * a.h_stride;
     asrc[i] = base + piece * 8;
@@ -281,7 +311,7 @@ void k_pre_gemm(ExpertGemmArgs a) {
 
   // Loads of stage c: always NLOADS per lane, so the wait count is a constant.
   auto issue = [&](int c) {
-    const uint32_t abase = lds_addr(s_dyn + (c % kStages) * Sh::STAGE);
+    const uint32_t abase = lds_addr(s_dyn + (c % NSTG) * Sh::STAGE);
     const uint32_t bbase = abase + Sh::A_BYTES, sbase = bbase + Sh::B_BYTES;
     const int k0 = c * KC;
     if (SS && c % SUPER == 0 && wave < Sh::SS_WAVES) {
@@ -331,7 +361,7 @@ void k_pre_gemm(ExpertGemmArgs a) {
                        : wn * CB * 32 + cb * 32;
   }
   const int arow = wm * 32 * RB + r;  // + rb * 32
-  const int bsw = b_swz<PB>(r);        // = b_swz(brow0[cb] + r): brow0 is a multiple of 32
+  const int bsw = b_swz<PB>(r);  // = b_swz(brow0[cb] + r): brow0 is a multiple of 32
 
   // row blocks of this wave that hold rows of the tile: a partly filled tile skips the
   // MFMAs of its empty 32-row blocks
@@ -343,7 +373,7 @@ void k_pre_gemm(ExpertGemmArgs a) {
   auto stage_mma = [&](auto nr_c, int c) {
     constexpr int NR = decltype(nr_c)::value;
     if constexpr (NR == 0) return;
-    const uint8_t* sa = s_dyn + (c % kStages) * Sh::STAGE;
+    const uint8_t* sa = s_dyn + (c % NSTG) * Sh::STAGE;
     const uint8_t* sbq = sa + Sh::A_BYTES;
     const uint8_t* ssc = sbq + Sh::B_BYTES;
     uint32_t q[CB][STEPS], sc[CB];
@@ -372,7 +402,7 @@ void k_pre_gemm(ExpertGemmArgs a) {
       for (int rb = 0; rb < NR; ++rb) {
         const int row = arow + rb * 32;
         av[rb][s] = *reinterpret_cast<const uint4*>(
-            sa + row * Sh::A_ROW + (((STEPS * half + s) ^ (row & (PA - 1))) << 4));
+            sa + row * Sh::A_ROW + (((STEPS * half + s) ^ a_swz<PA>(row)) << 4));
         __builtin_amdgcn_sched_barrier(0);  // keep the reads in the order they are used
       }
     }
@@ -391,20 +421,23 @@ void k_pre_gemm(ExpertGemmArgs a) {
     }
   };
 
-  issue(0);
-  if (nch > 1) issue(1);
+#pragma unroll
+  for (int i = 0; i < Sh::LEAD; ++i)
+    if (i < nch) issue(i);
   auto kloop = [&](auto nr_c) {
 #pragma unroll 1
     for (int c = 0; c < nch; ++c) {
-      // in flight: the loads of stage c+1 (with a super-stage of scales if it starts one)
-      if (c + 1 >= nch) {
-        wait_stage<0>();
-      } else if (SS && (c + 1) % SUPER == 0 && wave < Sh::SS_WAVES) {
-        wait_stage<Sh::NLOADS + NSS>();
-      } else {
-        wait_stage<Sh::NLOADS>();
+      // may stay in flight: stages c+1 .. c+LEAD-1 (fewer near the end), one of which may
+      // start a super-stage of scales (at most one: LEAD <= SUPER)
+      int inflight = nch - 1 - c;
+      inflight = inflight < Sh::LEAD - 1 ? inflight : Sh::LEAD - 1;
+      bool ss = false;
+      if (SS && wave < Sh::SS_WAVES) {
+        const int next = (c / SUPER + 1) * SUPER;  // first super-stage start after c
+        ss = next <= c + inflight;
       }
-      if (c + 2 < nch) issue(c + 2);
+      wait_inflight<Sh::NLOADS, NSS>(inflight, ss);
+      if (c + Sh::LEAD < nch) issue(c + Sh::LEAD);
       stage_mma(nr_c, c);
     }
   };
@@ -457,12 +490,12 @@ void k_pre_gemm(ExpertGemmArgs a) {
   }
 }
 
-template <int FMT, int KC, int RB, int WM, int CB, bool GATEUP, bool SS>
+template <int FMT, int KC, int NSTG, int RB, int WM, int CB, bool GATEUP, bool SS>
 static hipError_t launch_pre_ss(const ExpertGemmArgs& a, hipStream_t s) {
-  using Sh = PreShape<FMT, KC, RB, WM, CB, GATEUP, SS>;
+  using Sh = PreShape<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS>;
   const int N = GATEUP ? a.I : a.H;
   const int ncol = (N + Sh::NCOLS - 1) / Sh::NCOLS;
-  auto kern = k_pre_gemm<FMT, KC, RB, WM, CB, GATEUP, SS>;
+  auto kern = k_pre_gemm<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS>;
   static bool attr_set = false;  // one attribute call per instantiation and process
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -475,38 +508,42 @@ static hipError_t launch_pre_ss(const ExpertGemmArgs& a, hipStream_t s) {
 }
 
 // Super-staged scales when each scale row is a whole number of 16-byte pieces.
-template <int FMT, int KC, int RB, int WM, int CB, bool GATEUP>
+template <int FMT, int KC, int NSTG, int RB, int WM, int CB, bool GATEUP>
 static hipError_t launch_pre_shape(const ExpertGemmArgs& a, hipStream_t s) {
   const int K = GATEUP ? a.H : a.I;
   if (K % KC != 0) return hipErrorInvalidValue;
   const int sbytes = K / (FMT == 0 ? 16 : 32);
-  if (sbytes % 16 == 0) return launch_pre_ss<FMT, KC, RB, WM, CB, GATEUP, true>(a, s);
-  return launch_pre_ss<FMT, KC, RB, WM, CB, GATEUP, false>(a, s);
+  if (sbytes % 16 == 0) return launch_pre_ss<FMT, KC, NSTG, RB, WM, CB, GATEUP, true>(a, s);
+  return launch_pre_ss<FMT, KC, NSTG, RB, WM, CB, GATEUP, false>(a, s);
 }
 
 // Tile height MT -> stage width KC and block shape (row blocks per wave RB, waves along M
 // WM, column blocks per wave CB): 128 = 64-code stages, 2 x 2 x 4 (128 x 256 weight
 // rows); 64 = 64-code stages, 1 x 2 x 4 (64 x 256); 32 = 128-code stages, 1 x 1 x 4
 // (32 x 512). K that is not a multiple of 128 takes 64-code stages at height 32 too.
+#ifndef MOE_PRE_NSTG
+#define MOE_PRE_NSTG 3
+#endif
 template <bool GATEUP>
 static hipError_t launch_pre(const ExpertGemmArgs& a, int mt, hipStream_t s) {
   if (a.tile_bound <= 0) return hipSuccess;
   const int fmt = GATEUP ? a.gate.fmt : a.down.fmt;
   const int K = GATEUP ? a.H : a.I;
+  constexpr int NS3 = MOE_PRE_NSTG;
   if (fmt == 0) {
     if (mt == 32) {
-      return K % 128 == 0 ? launch_pre_shape<0, 128, 1, 1, 4, GATEUP>(a, s)
-                          : launch_pre_shape<0, 64, 1, 1, 4, GATEUP>(a, s);
+      return K % 128 == 0 ? launch_pre_shape<0, 128, 3, 1, 1, 4, GATEUP>(a, s)
+                          : launch_pre_shape<0, 64, 3, 1, 1, 4, GATEUP>(a, s);
     }
-    if (mt == 64) return launch_pre_shape<0, 64, 1, 2, 4, GATEUP>(a, s);
-    return launch_pre_shape<0, 64, 2, 2, 4, GATEUP>(a, s);
+    if (mt == 64) return launch_pre_shape<0, 64, 3, 1, 2, 4, GATEUP>(a, s);
+    return launch_pre_shape<0, 64, NS3, 2, 2, 4, GATEUP>(a, s);
   }
   if (mt == 32) {
-    return K % 128 == 0 ? launch_pre_shape<1, 128, 1, 1, 4, GATEUP>(a, s)
-                        : launch_pre_shape<1, 64, 1, 1, 4, GATEUP>(a, s);
+    return K % 128 == 0 ? launch_pre_shape<1, 128, 3, 1, 1, 4, GATEUP>(a, s)
+                        : launch_pre_shape<1, 64, 3, 1, 1, 4, GATEUP>(a, s);
   }
-  if (mt == 64) return launch_pre_shape<1, 64, 1, 2, 4, GATEUP>(a, s);
-  return launch_pre_shape<1, 64, 2, 2, 4, GATEUP>(a, s);
+  if (mt == 64) return launch_pre_shape<1, 64, 3, 1, 2, 4, GATEUP>(a, s);
+  return launch_pre_shape<1, 64, NS3, 2, 2, 4, GATEUP>(a, s);
 }
 
 hipError_t launch_prefill_gate_up(const ExpertGemmArgs& a, int mt, hipStream_t s) {

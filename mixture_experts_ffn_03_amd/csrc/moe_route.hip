@@ -48,16 +48,12 @@ hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, uint16_t* ou
 }
 
 // ---------------------------------------------------------------------------
-// Router GEMM, fp64 sums: partial[z][t][e] = sum_{h in slice z} x[t,h] * W_r[e,h].
-//
-// Few tokens (decode, T <= 64): fp64 matrix cores. A block computes 16 experts x all
-// tokens (up to four 16-token fragments) over one H slice with v_mfma_f64_16x16x4_f64 on
-// exactly widened bf16 operands; its four waves take interleaved 32-wide K chunks and
-// are summed in a fixed order at the end. H is split over blocks so the grid fills the
-// chip (z = slice).
-//
-// Many tokens (prefill): 64 tokens x 64 experts per block with a 4x4 fp64 register
-// block per thread over LDS tiles, H split in z so that the grid fills the chip.
+// Router GEMM, fp64 sums: partial[z][t][e] = sum_{h in slice z} x[t,h] * W_r[e,h], on
+// the fp64 matrix cores. A block computes 16 experts x MF 16-token fragments (a tile of
+// up to 64 tokens; blockIdx.y walks the token tiles) over one H slice with
+// v_mfma_f64_16x16x4_f64 on exactly widened bf16 operands; its four waves take
+// interleaved 32-wide K chunks and are summed in a fixed order at the end. H is split
+// over blocks so that the grid fills the chip (z = slice).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void bf16x8_to_f64(const uint4& v, double (&o)[8]) {
   const uint32_t d[4] = {v.x, v.y, v.z, v.w};
@@ -82,6 +78,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int idx = lane & 15, q = lane >> 4;
   const int e0 = blockIdx.x * 16;
+  const int tb = blockIdx.y * 16 * MF;  // first token of the tile
   const int kb = blockIdx.z * hsplit;
   const int ke = min(H, kb + hsplit);
   const int eload = e0 + idx < E ? e0 + idx : 0;  // rows past E: results not stored
@@ -90,7 +87,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
   bool tv[MF];
 #pragma unroll
   for (int m = 0; m < MF; ++m) {
-    const int t = m * 16 + idx;
+    const int t = tb + m * 16 + idx;
     tv[m] = t < T;
     xrow[m] = x + (size_t)(tv[m] ? t : 0) * H + 8 * q;
   }
@@ -126,93 +123,19 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
     const f64x4_t sum = ((acc[m] + s_red[0][m][lane]) + s_red[1][m][lane]) + s_red[2][m][lane];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int t = m * 16 + q + 4 * v;
+      const int t = tb + m * 16 + q + 4 * v;
       if (t < T) p[(size_t)t * E + e] = sum[v];
-    }
-  }
-}
-
-constexpr int kRt = 64;   // tokens per block tile
-constexpr int kRe = 64;   // experts per block tile
-constexpr int kRk = 16;   // K per LDS stage
-
-__global__ __launch_bounds__(256) void k_router_tiled(const uint16_t* __restrict__ x,
-                                                      const uint16_t* __restrict__ w,
-                                                      double* __restrict__ partial, int T, int E,
-                                                      int H, int hsplit) {
-  __shared__ __align__(16) double xs[kRk][kRt + 2];
-  __shared__ __align__(16) double ws[kRk][kRe + 2];
-  const int tid = threadIdx.x;
-  const int e0 = blockIdx.x * kRe, t0 = blockIdx.y * kRt;
-  const int kb = blockIdx.z * hsplit;
-  const int ke = min(H, kb + hsplit);
-  const int tx = tid & 15, ty = tid >> 4;  // experts 4*tx.., tokens 4*ty..
-  double acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-  // loader: threads 0..127 load x rows, 128..255 W rows; 16 k = two 16-byte pieces per row
-  const int lrow = (tid & 127) >> 1, lpiece = tid & 1;
-  const bool lx = tid < 128;
-  for (int k0 = kb; k0 < ke; k0 += kRk) {
-    double v[8];
-    const int k = k0 + lpiece * 8;
-    const int r = (lx ? t0 : e0) + lrow;
-    const int lim = lx ? T : E;
-    if (r < lim && k < ke) {
-      const uint16_t* src = (lx ? x : w) + (size_t)r * H + k;
-      bf16x8_to_f64(*reinterpret_cast<const uint4*>(src), v);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.0;
-    }
-    double(*dst)[kRt + 2] = lx ? xs : ws;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dst[lpiece * 8 + i][lrow] = v[i];
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < kRk; ++kk) {
-      double a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = xs[kk][ty * 4 + i];
-        b[i] = ws[kk][tx * 4 + i];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
-    }
-    __syncthreads();
-  }
-  double* p = partial + (size_t)blockIdx.z * T * E;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty * 4 + i;
-    if (t >= T) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx * 4 + j;
-      if (e < E) p[(size_t)t * E + e] = acc[i][j];
     }
   }
 }
 
 RouterPlan plan_router(int T, int E, int H) {
   RouterPlan r;
-  int ks;
-  if (T <= kRouterSmallMaxT) {
-    const int blocks = (E + 15) / 16;
-    ks = min((256 + blocks - 1) / blocks, min(kRouterMaxSplit, H / 32));
-    ks = max(ks, 1);
-    r.hsplit = ((H + ks - 1) / ks + 31) / 32 * 32;  // whole 32-wide chunks
-  } else {
-    const int blocks = ((E + kRe - 1) / kRe) * ((T + kRt - 1) / kRt);
-    ks = min((256 + blocks - 1) / blocks, min(kRouterMaxSplit, H / 64));
-    ks = max(ks, 1);
-    r.hsplit = ((H + ks - 1) / ks + kRk - 1) / kRk * kRk;
-  }
+  // enough H slices that the grid has about 512 blocks (two per CU)
+  const int blocks = max(1, ((E + 15) / 16) * ((T + 63) / 64));  // T = 0: no launch
+  int ks = min((512 + blocks - 1) / blocks, min(kRouterMaxSplit, H / 32));
+  ks = max(ks, 1);
+  r.hsplit = ((H + ks - 1) / ks + 31) / 32 * 32;  // whole 32-wide chunks
   r.ks = (H + r.hsplit - 1) / r.hsplit;
   return r;
 }
@@ -220,17 +143,12 @@ RouterPlan plan_router(int T, int E, int H) {
 hipError_t launch_router_partial(const uint16_t* x, const uint16_t* w, double* partial, int T,
                                  int E, int H, int ks, int hsplit, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (T <= kRouterSmallMaxT) {
-    const dim3 grid((E + 15) / 16, 1, ks);
-    const int mf = (T + 15) / 16;
-    if (mf == 1) hipLaunchKernelGGL(k_router_mfma<1>, grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
-    else if (mf == 2) hipLaunchKernelGGL(k_router_mfma<2>, grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
-    else if (mf == 3) hipLaunchKernelGGL(k_router_mfma<3>, grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
-    else hipLaunchKernelGGL(k_router_mfma<4>, grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
-  } else {
-    dim3 grid((E + kRe - 1) / kRe, (T + kRt - 1) / kRt, ks);
-    hipLaunchKernelGGL(k_router_tiled, grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
-  }
+  const int mf = T >= 64 ? 4 : (T + 15) / 16;  // 16-token fragments per block
+  const dim3 grid((E + 15) / 16, (T + 16 * mf - 1) / (16 * mf), ks);
+  if (mf == 1) hipLaunchKernelGGL(k_router_mfma<1>, grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
+  else if (mf == 2) hipLaunchKernelGGL(k_router_mfma<2>, grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
+  else if (mf == 3) hipLaunchKernelGGL(k_router_mfma<3>, grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
+  else hipLaunchKernelGGL(k_router_mfma<4>, grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
   return hipGetLastError();
 }
 

@@ -254,6 +254,9 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
   return r;
 }
 
+// chunks of 64 slots whose ids one wave loads at once
+constexpr int kDispatchBatch = 8;
+
 template <int NW, int EMAX>
 __device__ void dispatch_body(const DispatchArgs& a, const int32_t* ids, const int32_t* err_tok,
                               int (*s_wbase)[EMAX], int* s_off, int* s_tmp, int* s_err) {
@@ -266,16 +269,27 @@ __device__ void dispatch_body(const DispatchArgs& a, const int32_t* ids, const i
   for (int p = tid; p < a.shared_rows; p += NT) a.row_token[p] = p;
   __syncthreads();
 
-  // each wave owns one contiguous segment of the slots (keeps the sort stable)
+  // each wave owns one contiguous segment of the slots (keeps the sort stable); the ids
+  // of kDispatchBatch chunks of 64 slots are loaded together so that their latencies
+  // overlap
   const int seg = (S + NW - 1) / NW;
   const int sb = wave * seg, se = min(S, sb + seg);
   int err = 0;
-  for (int c0 = sb; c0 < se; c0 += kWave) {
-    const int s = c0 + lane;
-    if (s < se) {
-      const int e = ids[s];
-      if (e >= 0 && e < E) atomicAdd(&s_wbase[wave][e], 1);
-      else if (!(err_tok && e == -1) && !(e >= E && e < E + a.zero)) err |= 1;
+  for (int c0 = sb; c0 < se; c0 += kDispatchBatch * kWave) {
+    int ev[kDispatchBatch];
+#pragma unroll
+    for (int j = 0; j < kDispatchBatch; ++j) {
+      const int s = c0 + j * kWave + lane;
+      ev[j] = s < se ? ids[s] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kDispatchBatch; ++j) {
+      const int s = c0 + j * kWave + lane;
+      const int e = ev[j];
+      if (s < se) {
+        if (e >= 0 && e < E) atomicAdd(&s_wbase[wave][e], 1);
+        else if (!(err_tok && e == -1) && !(e >= E && e < E + a.zero)) err |= 1;
+      }
     }
   }
   if (err_tok)
@@ -300,31 +314,40 @@ __device__ void dispatch_body(const DispatchArgs& a, const int32_t* ids, const i
   __syncthreads();
 
   // stable scatter: lanes with equal ids are ranked by lane order within each chunk
-  for (int c0 = sb; c0 < se; c0 += kWave) {
-    const int s = c0 + lane;
-    const bool in = s < se;
-    const int e = in ? ids[s] : -1;
-    const bool valid = in && e >= 0 && e < E;
-    uint64_t m = __ballot(valid);
-    for (int b = 0; (1 << b) < E; ++b) {
-      const bool bit = valid && ((e >> b) & 1);
-      const uint64_t bb = __ballot(bit);
-      m &= bit ? bb : ~bb;
+  for (int c0 = sb; c0 < se; c0 += kDispatchBatch * kWave) {
+    int ev[kDispatchBatch];
+#pragma unroll
+    for (int j = 0; j < kDispatchBatch; ++j) {
+      const int s = c0 + j * kWave + lane;
+      ev[j] = s < se ? ids[s] : -1;
     }
-    if (valid) {
-      const uint64_t below = lane ? (m & ((~0ull) >> (64 - lane))) : 0ull;
-      const int rank = __popcll(below);
-      const int cntm = __popcll(m);
-      const int base = s_wbase[wave][e];
-      const int pos = s_off[e] + base + rank;
-      a.row_token[pos] = s / K;
-      a.inv[s] = pos;
-      if (rank == cntm - 1) s_wbase[wave][e] = base + cntm;
-    } else if (in) {
-      a.inv[s] = (e >= E && e < E + a.zero) ? -2 : -1;
+#pragma unroll
+    for (int j = 0; j < kDispatchBatch; ++j) {
+      const int s = c0 + j * kWave + lane;
+      const bool in = s < se;
+      const int e = ev[j];
+      const bool valid = in && e >= 0 && e < E;
+      uint64_t m = __ballot(valid);
+      for (int b = 0; (1 << b) < E; ++b) {
+        const bool bit = valid && ((e >> b) & 1);
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+      }
+      if (valid) {
+        const uint64_t below = lane ? (m & ((~0ull) >> (64 - lane))) : 0ull;
+        const int rank = __popcll(below);
+        const int cntm = __popcll(m);
+        const int base = s_wbase[wave][e];
+        const int pos = s_off[e] + base + rank;
+        a.row_token[pos] = s / K;
+        a.inv[s] = pos;
+        if (rank == cntm - 1) s_wbase[wave][e] = base + cntm;
+      } else if (in) {
+        a.inv[s] = (e >= E && e < E + a.zero) ? -2 : -1;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
   }
 
   // tile list: ceil(cnt / tile_h) runs per expert, experts in order

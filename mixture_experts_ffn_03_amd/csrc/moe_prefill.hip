@@ -416,7 +416,7 @@ void k_pre_gemm(ExpertGemmArgs a) {
         const bf16x8_t af = __builtin_bit_cast(bf16x8_t, av[rb][s]);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bo[cb], acc[rb][cb], 0, 0, 0);
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo[cb], af, acc[rb][cb], 0, 0, 0);
       }
     }
   };
@@ -449,25 +449,34 @@ void k_pre_gemm(ExpertGemmArgs a) {
     kloop(std::integral_constant<int, 0>{});
   }
 
-  // epilogue: lane holds column j = lane % 32 of each 32x32 block, rows 8*(v/4)+4*half+v%4
+  // epilogue. The weights are the MFMA's first operand, so block (rb, cb) holds
+  // out[token][n] transposed: lane l owns token row wm*32*RB + rb*32 + l % 32 and, in
+  // element v, column 8*(v/4) + 4*half + v%4 of the 32-column block, i.e. four runs of 4
+  // consecutive columns, each stored as one 8-byte write. Column blocks are 32-aligned
+  // and N is a multiple of 32, so a block is wholly inside N or wholly outside.
   if (GATEUP) {
     const float gs_g = FMT == 0 ? a.gate.global[e] : 1.0f;
     const float gs_u = FMT == 0 ? a.up.global[e] : 1.0f;
 #pragma unroll
     for (int cg = 0; cg < CH; ++cg) {
-      const int n = n0 + wn * CH * 32 + cg * 32 + r;
-      if (n >= N) continue;
+      const int nb = n0 + wn * CH * 32 + cg * 32;
+      if (nb >= N) continue;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
+        const int i = wm * 32 * RB + rb * 32 + r;
+        if (i >= t.count) continue;
+        uint16_t* hrow = a.h + (size_t)(t.row0 + i) * a.h_stride + nb + 4 * half;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int i = wm * 32 * RB + rb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
-          if (i < t.count) {
-            const float g = acc[rb][cg][v] * gs_g;
-            const float u = acc[rb][CH + cg][v] * gs_u;
-            const float hval = silu(g) * u;
-            a.h[(size_t)(t.row0 + i) * a.h_stride + n] = f32_to_bf16(hval);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          float hv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float g = acc[rb][cg][4 * g4 + j] * gs_g;
+            const float u = acc[rb][CH + cg][4 * g4 + j] * gs_u;
+            hv[j] = silu(g) * u;
           }
+          *reinterpret_cast<uint2*>(hrow + 8 * g4) =
+              make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
         }
       }
     }
@@ -476,14 +485,19 @@ void k_pre_gemm(ExpertGemmArgs a) {
     uint16_t* y = reinterpret_cast<uint16_t*>(a.y);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      const int n = n0 + wn * CB * 32 + cb * 32 + r;
-      if (n >= N) continue;
+      const int nb = n0 + wn * CB * 32 + cb * 32;
+      if (nb >= N) continue;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
+        const int i = wm * 32 * RB + rb * 32 + r;
+        if (i >= t.count) continue;
+        uint16_t* yrow = y + (size_t)(t.row0 + i) * a.H + nb + 4 * half;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int i = wm * 32 * RB + rb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
-          if (i < t.count) y[(size_t)(t.row0 + i) * a.H + n] = f32_to_bf16(acc[rb][cb][v] * gs);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x16_t& c = acc[rb][cb];
+          *reinterpret_cast<uint2*>(yrow + 8 * g4) =
+              make_uint2(pack_bf16x2(c[4 * g4] * gs, c[4 * g4 + 1] * gs),
+                         pack_bf16x2(c[4 * g4 + 2] * gs, c[4 * g4 + 3] * gs));
         }
       }
     }

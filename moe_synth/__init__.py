@@ -21,9 +21,12 @@ values on CPU and GPU, because the two devices use different generators; each
 is reproducible on its own.
 
 Storage layout (shared by both sides of the boundary):
-  packed  uint8 [E, N, K/2]   byte j of a row holds codes 2j (low nibble) and 2j+1 (high nibble)
-  scales  uint8 [E, N, K/16]  E4M3FN codes (NVFP4) or [E, N, K/32] E8M0 codes (MXFP4)
-  global  f32   [E]           NVFP4 only
+  FP4:  packed uint8 [E, N, K/2]  byte j of a row holds codes 2j (low nibble) and 2j+1 (high)
+        scales uint8 [E, N, K/16] E4M3FN codes (NVFP4) or [E, N, K/32] E8M0 codes (MXFP4)
+        global f32 [E]            NVFP4 only
+  FP8:  packed uint8 [E, N, K]    E4M3FN codes
+        scales f32 [E, ceil(N/128), ceil(K/128)]  one scale per 128 x 128 block
+  BF16: packed bf16 [E, N, K], no scales
 """
 from __future__ import annotations
 
@@ -35,6 +38,9 @@ import torch
 
 NVFP4 = 0
 MXFP4 = 1
+FP8 = 2
+BF16 = 3
+FP8_BLOCK = 128
 
 SOFTMAX = 0
 SIGMOID = 1
@@ -175,11 +181,47 @@ def quantize_mxfp4(w: torch.Tensor):
     return packed, code.contiguous()
 
 
+def quantize_fp8(w: torch.Tensor):
+    """Encode one fp32 tensor [N, K] as FP8: (E4M3FN codes [N, K], fp32 scales
+    [ceil(N/128), ceil(K/128)]). Each 128 x 128 block gets scale = amax_block / 448 (fp32),
+    so its largest value maps to the E4M3 maximum; codes are w / scale rounded to nearest
+    even by torch's float8_e4m3fn conversion (clamped to +-448 first)."""
+    n, k = w.shape
+    nb, kb = -(-n // FP8_BLOCK), -(-k // FP8_BLOCK)
+    pad = torch.zeros((nb * FP8_BLOCK, kb * FP8_BLOCK), dtype=torch.float32, device=w.device)
+    pad[:n, :k] = w
+    blocks = pad.reshape(nb, FP8_BLOCK, kb, FP8_BLOCK)
+    amax = blocks.abs().amax(dim=(1, 3))
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).to(torch.float32)
+    full = scale.repeat_interleave(FP8_BLOCK, 0).repeat_interleave(FP8_BLOCK, 1)[:n, :k]
+    codes = (w / full).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return codes.view(torch.uint8).contiguous(), scale.contiguous()
+
+
 def quantize(w: torch.Tensor, fmt: int):
+    """(packed, scales, global) of one [N, K] fp32 tensor in storage format ``fmt``."""
     if fmt == NVFP4:
         return quantize_nvfp4(w)
-    packed, sc = quantize_mxfp4(w)
-    return packed, sc, None
+    if fmt == MXFP4:
+        packed, sc = quantize_mxfp4(w)
+        return packed, sc, None
+    if fmt == FP8:
+        codes, sc = quantize_fp8(w)
+        return codes, sc, None
+    if fmt == BF16:
+        return w.to(torch.bfloat16).contiguous(), None, None
+    raise ValueError(f"unknown weight format {fmt}")
+
+
+def storage_shapes(fmt: int, n: int, k: int):
+    """((packed shape, dtype), (scales shape, dtype) or None) of one expert's [n, k] matrix."""
+    if fmt in (NVFP4, MXFP4):
+        return ((n, k // 2), torch.uint8), ((n, k // (16 if fmt == NVFP4 else 32)), torch.uint8)
+    if fmt == FP8:
+        return ((n, k), torch.uint8), ((-(-n // FP8_BLOCK), -(-k // FP8_BLOCK)), torch.float32)
+    if fmt == BF16:
+        return ((n, k), torch.bfloat16), None
+    raise ValueError(f"unknown weight format {fmt}")
 
 
 # ---------------------------------------------------------------------------
@@ -188,11 +230,12 @@ def quantize(w: torch.Tensor, fmt: int):
 
 @dataclasses.dataclass
 class Fp4Weight:
-    """One projection of all experts of a group, in storage form."""
+    """One projection of all experts of a group, in storage form (any weight format; the
+    layout of each format is in the module doc)."""
 
     fmt: int
-    packed: torch.Tensor          # uint8 [E, N, K/2]
-    scales: torch.Tensor          # uint8 [E, N, K/16] or [E, N, K/32]
+    packed: torch.Tensor          # FP4 uint8 [E, N, K/2]; FP8 uint8 [E, N, K]; BF16 [E, N, K]
+    scales: Optional[torch.Tensor]  # FP4 uint8 [E, N, K/16|32]; FP8 f32 [E, N/128, K/128]
     global_scale: Optional[torch.Tensor]  # f32 [E] (NVFP4) or None
     n: int
     k: int
@@ -236,12 +279,12 @@ def _normal(g, shape, std, device):
 
 def _expert_set(g, device, experts: int, hidden: int, inter: int, fmt: int) -> ExpertSet:
     """Draw gate [I,H], up [I,H], down [H,I] per expert (expert-major) ~ N(0, 0.02), then encode."""
-    sdiv = 16 if fmt == NVFP4 else 32
     parts = {}
     for name, (n, k) in (("gate", (inter, hidden)), ("up", (inter, hidden)), ("down", (hidden, inter))):
+        (pshape, pdt), sdesc = storage_shapes(fmt, n, k)
         parts[name] = (
-            torch.empty((experts, n, k // 2), dtype=torch.uint8, device=device),
-            torch.empty((experts, n, k // sdiv), dtype=torch.uint8, device=device),
+            torch.empty((experts,) + pshape, dtype=pdt, device=device),
+            torch.empty((experts,) + sdesc[0], dtype=sdesc[1], device=device) if sdesc else None,
             torch.empty((experts,), dtype=torch.float32, device=device) if fmt == NVFP4 else None,
             n, k)
     for e in range(experts):
@@ -250,7 +293,8 @@ def _expert_set(g, device, experts: int, hidden: int, inter: int, fmt: int) -> E
             w = _normal(g, (n, k), 0.02, device)
             p, s, gg = quantize(w, fmt)
             packed[e].copy_(p)
-            sc[e].copy_(s)
+            if sc is not None:
+                sc[e].copy_(s)
             if gs is not None:
                 gs[e] = gg
             del w
@@ -333,8 +377,19 @@ def random_codes_weight(g, device, experts: int, n: int, k: int, fmt: int,
                         scale_codes: Optional[torch.Tensor] = None) -> Fp4Weight:
     """A weight tensor with uniformly random codes and scales (edge-case tests).
 
-    E4M3 scales avoid the NaN code 0x7F/0xFF; E8M0 scales are drawn around 2^0.
+    E4M3 scales avoid the NaN code 0x7F/0xFF; E8M0 scales are drawn around 2^0. FP8: random
+    non-NaN E4M3 codes and fp32 block scales in [2^-8, 2^0); BF16: N(0, 1) values.
     """
+    if fmt == FP8:
+        codes = torch.randint(0, 254, (experts, n, k), generator=g, device=device, dtype=torch.int32)
+        codes = codes + (codes >= 0x7F).to(torch.int32)  # skip 0x7F (NaN); 0xFF is out of range
+        (_, _), ((nb, kb), _) = storage_shapes(FP8, n, k)
+        sc = torch.exp2(-8.0 * torch.rand((experts, nb, kb), generator=g, device=device))
+        return Fp4Weight(fmt, codes.to(torch.uint8).contiguous(), sc.to(torch.float32).contiguous(),
+                         None, n, k)
+    if fmt == BF16:
+        v = torch.randn((experts, n, k), generator=g, device=device, dtype=torch.float32)
+        return Fp4Weight(fmt, v.to(torch.bfloat16).contiguous(), None, None, n, k)
     packed = torch.randint(0, 256, (experts, n, k // 2), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
     if fmt == NVFP4:
         sc = torch.randint(0, 0x7F, (experts, n, k // 16), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
@@ -359,7 +414,11 @@ def count_unique_experts(ids: torch.Tensor, experts: int) -> int:
 
 
 def nbytes_fp4(n: int, k: int, fmt: int) -> float:
-    """Storage bytes of one [n, k] FP4 matrix including its scales (and global for NVFP4)."""
+    """Storage bytes of one [n, k] expert matrix including its scales (and global for NVFP4)."""
+    if fmt == FP8:
+        return n * k + 4 * (-(-n // FP8_BLOCK)) * (-(-k // FP8_BLOCK))
+    if fmt == BF16:
+        return 2 * n * k
     return n * k / 2 + n * k / (16 if fmt == NVFP4 else 32) + (4 if fmt == NVFP4 else 0)
 
 

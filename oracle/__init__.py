@@ -10,7 +10,8 @@ written from the MoE module pages of the Rust inference engine
 (spark_model/layers/moe/mod.rs: the module doc and the field docs of
 ``MoeLayer``; spark_model/layers/moe/init.rs: the constructor's validation and
 kernel set) and from the public OCP Microscaling v1.0 element definitions for
-E2M1, E4M3 and E8M0. Floating point is evaluated in fp64 (numpy), except where
+E2M1, E4M3 and E8M0. Expert weights come as NVFP4 or MXFP4 (FP4 codes with block
+scales), FP8 (E4M3 codes with one fp32 scale per 128 x 128 block) or BF16. Floating point is evaluated in fp64 (numpy), except where
 a decision is taken on a value the method defines in fp32 (router logits and
 the sigmoid selection key), which are rounded to fp32 exactly as defined.
 
@@ -35,6 +36,9 @@ import numpy as np
 
 NVFP4 = 0
 MXFP4 = 1
+FP8 = 2    # E4M3 (OCP "FN") elements, one fp32 scale per 128 x 128 block (N x K)
+BF16 = 3   # bf16 elements, no scale
+FP8_BLOCK = 128
 SOFTMAX = 0
 SIGMOID = 1
 SQRT_SOFTPLUS = 2
@@ -125,6 +129,41 @@ def dequant_fp4(packed: np.ndarray, scales: np.ndarray, fmt: int,
             raise ValueError("NVFP4 needs a global scale")
         out = out * float(np.float32(global_scale))
     return out
+
+
+def bf16_value(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp64 (the upper 16 bits of an fp32)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def dequant_fp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Decode one FP8 expert matrix [N, K] (E4M3 codes) to fp64: value = e4m3(code) *
+    scale[n // 128, k // 128], the fp32 scales [ceil(N/128), ceil(K/128)] of 128 x 128
+    blocks (the FP8 expert weights and block-scaled FP8 GEMMs of the MoE constructor and
+    module pages, e.g. the FP8 pointer tables and fp8_gemm_t_blockscaled)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    n, k = codes.shape
+    sv = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    nb, kb = -(-n // FP8_BLOCK), -(-k // FP8_BLOCK)
+    if sv.shape != (nb, kb):
+        raise ValueError(f"scale shape {sv.shape} does not match [{nb}, {kb}]")
+    full = np.repeat(np.repeat(sv, FP8_BLOCK, axis=0), FP8_BLOCK, axis=1)[:n, :k]
+    return _E4M3[codes] * full
+
+
+def dequant_weight(packed: np.ndarray, scales, fmt: int,
+                   global_scale: Optional[float] = None) -> np.ndarray:
+    """Decode one expert matrix in any storage format to fp64 [N, K]: FP4 (packed
+    [N, K/2]), FP8 (codes [N, K] + block scales) or BF16 (bits [N, K]; the pages' BF16
+    grouped GEMM for FP8-source models dequantised to BF16 at load)."""
+    if fmt in (NVFP4, MXFP4):
+        return dequant_fp4(packed, scales, fmt, global_scale)
+    if fmt == FP8:
+        return dequant_fp8(packed, scales)
+    if fmt == BF16:
+        return bf16_value(packed)
+    raise ValueError(f"unknown weight format {fmt}")
 
 
 # ---------------------------------------------------------------------------
@@ -320,8 +359,8 @@ class DequantCache:
             out = []
             for name in ("gate", "up", "down"):
                 fmt, packed, scales, gs = self.parts[name]
-                out.append(dequant_fp4(packed[e], scales[e], fmt,
-                                       None if gs is None else gs[e]))
+                out.append(dequant_weight(packed[e], None if scales is None else scales[e],
+                                          fmt, None if gs is None else gs[e]))
             self.cache[e] = tuple(out)
         return self.cache[e]
 

@@ -40,7 +40,8 @@ def oracle_cache(ws: S.ExpertSet) -> O.DequantCache:
     for n in ("gate", "up", "down"):
         w = getattr(ws, n)
         gs = None if w.global_scale is None else w.global_scale.cpu().numpy()
-        parts[n] = (w.fmt, LazyHost(w.packed), LazyHost(w.scales), gs)
+        packed = w.packed.view(torch.int16) if w.packed.dtype == torch.bfloat16 else w.packed
+        parts[n] = (w.fmt, LazyHost(packed), None if w.scales is None else LazyHost(w.scales), gs)
     return O.DequantCache(parts["gate"], parts["up"], parts["down"])
 
 

@@ -102,6 +102,60 @@ def test_dequant_layout_rows_and_block_columns():
             assert got[r, c] == e2m1[codes[r, c]] * 2.0 ** (int(sc[r, c // 32]) - 127)
 
 
+def test_fp8_every_code_times_block_scales():
+    # every E4M3 code (torch's float8_e4m3fn decoder) times fp32 block scales, power of
+    # two and not: the product is exact in fp64
+    codes = np.tile(np.arange(256, dtype=np.uint8), (2, 1))  # [2, 256]: two k-blocks
+    e4m3 = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    for s0, s1 in ((1.0, 0.5), (2.0 ** -7, 3.0), (float(np.float32(0.3711)), float(np.float32(1e-3)))):
+        sc = np.array([[s0, s1]], dtype=np.float32)
+        got = O.dequant_fp8(codes, sc)
+        want = np.concatenate([e4m3[:128] * float(np.float32(s0)), e4m3[128:] * float(np.float32(s1))])
+        want = np.tile(want, (2, 1))
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan], want[~nan])
+        assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def test_fp8_block_layout_rows_and_columns():
+    # one distinct scale per 128 x 128 block of a ragged [300, 200] matrix: a swapped or
+    # wrongly sized block index moves scales between positions
+    n, k = 300, 200
+    codes = np.full((n, k), 0x38, dtype=np.uint8)  # E4M3 1.0
+    sc = (np.arange(3 * 2, dtype=np.float32).reshape(3, 2) + 1.0) * 0.25
+    got = O.dequant_fp8(codes, sc)
+    for r in (0, 127, 128, 255, 256, 299):
+        for c in (0, 127, 128, 199):
+            assert got[r, c] == sc[r // 128, c // 128]
+    with pytest.raises(ValueError):
+        O.dequant_fp8(codes, sc[:, :1])
+
+
+def test_fp8_quantizer_round_trip_on_grid():
+    """Values on the E4M3 grid of their block (block amax = 448 * scale) survive the
+    test-only FP8 encoder exactly."""
+    g = torch.Generator().manual_seed(9)
+    n, k = 256, 384
+    code = torch.randint(0, 0x7E, (n, k), generator=g, dtype=torch.int32).to(torch.uint8)
+    sign = torch.randint(0, 2, (n, k), generator=g, dtype=torch.int32).to(torch.uint8) << 7
+    code = code | sign
+    vals = code.view(torch.float8_e4m3fn).float()
+    scale = torch.tensor([[0.5, 2.0 ** -9, 3.0], [0.25, 1.0, 2.0 ** -3]], dtype=torch.float32)
+    full = scale.repeat_interleave(128, 0).repeat_interleave(128, 1)
+    vals[::128, ::128] = 448.0  # pin each block's amax
+    w = vals * full
+    c2, s2 = S.quantize_fp8(w)
+    assert torch.equal(s2, scale)
+    assert np.array_equal(O.dequant_fp8(c2.numpy(), s2.numpy()), w.double().numpy())
+
+
+def test_bf16_weights_decode_to_their_values():
+    v = torch.randn(5, 64, dtype=torch.float32).to(torch.bfloat16)
+    bits = v.view(torch.int16).numpy()
+    assert np.array_equal(O.dequant_weight(bits, None, O.BF16), v.double().numpy())
+
+
 def test_quantizers_round_trip_on_grid():
     """On-grid weights survive the (independent) test-only encoders exactly."""
     g = torch.Generator().manual_seed(5)

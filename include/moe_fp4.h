@@ -61,11 +61,16 @@ enum {
   MOE_DEVERR_TABLE = 4      /* hash routing: a tid2eid entry outside [0, num_experts) */
 };
 
-/* Expert weight storage formats (MoE module page, doc of MoeLayer.experts_scale_kind). */
+/* Expert weight storage formats (MoE module page, doc of MoeLayer.experts_scale_kind;
+ * MoE constructor page: the FP8 expert kernels and pointer tables, and the BF16 grouped
+ * GEMM for FP8-source weights dequantised to BF16 at load). */
 enum {
   MOE_FMT_NVFP4 = 0, /* E2M1 codes + one FP8-E4M3 (OCP "FN") scale per 16 values along K
                         + one f32 global scale per expert tensor: w = e2m1 * e4m3 * global */
-  MOE_FMT_MXFP4 = 1  /* E2M1 codes + one E8M0 scale per 32 values along K: w = e2m1 * 2^(s-127) */
+  MOE_FMT_MXFP4 = 1, /* E2M1 codes + one E8M0 scale per 32 values along K: w = e2m1 * 2^(s-127) */
+  MOE_FMT_FP8 = 2,   /* E4M3 (OCP "FN") codes + one f32 scale per 128 x 128 block (rows x K):
+                        w = e4m3 * scale[n / 128][k / 128]; k <= 16384 */
+  MOE_FMT_BF16 = 3   /* bf16 values, no scales */
 };
 
 /* Routing score (MoE module page: doc of correction_bias_dev; constructor page: top-K kernels). */
@@ -104,12 +109,18 @@ enum {
 #define MOE_DECODE_MAX_LDS (160 * 1024) /* decode stages 4 activation rows per tile in LDS */
 
 /* One projection of a group of experts, in storage form (host struct, device pointers).
- *   packed       uint8 [experts, n, k/2]: byte j of a row holds code 2j in its low nibble
- *                and code 2j+1 in its high nibble (K contiguous per output row n)
- *   scales       uint8 [experts, n, k/16] E4M3 codes (NVFP4) or [experts, n, k/32] E8M0 (MXFP4)
- *   global_scale f32 [experts] for NVFP4; must be NULL for MXFP4
+ * K is contiguous per output row n in every format.
+ *   NVFP4 / MXFP4:
+ *     packed       uint8 [experts, n, k/2]: byte j of a row holds code 2j in its low nibble
+ *                  and code 2j+1 in its high nibble
+ *     scales       uint8 [experts, n, k/16] E4M3 codes (NVFP4) or [experts, n, k/32] E8M0
+ *     global_scale f32 [experts] for NVFP4; must be NULL for MXFP4
+ *   FP8:  packed uint8 [experts, n, k] E4M3 codes; scales f32 [experts, ceil(n/128),
+ *         ceil(k/128)]; global_scale NULL
+ *   BF16: packed bf16 [experts, n, k]; scales and global_scale NULL
  *   gate/up: n = inter, k = hidden.  down: n = hidden, k = inter.
- * packed and scales must be 16-byte aligned; k % 32 == 0. */
+ * packed and scales must be 16-byte aligned; k % 32 == 0. A weight whose pointers do not
+ * match its format tag is MOE_ERR_FORMAT. */
 typedef struct {
   int32_t format;
   const uint8_t* packed;

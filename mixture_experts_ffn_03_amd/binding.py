@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_fp4.so")
 
 MOE_OK = 0
-FMT_NVFP4, FMT_MXFP4 = 0, 1
+FMT_NVFP4, FMT_MXFP4, FMT_FP8, FMT_BF16 = 0, 1, 2, 3
 SCORE_SOFTMAX, SCORE_SIGMOID, SCORE_SQRT_SOFTPLUS, SCORE_SOFTMAX_BIAS = 0, 1, 2, 3
 SELECT_TOPK, SELECT_HASH = 0, 1
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
@@ -126,7 +126,8 @@ def make_config(tokens, hidden, num_experts, top_k, inter, score_mode=SCORE_SOFT
 
 
 def fp4_weight(w) -> MoeFp4Weight:
-    """Marshal an object with fmt, packed [E,N,K/2], scales, global_scale, n, k."""
+    """Marshal an object with fmt, packed ([E,N,K/2] FP4, [E,N,K] FP8 or BF16), scales (or
+    None for BF16), global_scale, n, k."""
     return MoeFp4Weight(w.fmt, _ptr(w.packed), _ptr(w.scales),
                         _ptr(w.global_scale) if w.global_scale is not None else None,
                         w.packed.shape[0], w.n, w.k)

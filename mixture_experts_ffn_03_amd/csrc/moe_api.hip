@@ -105,13 +105,25 @@ int check_config(const moe_config* c) {
 }
 
 int check_weight(const moe_fp4_weight& w, int experts, int n, int k) {
-  if (w.format != MOE_FMT_NVFP4 && w.format != MOE_FMT_MXFP4) return MOE_ERR_FORMAT;
-  if (w.format == MOE_FMT_NVFP4 && !w.global_scale) return MOE_ERR_FORMAT;
-  if (w.format == MOE_FMT_MXFP4 && w.global_scale) return MOE_ERR_FORMAT;
-  if (!w.packed || !w.scales) return MOE_ERR_INVALID_ARG;
+  switch (w.format) {
+    case MOE_FMT_NVFP4:
+      if (!w.global_scale) return MOE_ERR_FORMAT;
+      break;
+    case MOE_FMT_MXFP4:
+    case MOE_FMT_FP8:
+      if (w.global_scale) return MOE_ERR_FORMAT;
+      break;
+    case MOE_FMT_BF16:
+      if (w.global_scale || w.scales) return MOE_ERR_FORMAT;
+      break;
+    default:
+      return MOE_ERR_FORMAT;
+  }
+  if (!w.packed || (w.format != MOE_FMT_BF16 && !w.scales)) return MOE_ERR_INVALID_ARG;
+  if (w.format == MOE_FMT_FP8 && k > 16384) return MOE_ERR_UNSUPPORTED;
   if (w.experts != experts || w.n != n || w.k != k) return MOE_ERR_INVALID_ARG;
   if (k % 32 != 0 || n <= 0) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(w.packed) || !aligned16(w.scales)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w.packed) || (w.scales && !aligned16(w.scales))) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 

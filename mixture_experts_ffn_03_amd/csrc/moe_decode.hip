@@ -46,21 +46,76 @@ __device__ __forceinline__ bool resolve_tile(const TileSource& src, const int32_
   return true;
 }
 
-// Scale bytes of one 32-code chunk: NVFP4 two E4M3 codes (16-code blocks), MXFP4 one E8M0.
+// Weights are streamed in 16-byte chunks: 32 FP4 codes, 16 FP8 codes or 8 bf16 values.
 template <int FMT>
-__device__ __forceinline__ uint32_t load_chunk_scales(const uint8_t* row_scales, int c) {
-  if (FMT == 0) return *reinterpret_cast<const uint16_t*>(row_scales + 2 * c);
-  return row_scales[c];
+struct DecFmt {
+  static constexpr int CPC = FMT <= 1 ? 32 : (FMT == 2 ? 16 : 8);  // codes per chunk
+  static constexpr int XW = CPC / 2;  // activation dwords (bf16 pairs) per chunk
+};
+
+// Bytes of one weight row of K codes.
+template <int FMT>
+__device__ __forceinline__ size_t dec_row_bytes(int K) {
+  return FMT <= 1 ? (size_t)K / 2 : (size_t)K * (FMT == 2 ? 1 : 2);
 }
 
-// Dot of one 16-byte chunk (32 codes) with TT activation chunks: codes are decoded to exact
-// bf16 (scale 1), dotted by v_dot2_f32_bf16, and each 16- or 32-code block partial is
-// multiplied by its fp32 block scale.
+// Scale layout: FP4 rows of K/16 (NVFP4) or K/32 (MXFP4) bytes; FP8 one fp32 per 128 x 128
+// block, [ceil(N/128), ceil(K/128)] per expert; BF16 none. `stride` is the FP4 row bytes or
+// the FP8 block-row length ceil(K/128).
+template <int FMT>
+__device__ __forceinline__ int dec_scale_stride(int K) {
+  return FMT == 0 ? K / 16 : FMT == 1 ? K / 32 : FMT == 2 ? (K + 127) / 128 : 0;
+}
+template <int FMT>
+__device__ __forceinline__ size_t dec_scale_expert_bytes(int N, int K) {
+  if (FMT <= 1) return (size_t)N * dec_scale_stride<FMT>(K);
+  if (FMT == 2) return (size_t)((N + 127) / 128) * dec_scale_stride<FMT>(K) * 4;
+  return 0;
+}
+
+// Scale word of chunk c of row n: NVFP4 two E4M3 codes (16-code blocks), MXFP4 one E8M0,
+// FP8 the fp32 bits of the row's 128 x 128 block, BF16 nothing.
+template <int FMT>
+__device__ __forceinline__ uint32_t load_chunk_scales(const uint8_t* base, int n, int stride,
+                                                      int c) {
+  if (FMT == 0) return *reinterpret_cast<const uint16_t*>(base + (size_t)n * stride + 2 * c);
+  if (FMT == 1) return base[(size_t)n * stride + c];
+  if (FMT == 2)
+    return reinterpret_cast<const uint32_t*>(base)[(size_t)(n >> 7) * stride + (c >> 3)];
+  return 0u;
+}
+
+// Dot of one 16-byte chunk with TT activation chunks. FP4 and FP8 codes are decoded to
+// exact bf16 (scale 1), dotted by v_dot2_f32_bf16, and each block partial is multiplied by
+// its fp32 block scale (FP4: 16- or 32-code blocks; FP8: the chunk lies in one 128-block);
+// bf16 weights are dotted directly.
 template <int FMT, int TT>
 __device__ __forceinline__ void chunk_dot(const uint4& w, uint32_t sc,
-                                          const uint32_t (&xv)[TT][16], float (&acc)[TT]) {
+                                          const uint32_t (&xv)[TT][DecFmt<FMT>::XW],
+                                          float (&acc)[TT]) {
   const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-  if (FMT == 0) {
+  if (FMT == 3) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int t = 0; t < TT; ++t) acc[t] = dot2_bf16(wd[d], xv[t][d], acc[t]);
+  } else if (FMT == 2) {
+    float part[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) part[t] = 0.f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t b[2];
+      fp8x4_to_bf16(wd[d], b);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int t = 0; t < TT; ++t) part[t] = dot2_bf16(b[j], xv[t][2 * d + j], part[t]);
+    }
+    const float s = __uint_as_float(sc);
+#pragma unroll
+    for (int t = 0; t < TT; ++t) acc[t] = fmaf(part[t], s, acc[t]);
+  } else if (FMT == 0) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       float part[TT];
@@ -98,15 +153,15 @@ __device__ __forceinline__ void chunk_dot(const uint4& w, uint32_t sc,
   }
 }
 
-// Chunk c (32 codes) of the TT activation rows staged in LDS ([TT][K] bf16).
-template <int TT>
+// Chunk c (2 * XW values) of the TT activation rows staged in LDS ([TT][K] bf16).
+template <int TT, int XW>
 __device__ __forceinline__ void lds_act_chunk(const uint16_t* s_x, int K, int c,
-                                              uint32_t (&xv)[TT][16]) {
+                                              uint32_t (&xv)[TT][XW]) {
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
-    const uint4* p = reinterpret_cast<const uint4*>(s_x + (size_t)t * K + c * 32);
+    const uint4* p = reinterpret_cast<const uint4*>(s_x + (size_t)t * K + c * 2 * XW);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < XW / 4; ++q) {
       const uint4 v = p[q];
       xv[t][4 * q + 0] = v.x;
       xv[t][4 * q + 1] = v.y;
@@ -116,16 +171,16 @@ __device__ __forceinline__ void lds_act_chunk(const uint16_t* s_x, int K, int c,
   }
 }
 
-// Chunk c (32 codes) of the TT activation rows read straight from memory (rows[t] of src).
-template <int TT>
+// Chunk c (2 * XW values) of the TT activation rows read straight from memory.
+template <int TT, int XW>
 __device__ __forceinline__ void global_act_chunk(const uint16_t* src, size_t stride,
                                                  const int (&rows)[TT], int c,
-                                                 uint32_t (&xv)[TT][16]) {
+                                                 uint32_t (&xv)[TT][XW]) {
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
-    const uint4* p = reinterpret_cast<const uint4*>(src + (size_t)rows[t] * stride + c * 32);
+    const uint4* p = reinterpret_cast<const uint4*>(src + (size_t)rows[t] * stride + c * 2 * XW);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < XW / 4; ++q) {
       const uint4 v = p[q];
       xv[t][4 * q + 0] = v.x;
       xv[t][4 * q + 1] = v.y;
@@ -177,7 +232,7 @@ struct WSrc {
 // Loads of step `it` (pass it / nci, chunk-slot it % nci) of this lane; every address is
 // clamped to a valid row and chunk (out-of-range results are discarded).
 template <int FMT, int NI, int M, int G, int GR>
-__device__ __forceinline__ void load_step(const WSrc src, size_t row_bytes, int sbytes,
+__device__ __forceinline__ void load_step(const WSrc src, size_t row_bytes, int sstride,
                                           int n_base, int nmax, int sub, int lpr, int nci,
                                           int nchunk, int it, WStep<NI, M>& st) {
   const int pass = it / nci, ci = it - pass * nci;
@@ -186,10 +241,10 @@ __device__ __forceinline__ void load_step(const WSrc src, size_t row_bytes, int 
   for (int i = 0; i < NI; ++i) {
     const int n = min(n_base + pass * GR + G * i, nmax);
     st.w[i][0] = *reinterpret_cast<const uint4*>(src.p0 + (size_t)n * row_bytes + c * 16);
-    st.s[i][0] = load_chunk_scales<FMT>(src.s0 + (size_t)n * sbytes, c);
+    st.s[i][0] = load_chunk_scales<FMT>(src.s0, n, sstride, c);
     if (M > 1) {
       st.w[i][M - 1] = *reinterpret_cast<const uint4*>(src.p1 + (size_t)n * row_bytes + c * 16);
-      st.s[i][M - 1] = load_chunk_scales<FMT>(src.s1 + (size_t)n * sbytes, c);
+      st.s[i][M - 1] = load_chunk_scales<FMT>(src.s1, n, sstride, c);
     }
   }
 }
@@ -207,11 +262,13 @@ __device__ __forceinline__ void gate_up_body(const ExpertGemmArgs& a, const Tile
   const int sub = lane % LPR, grp = lane / LPR;
   const int H = a.H, I = a.I;
   const int e = tile.group;
-  const int nchunk = H / 32;
-  const size_t row_bytes = (size_t)H / 2;
-  const int sbytes = H / (FMT == 0 ? 16 : 32);
+  constexpr int XW = DecFmt<FMT>::XW;
+  const int nchunk = H / DecFmt<FMT>::CPC;
+  const size_t row_bytes = dec_row_bytes<FMT>(H);
+  const int sstride = dec_scale_stride<FMT>(H);
+  const size_t sexp = dec_scale_expert_bytes<FMT>(I, H);
   const WSrc src{a.gate.packed + (size_t)e * I * row_bytes, a.up.packed + (size_t)e * I * row_bytes,
-                 a.gate.scales + (size_t)e * I * sbytes, a.up.scales + (size_t)e * I * sbytes};
+                 a.gate.scales + e * sexp, a.up.scales + e * sexp};
   const float gsg = FMT == 0 ? a.gate.global[e] : 1.0f;
   const float gsu = FMT == 0 ? a.up.global[e] : 1.0f;
 
@@ -222,7 +279,7 @@ __device__ __forceinline__ void gate_up_body(const ExpertGemmArgs& a, const Tile
   // in parallel instead of in sequence)
   WStep<NI, 2> s0, s1;
   const int nbase = nwave0 + grp;
-  load_step<FMT, NI, 2, G, GR>(src, row_bytes, sbytes, nbase, I - 1, sub, LPR, nci, nchunk, 0, s0);
+  load_step<FMT, NI, 2, G, GR>(src, row_bytes, sstride, nbase, I - 1, sub, LPR, nci, nchunk, 0, s0);
   int rows[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t) rows[t] = t < tile.count ? tile.tok[t] : tile.tok[0];
@@ -237,9 +294,9 @@ __device__ __forceinline__ void gate_up_body(const ExpertGemmArgs& a, const Tile
     const int pass = it / nci, ci = it - pass * nci;
     const int c = sub + ci * LPR;
     if (c < nchunk) {
-      uint32_t xv[TT][16];
-      if (STAGED) lds_act_chunk<TT>(s_x, H, c, xv);
-      else global_act_chunk<TT>(a.x, (size_t)H, rows, c, xv);
+      uint32_t xv[TT][XW];
+      if (STAGED) lds_act_chunk<TT, XW>(s_x, H, c, xv);
+      else global_act_chunk<TT, XW>(a.x, (size_t)H, rows, c, xv);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
 #pragma unroll
@@ -280,11 +337,11 @@ __device__ __forceinline__ void gate_up_body(const ExpertGemmArgs& a, const Tile
   // two register sets renamed by a 2-step unroll (a copy of a set in flight would wait)
 #pragma unroll 1
   for (int it = 0; it < total; it += 2) {
-    load_step<FMT, NI, 2, G, GR>(src, row_bytes, sbytes, nbase, I - 1, sub, LPR, nci, nchunk,
+    load_step<FMT, NI, 2, G, GR>(src, row_bytes, sstride, nbase, I - 1, sub, LPR, nci, nchunk,
                                  min(it + 1, total - 1), s1);
     consume(it, s0);
     if (it + 1 >= total) break;
-    load_step<FMT, NI, 2, G, GR>(src, row_bytes, sbytes, nbase, I - 1, sub, LPR, nci, nchunk,
+    load_step<FMT, NI, 2, G, GR>(src, row_bytes, sstride, nbase, I - 1, sub, LPR, nci, nchunk,
                                  min(it + 2, total - 1), s0);
     consume(it + 1, s1);
   }
@@ -297,7 +354,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   if (!resolve_tile(a.src, a.row_token, blockIdx.y, tile)) return;
   if (blockIdx.x * kDecWaves * rpw >= a.I) return;
   // one step per wave (one pass, one chunk per lane and row): no staging, no pipeline
-  const bool one = rpw == kGateRowsPerPass && a.H / 32 <= LPR;
+  const bool one = rpw == kGateRowsPerPass && a.H / DecFmt<FMT>::CPC <= LPR;
   if (tile.count == 1) {
     if (one) gate_up_body<FMT, 1, LPR, false>(a, tile, rpw, s_x);
     else gate_up_body<FMT, 1, LPR, true>(a, tile, rpw, s_x);
@@ -323,11 +380,12 @@ __device__ __forceinline__ void down_body(const ExpertGemmArgs& a, const Tile& t
   const int sub = lane % LPR, grp = lane / LPR;
   const int H = a.H, I = a.I;
   const int e = tile.group;
-  const int nchunk = I / 32;
-  const size_t row_bytes = (size_t)I / 2;
-  const int sbytes = I / (FMT == 0 ? 16 : 32);
+  constexpr int XW = DecFmt<FMT>::XW;
+  const int nchunk = I / DecFmt<FMT>::CPC;
+  const size_t row_bytes = dec_row_bytes<FMT>(I);
+  const int sstride = dec_scale_stride<FMT>(I);
   const WSrc src{a.down.packed + (size_t)e * H * row_bytes, nullptr,
-                 a.down.scales + (size_t)e * H * sbytes, nullptr};
+                 a.down.scales + e * dec_scale_expert_bytes<FMT>(H, I), nullptr};
   const float gsd = FMT == 0 ? a.down.global[e] : 1.0f;
 
   const int nwave0 = blockIdx.x * (kDecWaves * rpw) + wave * rpw;
@@ -335,7 +393,7 @@ __device__ __forceinline__ void down_body(const ExpertGemmArgs& a, const Tile& t
   const int total = (rpw / DR) * nci;
   WStep<NI, 1> s0, s1;
   const int nbase = nwave0 + grp;
-  load_step<FMT, NI, 1, G, DR>(src, row_bytes, sbytes, nbase, H - 1, sub, LPR, nci, nchunk, 0, s0);
+  load_step<FMT, NI, 1, G, DR>(src, row_bytes, sstride, nbase, H - 1, sub, LPR, nci, nchunk, 0, s0);
   int rows[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t) rows[t] = tile.row0 + (t < tile.count ? t : 0);
@@ -348,9 +406,9 @@ __device__ __forceinline__ void down_body(const ExpertGemmArgs& a, const Tile& t
     const int pass = it / nci, ci = it - pass * nci;
     const int c = sub + ci * LPR;
     if (c < nchunk) {
-      uint32_t xv[TT][16];
-      if (STAGED) lds_act_chunk<TT>(s_x, I, c, xv);
-      else global_act_chunk<TT>(a.h, (size_t)a.h_stride, rows, c, xv);
+      uint32_t xv[TT][XW];
+      if (STAGED) lds_act_chunk<TT, XW>(s_x, I, c, xv);
+      else global_act_chunk<TT, XW>(a.h, (size_t)a.h_stride, rows, c, xv);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         float r[TT];
@@ -382,11 +440,11 @@ __device__ __forceinline__ void down_body(const ExpertGemmArgs& a, const Tile& t
   }
 #pragma unroll 1
   for (int it = 0; it < total; it += 2) {
-    load_step<FMT, NI, 1, G, DR>(src, row_bytes, sbytes, nbase, H - 1, sub, LPR, nci, nchunk,
+    load_step<FMT, NI, 1, G, DR>(src, row_bytes, sstride, nbase, H - 1, sub, LPR, nci, nchunk,
                                  min(it + 1, total - 1), s1);
     consume(it, s0);
     if (it + 1 >= total) break;
-    load_step<FMT, NI, 1, G, DR>(src, row_bytes, sbytes, nbase, H - 1, sub, LPR, nci, nchunk,
+    load_step<FMT, NI, 1, G, DR>(src, row_bytes, sstride, nbase, H - 1, sub, LPR, nci, nchunk,
                                  min(it + 2, total - 1), s0);
     consume(it + 1, s1);
   }
@@ -398,7 +456,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   Tile tile;
   if (!resolve_tile(a.src, a.row_token, blockIdx.y, tile)) return;
   if (blockIdx.x * kDecWaves * rpw >= a.H) return;
-  const bool one = rpw == kDownRowsPerPass && a.I / 32 <= LPR;
+  const bool one = rpw == kDownRowsPerPass && a.I / DecFmt<FMT>::CPC <= LPR;
   if (tile.count == 1) {
     if (one) down_body<FMT, 1, LPR, false>(a, tile, rpw, s_x);
     else down_body<FMT, 1, LPR, true>(a, tile, rpw, s_x);
@@ -467,47 +525,75 @@ static void launch_dn(const ExpertGemmArgs& a, int rpw, hipStream_t s) {
     default: LAUNCH<FMT, 8>(A, RPW, S); break;            \
   }
 
+// codes per 16-byte chunk of a format (host side of DecFmt)
+static int codes_per_chunk(int fmt) { return fmt <= 1 ? 32 : (fmt == 2 ? 16 : 8); }
+
 hipError_t launch_decode_gate_up(const ExpertGemmArgs& a, hipStream_t s) {
   if (a.tile_bound <= 0) return hipSuccess;
   const int rpw = pick_rows_per_wave(kGateRowsPerPass, a.I, a.tile_bound);
-  const int lpr = pick_lpr(a.H / 32);
-  if (a.gate.fmt == 0) { MOE_DISPATCH_LPR(launch_gu, 0, lpr, a, rpw, s); }
-  else { MOE_DISPATCH_LPR(launch_gu, 1, lpr, a, rpw, s); }
+  const int lpr = pick_lpr(a.H / codes_per_chunk(a.gate.fmt));
+  switch (a.gate.fmt) {
+    case 0: MOE_DISPATCH_LPR(launch_gu, 0, lpr, a, rpw, s); break;
+    case 1: MOE_DISPATCH_LPR(launch_gu, 1, lpr, a, rpw, s); break;
+    case 2: MOE_DISPATCH_LPR(launch_gu, 2, lpr, a, rpw, s); break;
+    default: MOE_DISPATCH_LPR(launch_gu, 3, lpr, a, rpw, s); break;
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_decode_down(const ExpertGemmArgs& a, hipStream_t s) {
   if (a.tile_bound <= 0) return hipSuccess;
   const int rpw = pick_rows_per_wave(kDownRowsPerPass, a.H, a.tile_bound);
-  const int lpr = pick_lpr(a.I / 32);
-  if (a.down.fmt == 0) { MOE_DISPATCH_LPR(launch_dn, 0, lpr, a, rpw, s); }
-  else { MOE_DISPATCH_LPR(launch_dn, 1, lpr, a, rpw, s); }
+  const int lpr = pick_lpr(a.I / codes_per_chunk(a.down.fmt));
+  switch (a.down.fmt) {
+    case 0: MOE_DISPATCH_LPR(launch_dn, 0, lpr, a, rpw, s); break;
+    case 1: MOE_DISPATCH_LPR(launch_dn, 1, lpr, a, rpw, s); break;
+    case 2: MOE_DISPATCH_LPR(launch_dn, 2, lpr, a, rpw, s); break;
+    default: MOE_DISPATCH_LPR(launch_dn, 3, lpr, a, rpw, s); break;
+  }
   return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------- debug
-// Decode one expert matrix to f32 [n, k] with the device routine of a path:
-// path 1 (decode GEMV): E2M1 -> bf16 (scale 1) -> f32, times the fp32 block scale;
-// path 2 (MFMA operand): the bf16 operand the grouped GEMM feeds its MFMAs.
-// Both then times the NVFP4 global scale (one fp32 rounding).
+// Decode one expert matrix to f32 [n, k] with the device routine of a path, 8 values per
+// thread: path 1 (decode GEMV): codes -> bf16 (scale 1) -> f32, times the fp32 block scale;
+// path 2 (MFMA operand): the bf16 operand the grouped GEMM feeds its MFMAs. FP4 then times
+// the NVFP4 global scale (one fp32 rounding); BF16 weights are their own values.
 __global__ void k_debug_dequant(WeightDesc w, int expert, int path, float* out) {
-  const int dwords_per_row = w.k / 8;
+  const int groups_per_row = w.k / 8;
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= w.n * dwords_per_row) return;
-  const int row = i / dwords_per_row, d = i % dwords_per_row;
-  const size_t rbytes = (size_t)w.k / 2;
-  const uint32_t q =
-      reinterpret_cast<const uint32_t*>(w.packed + ((size_t)expert * w.n + row) * rbytes)[d];
-  const int blk = w.fmt == 0 ? 16 : 32;
-  const uint8_t sb = w.scales[((size_t)expert * w.n + row) * (w.k / blk) + (d * 8) / blk];
-  const float g = w.fmt == 0 ? w.global[expert] : 1.0f;
+  if (i >= w.n * groups_per_row) return;
+  const int row = i / groups_per_row, d = i % groups_per_row;
+  const size_t erow = (size_t)expert * w.n + row;
   uint32_t b[4];
-  float scale_after = 1.0f;
-  if (path == 1) {
-    fp4x8_to_bf16(q, 1.0f, b);
-    scale_after = w.fmt == 0 ? e4m3_to_f32(sb) : e8m0_to_f32(sb);
+  float scale_after = 1.0f, g = 1.0f;
+  if (w.fmt <= 1) {
+    const size_t rbytes = (size_t)w.k / 2;
+    const uint32_t q = reinterpret_cast<const uint32_t*>(w.packed + erow * rbytes)[d];
+    const int blk = w.fmt == 0 ? 16 : 32;
+    const uint8_t sb = w.scales[erow * (w.k / blk) + (d * 8) / blk];
+    g = w.fmt == 0 ? w.global[expert] : 1.0f;
+    if (path == 1) {
+      fp4x8_to_bf16(q, 1.0f, b);
+      scale_after = w.fmt == 0 ? e4m3_to_f32(sb) : e8m0_to_f32(sb);
+    } else {
+      mfma_operand_fp4x8(w.fmt, q, sb, b);
+    }
+  } else if (w.fmt == 2) {
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(w.packed + erow * w.k) + 2 * d;
+    const int kb = (w.k + 127) / 128, nb = (w.n + 127) / 128;
+    const float sc = reinterpret_cast<const float*>(w.scales)[((size_t)expert * nb + row / 128) * kb +
+                                                             (d * 8) / 128];
+    if (path == 1) {
+      fp8x4_to_bf16(q[0], b);
+      fp8x4_to_bf16(q[1], b + 2);
+      scale_after = sc;
+    } else {
+      mfma_operand_fp8x8(q[0], q[1], sc, b);
+    }
   } else {
-    mfma_operand_fp4x8(w.fmt, q, sb, b);
+    const uint4 v = reinterpret_cast<const uint4*>(w.packed + erow * w.k * 2)[d];
+    b[0] = v.x; b[1] = v.y; b[2] = v.z; b[3] = v.w;
   }
   float* o = out + (size_t)row * w.k + d * 8;
 #pragma unroll

@@ -121,6 +121,27 @@ __device__ __forceinline__ void mfma_operand_fp4x8(int fmt, uint32_t q, uint32_t
   else mfma_operand_fp4x8<0>(q, sb, out);
 }
 
+// Four E4M3 codes (byte j = code j) -> two bf16 pairs, exact (E4M3's range and 3-bit
+// mantissa fit bf16; scale operand 1.0).
+__device__ __forceinline__ void fp8x4_to_bf16(uint32_t q, uint32_t out[2]) {
+  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, 1.0f, false));
+  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, 1.0f, true));
+}
+
+// The bf16 B operand of the grouped GEMM for 8 E4M3 codes (two dwords) of one 128 x 128
+// block with fp32 scale s: bf16(e4m3 * s), one rounding per element.
+__device__ __forceinline__ void mfma_operand_fp8x8(uint32_t q0, uint32_t q1, float s,
+                                                   uint32_t out[4]) {
+  const uint32_t q[2] = {q0, q1};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(q[i], 1.0f, false);
+    const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(q[i], 1.0f, true);
+    out[2 * i] = pack_bf16x2(a[0] * s, a[1] * s);
+    out[2 * i + 1] = pack_bf16x2(b[0] * s, b[1] * s);
+  }
+}
+
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), acc, false);

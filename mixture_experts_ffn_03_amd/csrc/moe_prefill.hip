@@ -42,6 +42,7 @@
 namespace moe {
 
 constexpr int kXcds = 8;
+constexpr int kFp8MaxKb = 128;  // FP8 prefill: K up to 128 * 128 codes (block-scale table)
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -98,11 +99,14 @@ __device__ __forceinline__ void wait_inflight(int r, bool ss) {
 // 8 of them, must land on distinct 16-byte bank groups. A rows of 8 pieces (128 bytes)
 // XOR the piece with a permutation of row bits 0..3 that is distinct over any 8
 // consecutive rows and over the 8 rows of each parity within 16; rows of 16 pieces use
-// row bits 0..3 directly. B rows of 2 pieces (32 bytes) flip the piece by row bit 2 xor
+// row bits 0..3 directly; rows of 4 pieces XOR with (row >> 1 ^ row >> 2) & 3, distinct over
+// the rows that share banks in either grouping. B rows of 2 pieces (32 bytes) flip the piece by row bit 2 xor
 // bit 3; of 4 pieces (64 bytes) by ((row >> 1) ^ (row >> 3)) & 3.
 template <int PA>
 __device__ __forceinline__ int a_swz(int row) {
-  return PA == 16 ? row & 15 : ((row >> 1) ^ ((row & 1) << 2)) & 7;
+  if (PA == 16) return row & 15;
+  if (PA == 8) return ((row >> 1) ^ ((row & 1) << 2)) & 7;
+  return ((row >> 1) ^ (row >> 2)) & 3;  // 4 pieces (64-byte rows)
 }
 template <int PB>
 __device__ __forceinline__ int b_swz(int row) {
@@ -175,14 +179,17 @@ struct PreShape {
   static constexpr int MT = 32 * RB * WM;
   static constexpr int BROWS = 32 * CB * WN;
   static constexpr int NCOLS = GATEUP ? BROWS / 2 : BROWS;  // output columns per block
+  static constexpr bool FP4 = FMT <= 1;
   static constexpr int STEPS = KC / 16;  // MFMA steps per stage (lane half: KC/2 codes)
-  static constexpr int PA = KC / 8;      // 16-byte pieces per A row per stage
-  static constexpr int PB = KC / 32;     // 16-byte pieces per B row per stage
+  static constexpr int PA = KC / 8;      // 16-byte pieces per A row per stage (bf16)
+  // B row bytes per stage: KC codes of 1/2 (FP4), 1 (FP8) or 2 (BF16) bytes
+  static constexpr int B_ROW = FP4 ? KC / 2 : (FMT == 2 ? KC : 2 * KC);
+  static constexpr int PB = B_ROW / 16;   // 16-byte pieces per B row per stage
+  static constexpr int WPS = B_ROW / 4 / (2 * STEPS);  // B dwords per lane per MFMA step
   static constexpr int A_ROW = 16 * PA;
-  static constexpr int B_ROW = 16 * PB;
-  static constexpr int SLOTS = KC / 64;                      // scale slots per row (SS off)
-  static constexpr int SROW = SS ? 0 : 4 * SLOTS;            // scale bytes per row per stage
-  static constexpr int SW = FMT == 0 ? KC / 32 : KC / 64;    // scale bytes per lane half
+  static constexpr int SLOTS = KC / 64;                            // FP4 scale slots per row
+  static constexpr int SROW = (SS || !FP4) ? 0 : 4 * SLOTS;        // scale bytes per row per stage
+  static constexpr int SW = FMT == 0 ? KC / 32 : KC / 64;          // FP4 scale bytes per lane half
   static constexpr int A_BYTES = MT * A_ROW;
   static constexpr int B_BYTES = BROWS * B_ROW;
   static constexpr int S_BYTES = BROWS * SROW;
@@ -197,9 +204,16 @@ struct PreShape {
   static constexpr int NSS = SS ? BROWS / (SS_WAVES * 64) : 0;  // per lane of those waves
   static constexpr int SS_BYTES = SS ? 2 * BROWS * 16 : 0;       // two super-stage slots
   static constexpr int LEAD = NSTG - 1;  // stages in flight ahead of the one computed
-  static constexpr size_t SMEM = (size_t)NSTG * STAGE + SS_BYTES;
+  // FP8: the fp32 scales of the block's weight rows (gate and up, or down), one per
+  // (128-row block, 128-code block), for K up to kFp8MaxKb * 128
+  static constexpr int MATS = GATEUP ? 2 : 1;
+  static constexpr int NBL = (NCOLS + 127) / 128;
+  static constexpr int TAB_BYTES = FMT == 2 ? MATS * NBL * kFp8MaxKb * 4 : 0;
+  static constexpr size_t SMEM = (size_t)NSTG * STAGE + SS_BYTES + TAB_BYTES;
   static constexpr int BLOCKS_PER_CU = SMEM <= 80 * 1024 ? 2 : 1;
-  static_assert(KC == 64 || KC == 128, "stage width");
+  static_assert(FP4 ? (KC == 64 || KC == 128) : KC == 32, "stage width");
+  static_assert(!SS || FP4, "super-staged scales are FP4 only");
+  static_assert(PB >= 2 && WPS * 2 * STEPS * 4 == B_ROW, "B row split over the lane halves");
   static_assert(NA * NT == MT * PA && NB * NT == BROWS * PB && NS * NT * 4 == S_BYTES,
                 "a stage must split evenly over the block");
   static_assert(!SS || NSS * SS_WAVES * 64 == BROWS, "one super-stage load per row");
@@ -242,10 +256,22 @@ void k_pre_gemm(ExpertGemmArgs a) {
   const int half = lane >> 5, r = lane & 31;
   const int e = t.group;
   const int n0 = ct * NCOLS;
-  const size_t row_bytes = (size_t)K / 2;
-  const int sbytes = K / (FMT == 0 ? 16 : 32);
+  const size_t row_bytes = (size_t)K * Sh::B_ROW / KC;
+  const int sbytes = Sh::FP4 ? K / (FMT == 0 ? 16 : 32) : 0;
   const WeightDesc& w0 = GATEUP ? a.gate : a.down;
   const WeightDesc& w1 = GATEUP ? a.up : a.down;
+  float* s_tab = reinterpret_cast<float*>(s_ss + Sh::SS_BYTES);  // FP8 block scales
+  if (FMT == 2) {
+    // [matrix][128-row block][128-code block] of the rows n0..n0+NCOLS-1 (0 past N)
+    const int kb = (K + 127) / 128, nbg = (N + 127) / 128;
+    for (int i = threadIdx.x; i < Sh::MATS * Sh::NBL * kb; i += NT) {
+      const int m = i / (Sh::NBL * kb), rest = i % (Sh::NBL * kb);
+      const int nb = n0 / 128 + rest / kb, kk = rest % kb;
+      const float* tab = reinterpret_cast<const float*>(m ? w1.scales : w0.scales);
+      s_tab[(m * Sh::NBL + rest / kb) * kFp8MaxKb + kk] =
+          nb < nbg ? tab[((size_t)e * nbg + nb) * kb + kk] : 0.0f;
+    }
+  }
 
   // gathered token (gate+up) or h row (down); rows past the tile's count repeat its
   // first row (results discarded)
@@ -295,8 +321,9 @@ void k_pre_gemm(ExpertGemmArgs a) {
   for (int i = 0; i < NS; ++i) {
     const WeightDesc* w;
     const int slot = (wave * NS + i) * 64 + lane;  // 4-byte slot u of its row: 64 codes
-    const size_t rw = wrow(slot / SLOTS, w);
-    ssrc[i] = w->scales + rw * sbytes + (slot % SLOTS) * (FMT == 0 ? 4 : 2);
+    constexpr int SL = SLOTS > 0 ? SLOTS : 1;  // (no such loads for FP8 / BF16)
+    const size_t rw = wrow(slot / SL, w);
+    ssrc[i] = w->scales + rw * sbytes + (slot % SL) * (FMT == 0 ? 4 : 2);
   }
   const uint8_t* sssrc[NSS > 0 ? NSS : 1];
 #pragma unroll
@@ -331,7 +358,7 @@ void k_pre_gemm(ExpertGemmArgs a) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int slot0 = (wave * NB + i) * 64;
-      dma16(bsrc[i] + k0 / 2, __builtin_amdgcn_readfirstlane(bbase + slot0 * 16));
+      dma16(bsrc[i] + (size_t)k0 * Sh::B_ROW / KC, __builtin_amdgcn_readfirstlane(bbase + slot0 * 16));
     }
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
@@ -376,7 +403,8 @@ void k_pre_gemm(ExpertGemmArgs a) {
     const uint8_t* sa = s_dyn + (c % NSTG) * Sh::STAGE;
     const uint8_t* sbq = sa + Sh::A_BYTES;
     const uint8_t* ssc = sbq + Sh::B_BYTES;
-    uint32_t q[CB][STEPS], sc[CB];
+    constexpr int WPS = Sh::WPS;
+    uint32_t q[CB][STEPS * WPS], sc[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const int srow = brow0[cb] + r;
@@ -386,12 +414,21 @@ void k_pre_gemm(ExpertGemmArgs a) {
         const uint4 v = *reinterpret_cast<const uint4*>(sbq + srow * Sh::B_ROW + ((piece ^ bsw) << 4));
         q[cb][4 * j] = v.x; q[cb][4 * j + 1] = v.y; q[cb][4 * j + 2] = v.z; q[cb][4 * j + 3] = v.w;
       }
-      // this lane's scale bytes of the stage (blocks of its codes: NVFP4 KC/32, MXFP4 KC/64)
-      const uint8_t* sp =
-          SS ? s_ss + ((c / SUPER) & 1) * BROWS * 16 + srow * 16 + (c % SUPER) * 2 * Sh::SW +
-                   half * Sh::SW
-             : ssc + srow * Sh::SROW + (SLOTS == 2 ? 4 * half : half * Sh::SW);
-      sc[cb] = lds_scale<Sh::SW>(sp);
+      if (Sh::FP4) {
+        // this lane's scale bytes of the stage (blocks of its codes: NVFP4 KC/32, MXFP4 KC/64)
+        const uint8_t* sp =
+            SS ? s_ss + ((c / SUPER) & 1) * BROWS * 16 + srow * 16 + (c % SUPER) * 2 * Sh::SW +
+                     half * Sh::SW
+               : ssc + srow * Sh::SROW + (SLOTS == 2 ? 4 * half : half * Sh::SW);
+        sc[cb] = lds_scale<Sh::SW>(sp);
+      } else if (FMT == 2) {
+        // the column block's 32 rows lie in one 128-row block; the stage in one 128-code block
+        const int m = GATEUP ? cb / CH : 0;
+        const int nbl = ((GATEUP ? brow0[cb] - m * (BROWS / 2) : brow0[cb])) / 128;
+        sc[cb] = __float_as_uint(s_tab[(m * Sh::NBL + nbl) * kFp8MaxKb + (c * KC) / 128]);
+      } else {
+        sc[cb] = 0u;
+      }
     }
     // every A operand of the stage is read up front, in the order of use, so that LDS
     // latency overlaps the MFMAs instead of stalling each step (LDS reads return in order)
@@ -410,7 +447,18 @@ void k_pre_gemm(ExpertGemmArgs a) {
     for (int s = 0; s < STEPS; ++s) {
       bf16x8_t bo[CB];
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) bo[cb] = b_operand<FMT>(q[cb][s], sc[cb], s);
+      for (int cb = 0; cb < CB; ++cb) {
+        if (Sh::FP4) {
+          bo[cb] = b_operand<FMT>(q[cb][s], sc[cb], s);
+        } else if (FMT == 2) {
+          uint32_t d[4];
+          mfma_operand_fp8x8(q[cb][2 * s], q[cb][2 * s + 1], __uint_as_float(sc[cb]), d);
+          bo[cb] = as_bf16x8(d);
+        } else {
+          const uint32_t d[4] = {q[cb][4 * s], q[cb][4 * s + 1], q[cb][4 * s + 2], q[cb][4 * s + 3]};
+          bo[cb] = as_bf16x8(d);
+        }
+      }
 #pragma unroll
       for (int rb = 0; rb < NR; ++rb) {
         const bf16x8_t af = __builtin_bit_cast(bf16x8_t, av[rb][s]);
@@ -526,9 +574,14 @@ template <int FMT, int KC, int NSTG, int RB, int WM, int CB, bool GATEUP>
 static hipError_t launch_pre_shape(const ExpertGemmArgs& a, hipStream_t s) {
   const int K = GATEUP ? a.H : a.I;
   if (K % KC != 0) return hipErrorInvalidValue;
-  const int sbytes = K / (FMT == 0 ? 16 : 32);
-  if (sbytes % 16 == 0) return launch_pre_ss<FMT, KC, NSTG, RB, WM, CB, GATEUP, true>(a, s);
-  return launch_pre_ss<FMT, KC, NSTG, RB, WM, CB, GATEUP, false>(a, s);
+  if constexpr (FMT >= 2) {
+    if (FMT == 2 && (K + 127) / 128 > kFp8MaxKb) return hipErrorInvalidValue;
+    return launch_pre_ss<FMT, KC, NSTG, RB, WM, CB, GATEUP, false>(a, s);
+  } else {
+    const int sbytes = K / (FMT == 0 ? 16 : 32);
+    if (sbytes % 16 == 0) return launch_pre_ss<FMT, KC, NSTG, RB, WM, CB, GATEUP, true>(a, s);
+    return launch_pre_ss<FMT, KC, NSTG, RB, WM, CB, GATEUP, false>(a, s);
+  }
 }
 
 // Tile height MT -> stage width KC and block shape (row blocks per wave RB, waves along M
@@ -552,12 +605,22 @@ static hipError_t launch_pre(const ExpertGemmArgs& a, int mt, hipStream_t s) {
     if (mt == 64) return launch_pre_shape<0, 64, 3, 1, 2, 4, GATEUP>(a, s);
     return launch_pre_shape<0, 64, NS3, 2, 2, 4, GATEUP>(a, s);
   }
-  if (mt == 32) {
+  if (mt == 32 && fmt == 1) {
     return K % 128 == 0 ? launch_pre_shape<1, 128, 3, 1, 1, 4, GATEUP>(a, s)
                         : launch_pre_shape<1, 64, 3, 1, 1, 4, GATEUP>(a, s);
   }
-  if (mt == 64) return launch_pre_shape<1, 64, 3, 1, 2, 4, GATEUP>(a, s);
-  return launch_pre_shape<1, 64, NS3, 2, 2, 4, GATEUP>(a, s);
+  if (fmt == 1) {
+    if (mt == 64) return launch_pre_shape<1, 64, 3, 1, 2, 4, GATEUP>(a, s);
+    return launch_pre_shape<1, 64, NS3, 2, 2, 4, GATEUP>(a, s);
+  }
+  // FP8 / BF16 weights: 32-code stages; 32-row tiles run in the 64-row shape (its second
+  // row block idle)
+  if (fmt == 2) {
+    if (mt <= 64) return launch_pre_shape<2, 32, 3, 1, 2, 4, GATEUP>(a, s);
+    return launch_pre_shape<2, 32, 3, 2, 2, 4, GATEUP>(a, s);
+  }
+  if (mt <= 64) return launch_pre_shape<3, 32, 3, 1, 2, 4, GATEUP>(a, s);
+  return launch_pre_shape<3, 32, 3, 2, 2, 4, GATEUP>(a, s);
 }
 
 hipError_t launch_prefill_gate_up(const ExpertGemmArgs& a, int mt, hipStream_t s) {

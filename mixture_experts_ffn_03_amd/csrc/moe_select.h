@@ -284,6 +284,7 @@ __device__ void dispatch_body(const DispatchArgs& a, const int32_t* ids, const i
     }
 #pragma unroll
     for (int j = 0; j < kDispatchBatch; ++j) {
+      if (c0 + j * kWave >= se) break;  // past the segment (wave-uniform)
       const int s = c0 + j * kWave + lane;
       const int e = ev[j];
       if (s < se) {
@@ -323,6 +324,7 @@ __device__ void dispatch_body(const DispatchArgs& a, const int32_t* ids, const i
     }
 #pragma unroll
     for (int j = 0; j < kDispatchBatch; ++j) {
+      if (c0 + j * kWave >= se) break;  // past the segment (wave-uniform)
       const int s = c0 + j * kWave + lane;
       const bool in = s < se;
       const int e = ev[j];

@@ -81,6 +81,54 @@ def test_dequant_random_block_layout():
                 assert np.array_equal(out.cpu().numpy(), want.astype(np.float32)), (fmt, e, path)
 
 
+def _fp8_expected(codes, scales, path):
+    """Device dequant of FP8 per path: decode GEMV = fp32(bf16(e4m3) * scale) (the bf16 of
+    an E4M3 value is exact); MFMA operand = bf16_rne(fp32(e4m3 * scale)). numpy's float32
+    multiply is correctly rounded, like the device's."""
+    v = O.dequant_fp8(codes, np.ones_like(scales)).astype(np.float32)
+    sc = np.repeat(np.repeat(scales.astype(np.float32), 128, 0), 128, 1)[:codes.shape[0], :codes.shape[1]]
+    prod = v * sc
+    if path == M.PATH_DECODE:
+        return prod
+    return torch.from_numpy(prod).to(torch.bfloat16).float().numpy()
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_dequant_fp8_every_code_times_block_scales(path):
+    _announce("dequant fp8", path)
+    # 256 rows x 256 codes: row r holds every E4M3 code rotated by r; 2 x 2 blocks with
+    # power-of-two and other fp32 scales
+    codes = (np.arange(256)[None, :] + np.arange(256)[:, None]).astype(np.uint8)
+    scales = np.array([[1.0, 2.0 ** -7], [np.float32(0.3711), np.float32(1e-3)]], dtype=np.float32)
+    w = S.Fp4Weight(S.FP8, torch.from_numpy(codes[None].copy()).to(DEV),
+                    torch.from_numpy(scales[None].copy()).to(DEV), None, 256, 256)
+    out = torch.full((256, 256), -7.0, dtype=torch.float32, device=DEV)
+    M.debug_dequant(M.fp4_weight(w), 0, path, out)
+    _sync()
+    got = out.cpu().numpy()
+    want = _fp8_expected(codes, scales, path)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def test_dequant_fp8_bf16_random_layout():
+    g = torch.Generator(device=DEV).manual_seed(4)
+    for fmt in (S.FP8, S.BF16):
+        w = S.random_codes_weight(g, DEV, 3, 200, 384, fmt)  # ragged 128-row blocks
+        for e in range(3):
+            for path in PATH_VALUES:
+                out = torch.empty((200, 384), dtype=torch.float32, device=DEV)
+                M.debug_dequant(M.fp4_weight(w), e, path, out)
+                _sync()
+                if fmt == S.FP8:
+                    want = _fp8_expected(w.packed[e].cpu().numpy(), w.scales[e].cpu().numpy(), path)
+                else:
+                    want = w.packed[e].float().cpu().numpy()
+                assert np.array_equal(out.cpu().numpy(), want), (fmt, e, path)
+
+
 # ----------------------------------------------------------------------------- routing
 
 def _route_gpu(cfg, logits=None, inp=None, corr=None, bias=None, token_ids=None, tid2eid=None):
@@ -211,6 +259,20 @@ SMALL = {
     # K a multiple of 64 but not of 128 at 32-row prefill tiles (64-code stages)
     "oddk_mini": S.LayerSpec(name="oddk_mini", tokens=9, hidden=320, experts=16, top_k=4,
                              inter=192, fmt=S.MXFP4, seed=1078),
+    # FP8 (E4M3, 128 x 128 block scales) and BF16 expert weights, with an NVFP4 or FP8
+    # shared expert; shapes not multiples of 128 exercise partial scale blocks
+    "fp8_mini": S.LayerSpec(name="fp8_mini", tokens=11, hidden=640, experts=32, top_k=4,
+                            inter=320, fmt=S.FP8, score=S.SIGMOID, renormalize=True,
+                            correction_bias=True, shared=True, shared_inter=192,
+                            shared_fmt=S.NVFP4, seed=1081),
+    "fp8_prefill_mini": S.LayerSpec(name="fp8_prefill_mini", tokens=300, hidden=512, experts=8,
+                                    top_k=3, inter=384, fmt=S.FP8, shared=True,
+                                    shared_inter=256, shared_fmt=S.FP8, seed=1082),
+    "bf16_mini": S.LayerSpec(name="bf16_mini", tokens=400, hidden=384, experts=12, top_k=3,
+                             inter=256, fmt=S.BF16, seed=1083),
+    "bf16_shared_mini": S.LayerSpec(name="bf16_shared_mini", tokens=9, hidden=256, experts=16,
+                                    top_k=4, inter=128, fmt=S.BF16, shared=True,
+                                    shared_inter=192, shared_fmt=S.BF16, seed=1084),
     # softmax+bias routing over 48 + 16 zero-computation experts (identity contributions)
     "zero_experts_mini": S.LayerSpec(name="zero_experts_mini", tokens=23, hidden=512,
                                      experts=48, top_k=8, inter=256, fmt=S.NVFP4,

@@ -59,7 +59,9 @@ def log(*a):
 
 
 def bytes_per_elem(fmt):
-    return 0.5 + (1.0 / 16 if fmt == 0 else 1.0 / 32)
+    """Storage bytes per weight element with its scales: NVFP4, MXFP4, FP8 (fp32 per
+    128 x 128 block), BF16."""
+    return [0.5 + 1.0 / 16, 0.5 + 1.0 / 32, 1.0 + 4.0 / (128 * 128), 2.0][fmt]
 
 
 class HipEvents:
@@ -285,6 +287,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qwen3_decode_t8", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="run the workload's layer at this many tokens (e.g. 2 or 3 for a "
+                         "multi-token verify step); 0 = the workload's own")
     ap.add_argument("--weight-sets", type=int, default=0, help="0 = workload default")
     ap.add_argument("--batches", type=int, default=8)
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
@@ -335,6 +340,8 @@ def main():
     M.load_library()
     name = args.workload
     spec = S.WORKLOADS[name]
+    if args.tokens > 0:
+        spec = S.scaled(spec, tokens=args.tokens)
     dev = "cuda"
     nsets = args.weight_sets or WEIGHT_SETS[name]
     path = {"auto": M.PATH_AUTO, "decode": M.PATH_DECODE, "prefill": M.PATH_PREFILL}[args.path]
@@ -471,7 +478,7 @@ def main():
         "metric": METRIC, "value": round(tokens_per_s, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "weights": "nvfp4" if spec.fmt == 0 else "mxfp4",
+        "dtype": "bf16", "weights": ["nvfp4", "mxfp4", "fp8", "bf16"][spec.fmt],
         "data": "synthetic (seeded; random-init FP4 weights, N(0,1) bf16 activations)",
         "config": {"workload": name, "description": DESCRIPTIONS[name], "tokens": T,
                    "hidden": H, "experts": E, "top_k": K, "inter": I,

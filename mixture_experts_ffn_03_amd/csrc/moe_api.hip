@@ -341,12 +341,13 @@ int launch_route(const moe_config& c, const Layout& L, const uint16_t* x,
                  const int32_t* token_ids, const int64_t* tid2eid, const float* logits_in,
                  float* logits_out, int32_t* ids, float* w, void* ws, hipStream_t s,
                  const StageMarks* marks = nullptr, bool* dispatched = nullptr) {
-  if (!logits_in)
-    MOE_HIP(launch_router_partial(x, router_w, at<double>(ws, L.partial), c.tokens,
-                                  c.num_experts + c.zero_experts, c.hidden, L.ks, L.hsplit, s));
+  const int NE = c.num_experts + c.zero_experts;
   const TopkArgs t = make_topk_args(c, L, logit_bias, corr, token_ids, tid2eid, logits_in,
                                     logits_out, ids, w, ws);
-  if (dispatched && fused_topk_dispatch_fits(c.tokens, c.num_experts + c.zero_experts, c.top_k)) {
+  if (!logits_in)
+    MOE_HIP(launch_router_partial(x, router_w, at<double>(ws, L.partial), c.tokens, NE,
+                                  c.hidden, L.ks, L.hsplit, s));
+  if (dispatched && fused_topk_dispatch_fits(c.tokens, NE, c.top_k)) {
     if (marks) MOE_HIP(marks->mark(MOE_STAGE_ROUTED));
     const DispatchArgs d = make_dispatch_args(c, L, ids, t.err_tok, ws);
     MOE_HIP(launch_topk_dispatch(t, d, s));

@@ -23,6 +23,10 @@ __global__ __launch_bounds__(kDispatchThreads) void k_dispatch(DispatchArgs a) {
   __shared__ int s_off[kMaxExperts];
   __shared__ int s_tmp[2 * kDispatchWaves + 1];
   __shared__ int s_err;
+  if (a.T * a.K <= kSmallDispatchSlots) {  // few slots: one wave
+    if (threadIdx.x < kWave) dispatch_small(a, a.ids, a.err_tok, s_wbase[0]);
+    return;
+  }
   dispatch_body<kDispatchWaves, kMaxExperts>(a, a.ids, a.err_tok, s_wbase, s_off, s_tmp, &s_err);
 }
 
@@ -53,6 +57,10 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_topk_dispatch(TopkArgs ta,
   for (int t = wave; t < ta.T; t += kFusedWaves)
     topk_token<NPL>(ta, t, s_logit[wave], s_id[wave], s_w[wave], s_ids, s_errt);
   __syncthreads();
+  if (da.T * da.K <= kSmallDispatchSlots) {  // few slots: one wave
+    if (wave == 0) dispatch_small(da, s_ids, s_errt, s_wbase[0]);
+    return;
+  }
   dispatch_body<kFusedWaves, kFusedMaxExperts>(da, s_ids, s_errt, s_wbase, s_off, s_tmp, &s_err);
 }
 

@@ -259,6 +259,11 @@ SMALL = {
     # K a multiple of 64 but not of 128 at 32-row prefill tiles (64-code stages)
     "oddk_mini": S.LayerSpec(name="oddk_mini", tokens=9, hidden=320, experts=16, top_k=4,
                              inter=192, fmt=S.MXFP4, seed=1078),
+    # few slots (T * k <= 64: the one-wave dispatch) with zero-computation experts
+    "zero_experts_small": S.LayerSpec(name="zero_experts_small", tokens=5, hidden=512,
+                                      experts=48, top_k=8, inter=256, fmt=S.NVFP4,
+                                      score=S.SOFTMAX_BIAS, renormalize=False,
+                                      correction_bias=True, zero_experts=16, seed=1079),
     # FP8 (E4M3, 128 x 128 block scales) and BF16 expert weights, with an NVFP4 or FP8
     # shared expert; shapes not multiples of 128 exercise partial scale blocks
     "fp8_mini": S.LayerSpec(name="fp8_mini", tokens=11, hidden=640, experts=32, top_k=4,
@@ -375,8 +380,9 @@ def test_bad_expert_ids_are_dropped_and_flagged():
     assert_layer_close(out.float().cpu().numpy(), want, None, "bad-ids")
 
 
-def test_hash_layer_bad_token_flags_error():
-    spec = SMALL["hash_mini"]
+@pytest.mark.parametrize("tokens", [77, 6])  # 6 tokens x 6 slots: the one-wave dispatch
+def test_hash_layer_bad_token_flags_error(tokens):
+    spec = S.scaled(SMALL["hash_mini"], tokens=tokens)
     inp = S.make_inputs(spec, device=DEV)
     inp.token_ids[3] = spec.vocab + 5
     out, _, ids, _, ws = run_layer(inp, path=M.PATH_DECODE)

@@ -16,7 +16,8 @@
 // * Both operands reach LDS by direct-to-LDS loads (global_load_lds_*: the activation
 //   rows gathered by row_token, the FP4 weight rows and their scale bytes) into a ring
 //   of three 64-wide K stages. Step c waits for stage c, synchronises the block once,
-//   issues stage c+2 into the slot freed by step c-1, then runs the MFMAs of stage c.
+//   reads stage c's operands from LDS, issues stage c+2 into the slot freed by step c-1,
+//   then runs the MFMAs of stage c.
 //   Loads therefore have two steps to land, and no registers are spent on them.
 // * A block takes at most 80 KB of LDS, so two blocks run on each CU; their barriers
 //   and LDS waits fall at different times, and each fills the other's MFMA gaps.
@@ -399,7 +400,10 @@ void k_pre_gemm(ExpertGemmArgs a) {
   // covering codes (KC/2)h..(KC/2)h+KC/2-1 of the stage (8 per step)
   auto stage_mma = [&](auto nr_c, int c) {
     constexpr int NR = decltype(nr_c)::value;
-    if constexpr (NR == 0) return;
+    if constexpr (NR == 0) {
+      if (c + Sh::LEAD < nch) issue(c + Sh::LEAD);
+      return;
+    }
     const uint8_t* sa = s_dyn + (c % NSTG) * Sh::STAGE;
     const uint8_t* sbq = sa + Sh::A_BYTES;
     const uint8_t* ssc = sbq + Sh::B_BYTES;
@@ -443,6 +447,9 @@ void k_pre_gemm(ExpertGemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);  // keep the reads in the order they are used
       }
     }
+    // the loads of stage c + LEAD go out while this stage's LDS reads are in flight
+    if (c + Sh::LEAD < nch) issue(c + Sh::LEAD);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
       bf16x8_t bo[CB];
@@ -485,7 +492,6 @@ void k_pre_gemm(ExpertGemmArgs a) {
         ss = next <= c + inflight;
       }
       wait_inflight<Sh::NLOADS, NSS>(inflight, ss);
-      if (c + Sh::LEAD < nch) issue(c + Sh::LEAD);
       stage_mma(nr_c, c);
     }
   };

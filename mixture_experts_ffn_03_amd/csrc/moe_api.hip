@@ -23,7 +23,8 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 struct Layout {
-  size_t partial, logits, ids, w, errtok, xn, row_token, inv, tiles, ntiles, h, y, total;
+  size_t partial, logits, ids, w, errtok, xn, row_token, inv, tiles, ntiles, h, y, wcnt,
+      errpart, total;
   int ks, hsplit;
   int rows;        // R
   int h_stride;
@@ -75,6 +76,10 @@ Layout make_layout(const moe_config& c) {
   L.ntiles = take(16);
   L.h = take((size_t)L.rows * L.h_stride * 2);
   L.y = take((size_t)L.rows * H * 4);
+  // multi-block dispatch (many slots): per-wave expert counts and per-block error bits
+  const int dblocks = S >= kDispMultiMinSlots ? dispatch_blocks(S) : 0;
+  L.wcnt = take((size_t)dblocks * E * 4);
+  L.errpart = take((size_t)dblocks * 4);
   L.total = off;
   return L;
 }
@@ -219,6 +224,8 @@ DispatchArgs make_dispatch_args(const moe_config& c, const Layout& L, const int3
   d.zero = c.zero_experts;
   d.shared_rows = c.has_shared ? c.tokens : 0;
   d.tile_h = path == MOE_PATH_PREFILL ? prefill_mt(c) : kDecodeTile;
+  d.wcnt = at<int32_t>(ws, L.wcnt);
+  d.err_part = at<int32_t>(ws, L.errpart);
   return d;
 }
 

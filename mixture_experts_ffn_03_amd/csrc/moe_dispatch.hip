@@ -30,7 +30,117 @@ __global__ __launch_bounds__(kDispatchThreads) void k_dispatch(DispatchArgs a) {
   dispatch_body<kDispatchWaves, kMaxExperts>(a, a.ids, a.err_tok, s_wbase, s_off, s_tmp, &s_err);
 }
 
+// ---------------------------------------------------------------------------
+// Many slots: the same counting sort over blocks of kDispChunk slots (16 waves, one chunk
+// of 64 slots each). Launch 1 counts each block's slots per expert (and ORs the error bits
+// of its slots and of its share of the tokens) into cntb [E, blocks] (expert-major, blocks
+// rounded up to a multiple of 4; the extra blocks count nothing). Launch 2: each block
+// sums the counts of the blocks before it and of all blocks per expert, recounts its own
+// waves' slots for their places inside the block, and scatters; its block 0 writes the
+// tile list, the tile count and the error word.
+// ---------------------------------------------------------------------------
+constexpr int kDispSeg = kDispChunk / kDispatchWaves;  // slots per wave (one chunk)
+static_assert(kDispSeg == kWave, "one chunk of 64 slots per wave");
+
+// per-wave expert counts of this block's slots into s_wc (zeroed here); returns error bits
+__device__ __forceinline__ int count_block_slots(const DispatchArgs& a, int (*s_wc)[kMaxExperts]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, S = a.T * a.K;
+  for (int i = tid; i < kDispatchWaves * E; i += kDispatchThreads) s_wc[i / E][i % E] = 0;
+  __syncthreads();
+  const int s = blockIdx.x * kDispChunk + wave * kDispSeg + lane;
+  const int e = s < S ? a.ids[s] : -1;
+  int err = 0;
+  if (s < S) {
+    if (e >= 0 && e < E) atomicAdd(&s_wc[wave][e], 1);
+    else if (!(a.err_tok && e == -1) && !(e >= E && e < E + a.zero)) err |= 1;
+  }
+  __syncthreads();
+  return err;
+}
+
+__global__ __launch_bounds__(kDispatchThreads) void k_dispatch_count(DispatchArgs a) {
+  __shared__ int s_wc[kDispatchWaves][kMaxExperts];
+  __shared__ int s_err;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_err = 0;
+  int err = count_block_slots(a, s_wc);
+  if (a.err_tok) {  // this block's share of the tokens
+    const int tpb = (a.T + gridDim.x - 1) / gridDim.x;
+    const int t1 = min(a.T, (int)(blockIdx.x + 1) * tpb);
+    for (int t = blockIdx.x * tpb + tid; t < t1; t += kDispatchThreads) err |= a.err_tok[t];
+  }
+  if (err) atomicOr(&s_err, err);
+  if (tid < a.E) {
+    int c = 0;
+    for (int w = 0; w < kDispatchWaves; ++w) c += s_wc[w][tid];
+    a.wcnt[(size_t)tid * gridDim.x + blockIdx.x] = c;
+  }
+  __syncthreads();
+  if (tid == 0) a.err_part[blockIdx.x] = s_err;
+}
+
+__global__ __launch_bounds__(kDispatchThreads) void k_dispatch_scatter(DispatchArgs a) {
+  __shared__ int s_wc[kDispatchWaves][kMaxExperts];
+  __shared__ int s_off[kMaxExperts];
+  __shared__ int s_tmp[2 * kDispatchWaves + 1];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int E = a.E, S = a.T * a.K;
+  const int nb = gridDim.x;  // a multiple of 4
+  // per expert: rows of the blocks before this one, and the group size
+  int cnt = 0, before = 0;
+  if (tid < E) {
+    const uint4* row = reinterpret_cast<const uint4*>(a.wcnt + (size_t)tid * nb);
+    for (int b = 0; b < nb; b += 32) {
+      uint4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = b + 4 * j < nb ? row[b / 4 + j] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c4[4] = {(int)v[j].x, (int)v[j].y, (int)v[j].z, (int)v[j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (b + 4 * j + q == (int)blockIdx.x) before = cnt;
+          cnt += c4[q];
+        }
+      }
+    }
+  }
+  int total = 0;
+  const int off = block_exclusive_scan<kDispatchWaves>(cnt, s_tmp, &total);
+  count_block_slots(a, s_wc);  // (synchronises the block)
+  if (tid < E) {
+    s_off[tid] = a.shared_rows + off;
+    int run = before;  // this block's waves, in order
+    for (int w = 0; w < kDispatchWaves; ++w) {
+      const int c = s_wc[w][tid];
+      s_wc[w][tid] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  const int sb = blockIdx.x * kDispChunk + wave * kDispSeg, se = min(S, sb + kDispSeg);
+  scatter_segment(a, a.ids, sb, se, s_wc[wave], s_off);
+  if (blockIdx.x != 0) return;
+  for (int p = tid; p < a.shared_rows; p += kDispatchThreads) a.row_token[p] = p;
+  int ntot = 0;
+  write_tiles<kDispatchWaves>(a, cnt, s_off, s_tmp, &ntot);  // prefill tiles: no tokens read
+  if (tid == 0) {
+    int err = 0;
+    for (int b = 0; b < nb; ++b) err |= a.err_part[b];
+    a.ntiles[0] = ntot;
+    a.err_word[0] = err;
+  }
+}
+
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
+  const int S = a.T * a.K;
+  if (dispatch_multi_block(S, a.tile_h)) {
+    const int blocks = dispatch_blocks(S);
+    hipLaunchKernelGGL(k_dispatch_count, dim3(blocks), dim3(kDispatchThreads), 0, s, a);
+    hipLaunchKernelGGL(k_dispatch_scatter, dim3(blocks), dim3(kDispatchThreads), 0, s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_dispatch, dim3(1), dim3(kDispatchThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -89,8 +89,19 @@ struct DispatchArgs {
   int32_t* err_word;
   int T, K, E, shared_rows, tile_h;
   int zero;               // ids in [E, E + zero): zero-computation experts (inv = -2)
+  int32_t* wcnt;          // multi-block dispatch: [E, blocks] slot counts
+  int32_t* err_part;      // multi-block dispatch: [blocks] error bits
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+// Many slots with prefill tiles: the dispatch runs as two multi-block launches (per-wave
+// expert counts, then scatter) over chunks of kDispChunk slots.
+constexpr int kDispChunk = 1024;  // slots per block (16 waves x 64)
+constexpr int kDispMultiMinSlots = 8192;
+inline bool dispatch_multi_block(int S, int tile_h) {
+  return S >= kDispMultiMinSlots && tile_h > kTileTok;
+}
+// blocks of the multi-block dispatch, a multiple of 4 (16-byte count rows)
+inline int dispatch_blocks(int S) { return ((S + kDispChunk - 1) / kDispChunk + 3) / 4 * 4; }
 
 // Top-K and dispatch fused in one block (few tokens: decode).
 constexpr int kFusedMaxTokens = 16;  // one block: beyond this, separate kernels are faster

@@ -321,6 +321,77 @@ __device__ void dispatch_small(const DispatchArgs& a, const int32_t* ids, const 
 // chunks of 64 slots whose ids one wave loads at once
 constexpr int kDispatchBatch = 8;
 
+// Stable scatter of slots [sb, se) by one wave: row_token and inv of every slot; s_wbase_w
+// (per expert) holds the wave's next row inside each expert group, s_off the groups' first
+// rows. Lanes with equal ids are ranked by lane order within each chunk of 64 slots.
+__device__ __forceinline__ void scatter_segment(const DispatchArgs& a, const int32_t* ids, int sb,
+                                                int se, int* s_wbase_w, const int* s_off) {
+  const int lane = threadIdx.x & 63;
+  const int E = a.E, K = a.K;
+  for (int c0 = sb; c0 < se; c0 += kDispatchBatch * kWave) {
+    int ev[kDispatchBatch];
+#pragma unroll
+    for (int j = 0; j < kDispatchBatch; ++j) {
+      const int s = c0 + j * kWave + lane;
+      ev[j] = s < se ? ids[s] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kDispatchBatch; ++j) {
+      if (c0 + j * kWave >= se) break;  // past the segment (wave-uniform)
+      const int s = c0 + j * kWave + lane;
+      const bool in = s < se;
+      const int e = ev[j];
+      const bool valid = in && e >= 0 && e < E;
+      uint64_t m = __ballot(valid);
+      for (int b = 0; (1 << b) < E; ++b) {
+        const bool bit = valid && ((e >> b) & 1);
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+      }
+      if (valid) {
+        const uint64_t below = lane ? (m & ((~0ull) >> (64 - lane))) : 0ull;
+        const int rank = __popcll(below);
+        const int cntm = __popcll(m);
+        const int base = s_wbase_w[e];
+        const int pos = s_off[e] + base + rank;
+        a.row_token[pos] = s / K;
+        a.inv[s] = pos;
+        if (rank == cntm - 1) s_wbase_w[e] = base + cntm;
+      } else if (in) {
+        a.inv[s] = (e >= E && e < E + a.zero) ? -2 : -1;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
+// Tile list of a block of NW waves: thread e < E holds its expert's row count `cnt`, s_off
+// the group's first row; ceil(cnt / tile_h) runs per expert, experts in order. Tiles of at
+// most kTileTok rows also carry their rows' tokens (row_token must be complete and visible).
+template <int NW>
+__device__ __forceinline__ void write_tiles(const DispatchArgs& a, int cnt, const int* s_off,
+                                            int* s_tmp, int* ntot) {
+  const int tid = threadIdx.x;
+  const int h = a.tile_h;
+  const int nt = (tid < a.E) ? (cnt + h - 1) / h : 0;
+  const int toff = block_exclusive_scan<NW>(nt, s_tmp, ntot);
+  __syncthreads();  // row_token of every routed row is written (read back below)
+  if (tid < a.E) {
+    for (int i = 0; i < nt; ++i) {
+      Tile tl;
+      tl.group = tid;
+      tl.row0 = s_off[tid] + i * h;
+      tl.count = min(h, cnt - i * h);
+      tl.pad = 0;
+#pragma unroll
+      for (int q = 0; q < kTileTok; ++q)
+        tl.tok[q] = (h <= kTileTok && q < tl.count) ? a.row_token[tl.row0 + q] : 0;
+      a.tiles[toff + i] = tl;
+    }
+  }
+}
+
 template <int NW, int EMAX>
 __device__ void dispatch_body(const DispatchArgs& a, const int32_t* ids, const int32_t* err_tok,
                               int (*s_wbase)[EMAX], int* s_off, int* s_tmp, int* s_err) {
@@ -379,62 +450,11 @@ __device__ void dispatch_body(const DispatchArgs& a, const int32_t* ids, const i
   __syncthreads();
 
   // stable scatter: lanes with equal ids are ranked by lane order within each chunk
-  for (int c0 = sb; c0 < se; c0 += kDispatchBatch * kWave) {
-    int ev[kDispatchBatch];
-#pragma unroll
-    for (int j = 0; j < kDispatchBatch; ++j) {
-      const int s = c0 + j * kWave + lane;
-      ev[j] = s < se ? ids[s] : -1;
-    }
-#pragma unroll
-    for (int j = 0; j < kDispatchBatch; ++j) {
-      if (c0 + j * kWave >= se) break;  // past the segment (wave-uniform)
-      const int s = c0 + j * kWave + lane;
-      const bool in = s < se;
-      const int e = ev[j];
-      const bool valid = in && e >= 0 && e < E;
-      uint64_t m = __ballot(valid);
-      for (int b = 0; (1 << b) < E; ++b) {
-        const bool bit = valid && ((e >> b) & 1);
-        const uint64_t bb = __ballot(bit);
-        m &= bit ? bb : ~bb;
-      }
-      if (valid) {
-        const uint64_t below = lane ? (m & ((~0ull) >> (64 - lane))) : 0ull;
-        const int rank = __popcll(below);
-        const int cntm = __popcll(m);
-        const int base = s_wbase[wave][e];
-        const int pos = s_off[e] + base + rank;
-        a.row_token[pos] = s / K;
-        a.inv[s] = pos;
-        if (rank == cntm - 1) s_wbase[wave][e] = base + cntm;
-      } else if (in) {
-        a.inv[s] = (e >= E && e < E + a.zero) ? -2 : -1;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-    }
-  }
+  scatter_segment(a, ids, sb, se, s_wbase[wave], s_off);
 
   // tile list: ceil(cnt / tile_h) runs per expert, experts in order
-  const int h = a.tile_h;
-  const int nt = (tid < E) ? (cnt + h - 1) / h : 0;
   int ntot = 0;
-  const int toff = block_exclusive_scan<NW>(nt, s_tmp, &ntot);
-  __syncthreads();  // row_token of every routed row is written (read back below)
-  if (tid < E) {
-    for (int i = 0; i < nt; ++i) {
-      Tile tl;
-      tl.group = tid;
-      tl.row0 = s_off[tid] + i * h;
-      tl.count = min(h, cnt - i * h);
-      tl.pad = 0;
-#pragma unroll
-      for (int q = 0; q < kTileTok; ++q)
-        tl.tok[q] = (h <= kTileTok && q < tl.count) ? a.row_token[tl.row0 + q] : 0;
-      a.tiles[toff + i] = tl;
-    }
-  }
+  write_tiles<NW>(a, cnt, s_off, s_tmp, &ntot);
   if (tid == 0) {
     a.ntiles[0] = ntot;
     a.err_word[0] = *s_err;

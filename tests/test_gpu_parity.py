@@ -259,6 +259,9 @@ SMALL = {
     # K a multiple of 64 but not of 128 at 32-row prefill tiles (64-code stages)
     "oddk_mini": S.LayerSpec(name="oddk_mini", tokens=9, hidden=320, experts=16, top_k=4,
                              inter=192, fmt=S.MXFP4, seed=1078),
+    # many slots (T * k >= 8192: the two-launch multi-block dispatch) with Zipf-skewed loads
+    "many_slots_mini": S.scaled(S.WORKLOADS["prefill_zipf_t4096"], tokens=1500, hidden=256,
+                                experts=16, inter=128),
     # few slots (T * k <= 64: the one-wave dispatch) with zero-computation experts
     "zero_experts_small": S.LayerSpec(name="zero_experts_small", tokens=5, hidden=512,
                                       experts=48, top_k=8, inter=256, fmt=S.NVFP4,
@@ -378,6 +381,30 @@ def test_bad_expert_ids_are_dropped_and_flagged():
     want = O.experts_forward(f32(inp.x), oids, w.cpu().numpy().astype(np.float64),
                              oracle_cache(inp.routed), f32(inp.residual))
     assert_layer_close(out.float().cpu().numpy(), want, None, "bad-ids")
+
+
+def test_bad_expert_ids_many_slots():
+    """Out-of-range ids among 9000 slots (multi-block dispatch): dropped, flagged, and the
+    other slots still match the oracle."""
+    spec = S.scaled(S.WORKLOADS["prefill_zipf_t4096"], tokens=1500, hidden=256, experts=16,
+                    inter=128)
+    inp = S.make_inputs(spec, device=DEV)
+    rng = np.random.default_rng(11)
+    T, k, E = spec.tokens, spec.top_k, spec.experts
+    oids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    oids[7, 2] = E + 3
+    oids[1400, 0] = -5
+    ow = rng.uniform(0.1, 1.0, size=(T, k)).astype(np.float32)
+    cfg = config_for(inp, M.PATH_PREFILL)
+    ws = M.alloc_workspace(cfg, DEV)
+    out = torch.empty_like(inp.x)
+    M.experts_forward(cfg, inp.x, torch.from_numpy(oids).to(DEV), torch.from_numpy(ow).to(DEV),
+                      M.expert_weights(inp.routed), None, inp.residual, out, ws)
+    assert M.get_device_error(ws) & M.DEVERR_EXPERT_ID
+    dropped = np.where((oids >= 0) & (oids < E), oids, -1)
+    want = O.experts_forward(f32(inp.x), dropped, ow.astype(np.float64),
+                             oracle_cache(inp.routed), f32(inp.residual))
+    assert_layer_close(out.float().cpu().numpy(), want, None, "bad-ids-many")
 
 
 @pytest.mark.parametrize("tokens", [77, 6])  # 6 tokens x 6 slots: the one-wave dispatch

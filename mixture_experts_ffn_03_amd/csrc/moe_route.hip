@@ -94,13 +94,29 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
   f64x4_t acc[MF];
 #pragma unroll
   for (int m = 0; m < MF; ++m) acc[m] = f64x4_t{0.0, 0.0, 0.0, 0.0};
-  for (int k0 = kb + 32 * wave; k0 < ke; k0 += 128) {
+  // the operands of the wave's next 32-wide chunk are loaded while the current chunk's
+  // MFMAs run
+  const int kstart = kb + 32 * wave;
+  uint4 wv = make_uint4(0, 0, 0, 0), xv[MF];
+#pragma unroll
+  for (int m = 0; m < MF; ++m) xv[m] = make_uint4(0, 0, 0, 0);
+  // (unconditional loads: rows past T read row 0 and are zeroed after the load; the last
+  // prefetch re-reads the current chunk)
+  auto load = [&](int k0, uint4& w_, uint4 (&x_)[MF]) {
+    w_ = *reinterpret_cast<const uint4*>(wrow + k0);
+#pragma unroll
+    for (int m = 0; m < MF; ++m) x_[m] = *reinterpret_cast<const uint4*>(xrow[m] + k0);
+  };
+  if (kstart < ke) load(kstart, wv, xv);
+  for (int k0 = kstart; k0 < ke; k0 += 128) {
+    uint4 wn, xn[MF];
+    load(k0 + 128 < ke ? k0 + 128 : k0, wn, xn);
     double wd[8];
-    bf16x8_to_f64(*reinterpret_cast<const uint4*>(wrow + k0), wd);
+    bf16x8_to_f64(wv, wd);
     double xd[MF][8];
 #pragma unroll
     for (int m = 0; m < MF; ++m) {
-      const uint4 v = tv[m] ? *reinterpret_cast<const uint4*>(xrow[m] + k0) : make_uint4(0, 0, 0, 0);
+      const uint4 v = tv[m] ? xv[m] : make_uint4(0, 0, 0, 0);
       bf16x8_to_f64(v, xd[m]);
     }
 #pragma unroll
@@ -108,6 +124,9 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
 #pragma unroll
       for (int m = 0; m < MF; ++m)
         acc[m] = __builtin_amdgcn_mfma_f64_16x16x4f64(xd[m][st], wd[st], acc[m], 0, 0, 0);
+    wv = wn;
+#pragma unroll
+    for (int m = 0; m < MF; ++m) xv[m] = xn[m];
   }
   if (wave > 0) {
 #pragma unroll

@@ -260,6 +260,7 @@ int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const 
   a.T = c.tokens;
   a.H = c.hidden;
   a.I = c.inter;
+  a.rows = L.rows;
   if (pre) {
     MOE_HIP(launch_prefill_gate_up(a, mt, s));
     MOE_HIP(marks.mark(MOE_STAGE_GATE_UP));

@@ -31,9 +31,11 @@ constexpr int kDecWaves = 4;
 __device__ __forceinline__ bool resolve_tile(const TileSource& src, const int32_t* row_token,
                                              int idx, Tile& t) {
   if (src.tiles) {
-    if (idx >= src.ntiles[0]) return false;
+    // both loads at once: idx is below the list's capacity (the grid's tile bound), so the
+    // entry is readable even past the count
+    const int n = src.ntiles[0];
     t = src.tiles[idx];
-    return true;
+    return idx < n;
   }
   const int r0 = idx * src.implicit_height;
   if (r0 >= src.implicit_rows) return false;
@@ -525,11 +527,162 @@ static void launch_dn(const ExpertGemmArgs& a, int rpw, hipStream_t s) {
     default: LAUNCH<FMT, 8>(A, RPW, S); break;            \
   }
 
+// ----------------------------------------------------------------------------- one step
+// Rows of at most 64 chunks (K <= 2048 FP4 codes): a lane owns one 16-byte chunk of each
+// of its rows (a group of LPR >= K / CPC lanes covers a row), so a wave loads all its
+// weights at once and there is nothing to pipeline. The tile's tokens are then taken one
+// after the other against the weights held in registers, their sums kept in registers
+// and stored after the token loop; register use does not grow with the tile's tokens
+// and stays within 128 VGPRs, so four waves share each SIMD.
+template <int LPR, int M>
+struct OneShape {
+  static constexpr int G = kWave / LPR;                 // row groups per wave
+  static constexpr int NI = (LPR < 8 ? LPR : 8) / M;    // rows per lane and matrix
+  static constexpr int GR = G * NI;                     // rows per wave
+  static constexpr int NV = NI * M;                     // sums per lane before the reduction
+  static_assert(NV <= LPR, "one reduced value per lane expected");
+};
+
+template <int FMT, int LPR, int M>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_one(ExpertGemmArgs a) {
+  using SH = OneShape<LPR, M>;
+  constexpr int G = SH::G, NI = SH::NI, GR = SH::GR, NV = SH::NV;
+  constexpr int XW = DecFmt<FMT>::XW, CPC = DecFmt<FMT>::CPC;
+  Tile tile;
+  if (!resolve_tile(a.src, a.row_token, blockIdx.y, tile)) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int sub = lane % LPR, grp = lane / LPR;
+  const int N = M == 2 ? a.I : a.H;  // output rows of each matrix
+  const int K = M == 2 ? a.H : a.I;  // reduction length
+  const int nbase = (blockIdx.x * kDecWaves + wave) * GR;
+  if (nbase >= N) return;  // whole wave
+  const int nchunk = K / CPC;
+  const bool live = sub < nchunk;
+  const int c = live ? sub : nchunk - 1;
+  const size_t row_bytes = dec_row_bytes<FMT>(K);
+  const int sstride = dec_scale_stride<FMT>(K);
+  const size_t sexp = dec_scale_expert_bytes<FMT>(N, K);
+  const WeightDesc& w0 = M == 2 ? a.gate : a.down;
+  const int e = tile.group;
+
+  // every weight of the wave at once (rows clamped; results past N are not stored)
+  uint4 w[NI][M];
+  uint32_t sc[NI][M];
+  const size_t eoff = (size_t)e * N * row_bytes;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int n = min(nbase + grp + G * i, N - 1);
+    w[i][0] = *reinterpret_cast<const uint4*>(w0.packed + eoff + (size_t)n * row_bytes + c * 16);
+    sc[i][0] = load_chunk_scales<FMT>(w0.scales + e * sexp, n, sstride, c);
+    if (M == 2) {
+      w[i][M - 1] = *reinterpret_cast<const uint4*>(a.up.packed + eoff + (size_t)n * row_bytes + c * 16);
+      sc[i][M - 1] = load_chunk_scales<FMT>(a.up.scales + e * sexp, n, sstride, c);
+    }
+  }
+  const float gs0 = FMT == 0 ? w0.global[e] : 1.0f;
+  const float gs1 = M == 2 && FMT == 0 ? a.up.global[e] : 1.0f;
+  const uint16_t* src = M == 2 ? a.x : a.h;
+  const size_t stride = M == 2 ? (size_t)a.H : (size_t)a.h_stride;
+
+  constexpr int kDiv = LPR / NV;  // lanes holding copies of one sum
+  float res[kTileTok];
+#pragma unroll
+  for (int q = 0; q < kTileTok; ++q) res[q] = 0.f;
+  int idx = 0;
+  for (int t = 0; t < tile.count; ++t) {
+    int tok = tile.tok[0];
+#pragma unroll
+    for (int q = 1; q < kTileTok; ++q) tok = t == q ? tile.tok[q] : tok;
+    const int rows[1] = {M == 2 ? tok : tile.row0 + t};
+    uint32_t xv[1][XW];
+    global_act_chunk<1, XW>(src, stride, rows, c, xv);
+    if (!live) {  // lanes past the row's chunks add nothing
+#pragma unroll
+      for (int q = 0; q < XW; ++q) xv[0][q] = 0u;
+    }
+    float acc[NV];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        // an opaque copy per token: decoding the weights once, outside the token loop,
+        // would not fit the register budget
+        uint4 wv = w[i][m];
+        uint32_t sv = sc[i][m];
+        asm volatile("" : "+v"(wv.x), "+v"(wv.y), "+v"(wv.z), "+v"(wv.w), "+v"(sv));
+        float r[1] = {0.f};
+        chunk_dot<FMT, 1>(wv, sv, xv, r);
+        acc[i * M + m] = r[0];
+      }
+    group_reduce_transpose<NV, LPR>(acc, lane);
+    idx = reduced_index<NV, LPR>(lane, 0);
+    float v;
+    if (M == 2) {  // gate / up partners differ in lane bit kDiv
+      const float other = shfl_xor_f(acc[0], kDiv);
+      v = silu(acc[0] * gs0) * (other * gs1);
+    } else {
+      v = acc[0] * gs0;
+    }
+#pragma unroll
+    for (int q = 0; q < kTileTok; ++q) res[q] = t == q ? v : res[q];
+  }
+  // (stores after the loop: a loop that stores and reads registers loaded before it makes
+  // the compiler wait for every load in flight before entering it)
+  const bool owner = M == 2 ? ((idx & 1) == 0 && (sub & (kDiv - 1)) == 0) : (sub & (kDiv - 1)) == 0;
+  const int n = nbase + grp + G * (M == 2 ? idx >> 1 : idx);
+  if (owner && n < N) {
+#pragma unroll
+    for (int q = 0; q < kTileTok; ++q) {
+      if (q < tile.count) {
+        if (M == 2) a.h[(size_t)(tile.row0 + q) * a.h_stride + n] = f32_to_bf16(res[q]);
+        else reinterpret_cast<float*>(a.y)[(size_t)(tile.row0 + q) * N + n] = res[q];
+      }
+    }
+  }
+}
+
+// Host side: FP4 weights, rows of at most 64 chunks, tiles of at most kTileTok rows.
+static int one_lanes(int nchunk) {
+  int l = 8;
+  while (l < nchunk) l <<= 1;
+  return l;
+}
+
+static bool one_fits(int fmt, int K, int tile_h) {
+  return fmt <= 1 && K / 32 <= 64 && tile_h <= kTileTok;
+}
+
+template <int FMT, int LPR, int M>
+static hipError_t launch_one_t(const ExpertGemmArgs& a, hipStream_t s) {
+  const int N = M == 2 ? a.I : a.H;
+  const int rows = kDecWaves * OneShape<LPR, M>::GR;
+  hipLaunchKernelGGL((k_dec_one<FMT, LPR, M>), dim3((N + rows - 1) / rows, a.tile_bound), dim3(256), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
+template <int M>
+static hipError_t launch_one(const ExpertGemmArgs& a, int fmt, int K, hipStream_t s) {
+  const int lpr = one_lanes(K / 32);
+#define MOE_ONE_LPR(FMT)                                    \
+  switch (lpr) {                                            \
+    case 8: return launch_one_t<FMT, 8, M>(a, s);           \
+    case 16: return launch_one_t<FMT, 16, M>(a, s);         \
+    case 32: return launch_one_t<FMT, 32, M>(a, s);         \
+    default: return launch_one_t<FMT, 64, M>(a, s);         \
+  }
+  if (fmt == 0) { MOE_ONE_LPR(0) }
+  MOE_ONE_LPR(1)
+#undef MOE_ONE_LPR
+}
+
 // codes per 16-byte chunk of a format (host side of DecFmt)
 static int codes_per_chunk(int fmt) { return fmt <= 1 ? 32 : (fmt == 2 ? 16 : 8); }
 
 hipError_t launch_decode_gate_up(const ExpertGemmArgs& a, hipStream_t s) {
   if (a.tile_bound <= 0) return hipSuccess;
+  if (one_fits(a.gate.fmt, a.H, a.src.tiles ? kDecodeTile : a.src.implicit_height))
+    return launch_one<2>(a, a.gate.fmt, a.H, s);
   const int rpw = pick_rows_per_wave(kGateRowsPerPass, a.I, a.tile_bound);
   const int lpr = pick_lpr(a.H / codes_per_chunk(a.gate.fmt));
   switch (a.gate.fmt) {
@@ -543,6 +696,8 @@ hipError_t launch_decode_gate_up(const ExpertGemmArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_down(const ExpertGemmArgs& a, hipStream_t s) {
   if (a.tile_bound <= 0) return hipSuccess;
+  if (one_fits(a.down.fmt, a.I, a.src.tiles ? kDecodeTile : a.src.implicit_height))
+    return launch_one<1>(a, a.down.fmt, a.I, s);
   const int rpw = pick_rows_per_wave(kDownRowsPerPass, a.H, a.tile_bound);
   const int lpr = pick_lpr(a.I / codes_per_chunk(a.down.fmt));
   switch (a.down.fmt) {

@@ -148,30 +148,38 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Top-K and dispatch in one block, for few tokens and experts: the block's waves select
 // the experts of the tokens (topk_token, ids kept in LDS), then sort the slots by expert
-// (dispatch_body). Saves a launch and a round trip of the ids through memory.
+// (dispatch_small for a handful of slots, else dispatch_bitmap). Saves a launch and a
+// round trip of the ids through memory.
 // ---------------------------------------------------------------------------
 constexpr int kFusedWaves = 16;
+static_assert(kFusedMaxSlots <= kFusedWaves * 64, "one thread per slot");
 
 template <int NPL>
 __global__ __launch_bounds__(kFusedWaves * 64) void k_topk_dispatch(TopkArgs ta, DispatchArgs da) {
-  __shared__ float s_logit[kFusedWaves][kFusedMaxExperts];
-  __shared__ int s_id[kFusedWaves][kMaxTopK];
-  __shared__ float s_w[kFusedWaves][kMaxTopK];
+  constexpr int kWords = kFusedMaxSlots / 64;
+  __shared__ uint64_t s_mask[kFusedMaxExperts * kWords];
   __shared__ int32_t s_ids[kFusedMaxSlots];
   __shared__ int32_t s_errt[kFusedMaxTokens];
-  __shared__ int s_wbase[kFusedWaves][kFusedMaxExperts];
   __shared__ int s_off[kFusedMaxExperts];
-  __shared__ int s_tmp[2 * kFusedWaves + 1];
+  __shared__ int s_toff[kFusedMaxExperts];
+  __shared__ int s_tot[kFusedWaves];
   __shared__ int s_err;
   const int wave = threadIdx.x >> 6;
-  for (int t = wave; t < ta.T; t += kFusedWaves)
-    topk_token<NPL>(ta, t, s_logit[wave], s_id[wave], s_w[wave], s_ids, s_errt);
+  const int S = da.T * da.K;
+  const bool small = S <= kSmallDispatchSlots;
+  if (!small) {  // clear the bitmaps while the waves select
+    const int nw = da.E * ((S + 63) / 64);
+    for (int i = threadIdx.x; i < nw; i += kFusedWaves * 64) s_mask[i] = 0ull;
+    if (threadIdx.x == 0) s_err = 0;
+  }
+  for (int t = wave; t < ta.T; t += kFusedWaves) topk_token<NPL>(ta, t, s_ids, s_errt);
   __syncthreads();
-  if (da.T * da.K <= kSmallDispatchSlots) {  // few slots: one wave
-    if (wave == 0) dispatch_small(da, s_ids, s_errt, s_wbase[0]);
+  if (small) {  // few slots: one wave
+    if (wave == 0) dispatch_small(da, s_ids, s_errt, s_off);
     return;
   }
-  dispatch_body<kFusedWaves, kFusedMaxExperts>(da, s_ids, s_errt, s_wbase, s_off, s_tmp, &s_err);
+  dispatch_bitmap<kFusedWaves, kFusedMaxExperts>(da, s_ids, s_errt, s_mask, s_off, s_toff, s_tot,
+                                                &s_err);
 }
 
 bool fused_topk_dispatch_fits(int T, int E, int K) {

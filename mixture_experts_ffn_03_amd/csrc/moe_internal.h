@@ -124,6 +124,7 @@ struct ExpertGemmArgs {
   int h_stride;
   void* y;                    // [R, H]: fp32 (decode) or bf16 (prefill)
   int T, H, I;
+  int rows;                   // R: rows of the row space (h and y)
 };
 hipError_t launch_decode_gate_up(const ExpertGemmArgs& a, hipStream_t s);
 hipError_t launch_decode_down(const ExpertGemmArgs& a, hipStream_t s);

@@ -178,13 +178,10 @@ constexpr int kTopkWaves = 4;
 
 template <int NPL>
 __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
-  __shared__ float s_logit[kTopkWaves][kMaxExperts];
-  __shared__ int s_id[kTopkWaves][kMaxTopK];
-  __shared__ float s_w[kTopkWaves][kMaxTopK];
   const int wave = threadIdx.x >> 6;
   const int t = blockIdx.x * kTopkWaves + wave;
   if (t >= a.T) return;  // whole wavefronts exit together
-  topk_token<NPL>(a, t, s_logit[wave], s_id[wave], s_w[wave], nullptr, nullptr);
+  topk_token<NPL>(a, t, nullptr, nullptr);
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {

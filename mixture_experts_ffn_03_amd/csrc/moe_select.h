@@ -11,45 +11,60 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Selection keys: a 64-bit composite (order-preserving key bits << 32 | ~index), so the
-// largest composite is the largest key, equal keys go to the lower expert index, -0 ==
-// +0, and NaN ranks below -inf. 0 is below every real composite (padding).
+// Selection keys: an order-preserving map of the fp32 key to uint32, so the largest
+// value is the largest key, -0 == +0, and NaN (1) ranks below -inf (0x007FFFFF). 0 marks
+// padding and experts already taken. Equal keys go to the lower expert index.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t ordered_key(float f) {
-  if (f != f) return 0u;         // NaN: below everything
+  if (f != f) return 1u;         // NaN: below every number
   uint32_t u = __float_as_uint(f);
   if (u == 0x80000000u) u = 0u;  // -0 == +0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t composite(float key, int idx) {
-  return ((uint64_t)ordered_key(key) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
-}
-
+// Wave-wide reductions by DPP inside each row of 16 lanes (quad swaps, then the half-row
+// and row mirrors), then the four rows' values read out and combined in row order. At
+// every step both lanes of a pair combine the same two values, so all lanes end with the
+// same result.
 template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
-  return ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x141>(v));  // row_half_mirror
+  v = max(v, dpp_u32<0x140>(v));  // row_mirror
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
 
-// Wave-wide maximum (result in every lane): DPP swaps inside each row of 16 lanes (quad
-// swaps, then the half-row and row mirrors), then the four row results are read out.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = max_u64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = max_u64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = max_u64(v, dpp_u64<0x141>(v));  // row_half_mirror
-  v = max_u64(v, dpp_u64<0x140>(v));  // row_mirror
-  uint64_t r[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * i);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * i);
-    r[i] = ((uint64_t)hi << 32) | lo;
-  }
-  return max_u64(max_u64(r[0], r[1]), max_u64(r[2], r[3]));
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)),
+               fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
 }
 
 // Per-expert score of the sigmoid (1) and sqrt-softplus (2) modes, in fp64: rounded once
@@ -65,13 +80,13 @@ __device__ __forceinline__ double score_f64(int score, float logit) {
 
 // ---------------------------------------------------------------------------
 // Scores + top-K of token t by one wavefront, its E keys spread over the 64 lanes (NPL
-// per lane). Selection is k rounds of a wave-wide arg-max on the composite. s_logit
-// (>= E floats), s_id and s_w (>= K) are this wave's LDS scratch. Writes ids / w (and
-// logits_out, err_tok) to global memory; lds_ids (if not null) also receives ids[t*K..].
+// per lane). Selection is k rounds of a wave-wide maximum of the ordered keys, ties to the
+// lowest expert index by ballot. Writes ids / w (and logits_out, err_tok) to global
+// memory; lds_ids / lds_err (if not null) also receive ids[t*K..] and the token's error.
 // ---------------------------------------------------------------------------
 template <int NPL>
-__device__ __forceinline__ void topk_token(const TopkArgs& a, int t, float* s_logit, int* s_id,
-                                           float* s_w, int32_t* lds_ids, int32_t* lds_err) {
+__device__ __forceinline__ void topk_token(const TopkArgs& a, int t, int32_t* lds_ids,
+                                           int32_t* lds_err) {
   const int lane = threadIdx.x & 63;
   const int E = a.E, K = a.K;
 
@@ -117,7 +132,6 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, int t, float* s_lo
     const int e = lane + kWave * i;
     if (e < E) {
       if (a.logits_out) a.logits_out[(size_t)t * E + e] = lg[i];
-      s_logit[e] = lg[i];
     } else {
       lg[i] = -__builtin_inff();  // padding: never selectable, no softmax mass
     }
@@ -136,13 +150,13 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, int t, float* s_lo
   if (a.score == 0 || a.score == 3) {
 #pragma unroll
     for (int i = 0; i < NPL; ++i) m = fmaxf(m, lg[i]);
-    m = wave_max(m);
+    m = wave_max_dpp(m);
   }
   if (a.score == 0) {
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
       if (lane + kWave * i < E) S += expf(lg[i] - m);
-    S = wave_sum(S);
+    S = wave_sum_dpp(S);
   } else if (a.score == 3) {
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
@@ -159,20 +173,23 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, int t, float* s_lo
   int err = 0;
   int my_id = -1;  // lane j < K: the expert of slot j
   if (a.select == 0) {
-    uint64_t comp[NPL];
+    uint32_t kv[NPL];  // ordered keys; 0 = padding or taken
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) comp[i] = lane + kWave * i < E ? composite(key[i], lane + kWave * i) : 0ull;
+    for (int i = 0; i < NPL; ++i) kv[i] = lane + kWave * i < E ? ordered_key(key[i]) : 0u;
     for (int j = 0; j < K; ++j) {
-      uint64_t best = 0;
+      uint32_t best = kv[0];
 #pragma unroll
-      for (int i = 0; i < NPL; ++i) best = max_u64(best, comp[i]);
-      const uint64_t g = wave_max_u64(best);
-      const int idx = (int)(0xFFFFFFFFu - (uint32_t)g);
-      if ((idx & 63) == lane) {
+      for (int i = 1; i < NPL; ++i) best = max(best, kv[i]);
+      const uint32_t g = wave_max_u32(best);
+      int idx = -1;  // lowest expert index holding the maximum (wave-uniform)
 #pragma unroll
-        for (int i = 0; i < NPL; ++i)
-          if (i == (idx >> 6)) comp[i] = 0;  // taken
+      for (int i = 0; i < NPL; ++i) {
+        const uint64_t mk = __ballot(kv[i] == g);
+        if (idx < 0 && mk) idx = kWave * i + __builtin_ctzll(mk);
       }
+#pragma unroll
+      for (int i = 0; i < NPL; ++i)
+        if (i == (idx >> 6) && lane == (idx & 63)) kv[i] = 0u;  // taken
       if (lane == j) my_id = idx;
     }
   } else {  // hash routing: ids from the static table, no selection
@@ -186,21 +203,27 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, int t, float* s_lo
     }
     err = __builtin_amdgcn_readfirstlane(err) | (int)(__ballot(err & 4) ? 4 : 0);
   }
-  (void)s_id;
-  (void)s_w;
-  __builtin_amdgcn_wave_barrier();  // s_logit written by every lane above
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+
+  // the selected experts' logits, fetched from their lanes (every lane takes part)
+  float l = 0.f;
+  {
+    const int src = my_id >= 0 ? my_id : 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const float c = __shfl(lg[i], src & 63, kWave);
+      if (i == (src >> 6)) l = c;
+    }
+  }
 
   // weights of the selected experts, one slot per lane, then the (optional) normalisation
   float wj = 0.f;
   if (lane < K && my_id >= 0) {
-    const float l = s_logit[my_id];
     wj = a.score == 0   ? expf(l - m) / S
          : a.score == 3 ? (float)(exp((double)l - (double)m) / S64)
                         : (float)score_f64(a.score, l);
   }
   if (a.renorm) {
-    const float sum = wave_sum(wj);
+    const float sum = wave_sum_dpp(wj);
     wj = sum > 0.f ? wj / sum : 0.f;
   }
   if (lane < K) {
@@ -315,6 +338,90 @@ __device__ void dispatch_small(const DispatchArgs& a, const int32_t* ids, const 
   if (lane == 0) {
     a.ntiles[0] = __popcll(smask);
     a.err_word[0] = errbits;
+  }
+}
+
+// Dispatch of at most 64 * WMAX slots by one block of NW waves (one thread per slot and
+// per expert), for ids already in LDS: the same row space, tile list and error bits as
+// dispatch_body, from a bitmap of the slots of each expert (s_mask[e * W + w], bit b =
+// slot 64 w + b, W = ceil(S / 64) words). An expert's rows are its slots in slot order,
+// so a slot's row inside the group is the number of the expert's bits below its own.
+// Tiles of at most kTileTok rows get their tokens from the slots (no read-back).
+// Two barriers after the ids are in place; s_mask must be zero on entry.
+template <int NW, int EMAX>
+__device__ void dispatch_bitmap(const DispatchArgs& a, const int32_t* ids, const int32_t* err_tok,
+                                uint64_t* s_mask, int* s_off, int* s_toff, int* s_tot,
+                                int* s_err) {
+  constexpr int NT = NW * kWave;
+  static_assert(EMAX <= NT, "one thread per expert");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, K = a.K, S = a.T * a.K, W = (S + 63) / 64, h = a.tile_h;
+
+  // slots into the experts' bitmaps; error bits
+  const bool in = tid < S;
+  const int e = in ? ids[tid] : -1;
+  const bool valid = in && e >= 0 && e < E;
+  int err = (in && !valid && !(err_tok && e == -1) && !(e >= E && e < E + a.zero)) ? 1 : 0;
+  if (err_tok && tid < a.T) err |= err_tok[tid];
+  if (valid) atomicOr((unsigned long long*)&s_mask[e * W + (tid >> 6)], 1ull << (tid & 63));
+  if (err) atomicOr(s_err, err);
+  for (int p = tid; p < a.shared_rows; p += NT) a.row_token[p] = p;
+  __syncthreads();
+
+  // per expert: row count and tile count, exclusive scans of both (packed in one int)
+  int cnt = 0;
+  if (tid < E)
+    for (int w = 0; w < W; ++w) cnt += __popcll(s_mask[tid * W + w]);
+  const int nt = (cnt + h - 1) / h;
+  const int packed = cnt | (nt << 16);  // S <= 64 * WMAX < 2^16
+  int inc = packed;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(inc, d, kWave);
+    if (lane >= d) inc += y;
+  }
+  constexpr int EW = (EMAX + 63) / 64;  // waves holding experts
+  if (lane == 63 && wave < EW) s_tot[wave] = inc;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < EW; ++w) {
+    const int v = w * kWave < E ? s_tot[w] : 0;
+    before += w < wave ? v : 0;
+    all += v;
+  }
+  const int excl = inc - packed + before;
+  const int row0 = a.shared_rows + (excl & 0xFFFF), toff = excl >> 16;
+  if (tid < E) {
+    s_off[tid] = row0;
+    s_toff[tid] = toff;
+    for (int i = 0; i < nt; ++i) {  // tile headers; short tiles' unused tokens are 0
+      const int c = min(h, cnt - i * h);
+      Tile* tl = a.tiles + toff + i;
+      *(int4*)tl = make_int4(tid, row0 + i * h, c, 0);
+#pragma unroll
+      for (int q = 0; q < kTileTok; ++q)
+        if (h > kTileTok || q >= c) tl->tok[q] = 0;
+    }
+  }
+  if (tid == 0) {
+    a.ntiles[0] = all >> 16;
+    a.err_word[0] = *s_err;
+  }
+  __syncthreads();
+
+  // each slot: its row, the row's token, the token field of its tile
+  if (valid) {
+    const int wb = tid >> 6;
+    int rank = __popcll(s_mask[e * W + wb] & ((1ull << (tid & 63)) - 1ull));
+    for (int w = 0; w < wb; ++w) rank += __popcll(s_mask[e * W + w]);
+    const int pos = s_off[e] + rank;
+    const int tok = tid / K;
+    a.row_token[pos] = tok;
+    a.inv[tid] = pos;
+    if (h <= kTileTok) a.tiles[s_toff[e] + rank / h].tok[rank % h] = tok;
+  } else if (in) {
+    a.inv[tid] = (e >= E && e < E + a.zero) ? -2 : -1;
   }
 }
 

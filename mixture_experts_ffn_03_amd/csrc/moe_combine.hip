@@ -27,6 +27,8 @@ __device__ __forceinline__ void load_y8(const void* y, size_t off, float (&v)[8]
   }
 }
 
+constexpr int kCombineBatch = 8;  // slots whose rows are loaded together
+
 template <bool YBF16>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const int t = blockIdx.y;
@@ -35,18 +37,29 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int j = 0; j < a.K; ++j) {
-    const int p = a.inv[(size_t)t * a.K + j];
-    if (p < 0 && p != -2) continue;
-    const float w = a.w[(size_t)t * a.K + j];
-    float v[8];
-    if (p >= 0) {
-      load_y8<YBF16>(a.y, (size_t)p * a.H + h0, v);
-    } else {  // zero expert: identity of the expert input
-      load_y8<true>(a.xe, (size_t)t * a.H + h0, v);
-    }
+  // batches of kCombineBatch slots: their rows and weights first, then every row's loads
+  // (a dropped slot's load reads row 0 and is discarded), then the sums in slot order
+  for (int j0 = 0; j0 < a.K; j0 += kCombineBatch) {
+    int p[kCombineBatch];
+    float w[kCombineBatch];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+    for (int jj = 0; jj < kCombineBatch; ++jj) {
+      const int j = min(j0 + jj, a.K - 1);
+      p[jj] = j0 + jj < a.K ? a.inv[(size_t)t * a.K + j] : -1;
+      w[jj] = a.w[(size_t)t * a.K + j];
+    }
+    float v[kCombineBatch][8];
+#pragma unroll
+    for (int jj = 0; jj < kCombineBatch; ++jj)
+      load_y8<YBF16>(a.y, (size_t)(p[jj] >= 0 ? p[jj] : 0) * a.H + h0, v[jj]);
+#pragma unroll
+    for (int jj = 0; jj < kCombineBatch; ++jj) {
+      if (p[jj] == -2) load_y8<true>(a.xe, (size_t)t * a.H + h0, v[jj]);  // zero expert: x_e[t]
+      if (p[jj] >= 0 || p[jj] == -2) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[jj], v[jj][i], acc[i]);
+      }
+    }
   }
   if (a.shared) {
     float v[8];

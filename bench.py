@@ -165,7 +165,7 @@ def summarize_trace(d, command):
 
 
 # the routed experts' kernels of one layer call, in launch order after the dispatch build
-_ROUTED_KERNELS = {"decode": ("k_dec_gate_up", "k_dec_down"),
+_ROUTED_KERNELS = {"decode": ("k_dec_", "k_dec_"),
                    "prefill": ("k_pre_gemm", "k_pre_gemm")}
 
 

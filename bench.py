@@ -294,6 +294,8 @@ def main():
     ap.add_argument("--batches", type=int, default=8)
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay timing (decode layers of at most 32 tokens)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 8 device-to-device copies of 1 GiB (a copy kernel of known "
@@ -435,6 +437,38 @@ def main():
     pre_ok = H % 64 == 0 and I % 64 == 0 and (not spec.shared or spec.shared_inter % 64 == 0)
     decode = (path == M.PATH_DECODE) or (path == M.PATH_AUTO and not (S_rows >= 4 * groups
                                                                        and pre_ok))
+
+    # the same steps replayed from a HIP graph (one capture of a whole period: every weight
+    # set and batch once), for decode layers of at most 32 tokens: launch gaps without the
+    # host in the loop
+    graph_replay = None
+    if decode and T <= 32 and not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(period):
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(period):
+                step(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // period)
+        start.record()
+        for _ in range(reps):
+            graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        g_ms = start.elapsed_time(end) / (reps * period)
+        if M.get_device_error(ws) != 0:
+            raise RuntimeError("device error word set during the graph replays")
+        graph_replay = {"ms_per_step": round(g_ms, 5), "value": round(T / (g_ms * 1e-3), 2),
+                        "steps": reps * period, "steps_per_replay": period}
+        del graph
+
     u_mean = sum(uniq[(args.warmup + i) % period] for i in range(args.steps)) / args.steps
     bpe = bytes_per_elem(spec.fmt)
     # algorithmic work of the dominant kernel per launch: each touched expert's weights
@@ -490,6 +524,8 @@ def main():
                   "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()}},
         "roofline": roof,
     }
+    if graph_replay is not None:
+        result["graph_replay"] = graph_replay
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle for about {args.cpu_seconds:.0f} s")
         result["cpu_baseline"] = cpu_baseline(spec, sets[0], name, args.cpu_seconds)

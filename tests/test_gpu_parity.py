@@ -281,6 +281,16 @@ SMALL = {
     "bf16_shared_mini": S.LayerSpec(name="bf16_shared_mini", tokens=9, hidden=256, experts=16,
                                     top_k=4, inter=128, fmt=S.BF16, shared=True,
                                     shared_inter=192, shared_fmt=S.BF16, seed=1084),
+    # the fused top-K + bitmap dispatch (at most 16 tokens, more than 16 slots): 32 slots per
+    # token (8 bitmap words per expert, several tiles per expert); 256 experts with a shared
+    # expert; a hash layer (token errors read from LDS); 3 tokens of the Qwen3-like layer
+    "wide_k_fused": S.LayerSpec(name="wide_k_fused", tokens=16, hidden=512, experts=64,
+                                top_k=32, inter=128, fmt=S.NVFP4, renormalize=True, seed=1085),
+    "fused_256": S.scaled(S.WORKLOADS["dsv3_decode_t32"], tokens=16, hidden=256, experts=256,
+                          inter=128, shared_inter=128, fmt=S.MXFP4),
+    "hash_fused": S.scaled(S.WORKLOADS["hash_mxfp4_t512"], tokens=12, hidden=512, experts=32,
+                           inter=256, shared_inter=128, vocab=1000),
+    "qwen3_t3": S.scaled(S.WORKLOADS["qwen3_decode_t8"], tokens=3),
     # softmax+bias routing over 48 + 16 zero-computation experts (identity contributions)
     "zero_experts_mini": S.LayerSpec(name="zero_experts_mini", tokens=23, hidden=512,
                                      experts=48, top_k=8, inter=256, fmt=S.NVFP4,
@@ -407,17 +417,41 @@ def test_bad_expert_ids_many_slots():
     assert_layer_close(out.float().cpu().numpy(), want, None, "bad-ids-many")
 
 
-@pytest.mark.parametrize("tokens", [77, 6])  # 6 tokens x 6 slots: the one-wave dispatch
+# 77 tokens: top-K and dispatch launches; 6 tokens (36 slots): the fused kernel's bitmap
+# dispatch; 2 tokens (12 slots): its one-wave dispatch
+@pytest.mark.parametrize("tokens", [77, 6, 2])
 def test_hash_layer_bad_token_flags_error(tokens):
     spec = S.scaled(SMALL["hash_mini"], tokens=tokens)
     inp = S.make_inputs(spec, device=DEV)
-    inp.token_ids[3] = spec.vocab + 5
+    bad = min(3, tokens - 1)
+    inp.token_ids[bad] = spec.vocab + 5
     out, _, ids, _, ws = run_layer(inp, path=M.PATH_DECODE)
     err = M.get_device_error(ws)
     assert err & M.DEVERR_TOKEN_ID and not err & M.DEVERR_EXPERT_ID
-    assert (ids[3] == -1).all()
+    assert (ids[bad] == -1).all()
     want, _, _, _ = oracle_layer(inp)
     assert_layer_close(out.float().cpu().numpy(), want, None, "bad-token")
+
+
+@pytest.mark.parametrize("tokens", [12, 2, 77])
+def test_hash_layer_repeated_experts(tokens):
+    """A hash table may name one expert twice for a token: both slots get their own row (in
+    slot order) and weight, on every dispatch size."""
+    _announce("hash repeated experts", tokens)
+    spec = S.scaled(SMALL["hash_mini"], tokens=tokens)
+    inp = S.make_inputs(spec, device=DEV)
+    inp.tid2eid[:, 1] = inp.tid2eid[:, 0]
+    inp.tid2eid[1::3, 5] = inp.tid2eid[1::3, 2]
+    for path in PATH_VALUES:
+        out, _, ids, w, ws = run_layer(inp, path=path)
+        _sync()
+        assert M.get_device_error(ws) == 0
+        want, _, oids, ow = oracle_layer(inp)
+        assert np.array_equal(ids.cpu().numpy(), oids)
+        assert (oids[:, 0] == oids[:, 1]).any()
+        assert np.allclose(w.cpu().numpy(), ow, rtol=W_RTOL, atol=1e-7)
+        assert_layer_close(out.float().cpu().numpy(), want, f32(inp.residual),
+                           f"hash-repeat/{tokens}/{path}")
 
 
 def test_zero_tokens_is_a_noop():

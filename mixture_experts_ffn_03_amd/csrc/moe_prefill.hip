@@ -593,7 +593,9 @@ static hipError_t launch_pre_shape(const ExpertGemmArgs& a, hipStream_t s) {
 // Tile height MT -> stage width KC and block shape (row blocks per wave RB, waves along M
 // WM, column blocks per wave CB): 128 = 64-code stages, 2 x 2 x 4 (128 x 256 weight
 // rows); 64 = 64-code stages, 1 x 2 x 4 (64 x 256); 32 = 128-code stages, 1 x 1 x 4
-// (32 x 512). K that is not a multiple of 128 takes 64-code stages at height 32 too.
+// (32 x 512). K that is not a multiple of 128 takes 64-code stages at height 32 too. The
+// shared expert's implicit list at height 32 with fewer than 512 blocks takes 32 x 256
+// (1 x 1 x 2: 80 KB of LDS, two blocks per CU) for twice the blocks.
 #ifndef MOE_PRE_NSTG
 #define MOE_PRE_NSTG 3
 #endif
@@ -603,8 +605,13 @@ static hipError_t launch_pre(const ExpertGemmArgs& a, int mt, hipStream_t s) {
   const int fmt = GATEUP ? a.gate.fmt : a.down.fmt;
   const int K = GATEUP ? a.H : a.I;
   constexpr int NS3 = MOE_PRE_NSTG;
+  // the implicit list (the shared expert) of few row tiles: half-width column tiles,
+  // twice the blocks
+  const bool narrow = a.src.tiles == nullptr && mt == 32 && K % 128 == 0 &&
+                      a.tile_bound * ((GATEUP ? a.I : a.H) / 256) < 512;
   if (fmt == 0) {
     if (mt == 32) {
+      if (narrow) return launch_pre_shape<0, 128, 3, 1, 1, 2, GATEUP>(a, s);
       return K % 128 == 0 ? launch_pre_shape<0, 128, 3, 1, 1, 4, GATEUP>(a, s)
                           : launch_pre_shape<0, 64, 3, 1, 1, 4, GATEUP>(a, s);
     }
@@ -612,6 +619,7 @@ static hipError_t launch_pre(const ExpertGemmArgs& a, int mt, hipStream_t s) {
     return launch_pre_shape<0, 64, NS3, 2, 2, 4, GATEUP>(a, s);
   }
   if (mt == 32 && fmt == 1) {
+    if (narrow) return launch_pre_shape<1, 128, 3, 1, 1, 2, GATEUP>(a, s);
     return K % 128 == 0 ? launch_pre_shape<1, 128, 3, 1, 1, 4, GATEUP>(a, s)
                         : launch_pre_shape<1, 64, 3, 1, 1, 4, GATEUP>(a, s);
   }

@@ -19,7 +19,10 @@
  *   moe_get_device_error, which synchronises `stream` to read the error word.
  *   Indices and weights stay on the device (module doc: no device-to-host sync).
  * - bf16 tensors are passed as uint16_t bit patterns; every activation is
- *   row-major [tokens, hidden].
+ *   row-major [tokens, hidden]. Activations (x, x_experts, out, residual), norm_gamma,
+ *   weight arrays and the workspace must be 16-byte aligned (the kernels use 128-bit
+ *   loads); a misaligned pointer is rejected (MOE_ERR_INVALID_ARG, or MOE_ERR_WORKSPACE
+ *   for the workspace).
  * - Host validation is O(1) and happens before any launch; a failing call
  *   enqueues nothing and returns a negative moe_status.
  * - Data errors that only the device can see (an expert id outside [0, E + Z), a
@@ -212,7 +215,7 @@ int moe_experts_forward(const moe_config* cfg, const uint16_t* x_experts,
                         size_t workspace_bytes, hipStream_t stream);
 
 /* The whole layer: [RMSNorm] -> router -> top-K -> experts -> blend.
- *   norm_gamma bf16 [H] (pre_norm only)
+ *   norm_gamma bf16 [H] (pre_norm only; 16-byte aligned)
  *   dbg_logits f32 [T, E + Z], dbg_ids int32 [T, top_k], dbg_w f32 [T, top_k]: optional
  *              copies of the routing decisions (NULL to skip)
  * Other arguments as in moe_route and moe_experts_forward. */

@@ -457,7 +457,7 @@ int moe_layer_forward(const moe_config* cfg, const uint16_t* x, const uint16_t* 
   if (!aligned16(x) || !aligned16(out) || (residual && !aligned16(residual)))
     return MOE_ERR_INVALID_ARG;
   if (out == x) return MOE_ERR_INVALID_ARG;
-  if (c.pre_norm && !norm_gamma) return MOE_ERR_INVALID_ARG;
+  if (c.pre_norm && (!norm_gamma || !aligned16(norm_gamma))) return MOE_ERR_INVALID_ARG;
   if ((r = check_route_ptrs(c, x, router_w, token_ids, tid2eid, nullptr)) != MOE_OK) return r;
   if ((r = check_group(routed, c.num_experts, c.hidden, c.inter)) != MOE_OK) return r;
   if (c.has_shared) {

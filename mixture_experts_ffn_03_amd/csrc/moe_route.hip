@@ -22,12 +22,23 @@ namespace moe {
 __global__ __launch_bounds__(256) void k_rmsnorm(const uint16_t* __restrict__ x,
                                                  const uint16_t* __restrict__ gamma,
                                                  uint16_t* __restrict__ out, int H, float eps) {
+  // 16-byte pieces (8 values; H is a multiple of 32), the second pass re-reading the row
+  // from the cache
   const int t = blockIdx.x;
-  const uint16_t* xr = x + (size_t)t * H;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)t * H);
+  const uint4* gr = reinterpret_cast<const uint4*>(gamma);
+  uint4* orow = reinterpret_cast<uint4*>(out + (size_t)t * H);
+  const int np = H / 8;
   float ss = 0.f;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) {
-    const float v = bf16_to_f32(xr[i]);
-    ss = fmaf(v, v, ss);
+  for (int i = threadIdx.x; i < np; i += blockDim.x) {
+    const uint4 q = xr[i];
+    const uint32_t d[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = bf16_to_f32(d[j] & 0xFFFFu), hi = bf16_to_f32(d[j] >> 16);
+      ss = fmaf(lo, lo, ss);
+      ss = fmaf(hi, hi, ss);
+    }
   }
   ss = wave_sum(ss);
   __shared__ float part[4];
@@ -35,11 +46,19 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const uint16_t* __restrict__ x,
   __syncthreads();
   const float tot = (part[0] + part[1]) + (part[2] + part[3]);
   const float r = 1.0f / sqrtf(tot / (float)H + eps);
-  uint16_t* orow = out + (size_t)t * H;
-  for (int i = threadIdx.x; i < H; i += blockDim.x)
-    orow[i] = f32_to_bf16((bf16_to_f32(xr[i]) * r) * bf16_to_f32(gamma[i]));
+  for (int i = threadIdx.x; i < np; i += blockDim.x) {
+    const uint4 q = xr[i], g = gr[i];
+    const uint32_t d[4] = {q.x, q.y, q.z, q.w}, e[4] = {g.x, g.y, g.z, g.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = (bf16_to_f32(d[j] & 0xFFFFu) * r) * bf16_to_f32(e[j] & 0xFFFFu);
+      const float hi = (bf16_to_f32(d[j] >> 16) * r) * bf16_to_f32(e[j] >> 16);
+      o[j] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    }
+    orow[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
 }
-
 hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, uint16_t* out, int T, int H,
                           float eps, hipStream_t s) {
   if (T == 0) return hipSuccess;

@@ -10,9 +10,10 @@
 //
 // Design (gfx950, v_mfma_f32_32x32x16_bf16):
 // * A block of 4 waves (one per SIMD) computes an MT-row tile of one expert against
-//   BROWS weight rows. Each wave owns RB 32-row blocks and four 32-column blocks of
-//   weight rows (gate+up: two of gate and the same two of up, so SwiGLU runs in the
-//   epilogue on values held by the same lane), i.e. 4*RB independent accumulators.
+//   BROWS weight rows. Each wave owns RB 32-row blocks and CB 32-column blocks of
+//   weight rows (gate+up: half of them gate and the same ones of up, so SwiGLU runs in
+//   the epilogue on values held by the same lane), i.e. RB*CB independent accumulators;
+//   each decoded B operand feeds RB MFMAs.
 // * Both operands reach LDS by direct-to-LDS loads (global_load_lds_*: the activation
 //   rows gathered by row_token, the FP4 weight rows and their scale bytes) into a ring
 //   of three 64-wide K stages. Step c waits for stage c, synchronises the block once,
@@ -499,6 +500,10 @@ void k_pre_gemm(ExpertGemmArgs a) {
     kloop(std::integral_constant<int, RB>{});
   } else if (nrb == 1) {
     kloop(std::integral_constant<int, 1>{});
+  } else if (nrb == 2) {  // (RB > 2 only)
+    kloop(std::integral_constant<int, (RB > 2 ? 2 : 1)>{});
+  } else if (nrb == 3) {  // (RB > 3 only)
+    kloop(std::integral_constant<int, (RB > 3 ? 3 : 1)>{});
   } else {
     kloop(std::integral_constant<int, 0>{});
   }
@@ -591,9 +596,9 @@ static hipError_t launch_pre_shape(const ExpertGemmArgs& a, hipStream_t s) {
 }
 
 // Tile height MT -> stage width KC and block shape (row blocks per wave RB, waves along M
-// WM, column blocks per wave CB): 128 = 64-code stages, 2 x 2 x 4 (128 x 256 weight
-// rows); 64 = 64-code stages, 1 x 2 x 4 (64 x 256); 32 = 128-code stages, 1 x 1 x 4
-// (32 x 512). K that is not a multiple of 128 takes 64-code stages at height 32 too. The
+// WM, column blocks per wave CB): FP4 128 = 64-code stages, 4 x 1 x 2 (128 x 256 weight
+// rows; each wave all 128 rows, so a decoded B operand feeds four MFMAs); FP4 64 = 64-code
+// stages, 2 x 1 x 2 (64 x 256); 32 = 128-code stages, 1 x 1 x 4 (32 x 512). K that is not a multiple of 128 takes 64-code stages at height 32 too. The
 // shared expert's implicit list at height 32 with fewer than 512 blocks takes 32 x 256
 // (1 x 1 x 2: 80 KB of LDS, two blocks per CU) for twice the blocks.
 #ifndef MOE_PRE_NSTG
@@ -615,8 +620,8 @@ static hipError_t launch_pre(const ExpertGemmArgs& a, int mt, hipStream_t s) {
       return K % 128 == 0 ? launch_pre_shape<0, 128, 3, 1, 1, 4, GATEUP>(a, s)
                           : launch_pre_shape<0, 64, 3, 1, 1, 4, GATEUP>(a, s);
     }
-    if (mt == 64) return launch_pre_shape<0, 64, 3, 1, 2, 4, GATEUP>(a, s);
-    return launch_pre_shape<0, 64, NS3, 2, 2, 4, GATEUP>(a, s);
+    if (mt == 64) return launch_pre_shape<0, 64, 3, 2, 1, 2, GATEUP>(a, s);
+    return launch_pre_shape<0, 64, NS3, 4, 1, 2, GATEUP>(a, s);
   }
   if (mt == 32 && fmt == 1) {
     if (narrow) return launch_pre_shape<1, 128, 3, 1, 1, 2, GATEUP>(a, s);
@@ -624,8 +629,8 @@ static hipError_t launch_pre(const ExpertGemmArgs& a, int mt, hipStream_t s) {
                         : launch_pre_shape<1, 64, 3, 1, 1, 4, GATEUP>(a, s);
   }
   if (fmt == 1) {
-    if (mt == 64) return launch_pre_shape<1, 64, 3, 1, 2, 4, GATEUP>(a, s);
-    return launch_pre_shape<1, 64, NS3, 2, 2, 4, GATEUP>(a, s);
+    if (mt == 64) return launch_pre_shape<1, 64, 3, 2, 1, 2, GATEUP>(a, s);
+    return launch_pre_shape<1, 64, NS3, 4, 1, 2, GATEUP>(a, s);
   }
   // FP8 / BF16 weights: 32-code stages; 32-row tiles run in the 64-row shape (its second
   // row block idle)

@@ -103,3 +103,30 @@ def test_null_arguments_are_rejected(lib):
     assert lib.moe_workspace_size(None, ctypes.byref(n)) == -1
     cfg = M.make_config(4, 256, 8, 2, 512)
     assert lib.moe_workspace_size(ctypes.byref(cfg), None) == -1
+
+
+def _fake_weights(E, H, I):
+    """Weight structs with aligned, never dereferenced device addresses: the host checks of
+    a call run before anything is launched."""
+    base = 1 << 40
+
+    def w(n, k, off):
+        return M.binding.MoeFp4Weight(M.FMT_MXFP4, base + off, base + off + (1 << 30), None, E, n, k)
+
+    return M.binding.MoeExpertWeights(w(I, H, 0), w(I, H, 1 << 32), w(H, I, 2 << 32))
+
+
+@pytest.mark.parametrize("what", ["x", "gamma", "out", "residual"])
+def test_misaligned_pointers_are_rejected_before_any_launch(lib, what):
+    T, H, E, K, I = 4, 256, 8, 2, 512
+    cfg = M.make_config(T, H, E, K, I, pre_norm=True)
+    routed = _fake_weights(E, H, I)
+    good = 1 << 41  # 16-byte aligned
+    ptr = {"x": good, "gamma": good + 4096, "out": good + 8192, "residual": good + 12288}
+    ptr[what] += 2  # bf16-aligned, not 16-byte aligned
+    n = ctypes.c_size_t(0)
+    assert lib.moe_workspace_size(ctypes.byref(cfg), ctypes.byref(n)) == 0
+    rc = lib.moe_layer_forward(ctypes.byref(cfg), ptr["x"], ptr["gamma"], good + 16384, None, None,
+                               None, None, ctypes.byref(routed), None, ptr["residual"], ptr["out"],
+                               None, None, None, good + (1 << 20), n.value, None)
+    assert rc == -1  # MOE_ERR_INVALID_ARG

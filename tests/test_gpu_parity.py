@@ -291,6 +291,9 @@ SMALL = {
     "hash_fused": S.scaled(S.WORKLOADS["hash_mxfp4_t512"], tokens=12, hidden=512, experts=32,
                            inter=256, shared_inter=128, vocab=1000),
     "qwen3_t3": S.scaled(S.WORKLOADS["qwen3_decode_t8"], tokens=3),
+    # 40 tokens on the decode path: the shared expert's implicit list of ten 4-token tiles
+    "dsv3_t40_mini": S.scaled(S.WORKLOADS["dsv3_decode_t32"], tokens=40, hidden=1024,
+                              experts=64, inter=256, shared_inter=192),
     # softmax+bias routing over 48 + 16 zero-computation experts (identity contributions)
     "zero_experts_mini": S.LayerSpec(name="zero_experts_mini", tokens=23, hidden=512,
                                      experts=48, top_k=8, inter=256, fmt=S.NVFP4,

@@ -626,8 +626,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 #pragma unroll
     for (int q = 0; q < kTileTok; ++q) res[q] = t == q ? v : res[q];
   }
-  // (stores after the loop: a loop that stores and reads registers loaded before it makes
-  // the compiler wait for every load in flight before entering it)
+  // one store per owned row and token, after the loop (the compiler waits for every load in
+  // flight before entering a loop that stores without loading anything itself)
   const bool owner = M == 2 ? ((idx & 1) == 0 && (sub & (kDiv - 1)) == 0) : (sub & (kDiv - 1)) == 0;
   const int n = nbase + grp + G * (M == 2 ? idx >> 1 : idx);
   if (owner && n < N) {

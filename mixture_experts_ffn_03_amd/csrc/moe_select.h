@@ -341,8 +341,8 @@ __device__ void dispatch_small(const DispatchArgs& a, const int32_t* ids, const 
   }
 }
 
-// Dispatch of at most 64 * WMAX slots by one block of NW waves (one thread per slot and
-// per expert), for ids already in LDS: the same row space, tile list and error bits as
+// Dispatch of at most NW * 64 slots and EMAX experts by one block of NW waves (one thread
+// per slot and per expert), for ids already in LDS: the same row space, tile list and error bits as
 // dispatch_body, from a bitmap of the slots of each expert (s_mask[e * W + w], bit b =
 // slot 64 w + b, W = ceil(S / 64) words). An expert's rows are its slots in slot order,
 // so a slot's row inside the group is the number of the expert's bits below its own.
@@ -353,7 +353,7 @@ __device__ void dispatch_bitmap(const DispatchArgs& a, const int32_t* ids, const
                                 uint64_t* s_mask, int* s_off, int* s_toff, int* s_tot,
                                 int* s_err) {
   constexpr int NT = NW * kWave;
-  static_assert(EMAX <= NT, "one thread per expert");
+  static_assert(EMAX <= NT && NT < (1 << 16), "one thread per expert; packed sums");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, K = a.K, S = a.T * a.K, W = (S + 63) / 64, h = a.tile_h;
 
@@ -373,7 +373,7 @@ __device__ void dispatch_bitmap(const DispatchArgs& a, const int32_t* ids, const
   if (tid < E)
     for (int w = 0; w < W; ++w) cnt += __popcll(s_mask[tid * W + w]);
   const int nt = (cnt + h - 1) / h;
-  const int packed = cnt | (nt << 16);  // S <= 64 * WMAX < 2^16
+  const int packed = cnt | (nt << 16);  // both sums <= S <= NW * 64 < 2^16
   int inc = packed;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {

@@ -20,6 +20,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -94,12 +95,23 @@ class HipEvents:
         self.lib.hipEventDestroy(ctypes.c_void_p(ev))
 
 
+_CODE_TOKENS = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'', re.S)
+
+
+def _code_only(text):
+    """C/C++ source without comments and with whitespace collapsed (string and character
+    literals kept), so that edits of comments leave the digest unchanged."""
+    text = _CODE_TOKENS.sub(lambda m: " " if m.group(0)[0] == "/" else m.group(0), text)
+    return " ".join(text.split())
+
+
 def source_digest():
+    """Digest of the kernels' sources (comments and layout excluded)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixture_experts_ffn_03_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -148,8 +148,8 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Top-K and dispatch in one block, for few tokens and experts: the block's waves select
 // the experts of the tokens (topk_token, ids kept in LDS), then sort the slots by expert
-// (dispatch_small for a handful of slots, else dispatch_bitmap). Saves a launch and a
-// round trip of the ids through memory.
+// (dispatch_bitmap: faster than the one-wave dispatch_small even for a handful of slots).
+// Saves a launch and a round trip of the ids through memory.
 // ---------------------------------------------------------------------------
 constexpr int kFusedWaves = 16;
 static_assert(kFusedMaxSlots <= kFusedWaves * 64, "one thread per slot");
@@ -166,18 +166,13 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_topk_dispatch(TopkArgs ta,
   __shared__ int s_err;
   const int wave = threadIdx.x >> 6;
   const int S = da.T * da.K;
-  const bool small = S <= kSmallDispatchSlots;
-  if (!small) {  // clear the bitmaps while the waves select
+  {  // clear the bitmaps while the waves select
     const int nw = da.E * ((S + 63) / 64);
     for (int i = threadIdx.x; i < nw; i += kFusedWaves * 64) s_mask[i] = 0ull;
     if (threadIdx.x == 0) s_err = 0;
   }
   for (int t = wave; t < ta.T; t += kFusedWaves) topk_token<NPL>(ta, t, s_ids, s_errt);
   __syncthreads();
-  if (small) {  // few slots: one wave
-    if (wave == 0) dispatch_small(da, s_ids, s_errt, s_off);
-    return;
-  }
   dispatch_bitmap<kFusedWaves, kFusedMaxExperts>(da, s_ids, s_errt, s_mask, s_off, s_toff, s_tot,
                                                 &s_err);
 }

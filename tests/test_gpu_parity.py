@@ -262,7 +262,7 @@ SMALL = {
     # many slots (T * k >= 8192: the two-launch multi-block dispatch) with Zipf-skewed loads
     "many_slots_mini": S.scaled(S.WORKLOADS["prefill_zipf_t4096"], tokens=1500, hidden=256,
                                 experts=16, inter=128),
-    # few slots (T * k <= 64: the one-wave dispatch) with zero-computation experts
+    # few slots (5 tokens x 8) with zero-computation experts
     "zero_experts_small": S.LayerSpec(name="zero_experts_small", tokens=5, hidden=512,
                                       experts=48, top_k=8, inter=256, fmt=S.NVFP4,
                                       score=S.SOFTMAX_BIAS, renormalize=False,
@@ -329,6 +329,22 @@ def test_layer_without_residual_and_experts_entry(path):
     M.experts_forward(cfg, inp.x, ids, w, M.expert_weights(inp.routed),
                       M.expert_weights(inp.shared), None, out2, ws)
     _sync()
+    assert torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("tokens", [1, 2])
+def test_experts_entry_one_wave_dispatch(tokens):
+    """moe_experts_forward builds its own dispatch (at most 16 slots: the one-wave build from
+    pairwise ranks); the layer's fused top-K uses the bitmap build. Same rows, same tiles:
+    bit-identical outputs."""
+    _announce("experts entry, one-wave dispatch", tokens)
+    inp = S.make_inputs(S.scaled(SMALL["qwen3_decode_t8"], tokens=tokens), device=DEV)
+    out, logits, ids, w, ws = run_layer(inp, path=M.PATH_DECODE, residual=False)
+    cfg = config_for(inp, M.PATH_DECODE)
+    out2 = torch.empty_like(out)
+    M.experts_forward(cfg, inp.x, ids, w, M.expert_weights(inp.routed), None, None, out2, ws)
+    _sync()
+    assert M.get_device_error(ws) == 0
     assert torch.equal(out, out2)
 
 
@@ -420,8 +436,8 @@ def test_bad_expert_ids_many_slots():
     assert_layer_close(out.float().cpu().numpy(), want, None, "bad-ids-many")
 
 
-# 77 tokens: top-K and dispatch launches; 6 tokens (36 slots): the fused kernel's bitmap
-# dispatch; 2 tokens (12 slots): its one-wave dispatch
+# 77 tokens: top-K and dispatch launches; 6 and 2 tokens (36 and 12 slots): the fused
+# kernel's bitmap dispatch
 @pytest.mark.parametrize("tokens", [77, 6, 2])
 def test_hash_layer_bad_token_flags_error(tokens):
     spec = S.scaled(SMALL["hash_mini"], tokens=tokens)

@@ -158,12 +158,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor_f(v, m));
-  return v;
-}
-
 // Sum NV per-lane values over each aligned group of L lanes (L a power of two <= 64),
 // halving the value count at each of the first log2(NV) butterfly distances so that
 // no lane reduces every value. On return a lane holds NF = max(1, NV / L) complete

@@ -23,11 +23,25 @@ __global__ __launch_bounds__(kDispatchThreads) void k_dispatch(DispatchArgs a) {
   __shared__ int s_off[kMaxExperts];
   __shared__ int s_tmp[2 * kDispatchWaves + 1];
   __shared__ int s_err;
-  if (a.T * a.K <= kSmallDispatchSlots) {  // few slots: one wave
-    if (threadIdx.x < kWave) dispatch_small(a, a.ids, a.err_tok, s_wbase[0]);
-    return;
-  }
   dispatch_body<kDispatchWaves, kMaxExperts>(a, a.ids, a.err_tok, s_wbase, s_off, s_tmp, &s_err);
+}
+
+// At most one slot per thread whose experts' bitmaps (E x ceil(S / 64) words, the dynamic
+// LDS of the launch) fit kBitmapMaxLds: the bitmap dispatch on ids in memory.
+constexpr size_t kBitmapMaxLds = 48 * 1024;
+
+__global__ __launch_bounds__(kDispatchThreads) void k_dispatch_bitmap(DispatchArgs a) {
+  extern __shared__ uint64_t s_mask[];
+  __shared__ int s_off[kMaxExperts];
+  __shared__ int s_toff[kMaxExperts];
+  __shared__ int s_tot[kDispatchWaves];
+  __shared__ int s_err;
+  const int n = a.E * ((a.T * a.K + 63) / 64);
+  for (int i = threadIdx.x; i < n; i += kDispatchThreads) s_mask[i] = 0ull;
+  if (threadIdx.x == 0) s_err = 0;
+  __syncthreads();
+  dispatch_bitmap<kDispatchWaves, kMaxExperts>(a, a.ids, a.err_tok, s_mask, s_off, s_toff, s_tot,
+                                               &s_err);
 }
 
 // ---------------------------------------------------------------------------
@@ -141,6 +155,11 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_dispatch_scatter, dim3(blocks), dim3(kDispatchThreads), 0, s, a);
     return hipGetLastError();
   }
+  const size_t mask_bytes = (size_t)a.E * ((S + 63) / 64) * sizeof(uint64_t);
+  if (S <= kDispatchThreads && mask_bytes <= kBitmapMaxLds) {
+    hipLaunchKernelGGL(k_dispatch_bitmap, dim3(1), dim3(kDispatchThreads), mask_bytes, s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_dispatch, dim3(1), dim3(kDispatchThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -148,7 +167,7 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Top-K and dispatch in one block, for few tokens and experts: the block's waves select
 // the experts of the tokens (topk_token, ids kept in LDS), then sort the slots by expert
-// (dispatch_bitmap: faster than the one-wave dispatch_small even for a handful of slots).
+// (dispatch_bitmap).
 // Saves a launch and a round trip of the ids through memory.
 // ---------------------------------------------------------------------------
 constexpr int kFusedWaves = 16;

@@ -110,9 +110,6 @@ constexpr int kFusedMaxSlots = 1024;
 bool fused_topk_dispatch_fits(int T, int E, int K);
 hipError_t launch_topk_dispatch(const TopkArgs& ta, const DispatchArgs& da, hipStream_t s);
 
-// up to this many slots one wave builds the dispatch (pairwise ranks, O(slots) per lane);
-// beyond it the block's counting sort is faster
-constexpr int kSmallDispatchSlots = 16;
 
 struct ExpertGemmArgs {
   const uint16_t* x;          // bf16 [T, H] expert input

@@ -277,70 +277,6 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
   return r;
 }
 
-// Dispatch of at most 64 slots (few tokens) by one wave, lane = slot: the same row space,
-// tile list and error bits as dispatch_body, from ranks found by comparing every pair of
-// slots (key = expert * 64 + slot: the stable order by expert, then token and slot).
-// s_tok: 64 ints of LDS (tokens of the rows in rank order).
-__device__ void dispatch_small(const DispatchArgs& a, const int32_t* ids, const int32_t* err_tok,
-                               int* s_tok) {
-  constexpr int kNone = 0x7fffffff;
-  const int lane = threadIdx.x & 63;
-  const int E = a.E, K = a.K, S = a.T * a.K;
-  const bool in = lane < S;
-  const int e = in ? ids[lane] : -1;
-  const bool valid = in && e >= 0 && e < E;
-  const bool zero = in && e >= E && e < E + a.zero;
-  int err = (in && !valid && !zero && !(err_tok && e == -1)) ? 1 : 0;
-  if (err_tok && lane < a.T) err |= err_tok[lane];
-  if (lane < a.shared_rows) a.row_token[lane] = lane;  // shared_rows = T <= 64
-  const int key = valid ? e * kWave + lane : kNone;
-  int rank = 0, rexp = 0, cexp = 0;  // rows before mine; of my expert before mine; of my expert
-  for (int j = 0; j < S; ++j) {  // lanes past S hold no slot
-    const int kj = __builtin_amdgcn_readlane(key, j);
-    const bool same = kj != kNone && (kj / kWave) == e;
-    rank += kj < key;
-    rexp += same && kj < key;
-    cexp += same;
-  }
-  const int pos = a.shared_rows + rank;
-  if (valid) {
-    a.row_token[pos] = lane / K;
-    a.inv[lane] = pos;
-    s_tok[rank] = lane / K;
-  } else if (in) {
-    a.inv[lane] = zero ? -2 : -1;
-  }
-  const int h = a.tile_h;
-  const bool start = valid && rexp % h == 0;
-  const uint64_t smask = __ballot(start);
-  int tidx = 0;  // tiles that start before mine
-  for (int j = 0; j < S; ++j) {
-    const int kj = __builtin_amdgcn_readlane(key, j);
-    tidx += ((smask >> j) & 1) && kj < key;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  if (start) {
-    Tile tl;
-    tl.group = e;
-    tl.row0 = pos;
-    tl.count = min(h, cexp - rexp);
-    tl.pad = 0;
-#pragma unroll
-    for (int q = 0; q < kTileTok; ++q)
-      tl.tok[q] = (h <= kTileTok && q < tl.count) ? s_tok[rank + q] : 0;
-    a.tiles[tidx] = tl;
-  }
-  int errbits = err;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) errbits |= __shfl_xor(errbits, m, kWave);
-  if (lane == 0) {
-    a.ntiles[0] = __popcll(smask);
-    a.err_word[0] = errbits;
-  }
-}
-
 // Dispatch of at most NW * 64 slots and EMAX experts by one block of NW waves (one thread
 // per slot and per expert), for ids already in LDS: the same row space, tile list and error bits as
 // dispatch_body, from a bitmap of the slots of each expert (s_mask[e * W + w], bit b =

@@ -332,12 +332,12 @@ def test_layer_without_residual_and_experts_entry(path):
     assert torch.equal(out, out2)
 
 
-@pytest.mark.parametrize("tokens", [1, 2])
-def test_experts_entry_one_wave_dispatch(tokens):
-    """moe_experts_forward builds its own dispatch (at most 16 slots: the one-wave build from
-    pairwise ranks); the layer's fused top-K uses the bitmap build. Same rows, same tiles:
-    bit-identical outputs."""
-    _announce("experts entry, one-wave dispatch", tokens)
+@pytest.mark.parametrize("tokens", [1, 2, 16])
+def test_experts_entry_own_dispatch(tokens):
+    """moe_experts_forward builds its own dispatch from the ids in memory (the standalone
+    dispatch kernel); the layer's fused top-K builds it from ids in LDS. Same rows, same
+    tiles: bit-identical outputs."""
+    _announce("experts entry, standalone dispatch", tokens)
     inp = S.make_inputs(S.scaled(SMALL["qwen3_decode_t8"], tokens=tokens), device=DEV)
     out, logits, ids, w, ws = run_layer(inp, path=M.PATH_DECODE, residual=False)
     cfg = config_for(inp, M.PATH_DECODE)

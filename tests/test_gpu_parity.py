@@ -294,6 +294,14 @@ SMALL = {
     # 40 tokens on the decode path: the shared expert's implicit list of ten 4-token tiles
     "dsv3_t40_mini": S.scaled(S.WORKLOADS["dsv3_decode_t32"], tokens=40, hidden=1024,
                               experts=64, inter=256, shared_inter=192),
+    # the library's limits, 1024 experts and 32 slots per token: 96 slots (the bitmap
+    # dispatch, two words per expert) and 1280 slots (the block counting sort)
+    "max_e1024_k32_t3": S.LayerSpec(name="max_e1024_k32_t3", tokens=3, hidden=256,
+                                    experts=1024, top_k=32, inter=64, fmt=S.NVFP4,
+                                    renormalize=True, seed=1086),
+    "max_e1024_k32_t40": S.LayerSpec(name="max_e1024_k32_t40", tokens=40, hidden=256,
+                                     experts=1024, top_k=32, inter=64, fmt=S.MXFP4,
+                                     renormalize=False, seed=1087),
     # softmax+bias routing over 48 + 16 zero-computation experts (identity contributions)
     "zero_experts_mini": S.LayerSpec(name="zero_experts_mini", tokens=23, hidden=512,
                                      experts=48, top_k=8, inter=256, fmt=S.NVFP4,

@@ -598,9 +598,11 @@ static hipError_t launch_pre_shape(const ExpertGemmArgs& a, hipStream_t s) {
 // Tile height MT -> stage width KC and block shape (row blocks per wave RB, waves along M
 // WM, column blocks per wave CB): FP4 128 = 64-code stages, 4 x 1 x 2 (128 x 256 weight
 // rows; each wave all 128 rows, so a decoded B operand feeds four MFMAs); FP4 64 = 64-code
-// stages, 2 x 1 x 2 (64 x 256); 32 = 128-code stages, 1 x 1 x 4 (32 x 512). K that is not a multiple of 128 takes 64-code stages at height 32 too. The
-// shared expert's implicit list at height 32 with fewer than 512 blocks takes 32 x 256
-// (1 x 1 x 2: 80 KB of LDS, two blocks per CU) for twice the blocks.
+// stages, 2 x 1 x 2 (64 x 256); FP4 32 = 128-code stages, 1 x 1 x 2 (32 x 256). A 128-code
+// stage reads half of each weight row's 128-byte line, the next stage the other half: 256
+// weight rows per block keep the lines that the blocks of an XCD have open within its L2
+// (512 rows filled it and lines were fetched twice). K that is not a multiple of 128 takes
+// 64-code stages, 1 x 1 x 4 (32 x 512), at height 32.
 #ifndef MOE_PRE_NSTG
 #define MOE_PRE_NSTG 3
 #endif
@@ -610,22 +612,16 @@ static hipError_t launch_pre(const ExpertGemmArgs& a, int mt, hipStream_t s) {
   const int fmt = GATEUP ? a.gate.fmt : a.down.fmt;
   const int K = GATEUP ? a.H : a.I;
   constexpr int NS3 = MOE_PRE_NSTG;
-  // the implicit list (the shared expert) of few row tiles: half-width column tiles,
-  // twice the blocks
-  const bool narrow = a.src.tiles == nullptr && mt == 32 && K % 128 == 0 &&
-                      a.tile_bound * ((GATEUP ? a.I : a.H) / 256) < 512;
   if (fmt == 0) {
     if (mt == 32) {
-      if (narrow) return launch_pre_shape<0, 128, 3, 1, 1, 2, GATEUP>(a, s);
-      return K % 128 == 0 ? launch_pre_shape<0, 128, 3, 1, 1, 4, GATEUP>(a, s)
+      return K % 128 == 0 ? launch_pre_shape<0, 128, 3, 1, 1, 2, GATEUP>(a, s)
                           : launch_pre_shape<0, 64, 3, 1, 1, 4, GATEUP>(a, s);
     }
     if (mt == 64) return launch_pre_shape<0, 64, 3, 2, 1, 2, GATEUP>(a, s);
     return launch_pre_shape<0, 64, NS3, 4, 1, 2, GATEUP>(a, s);
   }
   if (mt == 32 && fmt == 1) {
-    if (narrow) return launch_pre_shape<1, 128, 3, 1, 1, 2, GATEUP>(a, s);
-    return K % 128 == 0 ? launch_pre_shape<1, 128, 3, 1, 1, 4, GATEUP>(a, s)
+    return K % 128 == 0 ? launch_pre_shape<1, 128, 3, 1, 1, 2, GATEUP>(a, s)
                         : launch_pre_shape<1, 64, 3, 1, 1, 4, GATEUP>(a, s);
   }
   if (fmt == 1) {

@@ -113,23 +113,26 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
   f64x4_t acc[MF];
 #pragma unroll
   for (int m = 0; m < MF; ++m) acc[m] = f64x4_t{0.0, 0.0, 0.0, 0.0};
-  // the operands of the wave's next 32-wide chunk are loaded while the current chunk's
-  // MFMAs run
+  // the operands of the wave's next two 32-wide chunks are in flight while the current
+  // chunk's MFMAs run (one chunk ahead is shorter than a loaded HBM round trip)
   const int kstart = kb + 32 * wave;
-  uint4 wv = make_uint4(0, 0, 0, 0), xv[MF];
+  uint4 wv = make_uint4(0, 0, 0, 0), xv[MF], w1 = wv, x1[MF];
 #pragma unroll
-  for (int m = 0; m < MF; ++m) xv[m] = make_uint4(0, 0, 0, 0);
-  // (unconditional loads: rows past T read row 0 and are zeroed after the load; the last
-  // prefetch re-reads the current chunk)
+  for (int m = 0; m < MF; ++m) xv[m] = x1[m] = make_uint4(0, 0, 0, 0);
+  // (unconditional loads: rows past T read row 0 and are zeroed after the load; the
+  // prefetches past the slice re-read the current chunk)
   auto load = [&](int k0, uint4& w_, uint4 (&x_)[MF]) {
     w_ = *reinterpret_cast<const uint4*>(wrow + k0);
 #pragma unroll
     for (int m = 0; m < MF; ++m) x_[m] = *reinterpret_cast<const uint4*>(xrow[m] + k0);
   };
-  if (kstart < ke) load(kstart, wv, xv);
+  if (kstart < ke) {
+    load(kstart, wv, xv);
+    load(kstart + 128 < ke ? kstart + 128 : kstart, w1, x1);
+  }
   for (int k0 = kstart; k0 < ke; k0 += 128) {
     uint4 wn, xn[MF];
-    load(k0 + 128 < ke ? k0 + 128 : k0, wn, xn);
+    load(k0 + 256 < ke ? k0 + 256 : k0, wn, xn);
     double wd[8];
     bf16x8_to_f64(wv, wd);
     double xd[MF][8];
@@ -143,9 +146,13 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
 #pragma unroll
       for (int m = 0; m < MF; ++m)
         acc[m] = __builtin_amdgcn_mfma_f64_16x16x4f64(xd[m][st], wd[st], acc[m], 0, 0, 0);
-    wv = wn;
+    wv = w1;
+    w1 = wn;
 #pragma unroll
-    for (int m = 0; m < MF; ++m) xv[m] = xn[m];
+    for (int m = 0; m < MF; ++m) {
+      xv[m] = x1[m];
+      x1[m] = xn[m];
+    }
   }
   if (wave > 0) {
 #pragma unroll

@@ -533,18 +533,20 @@ static void launch_dn(const ExpertGemmArgs& a, int rpw, hipStream_t s) {
 // weights at once and there is nothing to pipeline. The tile's tokens are then taken one
 // after the other against the weights held in registers, their sums kept in registers
 // and stored after the token loop; register use does not grow with the tile's tokens
-// and stays within 128 VGPRs, so four waves share each SIMD.
+// and stays within 64 VGPRs, so eight waves share each SIMD: 4 KB of weights per wave
+// (4/M rows per lane and matrix) in twice as many waves turns over finer than 8 KB in
+// four.
 template <int LPR, int M>
 struct OneShape {
   static constexpr int G = kWave / LPR;                 // row groups per wave
-  static constexpr int NI = (LPR < 8 ? LPR : 8) / M;    // rows per lane and matrix
+  static constexpr int NI = (LPR < 4 ? LPR : 4) / M;    // rows per lane and matrix
   static constexpr int GR = G * NI;                     // rows per wave
   static constexpr int NV = NI * M;                     // sums per lane before the reduction
   static_assert(NV <= LPR, "one reduced value per lane expected");
 };
 
 template <int FMT, int LPR, int M>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_one(ExpertGemmArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k_dec_one(ExpertGemmArgs a) {
   using SH = OneShape<LPR, M>;
   constexpr int G = SH::G, NI = SH::NI, GR = SH::GR, NV = SH::NV;
   constexpr int XW = DecFmt<FMT>::XW, CPC = DecFmt<FMT>::CPC;

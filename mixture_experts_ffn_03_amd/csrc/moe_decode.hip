@@ -533,21 +533,23 @@ static void launch_dn(const ExpertGemmArgs& a, int rpw, hipStream_t s) {
 // weights at once and there is nothing to pipeline. The tile's tokens are then taken one
 // after the other against the weights held in registers, their sums kept in registers
 // and stored after the token loop; register use does not grow with the tile's tokens
-// and stays within 64 VGPRs, so eight waves share each SIMD: 4 KB of weights per wave
-// (4/M rows per lane and matrix) in twice as many waves turns over finer than 8 KB in
-// four.
-template <int LPR, int M>
+// and stays within 64 VGPRs at ROWS = 4 (4/M rows per lane and matrix, 4 KB of weights
+// per wave), so eight waves share each SIMD (five for MXFP4, whose scale decode needs more
+// registers): they turn over finer than 8 KB waves in four.
+// Grids of very many blocks (down projections onto a wide hidden size) take ROWS = 8:
+// 8 KB per wave, four waves per SIMD, half the blocks.
+template <int LPR, int M, int ROWS>
 struct OneShape {
   static constexpr int G = kWave / LPR;                 // row groups per wave
-  static constexpr int NI = (LPR < 4 ? LPR : 4) / M;    // rows per lane and matrix
+  static constexpr int NI = (LPR < ROWS ? LPR : ROWS) / M;  // rows per lane and matrix
   static constexpr int GR = G * NI;                     // rows per wave
   static constexpr int NV = NI * M;                     // sums per lane before the reduction
   static_assert(NV <= LPR, "one reduced value per lane expected");
 };
 
-template <int FMT, int LPR, int M>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k_dec_one(ExpertGemmArgs a) {
-  using SH = OneShape<LPR, M>;
+template <int FMT, int LPR, int M, int ROWS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ROWS == 4 ? (FMT == 0 ? 8 : 5) : 4))) void k_dec_one(ExpertGemmArgs a) {
+  using SH = OneShape<LPR, M, ROWS>;
   constexpr int G = SH::G, NI = SH::NI, GR = SH::GR, NV = SH::NV;
   constexpr int XW = DecFmt<FMT>::XW, CPC = DecFmt<FMT>::CPC;
   Tile tile;
@@ -654,27 +656,38 @@ static bool one_fits(int fmt, int K, int tile_h) {
   return fmt <= 1 && K / 32 <= 64 && tile_h <= kTileTok;
 }
 
-template <int FMT, int LPR, int M>
+template <int FMT, int LPR, int M, int ROWS>
 static hipError_t launch_one_t(const ExpertGemmArgs& a, hipStream_t s) {
   const int N = M == 2 ? a.I : a.H;
-  const int rows = kDecWaves * OneShape<LPR, M>::GR;
-  hipLaunchKernelGGL((k_dec_one<FMT, LPR, M>), dim3((N + rows - 1) / rows, a.tile_bound), dim3(256), 0,
-                     s, a);
+  const int rows = kDecWaves * OneShape<LPR, M, ROWS>::GR;
+  hipLaunchKernelGGL((k_dec_one<FMT, LPR, M, ROWS>), dim3((N + rows - 1) / rows, a.tile_bound),
+                     dim3(256), 0, s, a);
   return hipGetLastError();
 }
+
+// Down projections onto at least this many outputs per expert run 8 KB waves (ROWS = 8):
+// DeepSeek-V3-like H = 7168 at 32 tokens, about 204 vs 220 us with 4 KB waves; Qwen3-like
+// H = 2048 at 8 tokens, 13.4 vs 13.9 us the other way.
+constexpr int kOneWideMinN = 4096;
 
 template <int M>
 static hipError_t launch_one(const ExpertGemmArgs& a, int fmt, int K, hipStream_t s) {
   const int lpr = one_lanes(K / 32);
-#define MOE_ONE_LPR(FMT)                                    \
-  switch (lpr) {                                            \
-    case 8: return launch_one_t<FMT, 8, M>(a, s);           \
-    case 16: return launch_one_t<FMT, 16, M>(a, s);         \
-    case 32: return launch_one_t<FMT, 32, M>(a, s);         \
-    default: return launch_one_t<FMT, 64, M>(a, s);         \
+#define MOE_ONE_LPR(FMT, ROWS)                                    \
+  switch (lpr) {                                                  \
+    case 8: return launch_one_t<FMT, 8, M, ROWS>(a, s);           \
+    case 16: return launch_one_t<FMT, 16, M, ROWS>(a, s);         \
+    case 32: return launch_one_t<FMT, 32, M, ROWS>(a, s);         \
+    default: return launch_one_t<FMT, 64, M, ROWS>(a, s);         \
   }
-  if (fmt == 0) { MOE_ONE_LPR(0) }
-  MOE_ONE_LPR(1)
+  if constexpr (M == 1) {
+    if (a.H >= kOneWideMinN) {
+      if (fmt == 0) { MOE_ONE_LPR(0, 8) }
+      MOE_ONE_LPR(1, 8)
+    }
+  }
+  if (fmt == 0) { MOE_ONE_LPR(0, 4) }
+  MOE_ONE_LPR(1, 4)
 #undef MOE_ONE_LPR
 }
 

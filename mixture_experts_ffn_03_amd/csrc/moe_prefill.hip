@@ -598,11 +598,9 @@ static hipError_t launch_pre_shape(const ExpertGemmArgs& a, hipStream_t s) {
 // Tile height MT -> stage width KC and block shape (row blocks per wave RB, waves along M
 // WM, column blocks per wave CB): FP4 128 = 64-code stages, 4 x 1 x 2 (128 x 256 weight
 // rows; each wave all 128 rows, so a decoded B operand feeds four MFMAs); FP4 64 = 64-code
-// stages, 2 x 1 x 2 (64 x 256); FP4 32 = 128-code stages, 1 x 1 x 2 (32 x 256). A 128-code
-// stage reads half of each weight row's 128-byte line, the next stage the other half: 256
-// weight rows per block keep the lines that the blocks of an XCD have open within its L2
-// (512 rows filled it and lines were fetched twice). K that is not a multiple of 128 takes
-// 64-code stages, 1 x 1 x 4 (32 x 512), at height 32.
+// stages, 2 x 1 x 2 (64 x 256); FP4 32 = 128-code stages, 1 x 1 x 2 (32 x 256: twice the
+// blocks of 32 x 512, which balanced worse). K that is not a multiple of 128 takes 64-code
+// stages, 1 x 1 x 4 (32 x 512), at height 32.
 #ifndef MOE_PRE_NSTG
 #define MOE_PRE_NSTG 3
 #endif

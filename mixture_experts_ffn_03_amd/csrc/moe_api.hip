@@ -31,7 +31,15 @@ struct Layout {
   int tile_bound_dec, tile_bound_pre;
 };
 
-int tile_bound(int S, int E, int h) { return S / h + (S < E ? S : E) + 1; }
+// Tiles of at most h rows over S rows in at most min(S, E) groups: at most S / h + one
+// partial tile per group, and at most S (a tile holds a row). The decode grids have this
+// many tile columns; the ones past the device's count exit at once (Qwen3-like decode at
+// 8 tokens: 64 columns instead of 81; measured within noise, at most ~0.5 us per kernel).
+int tile_bound(int S, int E, int h) {
+  const int b = S / h + (S < E ? S : E) + 1;
+  const int m = b < S ? b : S;
+  return m > 1 ? m : 1;
+}
 
 // Prefill M-tile height from the mean rows per routed expert.
 int prefill_mt(const moe_config& c) {

@@ -48,7 +48,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = -1, /* null pointer, bad dimension, misaligned pointer, bad mode */
-  MOE_ERR_UNSUPPORTED = -2, /* valid request outside this build's limits (sizes, path) */
+  MOE_ERR_UNSUPPORTED = -2, /* valid request outside the library's limits (sizes, path) */
   MOE_ERR_WORKSPACE = -3,   /* workspace null or smaller than moe_workspace_size */
   MOE_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
   MOE_ERR_FORMAT = -5       /* weight format tag unknown or inconsistent with its scales;

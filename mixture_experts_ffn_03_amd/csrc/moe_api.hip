@@ -390,7 +390,7 @@ const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "MOE_OK";
     case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
-    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: outside this build's limits";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: outside the library's limits";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime or launch failure";
     case MOE_ERR_FORMAT: return "MOE_ERR_FORMAT: weight format tag inconsistent with its scales";

@@ -294,6 +294,18 @@ SMALL = {
     # 40 tokens on the decode path: the shared expert's implicit list of ten 4-token tiles
     "dsv3_t40_mini": S.scaled(S.WORKLOADS["dsv3_decode_t32"], tokens=40, hidden=1024,
                               experts=64, inter=256, shared_inter=192),
+    # a shared expert of the routed format and sizes: multi-step decode gate+up at hidden
+    # 2304 with a ragged last shared tile; one-step kernels with MXFP4 everywhere and ten
+    # shared tiles
+    "shared_merged_nv": S.LayerSpec(name="shared_merged_nv", tokens=13, hidden=2304,
+                                    experts=32, top_k=4, inter=256, fmt=S.NVFP4,
+                                    score=S.SIGMOID, renormalize=True, correction_bias=True,
+                                    shared=True, shared_inter=256, shared_fmt=S.NVFP4,
+                                    seed=1088),
+    "shared_merged_mx": S.LayerSpec(name="shared_merged_mx", tokens=40, hidden=1024,
+                                    experts=64, top_k=6, inter=192, fmt=S.MXFP4,
+                                    score=S.SOFTMAX, renormalize=False, shared=True,
+                                    shared_inter=192, shared_fmt=S.MXFP4, seed=1089),
     # the library's limits, 1024 experts and 32 slots per token: 96 slots (the bitmap
     # dispatch, two words per expert) and 1280 slots (the block counting sort)
     "max_e1024_k32_t3": S.LayerSpec(name="max_e1024_k32_t3", tokens=3, hidden=256,

@@ -9,17 +9,22 @@ Prints ONE JSON line on stdout (logs go to stderr):
              HIP events recorded on the kernel's own stream during the timed steps
   cpu_baseline  the CPU oracle timed on the host on a bounded sample of the workload
 
-The default workload is the Qwen3-30B-A3B-like decode layer at 8 tokens; --workload
-selects the others. Steps cycle through several weight sets and input batches so
-that weights are streamed from HBM rather than re-read from the 256 MB Infinity Cache.
+The default workload is the 4096-token prefill layer with Zipf-skewed expert loads (hidden
+4096, 64 MXFP4 experts, top-6); --workload selects the others. With the default workload
+the line also carries a compact entry per other workload ("other_workloads": step time,
+tokens/s, the dominant kernel's roofline fraction). Steps cycle through several weight
+sets and input batches so that weights are streamed from HBM rather than re-read from
+the 256 MB Infinity Cache.
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import gc
 import hashlib
 import json
 import os
+import platform
 import re
 import sys
 import time
@@ -252,6 +257,24 @@ def summarize_traffic(d, workload, path, commands):
     return out
 
 
+DEFAULT_WORKLOAD = "prefill_zipf_t4096"
+
+
+def host_cpu():
+    """(logical CPUs this process may run on, CPU model string)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, model
+
+
 def cpu_baseline(spec, inp, name, seconds):
     import numpy as np
     import oracle as O
@@ -287,72 +310,23 @@ def cpu_baseline(spec, inp, name, seconds):
         if el >= seconds:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    nproc, model = host_cpu()
     return {"value": round(done * n_rows / el, 4), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "host_nproc": nproc, "cpu_model": model,
             "sample": f"{done} oracle evaluation(s) of {n_rows} token(s) of one batch of the "
-                      f"same workload (numpy fp64, BLAS threads={threads}, {el:.1f} s)"}
+                      f"same workload ({el:.1f} s; numpy fp64: matrix products on {threads} "
+                      f"BLAS threads, weight decoding on one thread; host: {nproc} logical "
+                      f"CPUs, {model})"}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="qwen3_decode_t8", choices=sorted(DESCRIPTIONS))
-    ap.add_argument("--tokens", type=int, default=0,
-                    help="run the workload's layer at this many tokens (e.g. 2 or 3 for a "
-                         "multi-token verify step); 0 = the workload's own")
-    ap.add_argument("--weight-sets", type=int, default=0, help="0 = workload default")
-    ap.add_argument("--batches", type=int, default=8)
-    ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="skip the HIP-graph replay timing (decode layers of at most 32 tokens)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run 8 device-to-device copies of 1 GiB (a copy kernel of known "
-                         "size, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
-    ap.add_argument("--summarize-trace", metavar="DIR",
-                    help="print a kernel table of a rocprofv3 --stats csv output dir and exit")
-    ap.add_argument("--summarize-traffic", metavar="DIR",
-                    help="write the workload's HBM traffic file from rocprofv3 --pmc runs in "
-                         "DIR/{fetch,write,copy_fetch,copy_write} and exit")
-    ap.add_argument("--command", action="append", default=[],
-                    help="command line recorded in a summary (repeatable)")
-    args = ap.parse_args()
-    if args.summarize_trace:
-        print(summarize_trace(args.summarize_trace, " ; ".join(args.command)), end="")
-        return
-    if args.summarize_traffic:
-        path = "prefill" if args.workload in ("prefill_zipf_t4096", "hash_mxfp4_t512") \
-            else "decode"
-        print(summarize_traffic(args.summarize_traffic, args.workload, path, args.command))
-        return
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        if int(os.environ.get("RANK", "0")) == 0:
-            print(f"bench.py measures one GPU only: the library has no multi-GPU path "
-                  f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
-        sys.exit(2)
-
+def run_workload(name, args, with_cpu=True, with_graph=True, steps=None, warmup=None):
+    """Time `steps` layer calls of one workload; returns the result dict of the JSON line."""
     import torch
     import moe_synth as S
     import mixture_experts_ffn_03_amd as M
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    if args.copy_calibration:
-        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(8):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log("[bench] copy calibration: 8 copies of 1073741824 bytes")
-        return
-    M.load_library()
-    name = args.workload
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     spec = S.WORKLOADS[name]
     if args.tokens > 0:
         spec = S.scaled(spec, tokens=args.tokens)
@@ -399,9 +373,9 @@ def main():
     hip = HipEvents()
     nst = M.STAGE_COUNT
     # instrumented pass (untimed): every stage boundary, to find the dominant kernel
-    prof_steps = max(8, min(args.warmup, 64))
+    prof_steps = max(8, min(warmup, 64))
     evs = [[hip.create() for _ in range(nst)] for _ in range(prof_steps)]
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     arrs = []
@@ -422,22 +396,22 @@ def main():
     ks = M.STAGE_NAMES.index(kernel_stage)
 
     # timed steps: HIP events around the dominant kernel only (on the layer's stream)
-    kev = [(hip.create(), hip.create()) for _ in range(args.steps)]
+    kev = [(hip.create(), hip.create()) for _ in range(steps)]
     karrs = []
-    for i in range(args.steps):
+    for i in range(steps):
         arr = (ctypes.c_void_p * nst)()
         arr[ks - 1], arr[ks] = kev[i]
         karrs.append(arr)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for i in range(args.steps):
+    for i in range(steps):
         M.set_stage_events(karrs[i], nst)
-        step(args.warmup + i)
+        step(warmup + i)
     end.record()
     torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / args.steps
-    kernel_ms = sum(hip.elapsed_ms(a, b) for a, b in kev) / args.steps
+    ms_per_step = start.elapsed_time(end) / steps
+    kernel_ms = sum(hip.elapsed_ms(a, b) for a, b in kev) / steps
     for a, b in kev:
         hip.destroy(a)
         hip.destroy(b)
@@ -454,7 +428,7 @@ def main():
     # set and batch once), for decode layers of at most 32 tokens: launch gaps without the
     # host in the loop
     graph_replay = None
-    if decode and T <= 32 and not args.no_graph:
+    if decode and T <= 32 and with_graph and not args.no_graph:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -468,7 +442,7 @@ def main():
                 step(i)
         graph.replay()
         torch.cuda.synchronize()
-        reps = max(1, args.steps // period)
+        reps = max(1, steps // period)
         start.record()
         for _ in range(reps):
             graph.replay()
@@ -481,17 +455,17 @@ def main():
                         "steps": reps * period, "steps_per_replay": period}
         del graph
 
-    u_mean = sum(uniq[(args.warmup + i) % period] for i in range(args.steps)) / args.steps
+    u_mean = sum(uniq[(warmup + i) % period] for i in range(steps)) / steps
     bpe = bytes_per_elem(spec.fmt)
     # algorithmic work of the dominant kernel per launch: each touched expert's weights
-    # once, its input activations and its output rows; flops of the routed rows
+    # once, its input activations and its output rows (y in fp32); flops of the routed rows
     if kernel_stage == "gate_up":
         kbytes = u_mean * 2 * I * H * bpe + T * H * 2 + S_rows * I * 2
         kflops = 2 * S_rows * H * 2 * I
         unit_bytes = "2*I*H*b bytes per touched expert (b = 0.5625 NVFP4, 0.53125 MXFP4) + x in + h out"
         unit_flops = "4*H*I flops per routed row"
     else:
-        kbytes = u_mean * I * H * bpe + S_rows * I * 2 + S_rows * H * (4 if decode else 2)
+        kbytes = u_mean * I * H * bpe + S_rows * I * 2 + S_rows * H * 4
         kflops = 2 * S_rows * H * I
         unit_bytes = "I*H*b bytes per touched expert + h in + y out"
         unit_flops = "2*H*I flops per routed row"
@@ -507,7 +481,7 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4)}
         per_launch, unit_note = kflops, unit_flops
     kname = f"{'decode' if decode else 'prefill'}_{kernel_stage}"
-    roof["traffic"] = load_traffic(name, kname)
+    roof["traffic"] = load_traffic(name, kname) if args.tokens <= 0 else None
     roof["kernel"] = kname
     roof["kernel_ms"] = round(kernel_ms, 5)
     roof["per_launch"] = per_launch
@@ -519,10 +493,11 @@ def main():
     layer_bytes = u_mean * 3 * H * I * bpe + shared_bytes + E * H * 2 + 3 * T * H * 2
     layer_flops = T * K * 6 * H * I + (T * 6 * H * spec.shared_inter if spec.shared else 0) + 2 * T * H * E
     tokens_per_s = T / (ms_per_step * 1e-3)
+    layer_s = ms_per_step * 1e-3
 
     result = {
         "metric": METRIC, "value": round(tokens_per_s, 2), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "weights": ["nvfp4", "mxfp4", "fp8", "bf16"][spec.fmt],
         "data": "synthetic (seeded; random-init FP4 weights, N(0,1) bf16 activations)",
@@ -530,17 +505,110 @@ def main():
                    "hidden": H, "experts": E, "top_k": K, "inter": I,
                    "path": "decode" if decode else "prefill", "weight_sets": nsets,
                    "input_batches": args.batches, "unique_experts_mean": round(u_mean, 2)},
-        "layer": {"GB_per_s": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-                  "TFLOP_per_s": round(layer_flops / (ms_per_step * 1e-3) / 1e12, 2),
-                  "hbm_frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "layer": {"GB_per_s": round(layer_bytes / layer_s / 1e9, 1),
+                  "TFLOP_per_s": round(layer_flops / layer_s / 1e12, 2),
+                  "hbm_frac": round(layer_bytes / layer_s / 1e9 / HBM_PEAK_GBS, 4),
+                  "mfma_frac": round(layer_flops / layer_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                   "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()}},
         "roofline": roof,
     }
     if graph_replay is not None:
         result["graph_replay"] = graph_replay
-    if not args.no_cpu_baseline:
+    if with_cpu and not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle for about {args.cpu_seconds:.0f} s")
         result["cpu_baseline"] = cpu_baseline(spec, sets[0], name, args.cpu_seconds)
+    del sets, batches, routed, shared, ws, out, ids
+    gc.collect()
+    torch.cuda.empty_cache()
+    return result
+
+
+def brief(r):
+    """The compact entry of a workload in "other_workloads"."""
+    roof = r["roofline"]
+    b = {"ms_per_step": r["ms_per_step"], "value": r["value"], "unit": r["unit"],
+         "path": r["config"]["path"],
+         "roofline": {k: roof[k] for k in ("kernel", "bound", "achieved", "unit", "frac",
+                                           "kernel_ms")},
+         "layer": {k: r["layer"][k] for k in ("hbm_frac", "mfma_frac", "stage_ms")}}
+    if "graph_replay" in r:
+        b["graph_replay_ms_per_step"] = r["graph_replay"]["ms_per_step"]
+    return b
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="run the workload's layer at this many tokens (e.g. 2 or 3 for a "
+                         "multi-token verify step); 0 = the workload's own")
+    ap.add_argument("--weight-sets", type=int, default=0, help="0 = workload default")
+    ap.add_argument("--batches", type=int, default=8)
+    ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="with the default workload, skip the entries of the other workloads")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay timing (decode layers of at most 32 tokens)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--lib", default=None,
+                    help="path of the HIP library to load (default: the package's in-tree build)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 8 device-to-device copies of 1 GiB (a copy kernel of known "
+                         "size, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a kernel table of a rocprofv3 --stats csv output dir and exit")
+    ap.add_argument("--summarize-traffic", metavar="DIR",
+                    help="write the workload's HBM traffic file from rocprofv3 --pmc runs in "
+                         "DIR/{fetch,write,copy_fetch,copy_write} and exit")
+    ap.add_argument("--command", action="append", default=[],
+                    help="command line recorded in a summary (repeatable)")
+    args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, " ; ".join(args.command)), end="")
+        return
+    if args.summarize_traffic:
+        path = "prefill" if args.workload in ("prefill_zipf_t4096", "hash_mxfp4_t512") \
+            else "decode"
+        print(summarize_traffic(args.summarize_traffic, args.workload, path, args.command))
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print(f"bench.py measures one GPU only: the library has no multi-GPU path "
+                  f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mixture_experts_ffn_03_amd as M
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 8 copies of 1073741824 bytes")
+        return
+    if args.lib:
+        M.load_library(args.lib)
+    else:
+        M.load_library()
+    result = run_workload(args.workload, args)
+    if args.workload == DEFAULT_WORKLOAD and args.tokens <= 0 and not args.no_others:
+        others = {}
+        for name in ("qwen3_decode_t1", "qwen3_decode_t8", "dsv3_decode_t32",
+                     "hash_mxfp4_t512"):
+            others[name] = brief(run_workload(name, args, with_cpu=False))
+            log(f"[bench] {name}: {others[name]['ms_per_step']} ms/step")
+        result["other_workloads"] = others
     print(json.dumps(result), flush=True)
 
 

@@ -172,7 +172,12 @@ typedef struct {
 const char* moe_status_string(int status);
 
 /* Bytes of workspace that moe_route / moe_experts_forward / moe_layer_forward need for
- * `cfg` (host; pure function of the config). One workspace serves all three calls. */
+ * `cfg` (host; pure function of the config). One workspace serves all three calls.
+ * The MoE module page keeps the layer's scratch in fixed-size device buffers sized once
+ * at construction so that a captured graph can replay the layer (field docs of
+ * zero_accum_dev and of the routing/dispatch buffers); here the caller owns that memory
+ * and sizes it with this query. Returns MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED for a
+ * config the other calls would reject, else writes *bytes_out (host pointer). */
 int moe_workspace_size(const moe_config* cfg, size_t* bytes_out);
 
 /* Router + top-K selection (constructor page: router GEMM with fp32 output and the
@@ -214,7 +219,12 @@ int moe_experts_forward(const moe_config* cfg, const uint16_t* x_experts,
                         const uint16_t* residual, uint16_t* out, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
 
-/* The whole layer: [RMSNorm] -> router -> top-K -> experts -> blend.
+/* The whole layer: [RMSNorm] -> router -> top-K -> experts -> blend (MoE module page,
+ * module doc: router GEMM, top-K selection, gate+up with SiLU*up, down, then the
+ * routing-weighted sum blended into the residual; doc of pre_expert_norm for the
+ * optional RMSNorm of the expert input). Routing decisions stay on the device; the call
+ * never synchronises with the host (module doc). Errors as for moe_route and
+ * moe_experts_forward; nothing is enqueued when the host checks fail.
  *   norm_gamma bf16 [H] (pre_norm only; 16-byte aligned)
  *   dbg_logits f32 [T, E + Z], dbg_ids int32 [T, top_k], dbg_w f32 [T, top_k]: optional
  *              copies of the routing decisions (NULL to skip)

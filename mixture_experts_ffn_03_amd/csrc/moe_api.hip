@@ -301,8 +301,7 @@ int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const 
   }
   MOE_HIP(marks.mark(MOE_STAGE_SHARED));
   CombineArgs cb{};
-  cb.y = a.y;
-  cb.y_bf16 = pre ? 1 : 0;
+  cb.y = reinterpret_cast<const float*>(a.y);
   cb.xe = xe;
   cb.w = w;
   cb.inv = d.inv;

@@ -4,32 +4,33 @@
 //   out[t] = bf16_rne(residual[t] + sum_j w[t,j] * y[row(t,j)] + y_shared[t])
 // summed in fp32 in the fixed order j = 0..K-1, then the shared expert, then the residual.
 // A zero-computation expert's y is the expert input x_e[t] itself.
-// Each thread produces 8 consecutive outputs with 128-bit stores.
+// y is fp32 [rows, H] on both expert paths. Each thread produces 8 consecutive outputs
+// with 128-bit stores.
 #include "moe_device.h"
 
 namespace moe {
 
-template <bool YBF16>
-__device__ __forceinline__ void load_y8(const void* y, size_t off, float (&v)[8]) {
-  if (YBF16) {
-    const uint4 q = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(y) + off);
-    const uint32_t d[4] = {q.x, q.y, q.z, q.w};
+// 8 consecutive bf16 values -> fp32
+__device__ __forceinline__ void load_bf16x8(const uint16_t* p, float (&v)[8]) {
+  const uint4 q = *reinterpret_cast<const uint4*>(p);
+  const uint32_t d[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_to_f32(d[i] & 0xFFFFu);
-      v[2 * i + 1] = bf16_to_f32(d[i] >> 16);
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(y) + off);
-    const float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32(d[i] & 0xFFFFu);
+    v[2 * i + 1] = bf16_to_f32(d[i] >> 16);
   }
+}
+
+// 8 consecutive fp32 values of y
+__device__ __forceinline__ void load_y8(const float* y, size_t off, float (&v)[8]) {
+  const float4* p = reinterpret_cast<const float4*>(y + off);
+  const float4 a = p[0], b = p[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
 constexpr int kCombineBatch = 8;  // slots whose rows are loaded together
 
-template <bool YBF16>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const int t = blockIdx.y;
   const int h0 = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
@@ -51,10 +52,10 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     float v[kCombineBatch][8];
 #pragma unroll
     for (int jj = 0; jj < kCombineBatch; ++jj)
-      load_y8<YBF16>(a.y, (size_t)(p[jj] >= 0 ? p[jj] : 0) * a.H + h0, v[jj]);
+      load_y8(a.y, (size_t)(p[jj] >= 0 ? p[jj] : 0) * a.H + h0, v[jj]);
 #pragma unroll
     for (int jj = 0; jj < kCombineBatch; ++jj) {
-      if (p[jj] == -2) load_y8<true>(a.xe, (size_t)t * a.H + h0, v[jj]);  // zero expert: x_e[t]
+      if (p[jj] == -2) load_bf16x8(a.xe + (size_t)t * a.H + h0, v[jj]);  // zero expert: x_e[t]
       if (p[jj] >= 0 || p[jj] == -2) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[jj], v[jj][i], acc[i]);
@@ -63,18 +64,15 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   }
   if (a.shared) {
     float v[8];
-    load_y8<YBF16>(a.y, (size_t)t * a.H + h0, v);
+    load_y8(a.y, (size_t)t * a.H + h0, v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += v[i];
   }
   if (a.residual) {
-    const uint4 q = *reinterpret_cast<const uint4*>(a.residual + (size_t)t * a.H + h0);
-    const uint32_t d[4] = {q.x, q.y, q.z, q.w};
+    float v[8];
+    load_bf16x8(a.residual + (size_t)t * a.H + h0, v);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += bf16_to_f32(d[i] & 0xFFFFu);
-      acc[2 * i + 1] += bf16_to_f32(d[i] >> 16);
-    }
+    for (int i = 0; i < 8; ++i) acc[i] += v[i];
   }
   uint4 o;
   o.x = pack_bf16x2(acc[0], acc[1]);
@@ -87,8 +85,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const dim3 grid((a.H / 8 + 255) / 256, a.T);
-  if (a.y_bf16) hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

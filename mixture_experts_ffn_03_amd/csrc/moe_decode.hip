@@ -492,39 +492,45 @@ static int pick_rows_per_wave(int base, int n, int tile_bound) {
   return base * m;
 }
 
-// LDS for the staged activations: kTileTok rows of K bf16 (beyond 64 KB the kernel's
-// limit is raised once per instantiation; the host caps K so that it fits 160 KB).
-static hipError_t raise_lds(const void* kern, size_t smem, bool& done) {
-  if (smem <= 65536 || done) return hipSuccess;
-  const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  if (e == hipSuccess) done = true;
-  return e;
+// LDS for the staged activations: kTileTok rows of K bf16. Launches beyond 64 KB need the
+// kernel's dynamic-LDS limit raised; it is raised once per instantiation straight to the
+// largest size the host lets through (kDecodeMaxLds), so a later call with a longer row
+// never exceeds it. The function-local static makes the one call thread-safe.
+static hipError_t raise_lds(const void* kern) {
+  static_assert(kDecodeMaxLds <= 160 * 1024, "a CU has 160 KB of LDS");
+  return hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kDecodeMaxLds);
 }
 
 template <int FMT, int LPR>
-static void launch_gu(const ExpertGemmArgs& a, int rpw, hipStream_t s) {
+static hipError_t launch_gu(const ExpertGemmArgs& a, int rpw, hipStream_t s) {
   const dim3 grid((a.I + kDecWaves * rpw - 1) / (kDecWaves * rpw), a.tile_bound);
   const size_t smem = (size_t)kTileTok * a.H * sizeof(uint16_t);
-  static bool raised = false;
-  if (raise_lds(reinterpret_cast<const void*>(k_dec_gate_up<FMT, LPR>), smem, raised) != hipSuccess) return;
+  if (smem > 65536) {
+    static const hipError_t raised = raise_lds(reinterpret_cast<const void*>(k_dec_gate_up<FMT, LPR>));
+    if (raised != hipSuccess) return raised;
+  }
   hipLaunchKernelGGL((k_dec_gate_up<FMT, LPR>), grid, dim3(256), smem, s, a, rpw);
+  return hipGetLastError();
 }
 
 template <int FMT, int LPR>
-static void launch_dn(const ExpertGemmArgs& a, int rpw, hipStream_t s) {
+static hipError_t launch_dn(const ExpertGemmArgs& a, int rpw, hipStream_t s) {
   const dim3 grid((a.H + kDecWaves * rpw - 1) / (kDecWaves * rpw), a.tile_bound);
   const size_t smem = (size_t)kTileTok * a.I * sizeof(uint16_t);
-  static bool raised = false;
-  if (raise_lds(reinterpret_cast<const void*>(k_dec_down<FMT, LPR>), smem, raised) != hipSuccess) return;
+  if (smem > 65536) {
+    static const hipError_t raised = raise_lds(reinterpret_cast<const void*>(k_dec_down<FMT, LPR>));
+    if (raised != hipSuccess) return raised;
+  }
   hipLaunchKernelGGL((k_dec_down<FMT, LPR>), grid, dim3(256), smem, s, a, rpw);
+  return hipGetLastError();
 }
 
 #define MOE_DISPATCH_LPR(LAUNCH, FMT, LPR, A, RPW, S)     \
   switch (LPR) {                                          \
-    case 64: LAUNCH<FMT, 64>(A, RPW, S); break;           \
-    case 32: LAUNCH<FMT, 32>(A, RPW, S); break;           \
-    case 16: LAUNCH<FMT, 16>(A, RPW, S); break;           \
-    default: LAUNCH<FMT, 8>(A, RPW, S); break;            \
+    case 64: return LAUNCH<FMT, 64>(A, RPW, S);           \
+    case 32: return LAUNCH<FMT, 32>(A, RPW, S);           \
+    case 16: return LAUNCH<FMT, 16>(A, RPW, S);           \
+    default: return LAUNCH<FMT, 8>(A, RPW, S);            \
   }
 
 // ----------------------------------------------------------------------------- one step
@@ -701,12 +707,11 @@ hipError_t launch_decode_gate_up(const ExpertGemmArgs& a, hipStream_t s) {
   const int rpw = pick_rows_per_wave(kGateRowsPerPass, a.I, a.tile_bound);
   const int lpr = pick_lpr(a.H / codes_per_chunk(a.gate.fmt));
   switch (a.gate.fmt) {
-    case 0: MOE_DISPATCH_LPR(launch_gu, 0, lpr, a, rpw, s); break;
-    case 1: MOE_DISPATCH_LPR(launch_gu, 1, lpr, a, rpw, s); break;
-    case 2: MOE_DISPATCH_LPR(launch_gu, 2, lpr, a, rpw, s); break;
-    default: MOE_DISPATCH_LPR(launch_gu, 3, lpr, a, rpw, s); break;
+    case 0: MOE_DISPATCH_LPR(launch_gu, 0, lpr, a, rpw, s)
+    case 1: MOE_DISPATCH_LPR(launch_gu, 1, lpr, a, rpw, s)
+    case 2: MOE_DISPATCH_LPR(launch_gu, 2, lpr, a, rpw, s)
+    default: MOE_DISPATCH_LPR(launch_gu, 3, lpr, a, rpw, s)
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_decode_down(const ExpertGemmArgs& a, hipStream_t s) {
@@ -716,12 +721,11 @@ hipError_t launch_decode_down(const ExpertGemmArgs& a, hipStream_t s) {
   const int rpw = pick_rows_per_wave(kDownRowsPerPass, a.H, a.tile_bound);
   const int lpr = pick_lpr(a.I / codes_per_chunk(a.down.fmt));
   switch (a.down.fmt) {
-    case 0: MOE_DISPATCH_LPR(launch_dn, 0, lpr, a, rpw, s); break;
-    case 1: MOE_DISPATCH_LPR(launch_dn, 1, lpr, a, rpw, s); break;
-    case 2: MOE_DISPATCH_LPR(launch_dn, 2, lpr, a, rpw, s); break;
-    default: MOE_DISPATCH_LPR(launch_dn, 3, lpr, a, rpw, s); break;
+    case 0: MOE_DISPATCH_LPR(launch_dn, 0, lpr, a, rpw, s)
+    case 1: MOE_DISPATCH_LPR(launch_dn, 1, lpr, a, rpw, s)
+    case 2: MOE_DISPATCH_LPR(launch_dn, 2, lpr, a, rpw, s)
+    default: MOE_DISPATCH_LPR(launch_dn, 3, lpr, a, rpw, s)
   }
-  return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------- debug

@@ -119,7 +119,7 @@ struct ExpertGemmArgs {
   WeightDesc gate, up, down;
   uint16_t* h;                // bf16 [R, h_stride]
   int h_stride;
-  void* y;                    // [R, H]: fp32 (decode) or bf16 (prefill)
+  void* y;                    // [R, H] fp32
   int T, H, I;
   int rows;                   // R: rows of the row space (h and y)
 };
@@ -129,8 +129,7 @@ hipError_t launch_prefill_gate_up(const ExpertGemmArgs& a, int mt, hipStream_t s
 hipError_t launch_prefill_down(const ExpertGemmArgs& a, int mt, hipStream_t s);
 
 struct CombineArgs {
-  const void* y;          // [R, H] fp32 or bf16
-  int y_bf16;
+  const float* y;         // [R, H] fp32
   const float* w;         // [T, K]
   const int32_t* inv;     // [T, K] row of slot (t, j), -1 (dropped) or -2 (zero expert)
   const uint16_t* xe;     // [T, H] expert input (the identity of a zero expert)

@@ -511,7 +511,7 @@ void k_pre_gemm(ExpertGemmArgs a) {
   // epilogue. The weights are the MFMA's first operand, so block (rb, cb) holds
   // out[token][n] transposed: lane l owns token row wm*32*RB + rb*32 + l % 32 and, in
   // element v, column 8*(v/4) + 4*half + v%4 of the 32-column block, i.e. four runs of 4
-  // consecutive columns, each stored as one 8-byte write. Column blocks are 32-aligned
+  // consecutive columns, each stored as one write (8 bytes of h, 16 bytes of y). Column blocks are 32-aligned
   // and N is a multiple of 32, so a block is wholly inside N or wholly outside.
   if (GATEUP) {
     const float gs_g = FMT == 0 ? a.gate.global[e] : 1.0f;
@@ -540,8 +540,10 @@ void k_pre_gemm(ExpertGemmArgs a) {
       }
     }
   } else {
+    // y stays fp32 (the blend reads it once): rounding it to bf16 would add up to half
+    // a bf16 ulp of every expert output to the layer's error
     const float gs = FMT == 0 ? a.down.global[e] : 1.0f;
-    uint16_t* y = reinterpret_cast<uint16_t*>(a.y);
+    float* y = reinterpret_cast<float*>(a.y);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const int nb = n0 + wn * CB * 32 + cb * 32;
@@ -550,13 +552,13 @@ void k_pre_gemm(ExpertGemmArgs a) {
       for (int rb = 0; rb < RB; ++rb) {
         const int i = wm * 32 * RB + rb * 32 + r;
         if (i >= t.count) continue;
-        uint16_t* yrow = y + (size_t)(t.row0 + i) * a.H + nb + 4 * half;
+        float* yrow = y + (size_t)(t.row0 + i) * a.H + nb + 4 * half;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const f32x16_t& c = acc[rb][cb];
-          *reinterpret_cast<uint2*>(yrow + 8 * g4) =
-              make_uint2(pack_bf16x2(c[4 * g4] * gs, c[4 * g4 + 1] * gs),
-                         pack_bf16x2(c[4 * g4 + 2] * gs, c[4 * g4 + 3] * gs));
+          *reinterpret_cast<float4*>(yrow + 8 * g4) =
+              make_float4(c[4 * g4] * gs, c[4 * g4 + 1] * gs, c[4 * g4 + 2] * gs,
+                          c[4 * g4 + 3] * gs);
         }
       }
     }
@@ -569,13 +571,10 @@ static hipError_t launch_pre_ss(const ExpertGemmArgs& a, hipStream_t s) {
   const int N = GATEUP ? a.I : a.H;
   const int ncol = (N + Sh::NCOLS - 1) / Sh::NCOLS;
   auto kern = k_pre_gemm<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS>;
-  static bool attr_set = false;  // one attribute call per instantiation and process
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::SMEM);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // one attribute call per instantiation and process (a function-local static: thread-safe)
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::SMEM);
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3(ncol, a.tile_bound), dim3(Sh::NT), Sh::SMEM, s, a);
   return hipGetLastError();
 }

@@ -371,7 +371,7 @@ class DequantCache:
 def experts_forward(xe: np.ndarray, ids: np.ndarray, w: np.ndarray, routed: DequantCache,
                     residual: np.ndarray, shared: Optional[DequantCache] = None,
                     rows: Optional[np.ndarray] = None,
-                    num_experts: Optional[int] = None) -> np.ndarray:
+                    num_experts: Optional[int] = None, workers: int = 1) -> np.ndarray:
     """out[t] = residual[t] + sum_j w[t,j] y_{t,j} + y_shared[t] in fp64, for tokens ``rows``.
 
     The sum runs over slots j in order, then the shared expert (weight 1, own
@@ -379,6 +379,11 @@ def experts_forward(xe: np.ndarray, ids: np.ndarray, w: np.ndarray, routed: Dequ
     With ``num_experts`` = E given, ids E and above are zero-computation experts: their
     y is the expert input itself (the constructor page's zero-expert add kernel, which
     folds their weights into one identity contribution per token).
+
+    ``workers`` > 1 evaluates the experts on that many host threads (decoding a large
+    layer's weights dominates the time). Each expert's rows are computed exactly as in
+    the serial loop and stored in their own slots, and the sums are formed afterwards in
+    the same fixed order, so the result does not depend on ``workers``.
     """
     xe = np.asarray(xe, dtype=np.float64)
     t_all = xe.shape[0]
@@ -396,7 +401,7 @@ def experts_forward(xe: np.ndarray, ids: np.ndarray, w: np.ndarray, routed: Dequ
         for e in [e for e in by_expert if e >= num_experts]:
             for ri, t, j in by_expert.pop(e):
                 contrib[ri, j] = w[t, j] * xe[t]
-    for e in sorted(by_expert):
+    def one_expert(e):
         wg, wu, wd = routed.get(e)
         lst = by_expert[e]
         ts = np.array([t for _, t, _ in lst])
@@ -404,6 +409,14 @@ def experts_forward(xe: np.ndarray, ids: np.ndarray, w: np.ndarray, routed: Dequ
         for (ri, t, j), yy in zip(lst, y):
             contrib[ri, j] = w[t, j] * yy
         routed.drop(e)
+
+    if workers > 1:
+        import concurrent.futures
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one_expert, sorted(by_expert)))
+    else:
+        for e in sorted(by_expert):
+            one_expert(e)
     for j in range(ids.shape[1]):
         out += contrib[:, j]
     if shared is not None:
@@ -417,7 +430,7 @@ def layer_forward(x, residual, router_w, routed: DequantCache, top_k: int, *,
                   score=SOFTMAX, select=TOPK, renormalize=False, logit_bias=None,
                   correction_bias=None, token_ids=None, tid2eid=None, gamma=None,
                   norm_eps=1e-6, shared: Optional[DequantCache] = None,
-                  routed_scaling=1.0, rows=None, logits=None, zero_experts=0):
+                  routed_scaling=1.0, rows=None, logits=None, zero_experts=0, workers=1):
     """Whole layer -> (out fp64 [len(rows), H], logits fp32, ids, w).
 
     ``logits`` may be given to route from fixed fp32 logits (used by the
@@ -433,7 +446,7 @@ def layer_forward(x, residual, router_w, routed: DequantCache, top_k: int, *,
     # the normalised input is rounded once to bf16 before the expert GEMMs
     xe = bf16_round_f64(rms_norm(x, gamma, norm_eps)) if gamma is not None else x
     num_experts = np.asarray(logits).shape[1] - zero_experts if zero_experts else None
-    out = experts_forward(xe, ids, w, routed, residual, shared, rows, num_experts)
+    out = experts_forward(xe, ids, w, routed, residual, shared, rows, num_experts, workers)
     return out, logits, ids, w
 
 

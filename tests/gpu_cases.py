@@ -2,6 +2,8 @@
 and evaluate the CPU oracle on the same inputs (copied to the host)."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -69,7 +71,13 @@ def run_layer(inp: S.LayerInputs, path=M.PATH_AUTO, residual=True, stream=None):
     return out, logits, ids, w, ws
 
 
-def oracle_layer(inp: S.LayerInputs, rows=None, residual=True):
+def oracle_workers() -> int:
+    """Host threads for the oracle's expert loop (the GPU machine's CPU share is 16)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(16, n))
+
+
+def oracle_layer(inp: S.LayerInputs, rows=None, residual=True, workers=1):
     s = inp.spec
     res = inp.residual if residual else torch.zeros_like(inp.residual)
     return O.layer_forward(
@@ -80,7 +88,7 @@ def oracle_layer(inp: S.LayerInputs, rows=None, residual=True):
         tid2eid=None if inp.tid2eid is None else inp.tid2eid.cpu().numpy(),
         gamma=f32(inp.gamma), norm_eps=s.norm_eps,
         shared=oracle_cache(inp.shared) if inp.shared is not None else None, rows=rows,
-        zero_experts=s.zero_experts)
+        zero_experts=s.zero_experts, workers=workers)
 
 
 def bf16_half_ulp(v: np.ndarray) -> np.ndarray:

@@ -14,7 +14,7 @@ import mixture_experts_ffn_03_amd as M
 import zlib
 
 from gpu_cases import (W_RTOL, assert_layer_close, config_for, f32, oracle_cache, oracle_layer,
-                       run_layer)
+                       oracle_workers, run_layer)
 
 pytestmark = pytest.mark.gpu
 
@@ -353,19 +353,45 @@ def test_layer_without_residual_and_experts_entry(path):
 
 
 @pytest.mark.parametrize("tokens", [1, 2, 16])
-def test_experts_entry_own_dispatch(tokens):
-    """moe_experts_forward builds its own dispatch from the ids in memory (the standalone
-    dispatch kernel); the layer's fused top-K builds it from ids in LDS. Same rows, same
-    tiles: bit-identical outputs."""
-    _announce("experts entry, standalone dispatch", tokens)
+def test_qwen3_shape_small_batches_and_experts_entry(tokens):
+    """Qwen3-like decode layer at 1, 2 and 16 tokens against the oracle; then
+    moe_experts_forward builds its own dispatch from the ids in memory (the standalone
+    dispatch kernel) where the layer's fused top-K built it from ids in LDS: same rows,
+    same tiles, bit-identical outputs."""
+    _announce("qwen3 shape", tokens)
     inp = S.make_inputs(S.scaled(SMALL["qwen3_decode_t8"], tokens=tokens), device=DEV)
     out, logits, ids, w, ws = run_layer(inp, path=M.PATH_DECODE, residual=False)
+    _sync()
+    assert M.get_device_error(ws) == 0
+    want, ologits, oids, ow = oracle_layer(inp, residual=False)
+    assert np.array_equal(logits.cpu().numpy(), ologits)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    assert np.allclose(w.cpu().numpy(), ow, rtol=W_RTOL, atol=1e-7)
+    assert_layer_close(out.float().cpu().numpy(), want, None, f"qwen3 T={tokens}")
     cfg = config_for(inp, M.PATH_DECODE)
     out2 = torch.empty_like(out)
     M.experts_forward(cfg, inp.x, ids, w, M.expert_weights(inp.routed), None, None, out2, ws)
     _sync()
     assert M.get_device_error(ws) == 0
     assert torch.equal(out, out2)
+
+
+def test_decode_long_rows_growing_lds():
+    """Decode rows longer than 64 KB of staged activations, first hidden 10240 (80 KB of
+    LDS) then 16384 (128 KB) on the same kernel instantiation: the second launch needs
+    more LDS than the first and must still run (the kernel's limit is raised to the
+    library's maximum, not to the first size seen)."""
+    for hidden in (10240, 16384):
+        _announce("decode long rows", hidden)
+        spec = S.LayerSpec(name=f"long_rows_{hidden}", tokens=3, hidden=hidden, experts=4,
+                           top_k=2, inter=64, fmt=S.NVFP4, seed=1091)
+        inp = S.make_inputs(spec, device=DEV)
+        out, logits, ids, w, ws = run_layer(inp, path=M.PATH_DECODE)
+        _sync()
+        assert M.get_device_error(ws) == 0
+        want, ologits, oids, ow = oracle_layer(inp)
+        assert np.array_equal(ids.cpu().numpy(), oids)
+        assert_layer_close(out.float().cpu().numpy(), want, f32(inp.residual), f"H={hidden}")
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -516,21 +542,20 @@ FULL = ["qwen3_decode_t1", "qwen3_decode_t8", "dsv3_decode_t32", "prefill_zipf_t
         "hash_mxfp4_t512"]
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", FULL)
-def test_layer_parity_full_size_sampled(name):
+def test_layer_parity_full_size(name):
     """The workloads at their real sizes, in the launch configuration the benchmark uses
-    (automatic path), checked on sampled tokens the oracle evaluates one by one."""
+    (automatic path), every token against the oracle (its experts evaluated on several host
+    threads). The printed line gives the raw max-abs error, the error beyond the output's
+    own bf16 rounding (the bar) and the rel-L2 errors."""
     _announce("full", name)
     inp = S.make_inputs(S.WORKLOADS[name], device=DEV)
     out, logits, ids, w, ws = run_layer(inp)
     _sync()
     assert M.get_device_error(ws) == 0
-    T = inp.spec.tokens
-    rows = np.unique(np.linspace(0, T - 1, num=min(T, 3)).astype(int))
-    want, ologits, oids, ow = oracle_layer(inp, rows=rows)
+    want, ologits, oids, ow = oracle_layer(inp, workers=oracle_workers())
     assert np.array_equal(logits.cpu().numpy(), ologits)
     assert np.array_equal(ids.cpu().numpy(), oids)
     assert np.allclose(w.cpu().numpy(), ow, rtol=W_RTOL, atol=1e-7)
-    got = out.float().cpu().numpy()[rows]
-    assert_layer_close(got, want, f32(inp.residual)[rows], name)
-    assert np.isfinite(out.float().cpu().numpy()).all()
+    assert_layer_close(out.float().cpu().numpy(), want, f32(inp.residual), name)

@@ -526,6 +526,18 @@ def test_rows_subset_equals_full():
     assert np.allclose(sub, full[[4, 1]], rtol=1e-13, atol=1e-13)
 
 
+def test_expert_threads_give_the_serial_result_bitwise():
+    """The oracle's threaded expert loop (used on the full-size workloads) stores each
+    expert's rows in their own slots and sums them afterwards in slot order, so any thread
+    count gives exactly the serial result."""
+    inp = _small_layer(t=9, e=6, k=3, shared=True)
+    x, r, rw = inp.x.float().numpy(), inp.residual.float().numpy(), inp.router_w.float().numpy()
+    one, _, _, _ = O.layer_forward(x, r, rw, _cache(inp.routed), 3, shared=_cache(inp.shared))
+    many, _, _, _ = O.layer_forward(x, r, rw, _cache(inp.routed), 3, shared=_cache(inp.shared),
+                                    workers=4)
+    assert np.array_equal(one, many)
+
+
 def test_bf16_round_f64_matches_torch_and_ties_to_even():
     torch.manual_seed(13)
     v = torch.randn(10000, dtype=torch.float64) * 10

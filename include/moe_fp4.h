@@ -237,6 +237,28 @@ int moe_layer_forward(const moe_config* cfg, const uint16_t* x, const uint16_t* 
                       uint16_t* out, float* dbg_logits, int32_t* dbg_ids, float* dbg_w,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Largest workspace moe_layer_forward_noalloc can use (its fixed device array per GPU). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
+
+/* moe_layer_forward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments and results
+ * as moe_layer_forward, without the workspace: the layer's scratch is a fixed array of
+ * MOE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, which that GPU holds from the
+ * first such call on it until the process ends (that call also looks its address up, on the
+ * device of `stream`). The call itself allocates nothing. A config whose workspace
+ * (moe_workspace_size) exceeds MOE_NOALLOC_SCRATCH_BYTES is rejected with MOE_ERR_WORKSPACE
+ * before anything is enqueued. Every call on one GPU shares that GPU's array and leaves the
+ * last call's contents in it, so calls that may overlap on one GPU (different streams, or
+ * different host threads without ordering) race; order them on one stream. Nothing in the
+ * array needs to start at zero: every call writes what it reads. */
+int moe_layer_forward_noalloc(const moe_config* cfg, const uint16_t* x,
+                              const uint16_t* norm_gamma, const uint16_t* router_w,
+                              const float* logit_bias, const float* correction_bias,
+                              const int32_t* token_ids, const int64_t* tid2eid,
+                              const moe_expert_weights* routed, const moe_expert_weights* shared,
+                              const uint16_t* residual, uint16_t* out, float* dbg_logits,
+                              int32_t* dbg_ids, float* dbg_w, hipStream_t stream);
+
 /* Test entry: decode expert `expert` of `w` to f32 [n, k] with the device routine of
  * the chosen path (MOE_PATH_DECODE: E2M1 to bf16 then the block scale as an fp32
  * factor; MOE_PATH_PREFILL: the bf16 MFMA operand), times the NVFP4 global scale.

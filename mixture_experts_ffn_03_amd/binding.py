@@ -65,6 +65,9 @@ EXPORTS = {
     "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(MoeConfig)] + [_P] * 7 +
                           [ctypes.POINTER(MoeExpertWeights), ctypes.POINTER(MoeExpertWeights)] +
                           [_P] * 5 + [_P, _SZ, _P]),
+    "moe_layer_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(MoeConfig)] + [_P] * 7 +
+                                  [ctypes.POINTER(MoeExpertWeights),
+                                   ctypes.POINTER(MoeExpertWeights)] + [_P] * 5 + [_P]),
     "moe_debug_dequant_fp4": (ctypes.c_int, [ctypes.POINTER(MoeFp4Weight), ctypes.c_int32,
                                              ctypes.c_int32, _P, _P]),
     "moe_get_device_error": (ctypes.c_int, [_P, _SZ, ctypes.POINTER(ctypes.c_int32), _P]),
@@ -175,6 +178,22 @@ def layer_forward(cfg, x, router_w, routed: MoeExpertWeights, out, workspace, *,
         ctypes.byref(shared) if shared is not None else None, _ptr(residual), _ptr(out),
         _ptr(dbg_logits), _ptr(dbg_ids), _ptr(dbg_w), _ptr(workspace), workspace.numel(),
         _stream(stream)), "moe_layer_forward")
+
+
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
+
+
+def layer_forward_noalloc(cfg, x, router_w, routed: MoeExpertWeights, out, *,
+                          norm_gamma=None, logit_bias=None, correction_bias=None,
+                          token_ids=None, tid2eid=None, shared: Optional[MoeExpertWeights] = None,
+                          residual=None, dbg_logits=None, dbg_ids=None, dbg_w=None, stream=None):
+    """moe_layer_forward on the library's own fixed scratch array (no workspace argument)."""
+    _check(load_library().moe_layer_forward_noalloc(
+        ctypes.byref(cfg), _ptr(x), _ptr(norm_gamma), _ptr(router_w), _ptr(logit_bias),
+        _ptr(correction_bias), _ptr(token_ids), _ptr(tid2eid), ctypes.byref(routed),
+        ctypes.byref(shared) if shared is not None else None, _ptr(residual), _ptr(out),
+        _ptr(dbg_logits), _ptr(dbg_ids), _ptr(dbg_w), _stream(stream)),
+        "moe_layer_forward_noalloc")
 
 
 def debug_dequant(weight: MoeFp4Weight, expert: int, path: int, out: torch.Tensor, stream=None):

@@ -10,6 +10,7 @@
 // layout is an error, never a silent decode in the other format (MoE module page,
 // MoeLayer::e8m0_or).
 #include <cstring>
+#include <mutex>
 
 #include "moe_fp4.h"
 #include "moe_internal.h"
@@ -381,6 +382,38 @@ int check_route_ptrs(const moe_config& c, const uint16_t* x, const uint16_t* rou
   return MOE_OK;
 }
 
+// ------------------------------------------------------------ no-allocation entry point
+// The workspace of moe_layer_forward_noalloc: a fixed array of device memory. Every GPU the
+// library runs on holds its own copy (at its own address) until the process ends. In host
+// code `scratch` names a host-side stand-in, never the device memory: kernels and copies
+// only ever get the address hipGetSymbolAddress returns for the device in question.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};  // device address of `scratch`, per device
+
+// Device address of the scratch array on the device of `stream`, looked up once per device
+// with that device current.
+int scratch_address(hipStream_t stream, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return MOE_ERR_HIP;
+  int dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return MOE_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return MOE_ERR_HIP;
+    if (e != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -502,6 +535,24 @@ int moe_layer_forward(const moe_config* cfg, const uint16_t* x, const uint16_t* 
   if (dbg_ids) MOE_HIP(hipMemcpyAsync(dbg_ids, ids, slots * 4, hipMemcpyDeviceToDevice, stream));
   if (dbg_w) MOE_HIP(hipMemcpyAsync(dbg_w, w, slots * 4, hipMemcpyDeviceToDevice, stream));
   return MOE_OK;
+}
+
+int moe_layer_forward_noalloc(const moe_config* cfg, const uint16_t* x,
+                              const uint16_t* norm_gamma, const uint16_t* router_w,
+                              const float* logit_bias, const float* correction_bias,
+                              const int32_t* token_ids, const int64_t* tid2eid,
+                              const moe_expert_weights* routed, const moe_expert_weights* shared,
+                              const uint16_t* residual, uint16_t* out, float* dbg_logits,
+                              int32_t* dbg_ids, float* dbg_w, hipStream_t stream) {
+  int r = check_config(cfg);
+  if (r != MOE_OK) return r;
+  if (cfg->tokens == 0) return MOE_OK;  // no-op: no pointer is touched
+  if (make_layout(*cfg).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((r = scratch_address(stream, &ws)) != MOE_OK) return r;
+  return moe_layer_forward(cfg, x, norm_gamma, router_w, logit_bias, correction_bias, token_ids,
+                           tid2eid, routed, shared, residual, out, dbg_logits, dbg_ids, dbg_w, ws,
+                           (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int moe_debug_dequant_fp4(const moe_fp4_weight* w, int32_t expert, int32_t path, float* out,

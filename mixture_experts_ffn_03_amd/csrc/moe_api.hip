@@ -25,7 +25,7 @@ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 struct Layout {
   size_t partial, logits, ids, w, errtok, xn, row_token, inv, tiles, ntiles, h, y, wcnt,
-      errpart, total;
+      errpart, part, part_bytes, total;
   int ks, hsplit;
   int rows;        // R
   int h_stride;
@@ -41,6 +41,14 @@ int tile_bound(int S, int E, int h) {
   const int m = b < S ? b : S;
   return m > 1 ? m : 1;
 }
+
+// The shared expert on the MFMA kernels: from this many tokens a decode layer runs it as
+// one group over all its tokens (its weights read once per 32-64-128 rows) instead of the
+// GEMV's tiles of kDecodeTile tokens (its weights streamed once per 4 tokens).
+constexpr int kSharedMfmaMinTokens = 8;
+
+// Tile height of the shared expert: its one group holds every token.
+int shared_mt(int T) { return T < 48 ? 32 : (T < 96 ? 64 : 128); }
 
 // Prefill M-tile height from the mean rows per routed expert.
 int prefill_mt(const moe_config& c) {
@@ -89,6 +97,14 @@ Layout make_layout(const moe_config& c) {
   const int dblocks = S >= kDispMultiMinSlots ? dispatch_blocks(S) : 0;
   L.wcnt = take((size_t)dblocks * E * 4);
   L.errpart = take((size_t)dblocks * 4);
+  // K-split partial sums of the shared expert's MFMA launches
+  L.part_bytes = 0;
+  if (c.has_shared) {
+    const int nout = 2 * c.shared_inter > H ? 2 * c.shared_inter : H;
+    L.part_bytes = (size_t)kMaxKsplit * T * nout * sizeof(float);
+    if (L.part_bytes > kSplitPartMax) L.part_bytes = kSplitPartMax;
+  }
+  L.part = take(L.part_bytes);
   L.total = off;
   return L;
 }
@@ -197,6 +213,13 @@ int choose_path(const moe_config& c, int* path) {
   return MOE_OK;
 }
 
+// Whether the shared expert runs on the MFMA kernels: always on the prefill path; on the
+// decode path from kSharedMfmaMinTokens tokens when its sizes suit the MFMA tiles.
+bool shared_on_mfma(const moe_config& c, bool pre) {
+  if (pre) return true;
+  return c.tokens >= kSharedMfmaMinTokens && c.hidden % 64 == 0 && c.shared_inter % 64 == 0;
+}
+
 #define MOE_HIP(call)                          \
   do {                                         \
     if ((call) != hipSuccess) return MOE_ERR_HIP; \
@@ -281,20 +304,27 @@ int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const 
   }
   MOE_HIP(marks.mark(MOE_STAGE_DOWN));
   if (c.has_shared) {
+    // the shared expert: one group over rows [0, T) (implicit tile list), on the MFMA
+    // kernels (with K split over blocks when its tiles are few) unless a decode layer has
+    // too few tokens for them to pay
+    const bool sh_pre = shared_on_mfma(c, pre);
+    const int smt = sh_pre ? shared_mt(c.tokens) : kDecodeTile;
     ExpertGemmArgs b = a;
     b.src.tiles = nullptr;
     b.src.ntiles = nullptr;
     b.src.implicit_row0 = 0;
     b.src.implicit_rows = c.tokens;
-    b.src.implicit_height = mt;
-    b.tile_bound = ceil_div(c.tokens, mt);
+    b.src.implicit_height = smt;
+    b.tile_bound = ceil_div(c.tokens, smt);
     b.gate = desc(shared->gate);
     b.up = desc(shared->up);
     b.down = desc(shared->down);
     b.I = c.shared_inter;
-    if (pre) {
-      MOE_HIP(launch_prefill_gate_up(b, mt, s));
-      MOE_HIP(launch_prefill_down(b, mt, s));
+    b.part = at<float>(ws, L.part);
+    b.part_bytes = L.part_bytes;
+    if (sh_pre) {
+      MOE_HIP(launch_prefill_gate_up(b, smt, s));
+      MOE_HIP(launch_prefill_down(b, smt, s));
     } else {
       MOE_HIP(launch_decode_gate_up(b, s));
       MOE_HIP(launch_decode_down(b, s));

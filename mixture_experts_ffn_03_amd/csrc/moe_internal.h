@@ -122,7 +122,16 @@ struct ExpertGemmArgs {
   void* y;                    // [R, H] fp32
   int T, H, I;
   int rows;                   // R: rows of the row space (h and y)
+  // prefill over an implicit row list (the shared expert) may split K over blocks:
+  // fp32 partial sums [ksplit][implicit_rows][2*I (gate+up) or H (down)] in `part`
+  // (at most part_bytes), added in split order by a reduce kernel
+  float* part;
+  size_t part_bytes;
+  int ksplit;                 // set by the launcher
 };
+// Largest K split of a shared-expert GEMM and the cap on its partial sums.
+constexpr int kMaxKsplit = 16;
+constexpr size_t kSplitPartMax = (size_t)32 << 20;
 hipError_t launch_decode_gate_up(const ExpertGemmArgs& a, hipStream_t s);
 hipError_t launch_decode_down(const ExpertGemmArgs& a, hipStream_t s);
 hipError_t launch_prefill_gate_up(const ExpertGemmArgs& a, int mt, hipStream_t s);

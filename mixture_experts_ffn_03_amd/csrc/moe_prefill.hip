@@ -260,8 +260,12 @@ void k_pre_gemm(ExpertGemmArgs a) {
   const int n0 = ct * NCOLS;
   const size_t row_bytes = (size_t)K * Sh::B_ROW / KC;
   const int sbytes = Sh::FP4 ? K / (FMT == 0 ? 16 : 32) : 0;
-  const WeightDesc& w0 = GATEUP ? a.gate : a.down;
-  const WeightDesc& w1 = GATEUP ? a.up : a.down;
+  // the two weight matrices (gate, up) or the one (down), by value: taking addresses of
+  // the kernel argument's members would place the whole argument in private memory
+  const uint8_t* const pk0 = GATEUP ? a.gate.packed : a.down.packed;
+  const uint8_t* const pk1 = GATEUP ? a.up.packed : a.down.packed;
+  const uint8_t* const sc0 = GATEUP ? a.gate.scales : a.down.scales;
+  const uint8_t* const sc1 = GATEUP ? a.up.scales : a.down.scales;
   float* s_tab = reinterpret_cast<float*>(s_ss + Sh::SS_BYTES);  // FP8 block scales
   if (FMT == 2) {
     // [matrix][128-row block][128-code block] of the rows n0..n0+NCOLS-1 (0 past N)
@@ -269,7 +273,7 @@ void k_pre_gemm(ExpertGemmArgs a) {
     for (int i = threadIdx.x; i < Sh::MATS * Sh::NBL * kb; i += NT) {
       const int m = i / (Sh::NBL * kb), rest = i % (Sh::NBL * kb);
       const int nb = n0 / 128 + rest / kb, kk = rest % kb;
-      const float* tab = reinterpret_cast<const float*>(m ? w1.scales : w0.scales);
+      const float* tab = reinterpret_cast<const float*>(m ? sc1 : sc0);
       s_tab[(m * Sh::NBL + rest / kb) * kFp8MaxKb + kk] =
           nb < nbg ? tab[((size_t)e * nbg + nb) * kb + kk] : 0.0f;
     }
@@ -297,13 +301,13 @@ void k_pre_gemm(ExpertGemmArgs a) {
     asrc[i] = base + piece * 8;
   }
   // weight row of B-tile row brow; rows past N read row 0 of the expert (not stored)
-  auto wrow = [&](int brow, const WeightDesc*& w) -> size_t {
+  auto wrow = [&](int brow, bool& second) -> size_t {
     int n;
     if (GATEUP) {
-      w = brow < BROWS / 2 ? &w0 : &w1;
-      n = n0 + (brow < BROWS / 2 ? brow : brow - BROWS / 2);
+      second = brow >= BROWS / 2;
+      n = n0 + (second ? brow - BROWS / 2 : brow);
     } else {
-      w = &w0;
+      second = false;
       n = n0 + brow;
     }
     return (size_t)e * N + (n < N ? n : 0);
@@ -314,38 +318,42 @@ void k_pre_gemm(ExpertGemmArgs a) {
   for (int i = 0; i < NB; ++i) {
     const int slot = (wave * NB + i) * 64 + lane;
     const int brow = slot / PB, piece = (slot % PB) ^ b_swz<PB>(brow);
-    const WeightDesc* w;
-    const size_t rw = wrow(brow, w);
-    bsrc[i] = w->packed + rw * row_bytes + piece * 16;
+    bool m;
+    const size_t rw = wrow(brow, m);
+    bsrc[i] = (m ? pk1 : pk0) + rw * row_bytes + piece * 16;
   }
   const uint8_t* ssrc[NS > 0 ? NS : 1];
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
-    const WeightDesc* w;
+    bool m;
     const int slot = (wave * NS + i) * 64 + lane;  // 4-byte slot u of its row: 64 codes
     constexpr int SL = SLOTS > 0 ? SLOTS : 1;  // (no such loads for FP8 / BF16)
-    const size_t rw = wrow(slot / SL, w);
-    ssrc[i] = w->scales + rw * sbytes + (slot % SL) * (FMT == 0 ? 4 : 2);
+    const size_t rw = wrow(slot / SL, m);
+    ssrc[i] = (m ? sc1 : sc0) + rw * sbytes + (slot % SL) * (FMT == 0 ? 4 : 2);
   }
   const uint8_t* sssrc[NSS > 0 ? NSS : 1];
 #pragma unroll
   for (int i = 0; i < NSS; ++i) {
-    const WeightDesc* w;
+    bool m;
     const int row = (wave * NSS + i) * 64 + lane;  // one lane per row (waves < SS_WAVES)
-    const size_t rw = wrow(row < BROWS ? row : 0, w);
-    sssrc[i] = w->scales + rw * sbytes;
+    const size_t rw = wrow(row < BROWS ? row : 0, m);
+    sssrc[i] = (m ? sc1 : sc0) + rw * sbytes;
   }
 
-  const int nch = K / KC;
+  // split z of a.ksplit takes K codes [kbase, kbase + K / ksplit) (a whole number of
+  // super-stages when SS holds)
+  const int kspan = K / a.ksplit;
+  const int kbase = blockIdx.z * kspan;
+  const int nch = kspan / KC;
 
   // Loads of stage c: always NLOADS per lane, so the wait count is a constant.
-  auto issue = [&](int c) {
+  auto issue = [&](int c) __attribute__((always_inline)) {
     const uint32_t abase = lds_addr(s_dyn + (c % NSTG) * Sh::STAGE);
     const uint32_t bbase = abase + Sh::A_BYTES, sbase = bbase + Sh::B_BYTES;
-    const int k0 = c * KC;
+    const int k0 = kbase + c * KC;
     if (SS && c % SUPER == 0 && wave < Sh::SS_WAVES) {
-      const int j = c / SUPER;
-      const uint32_t ssbase = lds_addr(s_ss + (j & 1) * BROWS * 16);
+      const int j = (kbase / KC + c) / SUPER;  // 16-byte piece of the scale rows
+      const uint32_t ssbase = lds_addr(s_ss + ((c / SUPER) & 1) * BROWS * 16);
 #pragma unroll
       for (int i = 0; i < NSS; ++i) {
         const int slot0 = (wave * NSS + i) * 64;
@@ -399,7 +407,7 @@ void k_pre_gemm(ExpertGemmArgs a) {
 
   // MFMAs of stage c for the first NR row blocks: STEPS steps of K 16, lane half h
   // covering codes (KC/2)h..(KC/2)h+KC/2-1 of the stage (8 per step)
-  auto stage_mma = [&](auto nr_c, int c) {
+  auto stage_mma = [&](auto nr_c, int c) __attribute__((always_inline)) {
     constexpr int NR = decltype(nr_c)::value;
     if constexpr (NR == 0) {
       if (c + Sh::LEAD < nch) issue(c + Sh::LEAD);
@@ -430,24 +438,28 @@ void k_pre_gemm(ExpertGemmArgs a) {
         // the column block's 32 rows lie in one 128-row block; the stage in one 128-code block
         const int m = GATEUP ? cb / CH : 0;
         const int nbl = ((GATEUP ? brow0[cb] - m * (BROWS / 2) : brow0[cb])) / 128;
-        sc[cb] = __float_as_uint(s_tab[(m * Sh::NBL + nbl) * kFp8MaxKb + (c * KC) / 128]);
+        sc[cb] = __float_as_uint(s_tab[(m * Sh::NBL + nbl) * kFp8MaxKb + (kbase + c * KC) / 128]);
       } else {
         sc[cb] = 0u;
       }
     }
-    // every A operand of the stage is read up front, in the order of use, so that LDS
-    // latency overlaps the MFMAs instead of stalling each step (LDS reads return in order)
-    uint4 av[NR > 0 ? NR : 1][STEPS];
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
+    // A operands are read AHEAD steps before their MFMAs, in the order of use (LDS reads
+    // return in order), so that LDS latency overlaps the MFMAs of the steps before; two
+    // steps of RB x CB MFMAs cover it, and holding only AHEAD steps of operands leaves
+    // registers to spare under the budget of two waves per SIMD
+    constexpr int AHEAD = STEPS < 2 ? STEPS : 2;
+    uint4 av[NR > 0 ? NR : 1][AHEAD];
+    auto read_a = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
       for (int rb = 0; rb < NR; ++rb) {
         const int row = arow + rb * 32;
-        av[rb][s] = *reinterpret_cast<const uint4*>(
+        av[rb][s % AHEAD] = *reinterpret_cast<const uint4*>(
             sa + row * Sh::A_ROW + (((STEPS * half + s) ^ a_swz<PA>(row)) << 4));
         __builtin_amdgcn_sched_barrier(0);  // keep the reads in the order they are used
       }
-    }
+    };
+#pragma unroll
+    for (int s = 0; s < AHEAD; ++s) read_a(s);
     // the loads of stage c + LEAD go out while this stage's LDS reads are in flight
     if (c + Sh::LEAD < nch) issue(c + Sh::LEAD);
     __builtin_amdgcn_sched_barrier(0);
@@ -467,12 +479,15 @@ void k_pre_gemm(ExpertGemmArgs a) {
           bo[cb] = as_bf16x8(d);
         }
       }
+      bf16x8_t af[NR > 0 ? NR : 1];
+#pragma unroll
+      for (int rb = 0; rb < NR; ++rb) af[rb] = __builtin_bit_cast(bf16x8_t, av[rb][s % AHEAD]);
+      if (s + AHEAD < STEPS) read_a(s + AHEAD);
 #pragma unroll
       for (int rb = 0; rb < NR; ++rb) {
-        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, av[rb][s]);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo[cb], af, acc[rb][cb], 0, 0, 0);
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo[cb], af[rb], acc[rb][cb], 0, 0, 0);
       }
     }
   };
@@ -480,7 +495,7 @@ void k_pre_gemm(ExpertGemmArgs a) {
 #pragma unroll
   for (int i = 0; i < Sh::LEAD; ++i)
     if (i < nch) issue(i);
-  auto kloop = [&](auto nr_c) {
+  auto kloop = [&](auto nr_c) __attribute__((always_inline)) {
 #pragma unroll 1
     for (int c = 0; c < nch; ++c) {
       // may stay in flight: stages c+1 .. c+LEAD-1 (fewer near the end), one of which may
@@ -513,7 +528,31 @@ void k_pre_gemm(ExpertGemmArgs a) {
   // element v, column 8*(v/4) + 4*half + v%4 of the 32-column block, i.e. four runs of 4
   // consecutive columns, each stored as one write (8 bytes of h, 16 bytes of y). Column blocks are 32-aligned
   // and N is a multiple of 32, so a block is wholly inside N or wholly outside.
-  if (GATEUP) {
+  if (a.ksplit > 1) {
+    // split K: the raw fp32 sums of this split, [split][row][gate cols | up cols] or
+    // [split][row][H] (rows relative to the implicit list); scales and SwiGLU come with
+    // the reduce
+    const int NO = GATEUP ? 2 * a.I : a.H;
+    float* prow0 = a.part + (size_t)blockIdx.z * a.src.implicit_rows * NO;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int col = GATEUP ? n0 + wn * CH * 32 + (cb % CH) * 32 : n0 + wn * CB * 32 + cb * 32;
+      if (col >= N) continue;
+      const int ocol = GATEUP && cb >= CH ? a.I + col : col;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int i = wm * 32 * RB + rb * 32 + r;
+        if (i >= t.count) continue;
+        float* prow = prow0 + (size_t)(t.row0 + i - a.src.implicit_row0) * NO + ocol + 4 * half;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x16_t& cc = acc[rb][cb];
+          *reinterpret_cast<float4*>(prow + 8 * g4) =
+              make_float4(cc[4 * g4], cc[4 * g4 + 1], cc[4 * g4 + 2], cc[4 * g4 + 3]);
+        }
+      }
+    }
+  } else if (GATEUP) {
     const float gs_g = FMT == 0 ? a.gate.global[e] : 1.0f;
     const float gs_u = FMT == 0 ? a.up.global[e] : 1.0f;
 #pragma unroll
@@ -565,17 +604,101 @@ void k_pre_gemm(ExpertGemmArgs a) {
   }
 }
 
+// Sum of the K splits of a shared-expert GEMM, in split order, then the epilogue of the
+// unsplit kernel: gate+up x global scales, SiLU(gate) * up to bf16 h; down x global scale
+// to fp32 y. One thread per 4 consecutive outputs of a row.
+template <bool GATEUP>
+__global__ __launch_bounds__(256) void k_splitk_reduce(ExpertGemmArgs a) {
+  const int NC = GATEUP ? a.I : a.H;  // output columns
+  const int NO = GATEUP ? 2 * a.I : a.H;  // partial-sum columns
+  const int q = blockIdx.x * blockDim.x + threadIdx.x;
+  const int rows = a.src.implicit_rows;
+  if (q >= rows * (NC / 4)) return;
+  const int r = q / (NC / 4), n = (q % (NC / 4)) * 4;
+  const size_t split = (size_t)rows * NO;
+  const float* p = a.part + (size_t)r * NO + n;
+  float4 g = *reinterpret_cast<const float4*>(p);
+  float4 u = GATEUP ? *reinterpret_cast<const float4*>(p + a.I) : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int z = 1; z < a.ksplit; ++z) {
+    const float4 gz = *reinterpret_cast<const float4*>(p + z * split);
+    g.x += gz.x; g.y += gz.y; g.z += gz.z; g.w += gz.w;
+    if (GATEUP) {
+      const float4 uz = *reinterpret_cast<const float4*>(p + z * split + a.I);
+      u.x += uz.x; u.y += uz.y; u.z += uz.z; u.w += uz.w;
+    }
+  }
+  const int row = a.src.implicit_row0 + r;
+  if (GATEUP) {
+    const float gs_g = a.gate.fmt == 0 ? a.gate.global[0] : 1.0f;
+    const float gs_u = a.up.fmt == 0 ? a.up.global[0] : 1.0f;
+    const float h0 = silu(g.x * gs_g) * (u.x * gs_u), h1 = silu(g.y * gs_g) * (u.y * gs_u);
+    const float h2 = silu(g.z * gs_g) * (u.z * gs_u), h3 = silu(g.w * gs_g) * (u.w * gs_u);
+    *reinterpret_cast<uint2*>(a.h + (size_t)row * a.h_stride + n) =
+        make_uint2(pack_bf16x2(h0, h1), pack_bf16x2(h2, h3));
+  } else {
+    const float gs = a.down.fmt == 0 ? a.down.global[0] : 1.0f;
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + (size_t)row * a.H + n) =
+        make_float4(g.x * gs, g.y * gs, g.z * gs, g.w * gs);
+  }
+}
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  constexpr int kMaxDev = 64;
+  static int cus[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// K splits for a GEMM over an implicit row list (the shared expert) whose blocks would
+// not fill the resident slots: the largest split that keeps each split a whole number of
+// `unit` codes and at least MOE_SPLIT_MIN_STAGES stages, the grid within twice the slots,
+// and the partial sums within the workspace's share.
+#ifndef MOE_SPLIT_MIN_STAGES
+#define MOE_SPLIT_MIN_STAGES 4
+#endif
+static int pick_ksplit(const ExpertGemmArgs& a, int K, int KC, int unit, int blocks, int slots,
+                       int nout) {
+  if (a.src.tiles || !a.part || blocks >= slots) return 1;
+  const size_t per = (size_t)a.src.implicit_rows * nout * sizeof(float);
+  int best = 1;
+  for (int ks = 2; ks <= kMaxKsplit; ++ks) {
+    if (K % (ks * unit) != 0 || K / ks / KC < MOE_SPLIT_MIN_STAGES) continue;
+    if ((long long)blocks * ks > 2LL * slots || per * ks > a.part_bytes) continue;
+    best = ks;
+  }
+  return best;
+}
+
 template <int FMT, int KC, int NSTG, int RB, int WM, int CB, bool GATEUP, bool SS>
-static hipError_t launch_pre_ss(const ExpertGemmArgs& a, hipStream_t s) {
+static hipError_t launch_pre_ss(const ExpertGemmArgs& a0, hipStream_t s) {
   using Sh = PreShape<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS>;
-  const int N = GATEUP ? a.I : a.H;
+  const int N = GATEUP ? a0.I : a0.H;
+  const int K = GATEUP ? a0.H : a0.I;
   const int ncol = (N + Sh::NCOLS - 1) / Sh::NCOLS;
+  ExpertGemmArgs a = a0;
+  // FP8 / BF16 blocks keep the whole K (the FP8 block-scale table is per block)
+  a.ksplit = Sh::FP4 ? pick_ksplit(a, K, KC, SS ? KC * Sh::SUPER : KC, ncol * a.tile_bound,
+                                   device_cus() * Sh::BLOCKS_PER_CU, GATEUP ? 2 * a.I : a.H)
+                     : 1;
   auto kern = k_pre_gemm<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS>;
   // one attribute call per instantiation and process (a function-local static: thread-safe)
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::SMEM);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(ncol, a.tile_bound), dim3(Sh::NT), Sh::SMEM, s, a);
+  hipLaunchKernelGGL(kern, dim3(ncol, a.tile_bound, a.ksplit), dim3(Sh::NT), Sh::SMEM, s, a);
+  if (a.ksplit > 1) {
+    const int nc = GATEUP ? a.I : a.H;
+    const int threads = a.src.implicit_rows * (nc / 4);
+    hipLaunchKernelGGL(k_splitk_reduce<GATEUP>, dim3((threads + 255) / 256), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -29,9 +29,9 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+def _compile(src, build_dir=BUILD, defines=()):
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *("-D" + d for d in defines), "-c", src, "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (p.stdout + p.stderr).splitlines()
                     if "packed-fp32-ops" not in l)
@@ -40,22 +40,35 @@ def _compile(src):
     return obj, out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, defines=(), out_dir=None) -> str:
+    """Build the library (into the package, or with `defines` -- build flags such as
+    MOE_PRE_MX8=1 -- into out_dir/libmoe_fp4.so, a variant for bench.py --lib)."""
+    build_dir = BUILD if out_dir is None else os.path.join(out_dir, "_build")
+    lib = LIB if out_dir is None else os.path.join(out_dir, "libmoe_fp4.so")
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        results = list(ex.map(_compile, srcs))
+        results = list(ex.map(lambda s: _compile(s, build_dir, defines), srcs))
     for _, out in results:
         if verbose and out.strip():
             print(out)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError("link failed:\n" + p.stdout + p.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    import argparse
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("-v", action="store_true", help="print compiler output")
+    ap.add_argument("--define", action="append", default=[],
+                    help="build flag NAME=VALUE (variant builds need --out)")
+    ap.add_argument("--out", default=None, help="directory of a variant build")
+    args = ap.parse_args()
+    if args.define and not args.out:
+        ap.error("--define builds a variant: give --out")
+    print(build(verbose=args.v, defines=args.define, out_dir=args.out))

@@ -25,7 +25,7 @@ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 struct Layout {
   size_t partial, logits, ids, w, errtok, xn, row_token, inv, tiles, ntiles, h, y, wcnt,
-      errpart, part, part_bytes, total;
+      errpart, part, part_bytes, x8, xs8, h8, hs8, total;
   int ks, hsplit;
   int rows;        // R
   int h_stride;
@@ -105,6 +105,12 @@ Layout make_layout(const moe_config& c) {
     if (L.part_bytes > kSplitPartMax) L.part_bytes = kSplitPartMax;
   }
   L.part = take(L.part_bytes);
+#if MOE_PRE_MX8
+  L.x8 = take((size_t)T * H * 2);
+  L.xs8 = take((size_t)T * (H / 32) * 2);
+  L.h8 = take((size_t)L.rows * L.h_stride * 2);
+  L.hs8 = take((size_t)L.rows * (imax / 32) * 2);
+#endif
   L.total = off;
   return L;
 }
@@ -266,7 +272,7 @@ int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const 
                 const float* w, const int32_t* err_tok, const moe_expert_weights* routed,
                 const moe_expert_weights* shared, const uint16_t* residual, uint16_t* out,
                 void* ws, hipStream_t s, const StageMarks& marks = StageMarks(),
-                bool dispatched = false) {
+                bool dispatched = false, const TopkArgs* fused_topk = nullptr) {
   int path;
   int r = choose_path(c, &path);
   if (r != MOE_OK) return r;
@@ -294,11 +300,39 @@ int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const 
   a.I = c.inter;
   a.rows = L.rows;
   if (pre) {
+#if MOE_PRE_MX8
+    const bool mx8 = routed->gate.format == MOE_FMT_MXFP4 && mt == 128;
+    if (mx8) {
+      MOE_HIP(launch_quant_mx8(xe, c.tokens, c.hidden, c.hidden, at<uint8_t>(ws, L.x8),
+                               at<uint16_t>(ws, L.xs8), s));
+      a.a8 = at<uint8_t>(ws, L.x8);
+      a.a8s = at<uint16_t>(ws, L.xs8);
+    }
+#endif
     MOE_HIP(launch_prefill_gate_up(a, mt, s));
     MOE_HIP(marks.mark(MOE_STAGE_GATE_UP));
+#if MOE_PRE_MX8
+    if (mx8) {
+      MOE_HIP(launch_quant_mx8(a.h, L.rows, c.inter, L.h_stride, at<uint8_t>(ws, L.h8),
+                               at<uint16_t>(ws, L.hs8), s));
+      a.a8 = at<uint8_t>(ws, L.h8);
+      a.a8s = at<uint16_t>(ws, L.hs8);
+    }
+#endif
     MOE_HIP(launch_prefill_down(a, mt, s));
   } else {
-    MOE_HIP(launch_decode_gate_up(a, s));
+    if (fused_topk) {  // one token: selection and dispatch inside the gate+up kernel
+      FusedRoute fr{};
+      fr.row_token = d.row_token;
+      fr.inv = d.inv;
+      fr.tiles = d.tiles;
+      fr.ntiles = d.ntiles;
+      fr.err_word = d.err_word;
+      fr.shared_rows = d.shared_rows;
+      MOE_HIP(launch_decode_gate_up_topk(a, *fused_topk, fr, s));
+    } else {
+      MOE_HIP(launch_decode_gate_up(a, s));
+    }
     MOE_HIP(marks.mark(MOE_STAGE_GATE_UP));
     MOE_HIP(launch_decode_down(a, s));
   }
@@ -403,6 +437,15 @@ int launch_route(const moe_config& c, const Layout& L, const uint16_t* x,
   MOE_HIP(launch_topk(t, s));
   if (marks) MOE_HIP(marks->mark(MOE_STAGE_ROUTED));
   return MOE_OK;
+}
+
+// One token with top-K selection over at most 128 experts on the one-step decode GEMV: the
+// selection and the dispatch run inside the gate+up kernel (one launch fewer).
+bool topk_in_gate_up(const moe_config& c, const moe_expert_weights& routed) {
+  int path;
+  if (choose_path(c, &path) != MOE_OK || path != MOE_PATH_DECODE) return false;
+  return c.tokens == 1 && c.select_mode == MOE_SELECT_TOPK && c.zero_experts == 0 &&
+         decode_topk_fusable(routed.gate.format, c.hidden, c.num_experts);
 }
 
 int check_route_ptrs(const moe_config& c, const uint16_t* x, const uint16_t* router_w,
@@ -554,12 +597,24 @@ int moe_layer_forward(const moe_config* cfg, const uint16_t* x, const uint16_t* 
   int32_t* ids = at<int32_t>(workspace, L.ids);
   float* w = at<float>(workspace, L.w);
   bool dispatched = false;
-  r = launch_route(c, L, x, router_w, logit_bias, correction_bias, token_ids, tid2eid, nullptr,
-                   dbg_logits, ids, w, workspace, stream, &marks, &dispatched);
-  if (r != MOE_OK) return r;
+  TopkArgs fused{};
+  const bool fuse = topk_in_gate_up(c, *routed);
+  if (fuse) {
+    // one token, top-K: the router GEMM here, the selection inside the gate+up kernel
+    MOE_HIP(launch_router_partial(x, router_w, at<double>(workspace, L.partial), c.tokens,
+                                  c.num_experts, c.hidden, L.ks, L.hsplit, stream));
+    MOE_HIP(marks.mark(MOE_STAGE_ROUTED));
+    fused = make_topk_args(c, L, logit_bias, correction_bias, token_ids, tid2eid, nullptr,
+                           dbg_logits, ids, w, workspace);
+    dispatched = true;
+  } else {
+    r = launch_route(c, L, x, router_w, logit_bias, correction_bias, token_ids, tid2eid, nullptr,
+                     dbg_logits, ids, w, workspace, stream, &marks, &dispatched);
+    if (r != MOE_OK) return r;
+  }
   r = run_experts(c, L, xe, ids, w, at<int32_t>(workspace, L.errtok), routed,
                   c.has_shared ? shared : nullptr, residual, out, workspace, stream, marks,
-                  dispatched);
+                  dispatched, fuse ? &fused : nullptr);
   if (r != MOE_OK) return r;
   const size_t slots = (size_t)c.tokens * c.top_k;
   if (dbg_ids) MOE_HIP(hipMemcpyAsync(dbg_ids, ids, slots * 4, hipMemcpyDeviceToDevice, stream));

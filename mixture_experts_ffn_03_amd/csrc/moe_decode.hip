@@ -21,6 +21,7 @@
 // use within 256 VGPRs so that 2 waves share each SIMD; rows per wave (passes) grow when
 // the grid would otherwise run several short rounds of blocks.
 #include "moe_device.h"
+#include "moe_select.h"
 
 namespace moe {
 
@@ -554,12 +555,10 @@ struct OneShape {
 };
 
 template <int FMT, int LPR, int M, int ROWS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ROWS == 4 ? (FMT == 0 ? 8 : 5) : 4))) void k_dec_one(ExpertGemmArgs a) {
+__device__ __forceinline__ void dec_one_body(const ExpertGemmArgs& a, const Tile& tile) {
   using SH = OneShape<LPR, M, ROWS>;
   constexpr int G = SH::G, NI = SH::NI, GR = SH::GR, NV = SH::NV;
   constexpr int XW = DecFmt<FMT>::XW, CPC = DecFmt<FMT>::CPC;
-  Tile tile;
-  if (!resolve_tile(a.src, a.row_token, blockIdx.y, tile)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int sub = lane % LPR, grp = lane / LPR;
   const int N = M == 2 ? a.I : a.H;  // output rows of each matrix
@@ -651,6 +650,64 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ROWS == 4 ?
   }
 }
 
+template <int FMT, int LPR, int M, int ROWS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ROWS == 4 ? (FMT == 0 ? 8 : 5) : 4))) void k_dec_one(ExpertGemmArgs a) {
+  Tile tile;
+  if (!resolve_tile(a.src, a.row_token, blockIdx.y, tile)) return;
+  dec_one_body<FMT, LPR, M, ROWS>(a, tile);
+}
+
+// One token with top-K selection: the experts are chosen inside the gate+up kernel. The k
+// selected experts are distinct, so the dispatch is their order: slot j's row is
+// shared_rows + rank of its expert among the k, one 1-row tile per slot in expert order.
+// Every wave selects from the router's fp64 partials itself (no block barrier before the
+// weights are requested); block (0, 0)'s first wave also writes the routing outputs and the
+// dispatch (ids, weights, logits, row map, inverse map, tiles, tile count, error word) that
+// the down projection and the blend read.
+template <int FMT, int LPR, int NPL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FMT == 0 ? 8 : 5))) void k_dec_one_topk(ExpertGemmArgs a, TopkArgs ta, FusedRoute fr) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool writer = blockIdx.x == 0 && blockIdx.y == 0 && wave == 0;
+  TopkArgs t = ta;
+  if (!writer) {
+    t.ids = nullptr;
+    t.w = nullptr;
+    t.logits_out = nullptr;
+    t.err_tok = nullptr;
+  }
+  const int id = topk_token<NPL>(t, 0, nullptr, nullptr);
+  int rank = 0;  // distinct experts: rank = how many selected experts have a lower index
+  for (int j = 0; j < ta.K; ++j) rank += __shfl(id, j, kWave) < id ? 1 : 0;
+  if (writer && lane < ta.K) {
+    const int row = fr.shared_rows + rank;
+    fr.inv[lane] = row;
+    fr.row_token[row] = 0;
+    Tile tl;
+    tl.group = id;
+    tl.row0 = row;
+    tl.count = 1;
+    tl.pad = 0;
+#pragma unroll
+    for (int q = 0; q < kTileTok; ++q) tl.tok[q] = 0;
+    fr.tiles[rank] = tl;
+  }
+  if (writer && lane == 0) {
+    fr.ntiles[0] = ta.K;
+    fr.err_word[0] = 0;
+    if (fr.shared_rows) fr.row_token[0] = 0;
+  }
+  const uint64_t mine = __ballot(lane < ta.K && rank == (int)blockIdx.y);
+  if (!mine) return;
+  Tile tile;
+  tile.group = __shfl(id, __builtin_ctzll(mine), kWave);
+  tile.row0 = fr.shared_rows + (int)blockIdx.y;
+  tile.count = 1;
+  tile.pad = 0;
+#pragma unroll
+  for (int q = 0; q < kTileTok; ++q) tile.tok[q] = 0;
+  dec_one_body<FMT, LPR, 2, 4>(a, tile);
+}
+
 // Host side: FP4 weights, rows of at most 64 chunks, tiles of at most kTileTok rows.
 static int one_lanes(int nchunk) {
   int l = 8;
@@ -712,6 +769,36 @@ hipError_t launch_decode_gate_up(const ExpertGemmArgs& a, hipStream_t s) {
     case 2: MOE_DISPATCH_LPR(launch_gu, 2, lpr, a, rpw, s)
     default: MOE_DISPATCH_LPR(launch_gu, 3, lpr, a, rpw, s)
   }
+}
+
+// (at most 128 experts: two keys per lane keep the selection within the kernel's 64 VGPRs)
+bool decode_topk_fusable(int fmt, int H, int E) { return one_fits(fmt, H, kTileTok) && E <= 128; }
+
+template <int FMT, int LPR>
+static hipError_t launch_topk_t(const ExpertGemmArgs& a, const TopkArgs& ta, const FusedRoute& fr,
+                                hipStream_t s) {
+  const int rows = kDecWaves * OneShape<LPR, 2, 4>::GR;
+  const dim3 grid((a.I + rows - 1) / rows, ta.K);
+  const int npl = (ta.E + 63) / 64;
+  if (npl <= 1) hipLaunchKernelGGL((k_dec_one_topk<FMT, LPR, 1>), grid, dim3(256), 0, s, a, ta, fr);
+  else hipLaunchKernelGGL((k_dec_one_topk<FMT, LPR, 2>), grid, dim3(256), 0, s, a, ta, fr);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_gate_up_topk(const ExpertGemmArgs& a, const TopkArgs& ta,
+                                      const FusedRoute& fr, hipStream_t s) {
+  if (!decode_topk_fusable(a.gate.fmt, a.H, ta.E) || ta.T != 1) return hipErrorInvalidValue;
+  const int lpr = one_lanes(a.H / 32);
+#define MOE_TOPK_LPR(FMT)                                  \
+  switch (lpr) {                                           \
+    case 8: return launch_topk_t<FMT, 8>(a, ta, fr, s);    \
+    case 16: return launch_topk_t<FMT, 16>(a, ta, fr, s);  \
+    case 32: return launch_topk_t<FMT, 32>(a, ta, fr, s);  \
+    default: return launch_topk_t<FMT, 64>(a, ta, fr, s);  \
+  }
+  if (a.gate.fmt == 0) { MOE_TOPK_LPR(0) }
+  MOE_TOPK_LPR(1)
+#undef MOE_TOPK_LPR
 }
 
 hipError_t launch_decode_down(const ExpertGemmArgs& a, hipStream_t s) {

@@ -128,11 +128,34 @@ struct ExpertGemmArgs {
   float* part;
   size_t part_bytes;
   int ksplit;                 // set by the launcher
+#if MOE_PRE_MX8
+  // block-scaled MFMA variant (build flag, off by default; see moe_prefill.hip): activations
+  // as MXFP8 hi + lo pairs ([rows][K/32][32 hi bytes, 32 lo bytes], same row bytes as bf16)
+  // with E8M0 scales [rows][K/32] (hi | lo << 8)
+  const uint8_t* a8;
+  const uint16_t* a8s;
+#endif
 };
+#if MOE_PRE_MX8
+hipError_t launch_quant_mx8(const uint16_t* src, int rows, int K, int stride, uint8_t* dst,
+                            uint16_t* scales, hipStream_t s);
+#endif
 // Largest K split of a shared-expert GEMM and the cap on its partial sums.
 constexpr int kMaxKsplit = 16;
 constexpr size_t kSplitPartMax = (size_t)32 << 20;
 hipError_t launch_decode_gate_up(const ExpertGemmArgs& a, hipStream_t s);
+// One token, top-K selection: the selection and the dispatch run inside the gate+up kernel.
+struct FusedRoute {
+  int32_t* row_token;
+  int32_t* inv;
+  Tile* tiles;
+  int32_t* ntiles;
+  int32_t* err_word;
+  int shared_rows;
+};
+bool decode_topk_fusable(int fmt, int H, int E);
+hipError_t launch_decode_gate_up_topk(const ExpertGemmArgs& a, const TopkArgs& ta,
+                                      const FusedRoute& fr, hipStream_t s);
 hipError_t launch_decode_down(const ExpertGemmArgs& a, hipStream_t s);
 hipError_t launch_prefill_gate_up(const ExpertGemmArgs& a, int mt, hipStream_t s);
 hipError_t launch_prefill_down(const ExpertGemmArgs& a, int mt, hipStream_t s);

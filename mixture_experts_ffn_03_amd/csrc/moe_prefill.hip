@@ -37,6 +37,10 @@
 // * Block ids are remapped so that each XCD (ids dispatched round-robin over the 8
 //   XCDs) walks a contiguous run of (row tile, column tile) work, which keeps an A
 //   tile and an expert's weight rows in that XCD's L2 while they are reused.
+// * Build flag MOE_PRE_MX8 (off by default: measured slower, kept to reproduce the
+//   measurement): MXFP4 weights fed natively to the block-scaled MFMA
+//   (v_mfma_scale_f32_32x32x64_f8f6f4, the analogue of the pages' block-scaled FP4 MMA,
+//   MoE constructor page) with the activations quantised to MXFP8 hi + lo pairs.
 #include <type_traits>
 
 #include "moe_device.h"
@@ -195,11 +199,21 @@ struct PreShape {
   static constexpr int A_BYTES = MT * A_ROW;
   static constexpr int B_BYTES = BROWS * B_ROW;
   static constexpr int S_BYTES = BROWS * SROW;
-  static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+#if MOE_PRE_MX8
+  // block-scaled MFMA variant: MXFP8 hi/lo activations (MXFP4 weights, 64-code stages)
+  static constexpr bool MX8 = FMT == 1 && KC == 64 && !SS;
+#else
+  static constexpr bool MX8 = false;
+#endif
+  // activation scales: [row][2 blocks], one 4-byte LDS slot each (a 2-byte direct-to-LDS load
+  // still fills a dword per lane)
+  static constexpr int AS_BYTES = MX8 ? MT * 2 * 4 : 0;
+  static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES + AS_BYTES;
   static constexpr int NA = MT * PA / NT;        // 16-byte loads per lane (A)
   static constexpr int NB = BROWS * PB / NT;     // 16-byte loads per lane (B)
   static constexpr int NS = S_BYTES / 4 / NT;    // scale loads per lane (one per slot)
-  static constexpr int NLOADS = NA + NB + NS;
+  static constexpr int NAS = MX8 ? MT * 2 / NT : 0;  // activation-scale loads per lane (2 bytes)
+  static constexpr int NLOADS = NA + NB + NS + NAS;
   static constexpr int SUPER = (FMT == 0 ? 256 : 512) / KC;  // stages per 16 scale bytes
   // super-stage scale loads: one lane per row, issued by the first SS_WAVES waves
   static constexpr int SS_WAVES = SS ? (BROWS / 64 < NW ? BROWS / 64 : NW) : 0;
@@ -298,8 +312,20 @@ void k_pre_gemm(ExpertGemmArgs a) {
     const int row = slot / PA, piece = (slot % PA) ^ a_swz<PA>(row);
     const uint16_t* base = GATEUP ? a.x + (size_t)s_tok[row] * a.H
                                   : a.h + (size_t)s_tok[row] * a.h_stride;
+#if MOE_PRE_MX8
+    if (Sh::MX8)
+      base = reinterpret_cast<const uint16_t*>(a.a8) + (size_t)s_tok[row] * (GATEUP ? a.H : a.h_stride);
+#endif
     asrc[i] = base + piece * 8;
   }
+  // MX8: one (row, 32-code block) activation-scale pair of the stage per lane
+  const uint16_t* assrc = nullptr;
+#if MOE_PRE_MX8
+  if (Sh::MX8) {
+    const int pi = (wave * 64 + lane) % (MT * 2);
+    assrc = a.a8s + (size_t)s_tok[pi / 2] * (K / 32) + (pi % 2);
+  }
+#endif
   // weight row of B-tile row brow; rows past N read row 0 of the expert (not stored)
   auto wrow = [&](int brow, bool& second) -> size_t {
     int n;
@@ -369,6 +395,10 @@ void k_pre_gemm(ExpertGemmArgs a) {
     for (int i = 0; i < NB; ++i) {
       const int slot0 = (wave * NB + i) * 64;
       dma16(bsrc[i] + (size_t)k0 * Sh::B_ROW / KC, __builtin_amdgcn_readfirstlane(bbase + slot0 * 16));
+    }
+    if (Sh::MX8) {
+      const uint32_t asbase = sbase + Sh::S_BYTES;
+      dma2(assrc + k0 / 32, __builtin_amdgcn_readfirstlane(asbase + wave * 64 * 4));
     }
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
@@ -443,6 +473,42 @@ void k_pre_gemm(ExpertGemmArgs a) {
         sc[cb] = 0u;
       }
     }
+#if MOE_PRE_MX8
+    if constexpr (Sh::MX8) {
+      // block-scaled MFMA, K = 64: weights (E2M1, lane half h: codes 32h..32h+31, one E8M0
+      // scale) first; activations second as an MXFP8 hi and lo pair, lane half h holding
+      // codes 16h..16h+15 and 32+16h..47+16h (pieces h, 4+h of hi; 2+h, 6+h of lo), with
+      // the E8M0 scales of block h
+      const uint8_t* sas = ssc + Sh::S_BYTES;
+      typedef int v8i_t __attribute__((ext_vector_type(8)));
+      v8i_t wq[CB];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        wq[cb] = v8i_t{(int)q[cb][0], (int)q[cb][1], (int)q[cb][2], (int)q[cb][3], 0, 0, 0, 0};
+      if (c + Sh::LEAD < nch) issue(c + Sh::LEAD);
+#pragma unroll
+      for (int rb = 0; rb < NR; ++rb) {
+        const int row = arow + rb * 32;
+        const uint8_t* rp = sa + row * Sh::A_ROW;
+        const int sw = a_swz<PA>(row);
+        const uint4 h0 = *reinterpret_cast<const uint4*>(rp + ((half ^ sw) << 4));
+        const uint4 h1 = *reinterpret_cast<const uint4*>(rp + (((4 + half) ^ sw) << 4));
+        const uint4 l0 = *reinterpret_cast<const uint4*>(rp + (((2 + half) ^ sw) << 4));
+        const uint4 l1 = *reinterpret_cast<const uint4*>(rp + (((6 + half) ^ sw) << 4));
+        const uint32_t s2 = *reinterpret_cast<const uint16_t*>(sas + (row * 2 + half) * 4);
+        const v8i_t vh{(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w, (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
+        const v8i_t vl{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              wq[cb], vh, acc[rb][cb], 4, 0, 0, (int)sc[cb], 0, (int)(s2 & 0xFFu));
+          acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              wq[cb], vl, acc[rb][cb], 4, 0, 0, (int)sc[cb], 0, (int)(s2 >> 8));
+        }
+      }
+      return;
+    }
+#endif
     // A operands are read AHEAD steps before their MFMAs, in the order of use (LDS reads
     // return in order), so that LDS latency overlaps the MFMAs of the steps before; two
     // steps of RB x CB MFMAs cover it, and holding only AHEAD steps of operands leaves
@@ -712,6 +778,9 @@ static hipError_t launch_pre_shape(const ExpertGemmArgs& a, hipStream_t s) {
     return launch_pre_ss<FMT, KC, NSTG, RB, WM, CB, GATEUP, false>(a, s);
   } else {
     const int sbytes = K / (FMT == 0 ? 16 : 32);
+#if MOE_PRE_MX8
+    if (FMT == 1 && KC == 64) return launch_pre_ss<FMT, KC, NSTG, RB, WM, CB, GATEUP, false>(a, s);
+#endif
     if (sbytes % 16 == 0) return launch_pre_ss<FMT, KC, NSTG, RB, WM, CB, GATEUP, true>(a, s);
     return launch_pre_ss<FMT, KC, NSTG, RB, WM, CB, GATEUP, false>(a, s);
   }
@@ -757,6 +826,84 @@ static hipError_t launch_pre(const ExpertGemmArgs& a, int mt, hipStream_t s) {
   if (mt <= 64) return launch_pre_shape<3, 32, 3, 1, 2, 4, GATEUP>(a, s);
   return launch_pre_shape<3, 32, 3, 2, 2, 4, GATEUP>(a, s);
 }
+
+#if MOE_PRE_MX8
+// Block-scaled MFMA variant: each 32-value block of a bf16 row as an MXFP8 (E4M3 + E8M0) hi
+// value and an
+// MXFP8 lo value of the residual x - hi. Scale 2^(floor(log2 amax) - 7) (the block's amax
+// lands in [128, 256), inside E4M3's range). Output row: per block 32 hi bytes then 32 lo.
+__global__ __launch_bounds__(256) void k_quant_mx8(const uint16_t* src, int rows, int K, int stride,
+                                                  uint8_t* dst, uint16_t* scales) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int nb = K / 32;
+  if (i >= rows * nb) return;
+  const int r = i / nb, b = i % nb;
+  const uint4* p = reinterpret_cast<const uint4*>(src + (size_t)r * stride + b * 32);
+  float x[32];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 v = p[q];
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[8 * q + 2 * j] = bf16_to_f32(d[j] & 0xFFFFu);
+      x[8 * q + 2 * j + 1] = bf16_to_f32(d[j] >> 16);
+    }
+  }
+  auto scale_byte = [](float amax) -> int {
+    if (!(amax > 0.f)) return 0;
+    const int ex = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127;  // floor(log2), normals
+    const int e = ex - 7;
+    return e + 127 < 0 ? 0 : (e + 127 > 254 ? 254 : e + 127);
+  };
+  auto pow2 = [](int e) { return __uint_as_float((uint32_t)(e + 127) << 23); };  // e in [-126, 127]
+  uint32_t packed[2][8];
+  int sb[2];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(x[j]));
+    sb[pass] = scale_byte(amax);
+    const int e = sb[pass] - 127;
+    // x * 2^-e in two exact power-of-two steps (2^-e alone may not be a normal float)
+    const float m1 = pow2(-e / 2), m2 = pow2(-e - (-e / 2));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int w = 0;
+      w = __builtin_amdgcn_cvt_pk_fp8_f32((x[4 * j] * m1) * m2, (x[4 * j + 1] * m1) * m2, w, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32((x[4 * j + 2] * m1) * m2, (x[4 * j + 3] * m1) * m2, w, true);
+      packed[pass][j] = (uint32_t)w;
+    }
+    if (pass == 0) {  // residual of the hi values
+      const float u1 = pow2(e / 2), u2 = pow2(e - e / 2);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int w = (int)packed[0][j];
+        const float hv[4] = {__builtin_amdgcn_cvt_f32_fp8(w, 0), __builtin_amdgcn_cvt_f32_fp8(w, 1),
+                             __builtin_amdgcn_cvt_f32_fp8(w, 2), __builtin_amdgcn_cvt_f32_fp8(w, 3)};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[4 * j + t] -= (hv[t] * u1) * u2;
+      }
+    }
+  }
+  uint4* o = reinterpret_cast<uint4*>(dst + (size_t)r * stride * 2 + b * 64);
+  o[0] = make_uint4(packed[0][0], packed[0][1], packed[0][2], packed[0][3]);
+  o[1] = make_uint4(packed[0][4], packed[0][5], packed[0][6], packed[0][7]);
+  o[2] = make_uint4(packed[1][0], packed[1][1], packed[1][2], packed[1][3]);
+  o[3] = make_uint4(packed[1][4], packed[1][5], packed[1][6], packed[1][7]);
+  scales[(size_t)r * nb + b] = (uint16_t)(sb[0] | (sb[1] << 8));
+}
+
+hipError_t launch_quant_mx8(const uint16_t* src, int rows, int K, int stride, uint8_t* dst,
+                            uint16_t* scales, hipStream_t s) {
+  const int n = rows * (K / 32);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quant_mx8, dim3((n + 255) / 256), dim3(256), 0, s, src, rows, K, stride,
+                     dst, scales);
+  return hipGetLastError();
+}
+#endif
 
 hipError_t launch_prefill_gate_up(const ExpertGemmArgs& a, int mt, hipStream_t s) {
   return launch_pre<true>(a, mt, s);

@@ -84,9 +84,11 @@ __device__ __forceinline__ double score_f64(int score, float logit) {
 // lowest expert index by ballot. Writes ids / w (and logits_out, err_tok) to global
 // memory; lds_ids / lds_err (if not null) also receive ids[t*K..] and the token's error.
 // ---------------------------------------------------------------------------
+// Returns, in lane j < K, the expert of slot j (-1 for a dropped slot; other lanes -1). The
+// global outputs (ids, w, err_tok, logits_out) are written where their pointers are set.
 template <int NPL>
-__device__ __forceinline__ void topk_token(const TopkArgs& a, int t, int32_t* lds_ids,
-                                           int32_t* lds_err) {
+__device__ __forceinline__ int topk_token(const TopkArgs& a, int t, int32_t* lds_ids,
+                                          int32_t* lds_err) {
   const int lane = threadIdx.x & 63;
   const int E = a.E, K = a.K;
 
@@ -227,14 +229,15 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, int t, int32_t* ld
     wj = sum > 0.f ? wj / sum : 0.f;
   }
   if (lane < K) {
-    a.w[(size_t)t * K + lane] = wj * a.scaling;
-    a.ids[(size_t)t * K + lane] = my_id;
+    if (a.w) a.w[(size_t)t * K + lane] = wj * a.scaling;
+    if (a.ids) a.ids[(size_t)t * K + lane] = my_id;
     if (lds_ids) lds_ids[t * K + lane] = my_id;
   }
   if (lane == 0) {
     if (a.err_tok) a.err_tok[t] = err;
     if (lds_err) lds_err[t] = err;
   }
+  return lane < K ? my_id : -1;
 }
 
 // ---------------------------------------------------------------------------

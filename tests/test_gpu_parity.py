@@ -291,6 +291,12 @@ SMALL = {
     "hash_fused": S.scaled(S.WORKLOADS["hash_mxfp4_t512"], tokens=12, hidden=512, experts=32,
                            inter=256, shared_inter=128, vocab=1000),
     "qwen3_t3": S.scaled(S.WORKLOADS["qwen3_decode_t8"], tokens=3),
+    # one token with top-K over at most 128 experts: the selection and the dispatch inside
+    # the gate+up kernel; with a shared expert (its row first) and with MXFP4 weights
+    "t1_fused_shared": S.scaled(S.WORKLOADS["dsv3_decode_t32"], tokens=1, hidden=1024,
+                                experts=64, inter=256, shared_inter=192),
+    "t1_fused_mxfp4": S.LayerSpec(name="t1_fused_mxfp4", tokens=1, hidden=512, experts=128,
+                                  top_k=6, inter=256, fmt=S.MXFP4, renormalize=True, seed=1092),
     # 40 tokens on the decode path: the shared expert's implicit list of ten 4-token tiles
     "dsv3_t40_mini": S.scaled(S.WORKLOADS["dsv3_decode_t32"], tokens=40, hidden=1024,
                               experts=64, inter=256, shared_inter=192),

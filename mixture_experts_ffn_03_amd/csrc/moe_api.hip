@@ -47,7 +47,9 @@ int tile_bound(int S, int E, int h) {
 // GEMV's tiles of kDecodeTile tokens (its weights streamed once per 4 tokens).
 constexpr int kSharedMfmaMinTokens = 8;
 
-// Tile height of the shared expert: its one group holds every token.
+// Tile height of the shared expert: its one group holds every token. (Choosing 32-row tiles
+// whenever taller ones leave the chip's block slots unfilled, and splitting their K, was
+// slower: hash layer shared stage 88.7 us against 71.7 us with 128-row tiles.)
 int shared_mt(int T) { return T < 48 ? 32 : (T < 96 ? 64 : 128); }
 
 // Prefill M-tile height from the mean rows per routed expert.

@@ -92,7 +92,7 @@ Layout make_layout(const moe_config& c) {
   L.row_token = take((size_t)L.rows * 4);
   L.inv = take((size_t)S * 4);
   L.tiles = take((size_t)tb * sizeof(Tile));
-  L.ntiles = take(16);
+  L.ntiles = take(kTileCountBytes);  // the tile count and the GEMMs' work counters
   L.h = take((size_t)L.rows * L.h_stride * 2);
   L.y = take((size_t)L.rows * H * 4);
   // multi-block dispatch (many slots): per-wave expert counts and per-block error bits
@@ -302,6 +302,7 @@ int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const 
   a.I = c.inter;
   a.rows = L.rows;
   if (pre) {
+    a.work = d.ntiles + kWorkCtrOffset;
 #if MOE_PRE_MX8
     const bool mx8 = routed->gate.format == MOE_FMT_MXFP4 && mt == 128;
     if (mx8) {
@@ -313,6 +314,7 @@ int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const 
 #endif
     MOE_HIP(launch_prefill_gate_up(a, mt, s));
     MOE_HIP(marks.mark(MOE_STAGE_GATE_UP));
+    a.work = d.ntiles + kWorkCtrOffset + kXcds * kWorkCtrStride;
 #if MOE_PRE_MX8
     if (mx8) {
       MOE_HIP(launch_quant_mx8(a.h, L.rows, c.inter, L.h_stride, at<uint8_t>(ws, L.h8),
@@ -348,6 +350,7 @@ int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const 
     ExpertGemmArgs b = a;
     b.src.tiles = nullptr;
     b.src.ntiles = nullptr;
+    b.work = nullptr;
     b.src.implicit_row0 = 0;
     b.src.implicit_rows = c.tokens;
     b.src.implicit_height = smt;

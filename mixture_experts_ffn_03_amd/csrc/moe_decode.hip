@@ -692,7 +692,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FMT == 0 ? 
     fr.tiles[rank] = tl;
   }
   if (writer && lane == 0) {
-    fr.ntiles[0] = ta.K;
+    publish_tile_count(fr.ntiles, ta.K);
     fr.err_word[0] = 0;
     if (fr.shared_rows) fr.row_token[0] = 0;
   }

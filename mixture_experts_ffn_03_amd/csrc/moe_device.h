@@ -18,6 +18,14 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
 
+// Tile count of a dispatch, written with the persistent GEMMs' work counters zeroed
+// (one thread; the GEMMs run after the dispatch on the same stream).
+__device__ __forceinline__ void publish_tile_count(int32_t* ntiles, int n) {
+  ntiles[0] = n;
+#pragma unroll
+  for (int i = 0; i < kWorkCtrSets * kXcds; ++i) ntiles[kWorkCtrOffset + i * kWorkCtrStride] = 0;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
 
 // Round-to-nearest-even fp32 -> bf16 (gfx950 converts natively; denormals kept).

@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kDispatchThreads) void k_dispatch_scatter(DispatchA
   if (tid == 0) {
     int err = 0;
     for (int b = 0; b < nb; ++b) err |= a.err_part[b];
-    a.ntiles[0] = ntot;
+    publish_tile_count(a.ntiles, ntot);
     a.err_word[0] = err;
   }
 }

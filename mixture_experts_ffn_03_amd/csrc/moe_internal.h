@@ -41,6 +41,16 @@ struct TileSource {
   int32_t implicit_height; // implicit list: rows per tile
 };
 
+// Work counters of the persistent prefill GEMMs, beside the tile count: one per XCD and
+// launch (gate+up, down), each on its own 64-byte line, after the count's 256-byte line.
+// Every writer of the tile count zeroes them (publish_tile_count), so each call's GEMMs
+// start from zero without a memset.
+constexpr int kXcds = 8;             // XCDs of the chip; block ids go round-robin over them
+constexpr int kWorkCtrOffset = 64;   // int32 index of the first counter
+constexpr int kWorkCtrStride = 16;   // int32s between counters
+constexpr int kWorkCtrSets = 2;      // gate+up, down
+constexpr size_t kTileCountBytes = (size_t)(kWorkCtrOffset + kWorkCtrSets * kXcds * kWorkCtrStride) * 4;
+
 constexpr int kMaxExperts = 1024;  // MOE_MAX_EXPERTS
 constexpr int kMaxTopK = 32;       // MOE_MAX_TOP_K
 constexpr int kDecodeTile = 4;     // rows (tokens) per decode tile
@@ -128,6 +138,9 @@ struct ExpertGemmArgs {
   float* part;
   size_t part_bytes;
   int ksplit;                 // set by the launcher
+  // per-XCD work counters of a persistent launch over the device tile list (zeroed by the
+  // dispatch), or nullptr: one block per tile
+  int32_t* work;
 #if MOE_PRE_MX8
   // block-scaled MFMA variant (build flag, off by default; see moe_prefill.hip): activations
   // as MXFP8 hi + lo pairs ([rows][K/32][32 hi bytes, 32 lo bytes], same row bytes as bf16)

@@ -37,6 +37,9 @@
 // * Block ids are remapped so that each XCD (ids dispatched round-robin over the 8
 //   XCDs) walks a contiguous run of (row tile, column tile) work, which keeps an A
 //   tile and an expert's weight rows in that XCD's L2 while they are reused.
+// * Down projections of FP4 weights with per-stage scales run as a persistent grid over
+//   the tile list when it exceeds the resident slots (see k_pre_gemm's PERSIST form; build
+//   flag MOE_PRE_PERSIST=0 gives one block per tile instead).
 // * Build flag MOE_PRE_MX8 (off by default: measured slower, kept to reproduce the
 //   measurement): MXFP4 weights fed natively to the block-scaled MFMA
 //   (v_mfma_scale_f32_32x32x64_f8f6f4, the analogue of the pages' block-scaled FP4 MMA,
@@ -47,7 +50,6 @@
 
 namespace moe {
 
-constexpr int kXcds = 8;
 constexpr int kFp8MaxKb = 128;  // FP8 prefill: K up to 128 * 128 codes (block-scale table)
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -155,6 +157,28 @@ __device__ __forceinline__ bool pre_resolve(const ExpertGemmArgs& a, int ncol_ti
   return true;
 }
 
+// A float at a block-uniform address, through the scalar cache (the memory is read-only
+// while the kernel runs): the wait for it is on the scalar counter, never on the
+// vector-memory counter that tracks the stage loads.
+__device__ __forceinline__ float load_uniform_f32(const float* p, int i) {
+  typedef __attribute__((address_space(4))) const float cf32_t;
+  return *((cf32_t*)p + __builtin_amdgcn_readfirstlane(i));
+}
+
+// Header (group, first row, row count) of a tile at a block-uniform index, through the
+// scalar cache; the fields stay in scalar registers.
+__device__ __forceinline__ Tile load_tile_header(const Tile* tiles, int i) {
+  typedef int i32x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(4))) const i32x4_t ci32x4_t;
+  const i32x4_t h = *(ci32x4_t*)(tiles + i);
+  Tile t;
+  t.group = __builtin_amdgcn_readfirstlane(h[0]);
+  t.row0 = __builtin_amdgcn_readfirstlane(h[1]);
+  t.count = __builtin_amdgcn_readfirstlane(h[2]);
+  t.pad = 0;
+  return t;
+}
+
 // Operand for MFMA step s (codes 8s..8s+7 of the lane's codes of the stage).
 template <int FMT>
 __device__ __forceinline__ bf16x8_t b_operand(const uint32_t q, const uint32_t sc_word, int s) {
@@ -245,7 +269,19 @@ struct PreShape {
 template <int FMT, int KC, int NSTG, int RB, int WM, int CB, bool GATEUP, bool SS>
 constexpr int kPreWaves = PreShape<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS>::BLOCKS_PER_CU;
 
+// Persistent form (PERSIST): gridDim.x blocks (a multiple of kXcds, at most the resident
+// slots) walk the work list of (row tile, column tile) items. The items are split into
+// kXcds contiguous ranges, one per XCD; block b (on XCD b % kXcds) starts at item
+// b / kXcds of its range and then takes the next unclaimed item of the range from the
+// XCD's work counter. The stage ring runs on across items: the next item is claimed at
+// step 0 of the current one, its tile read at step 2, and its first LEAD stages issued
+// during the current item's last LEAD steps, so neither the pipeline fill nor the
+// epilogue leaves the CU idle (MoE constructor page: the grouped GEMM runs as a
+// persistent grid over the compacted tile work list).
 template <int FMT, int KC, int NSTG, int RB, int WM, int CB, bool GATEUP, bool SS>
+constexpr int kPersistLds = PreShape<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS>::SMEM + 16;
+
+template <int FMT, int KC, int NSTG, int RB, int WM, int CB, bool GATEUP, bool SS, bool PERSIST>
 __global__ __launch_bounds__(256) __attribute__((
     amdgpu_waves_per_eu(kPreWaves<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS>, 2)))
 void k_pre_gemm(ExpertGemmArgs a) {
@@ -254,24 +290,45 @@ void k_pre_gemm(ExpertGemmArgs a) {
   constexpr int WN = Sh::WN, BROWS = Sh::BROWS, NCOLS = Sh::NCOLS, MT = Sh::MT;
   constexpr int NA = Sh::NA, NB = Sh::NB, NS = Sh::NS, NSS = Sh::NSS, SUPER = Sh::SUPER;
   constexpr int PA = Sh::PA, PB = Sh::PB, STEPS = Sh::STEPS, SLOTS = Sh::SLOTS;
+  constexpr int LEAD = Sh::LEAD;
+  static_assert(!PERSIST || (Sh::FP4 && !SS && !GATEUP && !Sh::MX8),
+                "persistent form: FP4 down projections with per-stage scales");
+  static_assert(!PERSIST || kPersistLds<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS> * Sh::BLOCKS_PER_CU <=
+                                160 * 1024, "the claimed-item word must fit beside the ring");
   extern __shared__ __align__(16) uint8_t s_dyn[];
   uint8_t* s_ss = s_dyn + NSTG * Sh::STAGE;  // super-stage scale slots (SS)
   // source row of each A tile row; lives in the last stage slot, which the first load
   // into it (stage LEAD, issued after the first barrier of the main loop) overwrites
-  int* s_tok = reinterpret_cast<int*>(s_dyn + Sh::LEAD * Sh::STAGE);
+  int* s_tok = reinterpret_cast<int*>(s_dyn + LEAD * Sh::STAGE);
+  int* s_claim = reinterpret_cast<int*>(s_dyn + Sh::SMEM);  // PERSIST: claimed item
 
   const int N = GATEUP ? a.I : a.H;  // rows of each weight matrix
   const int K = GATEUP ? a.H : a.I;  // a multiple of KC
   const int ncol_tiles = (N + NCOLS - 1) / NCOLS;
   Tile t;
   int ct;
-  if (!pre_resolve(a, ncol_tiles, t, ct)) return;
+  // PERSIST: this block's XCD, its range of items [wlo, wlo + wcnt), the XCD's blocks
+  int wx = 0, wlo = 0, wcnt = 0, wnb = 0;
+  if constexpr (PERSIST) {
+    const int real = a.src.ntiles[0] * ncol_tiles;
+    wx = blockIdx.x % kXcds;
+    wnb = gridDim.x / kXcds;
+    const int q = real / kXcds, rem = real % kXcds;
+    wlo = wx * q + (wx < rem ? wx : rem);
+    wcnt = q + (wx < rem ? 1 : 0);
+    const int j = blockIdx.x / kXcds;
+    if (j >= wcnt) return;
+    t = load_tile_header(a.src.tiles, (wlo + j) / ncol_tiles);
+    ct = (wlo + j) % ncol_tiles;
+  } else {
+    if (!pre_resolve(a, ncol_tiles, t, ct)) return;
+  }
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave / WN, wn = wave % WN;
   const int half = lane >> 5, r = lane & 31;
-  const int e = t.group;
-  const int n0 = ct * NCOLS;
+  int e = t.group;
+  int n0 = ct * NCOLS;
   const size_t row_bytes = (size_t)K * Sh::B_ROW / KC;
   const int sbytes = Sh::FP4 ? K / (FMT == 0 ? 16 : 32) : 0;
   // the two weight matrices (gate, up) or the one (down), by value: taking addresses of
@@ -294,77 +351,88 @@ void k_pre_gemm(ExpertGemmArgs a) {
   }
 
   // gathered token (gate+up) or h row (down); rows past the tile's count repeat its
-  // first row (results discarded)
-  for (int i = threadIdx.x; i < MT; i += NT) {
-    const int ii = i < t.count ? i : 0;
-    s_tok[i] = GATEUP ? a.row_token[t.row0 + ii] : t.row0 + ii;
-  }
-  __syncthreads();
-
-  // Source address of each load of this lane (fixed across stages, + the stage's K
-  // offset). The i-th load of a wave fills LDS slots (wave * n + i) * 64 + lane of its
-  // region; a slot holds the source piece that the swizzle assigns to it.
-  // A: PA pieces of 16 bytes per row, slot = piece ^ a_swz(row).
-  const uint16_t* asrc[NA];
-#pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int slot = (wave * NA + i) * 64 + lane;
-    const int row = slot / PA, piece = (slot % PA) ^ a_swz<PA>(row);
-    const uint16_t* base = GATEUP ? a.x + (size_t)s_tok[row] * a.H
-                                  : a.h + (size_t)s_tok[row] * a.h_stride;
-#if MOE_PRE_MX8
-    if (Sh::MX8)
-      base = reinterpret_cast<const uint16_t*>(a.a8) + (size_t)s_tok[row] * (GATEUP ? a.H : a.h_stride);
-#endif
-    asrc[i] = base + piece * 8;
-  }
-  // MX8: one (row, 32-code block) activation-scale pair of the stage per lane
-  const uint16_t* assrc = nullptr;
-#if MOE_PRE_MX8
-  if (Sh::MX8) {
-    const int pi = (wave * 64 + lane) % (MT * 2);
-    assrc = a.a8s + (size_t)s_tok[pi / 2] * (K / 32) + (pi % 2);
-  }
-#endif
-  // weight row of B-tile row brow; rows past N read row 0 of the expert (not stored)
-  auto wrow = [&](int brow, bool& second) -> size_t {
-    int n;
-    if (GATEUP) {
-      second = brow >= BROWS / 2;
-      n = n0 + (second ? brow - BROWS / 2 : brow);
-    } else {
-      second = false;
-      n = n0 + brow;
+  // first row (results discarded). The persistent form (down only) computes the rows.
+  if constexpr (!PERSIST) {
+    for (int i = threadIdx.x; i < MT; i += NT) {
+      const int ii = i < t.count ? i : 0;
+      s_tok[i] = GATEUP ? a.row_token[t.row0 + ii] : t.row0 + ii;
     }
-    return (size_t)e * N + (n < N ? n : 0);
-  };
-  // B: PB pieces of 16 bytes per row, slot = piece ^ b_swz(row)
+    __syncthreads();
+  }
+
+  // Source address of each load of this lane for the tile (tt, column tile ctt) (fixed
+  // across stages, + the stage's K offset). The i-th load of a wave fills LDS slots
+  // (wave * n + i) * 64 + lane of its region; a slot holds the source piece that the
+  // swizzle assigns to it.
+  const uint16_t* asrc[NA];
+  const uint16_t* assrc = nullptr;
   const uint8_t* bsrc[NB];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int slot = (wave * NB + i) * 64 + lane;
-    const int brow = slot / PB, piece = (slot % PB) ^ b_swz<PB>(brow);
-    bool m;
-    const size_t rw = wrow(brow, m);
-    bsrc[i] = (m ? pk1 : pk0) + rw * row_bytes + piece * 16;
-  }
   const uint8_t* ssrc[NS > 0 ? NS : 1];
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    bool m;
-    const int slot = (wave * NS + i) * 64 + lane;  // 4-byte slot u of its row: 64 codes
-    constexpr int SL = SLOTS > 0 ? SLOTS : 1;  // (no such loads for FP8 / BF16)
-    const size_t rw = wrow(slot / SL, m);
-    ssrc[i] = (m ? sc1 : sc0) + rw * sbytes + (slot % SL) * (FMT == 0 ? 4 : 2);
-  }
   const uint8_t* sssrc[NSS > 0 ? NSS : 1];
+  auto set_sources = [&](const Tile& tt, int ctt) __attribute__((always_inline)) {
+    const int te = tt.group, tn0 = ctt * NCOLS;
+    // persistent form: the lane index behind an empty asm, so that the per-lane slot
+    // arithmetic below is redone at each call instead of held in registers across the loop
+    int lane = threadIdx.x & 63;
+    if constexpr (PERSIST) asm volatile("" : "+v"(lane));
+    // A: PA pieces of 16 bytes per row, slot = piece ^ a_swz(row)
 #pragma unroll
-  for (int i = 0; i < NSS; ++i) {
-    bool m;
-    const int row = (wave * NSS + i) * 64 + lane;  // one lane per row (waves < SS_WAVES)
-    const size_t rw = wrow(row < BROWS ? row : 0, m);
-    sssrc[i] = (m ? sc1 : sc0) + rw * sbytes;
-  }
+    for (int i = 0; i < NA; ++i) {
+      const int slot = (wave * NA + i) * 64 + lane;
+      const int row = slot / PA, piece = (slot % PA) ^ a_swz<PA>(row);
+      const int src = PERSIST ? tt.row0 + (row < tt.count ? row : 0) : s_tok[row];
+      const uint16_t* base = GATEUP ? a.x + (size_t)src * a.H : a.h + (size_t)src * a.h_stride;
+#if MOE_PRE_MX8
+      if (Sh::MX8)
+        base = reinterpret_cast<const uint16_t*>(a.a8) + (size_t)src * (GATEUP ? a.H : a.h_stride);
+#endif
+      asrc[i] = base + piece * 8;
+    }
+    // MX8: one (row, 32-code block) activation-scale pair of the stage per lane
+#if MOE_PRE_MX8
+    if (Sh::MX8) {
+      const int pi = (wave * 64 + lane) % (MT * 2);
+      assrc = a.a8s + (size_t)s_tok[pi / 2] * (K / 32) + (pi % 2);
+    }
+#endif
+    // weight row of B-tile row brow; rows past N read row 0 of the expert (not stored)
+    auto wrow = [&](int brow, bool& second) -> size_t {
+      int n;
+      if (GATEUP) {
+        second = brow >= BROWS / 2;
+        n = tn0 + (second ? brow - BROWS / 2 : brow);
+      } else {
+        second = false;
+        n = tn0 + brow;
+      }
+      return (size_t)te * N + (n < N ? n : 0);
+    };
+    // B: PB pieces of 16 bytes per row, slot = piece ^ b_swz(row)
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int slot = (wave * NB + i) * 64 + lane;
+      const int brow = slot / PB, piece = (slot % PB) ^ b_swz<PB>(brow);
+      bool m;
+      const size_t rw = wrow(brow, m);
+      bsrc[i] = (m ? pk1 : pk0) + rw * row_bytes + piece * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      bool m;
+      const int slot = (wave * NS + i) * 64 + lane;  // 4-byte slot u of its row: 64 codes
+      constexpr int SL = SLOTS > 0 ? SLOTS : 1;  // (no such loads for FP8 / BF16)
+      const size_t rw = wrow(slot / SL, m);
+      ssrc[i] = (m ? sc1 : sc0) + rw * sbytes + (slot % SL) * (FMT == 0 ? 4 : 2);
+    }
+#pragma unroll
+    for (int i = 0; i < NSS; ++i) {
+      bool m;
+      const int row = (wave * NSS + i) * 64 + lane;  // one lane per row (waves < SS_WAVES)
+      const size_t rw = wrow(row < BROWS ? row : 0, m);
+      sssrc[i] = (m ? sc1 : sc0) + rw * sbytes;
+    }
+  };
+  set_sources(t, ct);
 
   // split z of a.ksplit takes K codes [kbase, kbase + K / ksplit) (a whole number of
   // super-stages when SS holds)
@@ -372,9 +440,10 @@ void k_pre_gemm(ExpertGemmArgs a) {
   const int kbase = blockIdx.z * kspan;
   const int nch = kspan / KC;
 
-  // Loads of stage c: always NLOADS per lane, so the wait count is a constant.
-  auto issue = [&](int c) __attribute__((always_inline)) {
-    const uint32_t abase = lds_addr(s_dyn + (c % NSTG) * Sh::STAGE);
+  // Loads of stage c into ring slot `slot`: always NLOADS per lane, so the wait count is a
+  // constant.
+  auto issue = [&](int c, int slot) __attribute__((always_inline)) {
+    const uint32_t abase = lds_addr(s_dyn + slot * Sh::STAGE);
     const uint32_t bbase = abase + Sh::A_BYTES, sbase = bbase + Sh::B_BYTES;
     const int k0 = kbase + c * KC;
     if (SS && c % SUPER == 0 && wave < Sh::SS_WAVES) {
@@ -412,6 +481,23 @@ void k_pre_gemm(ExpertGemmArgs a) {
     }
   };
 
+  // ring slot of the current tile's stage 0 (the persistent form carries the ring on
+  // from tile to tile), and whether a next tile was claimed (persistent form, from step 2)
+  int ring0 = 0;
+  bool has_next = false;
+  Tile tn{};
+  int ctn = 0;
+  // loads issued after the MFMA step of stage c: stage c + LEAD of this tile, or of the next
+  auto issue_after = [&](int c) __attribute__((always_inline)) {
+    const int n = c + LEAD;
+    const int slot = (ring0 + n) % NSTG;
+    if (n < nch) {
+      issue(n, slot);
+    } else if (PERSIST && has_next) {
+      issue(n - nch, slot);
+    }
+  };
+
   f32x16_t acc[RB][CB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -430,20 +516,16 @@ void k_pre_gemm(ExpertGemmArgs a) {
   const int arow = wm * 32 * RB + r;  // + rb * 32
   const int bsw = b_swz<PB>(r);  // = b_swz(brow0[cb] + r): brow0 is a multiple of 32
 
-  // row blocks of this wave that hold rows of the tile: a partly filled tile skips the
-  // MFMAs of its empty 32-row blocks
-  int nrb = (t.count - wm * 32 * RB + 31) / 32;
-  nrb = nrb < 0 ? 0 : (nrb > RB ? RB : nrb);
 
   // MFMAs of stage c for the first NR row blocks: STEPS steps of K 16, lane half h
   // covering codes (KC/2)h..(KC/2)h+KC/2-1 of the stage (8 per step)
   auto stage_mma = [&](auto nr_c, int c) __attribute__((always_inline)) {
     constexpr int NR = decltype(nr_c)::value;
     if constexpr (NR == 0) {
-      if (c + Sh::LEAD < nch) issue(c + Sh::LEAD);
+      issue_after(c);
       return;
     }
-    const uint8_t* sa = s_dyn + (c % NSTG) * Sh::STAGE;
+    const uint8_t* sa = s_dyn + ((ring0 + c) % NSTG) * Sh::STAGE;
     const uint8_t* sbq = sa + Sh::A_BYTES;
     const uint8_t* ssc = sbq + Sh::B_BYTES;
     constexpr int WPS = Sh::WPS;
@@ -485,7 +567,7 @@ void k_pre_gemm(ExpertGemmArgs a) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
         wq[cb] = v8i_t{(int)q[cb][0], (int)q[cb][1], (int)q[cb][2], (int)q[cb][3], 0, 0, 0, 0};
-      if (c + Sh::LEAD < nch) issue(c + Sh::LEAD);
+      issue_after(c);
 #pragma unroll
       for (int rb = 0; rb < NR; ++rb) {
         const int row = arow + rb * 32;
@@ -527,7 +609,7 @@ void k_pre_gemm(ExpertGemmArgs a) {
 #pragma unroll
     for (int s = 0; s < AHEAD; ++s) read_a(s);
     // the loads of stage c + LEAD go out while this stage's LDS reads are in flight
-    if (c + Sh::LEAD < nch) issue(c + Sh::LEAD);
+    issue_after(c);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
@@ -559,15 +641,15 @@ void k_pre_gemm(ExpertGemmArgs a) {
   };
 
 #pragma unroll
-  for (int i = 0; i < Sh::LEAD; ++i)
-    if (i < nch) issue(i);
+  for (int i = 0; i < LEAD; ++i)
+    if (i < nch) issue(i, i % NSTG);
   auto kloop = [&](auto nr_c) __attribute__((always_inline)) {
 #pragma unroll 1
     for (int c = 0; c < nch; ++c) {
       // may stay in flight: stages c+1 .. c+LEAD-1 (fewer near the end), one of which may
       // start a super-stage of scales (at most one: LEAD <= SUPER)
       int inflight = nch - 1 - c;
-      inflight = inflight < Sh::LEAD - 1 ? inflight : Sh::LEAD - 1;
+      inflight = inflight < LEAD - 1 ? inflight : LEAD - 1;
       bool ss = false;
       if (SS && wave < Sh::SS_WAVES) {
         const int next = (c / SUPER + 1) * SUPER;  // first super-stage start after c
@@ -577,96 +659,163 @@ void k_pre_gemm(ExpertGemmArgs a) {
       stage_mma(nr_c, c);
     }
   };
-  if (nrb >= RB) {
-    kloop(std::integral_constant<int, RB>{});
-  } else if (nrb == 1) {
-    kloop(std::integral_constant<int, 1>{});
-  } else if (nrb == 2) {  // (RB > 2 only)
-    kloop(std::integral_constant<int, (RB > 2 ? 2 : 1)>{});
-  } else if (nrb == 3) {  // (RB > 3 only)
-    kloop(std::integral_constant<int, (RB > 3 ? 3 : 1)>{});
-  } else {
-    kloop(std::integral_constant<int, 0>{});
-  }
+  // persistent form: the same steps in two runs. Steps 0 .. nch - LEAD - 1 claim the next
+  // tile (step 0 takes the item, step 1 publishes it in LDS); between the runs every wave
+  // reads the claim, the next tile's header and its load sources; steps nch - LEAD .. nch - 1
+  // then issue the next tile's first LEAD stages (nch >= LEAD + 3, checked by the launcher).
+  // No next-tile state is carried from step to step.
+  int claim = 0;
+  auto kloop_persist = [&](auto nr_c) __attribute__((always_inline)) {
+#pragma unroll 1
+    for (int c = 0; c < nch - LEAD; ++c) {
+      wait_inflight<Sh::NLOADS, NSS>(LEAD - 1, false);
+      if (c == 0) {
+        // claimed before this step's loads, so the next step's wait covers it; an
+        // increment that wraps only at 2^32 - 1 (not an add, which the compiler would
+        // spread over the wave and wait for at once)
+        if (threadIdx.x == 0)
+          claim = (int)__builtin_amdgcn_atomic_inc32(
+              reinterpret_cast<unsigned*>(a.work + wx * kWorkCtrStride), 0xFFFFFFFFu,
+              __ATOMIC_RELAXED, "agent");
+      } else if (c == 1) {
+        if (threadIdx.x == 0) *s_claim = claim;
+      }
+      stage_mma(nr_c, c);
+    }
+    // (the claim was written at step 1 and the barrier of step 2 has passed)
+    const int jn = wnb + __builtin_amdgcn_readfirstlane(*s_claim);
+    has_next = jn < wcnt;
+    if (has_next) {
+      tn = load_tile_header(a.src.tiles, (wlo + jn) / ncol_tiles);
+      ctn = (wlo + jn) % ncol_tiles;
+      set_sources(tn, ctn);
+    }
+#pragma unroll 1
+    for (int c = nch - LEAD; c < nch; ++c) {
+      int inflight = LEAD - 1;
+      if (!has_next && nch - 1 - c < inflight) inflight = nch - 1 - c;
+      wait_inflight<Sh::NLOADS, NSS>(inflight, false);
+      stage_mma(nr_c, c);
+    }
+  };
+  // row blocks of this wave that hold rows of the tile: a partly filled tile skips the
+  // MFMAs of its empty 32-row blocks
+  auto run_tile = [&](auto loop) __attribute__((always_inline)) {
+    int nrb = (t.count - wm * 32 * RB + 31) / 32;
+    nrb = nrb < 0 ? 0 : (nrb > RB ? RB : nrb);
+    if (nrb >= RB) {
+      loop(std::integral_constant<int, RB>{});
+    } else if (nrb == 1) {
+      loop(std::integral_constant<int, 1>{});
+    } else if (nrb == 2) {  // (RB > 2 only)
+      loop(std::integral_constant<int, (RB > 2 ? 2 : 1)>{});
+    } else if (nrb == 3) {  // (RB > 3 only)
+      loop(std::integral_constant<int, (RB > 3 ? 3 : 1)>{});
+    } else {
+      loop(std::integral_constant<int, 0>{});
+    }
+  };
 
   // epilogue. The weights are the MFMA's first operand, so block (rb, cb) holds
   // out[token][n] transposed: lane l owns token row wm*32*RB + rb*32 + l % 32 and, in
   // element v, column 8*(v/4) + 4*half + v%4 of the 32-column block, i.e. four runs of 4
   // consecutive columns, each stored as one write (8 bytes of h, 16 bytes of y). Column blocks are 32-aligned
   // and N is a multiple of 32, so a block is wholly inside N or wholly outside.
-  if (a.ksplit > 1) {
-    // split K: the raw fp32 sums of this split, [split][row][gate cols | up cols] or
-    // [split][row][H] (rows relative to the implicit list); scales and SwiGLU come with
-    // the reduce
-    const int NO = GATEUP ? 2 * a.I : a.H;
-    float* prow0 = a.part + (size_t)blockIdx.z * a.src.implicit_rows * NO;
+  auto epilogue = [&]() __attribute__((always_inline)) {
+    if (!PERSIST && a.ksplit > 1) {  // (the persistent form never splits K)
+      // split K: the raw fp32 sums of this split, [split][row][gate cols | up cols] or
+      // [split][row][H] (rows relative to the implicit list); scales and SwiGLU come with
+      // the reduce
+      const int NO = GATEUP ? 2 * a.I : a.H;
+      float* prow0 = a.part + (size_t)blockIdx.z * a.src.implicit_rows * NO;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int col = GATEUP ? n0 + wn * CH * 32 + (cb % CH) * 32 : n0 + wn * CB * 32 + cb * 32;
-      if (col >= N) continue;
-      const int ocol = GATEUP && cb >= CH ? a.I + col : col;
+      for (int cb = 0; cb < CB; ++cb) {
+        const int col = GATEUP ? n0 + wn * CH * 32 + (cb % CH) * 32 : n0 + wn * CB * 32 + cb * 32;
+        if (col >= N) continue;
+        const int ocol = GATEUP && cb >= CH ? a.I + col : col;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int i = wm * 32 * RB + rb * 32 + r;
-        if (i >= t.count) continue;
-        float* prow = prow0 + (size_t)(t.row0 + i - a.src.implicit_row0) * NO + ocol + 4 * half;
+        for (int rb = 0; rb < RB; ++rb) {
+          const int i = wm * 32 * RB + rb * 32 + r;
+          if (i >= t.count) continue;
+          float* prow = prow0 + (size_t)(t.row0 + i - a.src.implicit_row0) * NO + ocol + 4 * half;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x16_t& cc = acc[rb][cb];
-          *reinterpret_cast<float4*>(prow + 8 * g4) =
-              make_float4(cc[4 * g4], cc[4 * g4 + 1], cc[4 * g4 + 2], cc[4 * g4 + 3]);
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x16_t& cc = acc[rb][cb];
+            *reinterpret_cast<float4*>(prow + 8 * g4) =
+                make_float4(cc[4 * g4], cc[4 * g4 + 1], cc[4 * g4 + 2], cc[4 * g4 + 3]);
+          }
+        }
+      }
+    } else if (GATEUP) {
+      const float gs_g = FMT == 0 ? a.gate.global[e] : 1.0f;
+      const float gs_u = FMT == 0 ? a.up.global[e] : 1.0f;
+#pragma unroll
+      for (int cg = 0; cg < CH; ++cg) {
+        const int nb = n0 + wn * CH * 32 + cg * 32;
+        if (nb >= N) continue;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int i = wm * 32 * RB + rb * 32 + r;
+          if (i >= t.count) continue;
+          uint16_t* hrow = a.h + (size_t)(t.row0 + i) * a.h_stride + nb + 4 * half;
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            float hv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float g = acc[rb][cg][4 * g4 + j] * gs_g;
+              const float u = acc[rb][CH + cg][4 * g4 + j] * gs_u;
+              hv[j] = silu(g) * u;
+            }
+            *reinterpret_cast<uint2*>(hrow + 8 * g4) =
+                make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+          }
+        }
+      }
+    } else {
+      // y stays fp32 (the blend reads it once): rounding it to bf16 would add up to half
+      // a bf16 ulp of every expert output to the layer's error
+      const float gs = FMT == 0 ? load_uniform_f32(a.down.global, e) : 1.0f;
+      float* y = reinterpret_cast<float*>(a.y);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int nb = n0 + wn * CB * 32 + cb * 32;
+        if (nb >= N) continue;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int i = wm * 32 * RB + rb * 32 + r;
+          if (i >= t.count) continue;
+          float* yrow = y + (size_t)(t.row0 + i) * a.H + nb + 4 * half;
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x16_t& c = acc[rb][cb];
+            *reinterpret_cast<float4*>(yrow + 8 * g4) =
+                make_float4(c[4 * g4] * gs, c[4 * g4 + 1] * gs, c[4 * g4 + 2] * gs,
+                            c[4 * g4 + 3] * gs);
+          }
         }
       }
     }
-  } else if (GATEUP) {
-    const float gs_g = FMT == 0 ? a.gate.global[e] : 1.0f;
-    const float gs_u = FMT == 0 ? a.up.global[e] : 1.0f;
+  };
+
+  if constexpr (PERSIST) {
+    for (;;) {
+      run_tile(kloop_persist);
+      epilogue();
+      if (!has_next) break;
+      t = tn;
+      ct = ctn;
+      e = t.group;
+      n0 = ct * NCOLS;
+      ring0 = (ring0 + nch) % NSTG;
 #pragma unroll
-    for (int cg = 0; cg < CH; ++cg) {
-      const int nb = n0 + wn * CH * 32 + cg * 32;
-      if (nb >= N) continue;
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int i = wm * 32 * RB + rb * 32 + r;
-        if (i >= t.count) continue;
-        uint16_t* hrow = a.h + (size_t)(t.row0 + i) * a.h_stride + nb + 4 * half;
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          float hv[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float g = acc[rb][cg][4 * g4 + j] * gs_g;
-            const float u = acc[rb][CH + cg][4 * g4 + j] * gs_u;
-            hv[j] = silu(g) * u;
-          }
-          *reinterpret_cast<uint2*>(hrow + 8 * g4) =
-              make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
-        }
-      }
+        for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x16_t{};
     }
   } else {
-    // y stays fp32 (the blend reads it once): rounding it to bf16 would add up to half
-    // a bf16 ulp of every expert output to the layer's error
-    const float gs = FMT == 0 ? a.down.global[e] : 1.0f;
-    float* y = reinterpret_cast<float*>(a.y);
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int nb = n0 + wn * CB * 32 + cb * 32;
-      if (nb >= N) continue;
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int i = wm * 32 * RB + rb * 32 + r;
-        if (i >= t.count) continue;
-        float* yrow = y + (size_t)(t.row0 + i) * a.H + nb + 4 * half;
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x16_t& c = acc[rb][cb];
-          *reinterpret_cast<float4*>(yrow + 8 * g4) =
-              make_float4(c[4 * g4] * gs, c[4 * g4 + 1] * gs, c[4 * g4 + 2] * gs,
-                          c[4 * g4 + 3] * gs);
-        }
-      }
-    }
+    run_tile(kloop);
+    epilogue();
   }
 }
 
@@ -743,22 +892,54 @@ static int pick_ksplit(const ExpertGemmArgs& a, int K, int KC, int unit, int blo
   return best;
 }
 
+// The persistent form (down projections of FP4 weights with per-stage scales, over the
+// device tile list): when the tile grid exceeds the resident block slots and each tile
+// has enough stages for the claim of the next one to land first.
+#ifndef MOE_PRE_PERSIST
+#define MOE_PRE_PERSIST 1
+#endif
+template <int FMT, int KC, int NSTG, int RB, int WM, int CB, bool GATEUP, bool SS>
+constexpr bool kCanPersist = MOE_PRE_PERSIST && !GATEUP && !SS && FMT <= 1 &&
+                             !PreShape<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS>::MX8;
+
+template <int FMT, int KC, int NSTG, int RB, int WM, int CB, bool GATEUP, bool SS, bool PERSIST>
+static hipError_t set_lds_limit() {
+  using Sh = PreShape<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS>;
+  const int bytes = PERSIST ? kPersistLds<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS> : (int)Sh::SMEM;
+  // one attribute call per instantiation and process (a function-local static: thread-safe)
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(k_pre_gemm<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS, PERSIST>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  return attr;
+}
+
 template <int FMT, int KC, int NSTG, int RB, int WM, int CB, bool GATEUP, bool SS>
 static hipError_t launch_pre_ss(const ExpertGemmArgs& a0, hipStream_t s) {
   using Sh = PreShape<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS>;
   const int N = GATEUP ? a0.I : a0.H;
   const int K = GATEUP ? a0.H : a0.I;
   const int ncol = (N + Sh::NCOLS - 1) / Sh::NCOLS;
+  const int slots = device_cus() * Sh::BLOCKS_PER_CU;
   ExpertGemmArgs a = a0;
   // FP8 / BF16 blocks keep the whole K (the FP8 block-scale table is per block)
-  a.ksplit = Sh::FP4 ? pick_ksplit(a, K, KC, SS ? KC * Sh::SUPER : KC, ncol * a.tile_bound,
-                                   device_cus() * Sh::BLOCKS_PER_CU, GATEUP ? 2 * a.I : a.H)
+  a.ksplit = Sh::FP4 ? pick_ksplit(a, K, KC, SS ? KC * Sh::SUPER : KC, ncol * a.tile_bound, slots,
+                                   GATEUP ? 2 * a.I : a.H)
                      : 1;
-  auto kern = k_pre_gemm<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS>;
-  // one attribute call per instantiation and process (a function-local static: thread-safe)
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::SMEM);
+  if constexpr (kCanPersist<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS>) {
+    const int grid = slots / kXcds * kXcds;
+    if (a.work && a.src.tiles && a.ksplit == 1 && K / KC >= Sh::LEAD + 3 && grid > 0 &&
+        (long long)ncol * a.tile_bound > grid) {
+      const hipError_t attr = set_lds_limit<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS, true>();
+      if (attr != hipSuccess) return attr;
+      constexpr int lds = kPersistLds<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS>;
+      auto kern = k_pre_gemm<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS, true>;
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(Sh::NT), lds, s, a);
+      return hipGetLastError();
+    }
+  }
+  const hipError_t attr = set_lds_limit<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS, false>();
   if (attr != hipSuccess) return attr;
+  auto kern = k_pre_gemm<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS, false>;
   hipLaunchKernelGGL(kern, dim3(ncol, a.tile_bound, a.ksplit), dim3(Sh::NT), Sh::SMEM, s, a);
   if (a.ksplit > 1) {
     const int nc = GATEUP ? a.I : a.H;

@@ -344,7 +344,7 @@ __device__ void dispatch_bitmap(const DispatchArgs& a, const int32_t* ids, const
     }
   }
   if (tid == 0) {
-    a.ntiles[0] = all >> 16;
+    publish_tile_count(a.ntiles, all >> 16);
     a.err_word[0] = *s_err;
   }
   __syncthreads();
@@ -502,7 +502,7 @@ __device__ void dispatch_body(const DispatchArgs& a, const int32_t* ids, const i
   int ntot = 0;
   write_tiles<NW>(a, cnt, s_off, s_tmp, &ntot);
   if (tid == 0) {
-    a.ntiles[0] = ntot;
+    publish_tile_count(a.ntiles, ntot);
     a.err_word[0] = *s_err;
   }
 }

@@ -444,6 +444,62 @@ def test_prefill_partly_filled_tiles(fmt):
     assert_layer_close(out.float().cpu().numpy(), want, f32(inp.residual), "partial-tiles")
 
 
+def _distinct_pairs(T, E, rng):
+    """[T, 2] expert ids, two distinct experts per token, Zipf-like expert popularity."""
+    pop = 1.0 / np.arange(1, E + 1) ** 0.8
+    pop /= pop.sum()
+    first = rng.choice(E, size=T, p=pop)
+    second = (first + 1 + rng.choice(E - 1, size=T)) % E
+    return np.stack([first, second], axis=1).astype(np.int32)
+
+
+@pytest.mark.parametrize("fmt", [S.NVFP4, S.MXFP4])
+@pytest.mark.parametrize("shape", ["mt128", "mt64", "mt32_5stages"])
+def test_prefill_persistent_down(fmt, shape):
+    """Down projections on the persistent grid: more (row tile, column tile) items at
+    hidden 4096 than the chip has block slots, so blocks claim further tiles from their
+    XCD's counter and run the stage ring on from tile to tile, with ragged last tiles.
+    Tile heights 128, 64 and 32 (the 32-row case with 5 stages of 128 codes, the fewest
+    the persistent form takes)."""
+    E, I, T = {"mt128": (8, 512, 2074), "mt64": (64, 512, 2048),
+               "mt32_5stages": (128, 640, 2048)}[shape]
+    _announce("persistent down", shape, fmt)
+    spec = S.LayerSpec(name=f"persist_{shape}", tokens=T, hidden=4096, experts=E, top_k=2,
+                       inter=I, fmt=fmt, seed=1200 + fmt)
+    inp = S.make_inputs(spec, device=DEV)
+    rng = np.random.default_rng(11)
+    if shape == "mt128":
+        counts = [2049, 1101, 513, 257, 129, 65, 33, 1]  # ragged last tiles, 39 tiles
+        labels = np.repeat(np.arange(E), counts)
+        oids = np.stack([labels[:T], labels[T:]], axis=1).astype(np.int32)
+    else:
+        oids = _distinct_pairs(T, E, rng)
+    assert (oids[:, 0] != oids[:, 1]).all()
+    ow = rng.uniform(0.1, 1.0, size=(T, 2)).astype(np.float32)
+    # the launch is persistent: column tiles x tile bound above the resident slots
+    mt = 128 if shape == "mt128" else (64 if shape == "mt64" else 32)
+    tiles = sum(-(-int(c) // mt) for c in np.bincount(oids.ravel(), minlength=E))
+    slots = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    assert (4096 // 256) * tiles > slots, (tiles, slots)
+    cfg = config_for(inp, M.PATH_PREFILL)
+    ws = M.alloc_workspace(cfg, DEV)
+    out = torch.empty_like(inp.x)
+    M.experts_forward(cfg, inp.x, torch.from_numpy(oids).to(DEV), torch.from_numpy(ow).to(DEV),
+                      M.expert_weights(inp.routed), None, inp.residual, out, ws)
+    _sync()
+    assert M.get_device_error(ws) == 0
+    want = O.experts_forward(f32(inp.x), oids, ow.astype(np.float64),
+                             oracle_cache(inp.routed), f32(inp.residual),
+                             workers=oracle_workers())
+    assert_layer_close(out.float().cpu().numpy(), want, f32(inp.residual), f"persist-{shape}")
+    # a second call on the same workspace: the counters start again from zero
+    out2 = torch.empty_like(out)
+    M.experts_forward(cfg, inp.x, torch.from_numpy(oids).to(DEV), torch.from_numpy(ow).to(DEV),
+                      M.expert_weights(inp.routed), None, inp.residual, out2, ws)
+    _sync()
+    assert torch.equal(out, out2)
+
+
 def spec_e(inp):
     return inp.spec.experts
 

@@ -19,6 +19,7 @@ the 256 MB Infinity Cache.
 from __future__ import annotations
 
 import argparse
+import statistics
 import ctypes
 import gc
 import hashlib
@@ -536,6 +537,73 @@ def brief(r):
     return b
 
 
+PEAK_HBM_TBPS = 8.0          # MI355X published HBM3E bandwidth
+PEAK_BF16_TFLOPS = 2500.0    # dense bf16 MFMA
+PEAK_FP4_TFLOPS = 10100.0    # dense fp6/fp4 MFMA (the FP4 x FP8 probe runs at the fp8 rate)
+PEAK_FP8_TFLOPS = 5000.0
+
+
+def microbench(M, torch):
+    """Achievable rates of the paths the kernels use (moe_probe_* entry points): streaming
+    read of 16 MB .. 512 MB regions rotated through a 2 GiB pool (so that the 256 MB Infinity
+    Cache does not serve a repeat), and the MFMA probes at one and two blocks per CU, each
+    with the shader clock it sustained (its s_memtime cycles over the event time)."""
+    res = {"metric": "microbench", "read": [], "mfma": []}
+    pool = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    pool.fill_(1)
+    sink = torch.zeros(M.PROBE_READ_BLOCKS, dtype=torch.float32, device="cuda")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for mb in (16, 84, 200, 512):
+        n = mb << 20
+        regions = max(1, pool.numel() // n)
+        times = []
+        for rep in range(3 * regions + 2):
+            src = pool[(rep % regions) * n:(rep % regions) * n + n]
+            ev0.record()
+            M.probe_stream_read(src, sink)
+            ev1.record()
+            ev1.synchronize()
+            if rep >= 2:
+                times.append(ev0.elapsed_time(ev1) * 1e-3)
+        best, med = min(times), statistics.median(times)
+        res["read"].append({"MB": mb, "TBps_best": round(n / best / 1e12, 3),
+                            "TBps_median": round(n / med / 1e12, 3),
+                            "frac_of_8TBps": round(n / med / 1e12 / PEAK_HBM_TBPS, 3)})
+        log(f"[microbench] read {mb} MB: {res['read'][-1]}")
+    names = {0: ("bf16 32x32x16", 32768, PEAK_BF16_TFLOPS),
+             1: ("scaled fp4 x fp8 32x32x64", 131072, PEAK_FP8_TFLOPS),
+             2: ("mxfp4 decode + bf16 32x32x16 (GEMM step mix)", 32768, PEAK_BF16_TFLOPS)}
+    for kind, (name, flop, peak) in names.items():
+        for bpc in (1, 2):
+            blocks = M.probe_mfma_blocks(bpc)
+            msink = torch.zeros(blocks, dtype=torch.float32, device="cuda")
+            cyc = torch.zeros(blocks, dtype=torch.int64, device="cuda")
+            iters = 4096
+            M.probe_mfma(kind, 64, bpc, msink, cyc)  # warm up
+            ts = []
+            for _ in range(5):
+                ev0.record()
+                M.probe_mfma(kind, iters, bpc, msink, cyc)
+                ev1.record()
+                ev1.synchronize()
+                ts.append(ev0.elapsed_time(ev1) * 1e-3)
+            t = statistics.median(ts)
+            flops = blocks * 4 * iters * 8 * flop
+            tf = flops / t / 1e12
+            entry = {"kind": name, "blocks_per_cu": bpc, "TFLOPs": round(tf, 1),
+                     "frac_of_published": round(tf / peak, 3)}
+            if bpc == 1:
+                # one block per CU: every block runs for the whole launch, so its cycles over
+                # the launch time give the clock (with two, a block's lifetime is not the
+                # launch's)
+                clock = float(cyc.double().mean().item()) / t / 1e9
+                entry["clock_GHz"] = round(clock, 3)
+                entry["frac_at_that_clock"] = round(tf / (peak * clock / 2.4), 3)
+            res["mfma"].append(entry)
+            log(f"[microbench] mfma: {res['mfma'][-1]}")
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -564,6 +632,9 @@ def main():
     ap.add_argument("--summarize-traffic", metavar="DIR",
                     help="write the workload's HBM traffic file from rocprofv3 --pmc runs in "
                          "DIR/{fetch,write,copy_fetch,copy_write} and exit")
+    ap.add_argument("--microbench", action="store_true",
+                    help="only measure the achievable rates (streaming read, MFMA probes with "
+                         "their sustained clock) and print them as one JSON line")
     ap.add_argument("--command", action="append", default=[],
                     help="command line recorded in a summary (repeatable)")
     args = ap.parse_args()
@@ -601,6 +672,9 @@ def main():
         M.load_library(args.lib)
     else:
         M.load_library()
+    if args.microbench:
+        microbench(M, torch)
+        return
     result = run_workload(args.workload, args)
     if args.workload == DEFAULT_WORKLOAD and args.tokens <= 0 and not args.no_others:
         others = {}

@@ -266,6 +266,31 @@ int moe_layer_forward_noalloc(const moe_config* cfg, const uint16_t* x,
 int moe_debug_dequant_fp4(const moe_fp4_weight* w, int32_t expert, int32_t path, float* out,
                           hipStream_t stream);
 
+/* Measurement probes (not part of the layer): the achievable rates that the kernels'
+ * rooflines are read against, reproducible with bench.py --microbench. Each enqueues one
+ * kernel on `stream` and returns at once; the caller times it (events) and owns every
+ * buffer. None reads or writes anything but the buffers named here.
+ *
+ * moe_probe_stream_read: reads `bytes` (a multiple of 16) from `src` (16-byte aligned)
+ *   with 16-byte loads, one contiguous chunk per block of 256 threads over
+ *   MOE_PROBE_READ_BLOCKS blocks, eight loads in flight per thread. `sink`:
+ *   MOE_PROBE_READ_BLOCKS floats, written only on a data pattern that never occurs (it
+ *   keeps the loads). MOE_ERR_INVALID_ARG on a null or misaligned pointer or a bad size.
+ * moe_probe_mfma_blocks: blocks that moe_probe_mfma launches for `blocks_per_cu` (1 or 2):
+ *   compute units x blocks_per_cu, or a negative moe_status.
+ * moe_probe_mfma: each 4-wave block (one wave per SIMD) runs `iters` rounds of 8
+ *   independent MFMAs on register operands. kind 0: v_mfma_f32_32x32x16_bf16 (32768
+ *   flops each); kind 1: v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 x E4M3 operands
+ *   (131072 flops each; the pages' block-scaled FP4 MMA, MoE constructor page); kind 2:
+ *   the prefill GEMM's step, two MXFP4 operands decoded to bf16 per 8 bf16 MFMAs.
+ *   `sink`, `cycles`: moe_probe_mfma_blocks(blocks_per_cu) entries each; cycles[b] =
+ *   shader-clock cycles (s_memtime) between block b's first and last instruction. */
+#define MOE_PROBE_READ_BLOCKS 2048
+int moe_probe_stream_read(const void* src, size_t bytes, float* sink, hipStream_t stream);
+int moe_probe_mfma_blocks(int32_t blocks_per_cu);
+int moe_probe_mfma(int32_t kind, int32_t iters, int32_t blocks_per_cu, float* sink,
+                   uint64_t* cycles, hipStream_t stream);
+
 /* Profiling aid: stage boundaries of moe_layer_forward, in launch order. */
 enum {
   MOE_STAGE_BEGIN = 0,        /* before the first kernel of the call */

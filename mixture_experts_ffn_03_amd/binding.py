@@ -72,7 +72,11 @@ EXPORTS = {
                                              ctypes.c_int32, _P, _P]),
     "moe_get_device_error": (ctypes.c_int, [_P, _SZ, ctypes.POINTER(ctypes.c_int32), _P]),
     "moe_set_stage_events": (ctypes.c_int, [_P, ctypes.c_int32]),
+    "moe_probe_stream_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
+    "moe_probe_mfma_blocks": (ctypes.c_int, [ctypes.c_int32]),
+    "moe_probe_mfma": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
 }
+PROBE_READ_BLOCKS = 2048
 
 STAGE_COUNT = 7
 STAGE_NAMES = ["begin", "routed", "dispatched", "gate_up", "down", "shared", "combined"]
@@ -215,3 +219,26 @@ def set_stage_events(events_array, count: int):
     _check(load_library().moe_set_stage_events(
         ctypes.cast(events_array, ctypes.c_void_p) if events_array is not None else None, count),
         "moe_set_stage_events")
+
+
+def probe_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Enqueue the streaming-read probe over all of `src` (bytes a multiple of 16);
+    `sink`: PROBE_READ_BLOCKS float32."""
+    _check(load_library().moe_probe_stream_read(_ptr(src), src.numel() * src.element_size(),
+                                                _ptr(sink), _stream(stream)),
+           "moe_probe_stream_read")
+
+
+def probe_mfma_blocks(blocks_per_cu: int) -> int:
+    n = load_library().moe_probe_mfma_blocks(blocks_per_cu)
+    if n < 0:
+        raise MoeError(n, "moe_probe_mfma_blocks")
+    return n
+
+
+def probe_mfma(kind: int, iters: int, blocks_per_cu: int, sink: torch.Tensor,
+               cycles: torch.Tensor, stream=None):
+    """Enqueue the MFMA-rate probe (kind 0 bf16, 1 scaled FP4 x FP8, 2 MXFP4 decode + bf16);
+    `sink` float32 and `cycles` int64, probe_mfma_blocks(blocks_per_cu) entries each."""
+    _check(load_library().moe_probe_mfma(kind, iters, blocks_per_cu, _ptr(sink), _ptr(cycles),
+                                         _stream(stream)), "moe_probe_mfma")

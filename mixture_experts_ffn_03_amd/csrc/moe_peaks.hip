@@ -1,0 +1,149 @@
+// Measurement probes: the achievable rates of the hardware paths the layer's kernels are
+// built on, so that the peaks their rooflines are read against can be reproduced
+// (streaming HBM read with 16-byte loads; the bf16 32x32x16 MFMA; the block-scaled
+// FP4 x FP8 32x32x64 MFMA; and the prefill GEMM's inner mix of MXFP4 operand decodes and
+// bf16 MFMAs). Each MFMA probe also returns the shader-clock cycles its blocks ran for, so
+// that the clock the chip sustains under that load can be read off next to the rate.
+#include "moe_fp4.h"
+#include "moe_device.h"
+
+namespace moe {
+
+constexpr int kProbeReadBlocks = 2048;  // MOE_PROBE_READ_BLOCKS
+constexpr int kProbeThreads = 256;      // four waves, one per SIMD
+constexpr int kProbeChains = 8;         // independent MFMA accumulators per wave
+
+// Streaming read: block b reads the b-th contiguous chunk of the region, each thread eight
+// 16-byte pieces in flight per round (the fastest of the grid-stride and per-block-chunk
+// shapes measured, 2048 x 256 threads). The pieces' XOR feeds the output, so no load can
+// be dropped; a block writes its sink slot only if its XOR hits one particular value.
+__global__ __launch_bounds__(kProbeThreads) void k_probe_read(const uint4* __restrict__ p,
+                                                             size_t n, float* sink) {
+  constexpr int U = 8;
+  const size_t per = (n + gridDim.x - 1) / gridDim.x;
+  const size_t b0 = (size_t)blockIdx.x * per;
+  const size_t b1 = b0 + per < n ? b0 + per : n;
+  uint32_t acc = 0;
+  size_t i = b0 + threadIdx.x;
+  for (; i + (U - 1) * kProbeThreads < b1; i += U * kProbeThreads) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = p[i + u * kProbeThreads];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < b1; i += kProbeThreads) {
+    const uint4 a = p[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x] = 1.0f;
+}
+
+// MFMA issue rate: each wave runs `iters` rounds of kProbeChains independent MFMAs on
+// register operands. KIND 0: v_mfma_f32_32x32x16_bf16. KIND 1: the block-scaled
+// v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 first and E4M3 second operands. KIND 2: the
+// prefill GEMM's step, two MXFP4 operands decoded to bf16 (scaled converts) per eight bf16
+// MFMAs (four row blocks x two column blocks), the codes changing every round.
+template <int KIND>
+__global__ __launch_bounds__(kProbeThreads) void k_probe_mfma(int iters, float* sink,
+                                                             unsigned long long* cycles) {
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const int lane = threadIdx.x & 63;
+  f32x16_t acc[kProbeChains];
+#pragma unroll
+  for (int j = 0; j < kProbeChains; ++j) acc[j] = f32x16_t{};
+  if constexpr (KIND == 0) {
+    uint32_t d[4] = {0x3F803F80u + lane, 0x3F003F00u, 0x3E803E80u, 0x3F803F80u};
+    bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(d[0], d[1], d[2], d[3]));
+    bf16x8_t b = __builtin_bit_cast(bf16x8_t, make_uint4(d[3], d[2], d[1], d[0]));
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < kProbeChains; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+    }
+  } else if constexpr (KIND == 1) {
+    typedef int v8i_t __attribute__((ext_vector_type(8)));
+    const v8i_t a{0x22222222 + lane, 0x11111111, 0x33333333, 0x12121212, 0, 0, 0, 0};
+    const v8i_t b{0x38383838, 0x30303030 + lane, 0x38303830, 0x30383038,
+                  0x38383838, 0x30303030, 0x38303830, 0x30383038};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < kProbeChains; ++j)
+        acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[j], 4, 0, 0, 127, 0, 127);
+    }
+  } else {
+    uint32_t q0 = 0x12345678u + lane, q1 = 0x9ABCDEF0u - lane;
+    uint32_t d[4] = {0x3F803F80u + lane, 0x3F003F00u, 0x3E803E80u, 0x3F803F80u};
+    bf16x8_t av[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      av[r] = __builtin_bit_cast(bf16x8_t, make_uint4(d[r & 3] + r, d[(r + 1) & 3], d[2], d[3]));
+    for (int it = 0; it < iters; ++it) {
+      uint32_t b0[4], b1[4];
+      mfma_operand_fp4x8<1>(q0 ^ (uint32_t)it, 127u, b0);
+      mfma_operand_fp4x8<1>(q1 + (uint32_t)it, 126u, b1);
+      const bf16x8_t bo0 = __builtin_bit_cast(bf16x8_t, make_uint4(b0[0], b0[1], b0[2], b0[3]));
+      const bf16x8_t bo1 = __builtin_bit_cast(bf16x8_t, make_uint4(b1[0], b1[1], b1[2], b1[3]));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        acc[2 * r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo0, av[r], acc[2 * r], 0, 0, 0);
+        acc[2 * r + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo1, av[r], acc[2 * r + 1], 0, 0, 0);
+      }
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kProbeChains; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s += acc[j][v];
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  if (s != s) sink[blockIdx.x] = s;  // keeps the MFMAs: finite operands never give a NaN
+  if (threadIdx.x == 0) cycles[blockIdx.x] = t1 - t0;
+}
+
+static int probe_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  return n;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+int moe_probe_stream_read(const void* src, size_t bytes, float* sink, hipStream_t stream) {
+  using namespace moe;
+  if (!src || !sink || bytes == 0 || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(src) & 15u))
+    return MOE_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(k_probe_read, dim3(kProbeReadBlocks), dim3(kProbeThreads), 0, stream,
+                     reinterpret_cast<const uint4*>(src), bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_probe_mfma_blocks(int32_t blocks_per_cu) {
+  using namespace moe;
+  if (blocks_per_cu < 1 || blocks_per_cu > 2) return MOE_ERR_INVALID_ARG;
+  const int cus = probe_cus();
+  if (cus <= 0) return MOE_ERR_HIP;
+  return cus * blocks_per_cu;
+}
+
+int moe_probe_mfma(int32_t kind, int32_t iters, int32_t blocks_per_cu, float* sink,
+                   uint64_t* cycles, hipStream_t stream) {
+  using namespace moe;
+  if (!sink || !cycles || iters < 1 || kind < 0 || kind > 2) return MOE_ERR_INVALID_ARG;
+  const int blocks = moe_probe_mfma_blocks(blocks_per_cu);
+  if (blocks < 0) return blocks;
+  auto* cyc = reinterpret_cast<unsigned long long*>(cycles);
+  if (kind == 0) {
+    hipLaunchKernelGGL(k_probe_mfma<0>, dim3(blocks), dim3(kProbeThreads), 0, stream, iters, sink, cyc);
+  } else if (kind == 1) {
+    hipLaunchKernelGGL(k_probe_mfma<1>, dim3(blocks), dim3(kProbeThreads), 0, stream, iters, sink, cyc);
+  } else {
+    hipLaunchKernelGGL(k_probe_mfma<2>, dim3(blocks), dim3(kProbeThreads), 0, stream, iters, sink, cyc);
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // extern "C"

@@ -10,7 +10,9 @@
 // layout is an error, never a silent decode in the other format (MoE module page,
 // MoeLayer::e8m0_or).
 #include <cstring>
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "moe_fp4.h"
 #include "moe_internal.h"
@@ -237,6 +239,53 @@ bool shared_on_mfma(const moe_config& c, bool pre) {
 thread_local hipEvent_t* t_stage_events = nullptr;
 thread_local int t_stage_count = 0;
 
+// The shared expert on a secondary stream (MoE constructor page: the shared expert overlaps
+// the routed experts on a second stream, joined by an event pair before the blend). Each
+// caller stream gets its own side stream and fork / join events, created on first use
+// (never while the caller's stream is being captured into a graph) and kept until the
+// process ends; the side stream is non-blocking and of default priority. Calls on one
+// caller stream are ordered by the caller, so its side stream and events are never used by
+// two calls at once.
+#ifndef MOE_SHARED_SIDE_STREAM
+#define MOE_SHARED_SIDE_STREAM 1
+#endif
+struct SideStream {
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+std::map<std::pair<int, hipStream_t>, SideStream> g_side;
+
+// The side stream of `s`, or nullptr (run the shared expert on `s` itself) when it cannot be
+// had without creating it during a capture, or when creating it fails.
+const SideStream* side_stream(hipStream_t s) {
+  if (!MOE_SHARED_SIDE_STREAM) return nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  if (s && hipStreamGetDevice(s, &dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  auto it = g_side.find({dev, s});
+  if (it != g_side.end()) return &it->second;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+    return nullptr;
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+  SideStream ss;
+  bool ok = hipStreamCreateWithFlags(&ss.side, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
+  if (cur != dev) ok = (hipSetDevice(cur) == hipSuccess) && ok;
+  if (!ok) {
+    if (ss.join) (void)hipEventDestroy(ss.join);
+    if (ss.fork) (void)hipEventDestroy(ss.fork);
+    if (ss.side) (void)hipStreamDestroy(ss.side);
+    return nullptr;
+  }
+  return &(g_side[{dev, s}] = ss);
+}
+
 struct StageMarks {
   hipEvent_t* ev = nullptr;
   int n = 0;
@@ -270,30 +319,51 @@ DispatchArgs make_dispatch_args(const moe_config& c, const Layout& L, const int3
 }
 
 // Dispatch (unless the caller already built it) + experts + blend on a validated config.
+// The shared expert: one group over rows [0, T) (implicit tile list), on the MFMA kernels
+// (with K split over blocks when its tiles are few) unless a decode layer has too few
+// tokens for them to pay. `base` carries the input, h, y and sizes of the call.
+int launch_shared(const moe_config& c, const Layout& L, const ExpertGemmArgs& base,
+                  const moe_expert_weights* shared, bool pre, void* ws, hipStream_t s) {
+  const bool sh_pre = shared_on_mfma(c, pre);
+  const int smt = sh_pre ? shared_mt(c.tokens) : kDecodeTile;
+  ExpertGemmArgs b = base;
+  b.src.tiles = nullptr;
+  b.src.ntiles = nullptr;
+  b.work = nullptr;
+  b.src.implicit_row0 = 0;
+  b.src.implicit_rows = c.tokens;
+  b.src.implicit_height = smt;
+  b.tile_bound = ceil_div(c.tokens, smt);
+  b.gate = desc(shared->gate);
+  b.up = desc(shared->up);
+  b.down = desc(shared->down);
+  b.I = c.shared_inter;
+  b.part = at<float>(ws, L.part);
+  b.part_bytes = L.part_bytes;
+  if (sh_pre) {
+    MOE_HIP(launch_prefill_gate_up(b, smt, s));
+    MOE_HIP(launch_prefill_down(b, smt, s));
+  } else {
+    MOE_HIP(launch_decode_gate_up(b, s));
+    MOE_HIP(launch_decode_down(b, s));
+  }
+  return MOE_OK;
+}
+
 int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const int32_t* ids,
                 const float* w, const int32_t* err_tok, const moe_expert_weights* routed,
                 const moe_expert_weights* shared, const uint16_t* residual, uint16_t* out,
                 void* ws, hipStream_t s, const StageMarks& marks = StageMarks(),
-                bool dispatched = false, const TopkArgs* fused_topk = nullptr) {
+                bool dispatched = false, const TopkArgs* fused_topk = nullptr,
+                bool allow_side = true) {
   int path;
   int r = choose_path(c, &path);
   if (r != MOE_OK) return r;
   const bool pre = path == MOE_PATH_PREFILL;
   const int mt = pre ? prefill_mt(c) : kDecodeTile;
 
-  const DispatchArgs d = make_dispatch_args(c, L, ids, err_tok, ws);
-  if (!dispatched) MOE_HIP(launch_dispatch(d, s));
-  MOE_HIP(marks.mark(MOE_STAGE_DISPATCHED));
-
   ExpertGemmArgs a{};
   a.x = xe;
-  a.row_token = d.row_token;
-  a.src.tiles = d.tiles;
-  a.src.ntiles = d.ntiles;
-  a.tile_bound = pre ? L.tile_bound_pre : L.tile_bound_dec;
-  a.gate = desc(routed->gate);
-  a.up = desc(routed->up);
-  a.down = desc(routed->down);
   a.h = at<uint16_t>(ws, L.h);
   a.h_stride = L.h_stride;
   a.y = at<void>(ws, L.y);
@@ -301,6 +371,27 @@ int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const 
   a.H = c.hidden;
   a.I = c.inter;
   a.rows = L.rows;
+  // the shared expert needs only the input: with a side stream it starts now and runs
+  // beside the dispatch and the routed experts, joined before the blend
+  const SideStream* side = c.has_shared && allow_side ? side_stream(s) : nullptr;
+  if (side) {
+    MOE_HIP(hipEventRecord(side->fork, s));
+    MOE_HIP(hipStreamWaitEvent(side->side, side->fork, 0));
+    if ((r = launch_shared(c, L, a, shared, pre, ws, side->side)) != MOE_OK) return r;
+    MOE_HIP(hipEventRecord(side->join, side->side));
+  }
+
+  const DispatchArgs d = make_dispatch_args(c, L, ids, err_tok, ws);
+  if (!dispatched) MOE_HIP(launch_dispatch(d, s));
+  MOE_HIP(marks.mark(MOE_STAGE_DISPATCHED));
+
+  a.row_token = d.row_token;
+  a.src.tiles = d.tiles;
+  a.src.ntiles = d.ntiles;
+  a.tile_bound = pre ? L.tile_bound_pre : L.tile_bound_dec;
+  a.gate = desc(routed->gate);
+  a.up = desc(routed->up);
+  a.down = desc(routed->down);
   if (pre) {
     a.work = d.ntiles + kWorkCtrOffset;
 #if MOE_PRE_MX8
@@ -341,33 +432,10 @@ int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const 
     MOE_HIP(launch_decode_down(a, s));
   }
   MOE_HIP(marks.mark(MOE_STAGE_DOWN));
-  if (c.has_shared) {
-    // the shared expert: one group over rows [0, T) (implicit tile list), on the MFMA
-    // kernels (with K split over blocks when its tiles are few) unless a decode layer has
-    // too few tokens for them to pay
-    const bool sh_pre = shared_on_mfma(c, pre);
-    const int smt = sh_pre ? shared_mt(c.tokens) : kDecodeTile;
-    ExpertGemmArgs b = a;
-    b.src.tiles = nullptr;
-    b.src.ntiles = nullptr;
-    b.work = nullptr;
-    b.src.implicit_row0 = 0;
-    b.src.implicit_rows = c.tokens;
-    b.src.implicit_height = smt;
-    b.tile_bound = ceil_div(c.tokens, smt);
-    b.gate = desc(shared->gate);
-    b.up = desc(shared->up);
-    b.down = desc(shared->down);
-    b.I = c.shared_inter;
-    b.part = at<float>(ws, L.part);
-    b.part_bytes = L.part_bytes;
-    if (sh_pre) {
-      MOE_HIP(launch_prefill_gate_up(b, smt, s));
-      MOE_HIP(launch_prefill_down(b, smt, s));
-    } else {
-      MOE_HIP(launch_decode_gate_up(b, s));
-      MOE_HIP(launch_decode_down(b, s));
-    }
+  if (side) {
+    MOE_HIP(hipStreamWaitEvent(s, side->join, 0));
+  } else if (c.has_shared) {
+    if ((r = launch_shared(c, L, a, shared, pre, ws, s)) != MOE_OK) return r;
   }
   MOE_HIP(marks.mark(MOE_STAGE_SHARED));
   CombineArgs cb{};
@@ -560,13 +628,16 @@ int moe_experts_forward(const moe_config* cfg, const uint16_t* x_experts,
                      c.has_shared ? shared : nullptr, residual, out, workspace, stream);
 }
 
-int moe_layer_forward(const moe_config* cfg, const uint16_t* x, const uint16_t* norm_gamma,
-                      const uint16_t* router_w, const float* logit_bias,
-                      const float* correction_bias, const int32_t* token_ids,
-                      const int64_t* tid2eid, const moe_expert_weights* routed,
-                      const moe_expert_weights* shared, const uint16_t* residual,
-                      uint16_t* out, float* dbg_logits, int32_t* dbg_ids, float* dbg_w,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// moe_layer_forward; allow_side = false keeps the shared expert on `stream` (the
+// no-allocation entry creates no side stream).
+static int layer_forward_impl(const moe_config* cfg, const uint16_t* x,
+                              const uint16_t* norm_gamma, const uint16_t* router_w,
+                              const float* logit_bias, const float* correction_bias,
+                              const int32_t* token_ids, const int64_t* tid2eid,
+                              const moe_expert_weights* routed, const moe_expert_weights* shared,
+                              const uint16_t* residual, uint16_t* out, float* dbg_logits,
+                              int32_t* dbg_ids, float* dbg_w, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream, bool allow_side) {
   int r = check_config(cfg);
   if (r != MOE_OK) return r;
   const moe_config& c = *cfg;
@@ -619,12 +690,24 @@ int moe_layer_forward(const moe_config* cfg, const uint16_t* x, const uint16_t* 
   }
   r = run_experts(c, L, xe, ids, w, at<int32_t>(workspace, L.errtok), routed,
                   c.has_shared ? shared : nullptr, residual, out, workspace, stream, marks,
-                  dispatched, fuse ? &fused : nullptr);
+                  dispatched, fuse ? &fused : nullptr, allow_side);
   if (r != MOE_OK) return r;
   const size_t slots = (size_t)c.tokens * c.top_k;
   if (dbg_ids) MOE_HIP(hipMemcpyAsync(dbg_ids, ids, slots * 4, hipMemcpyDeviceToDevice, stream));
   if (dbg_w) MOE_HIP(hipMemcpyAsync(dbg_w, w, slots * 4, hipMemcpyDeviceToDevice, stream));
   return MOE_OK;
+}
+
+int moe_layer_forward(const moe_config* cfg, const uint16_t* x, const uint16_t* norm_gamma,
+                      const uint16_t* router_w, const float* logit_bias,
+                      const float* correction_bias, const int32_t* token_ids,
+                      const int64_t* tid2eid, const moe_expert_weights* routed,
+                      const moe_expert_weights* shared, const uint16_t* residual,
+                      uint16_t* out, float* dbg_logits, int32_t* dbg_ids, float* dbg_w,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return layer_forward_impl(cfg, x, norm_gamma, router_w, logit_bias, correction_bias,
+                            token_ids, tid2eid, routed, shared, residual, out, dbg_logits,
+                            dbg_ids, dbg_w, workspace, workspace_bytes, stream, true);
 }
 
 int moe_layer_forward_noalloc(const moe_config* cfg, const uint16_t* x,
@@ -640,9 +723,9 @@ int moe_layer_forward_noalloc(const moe_config* cfg, const uint16_t* x,
   if (make_layout(*cfg).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
   void* ws = nullptr;
   if ((r = scratch_address(stream, &ws)) != MOE_OK) return r;
-  return moe_layer_forward(cfg, x, norm_gamma, router_w, logit_bias, correction_bias, token_ids,
-                           tid2eid, routed, shared, residual, out, dbg_logits, dbg_ids, dbg_w, ws,
-                           (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
+  return layer_forward_impl(cfg, x, norm_gamma, router_w, logit_bias, correction_bias,
+                            token_ids, tid2eid, routed, shared, residual, out, dbg_logits,
+                            dbg_ids, dbg_w, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream, false);
 }
 
 int moe_debug_dequant_fp4(const moe_fp4_weight* w, int32_t expert, int32_t path, float* out,

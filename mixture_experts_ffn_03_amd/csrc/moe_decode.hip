@@ -29,8 +29,7 @@ constexpr int kGateRowsPerPass = 8;   // gate rows (and as many up rows) per wav
 constexpr int kDownRowsPerPass = 16;  // down rows per wave pass
 constexpr int kDecWaves = 4;
 
-__device__ __forceinline__ bool resolve_tile(const TileSource& src, const int32_t* row_token,
-                                             int idx, Tile& t) {
+__device__ __forceinline__ bool resolve_tile(const TileSource& src, int idx, Tile& t) {
   if (src.tiles) {
     // both loads at once: idx is below the list's capacity (the grid's tile bound), so the
     // entry is readable even past the count
@@ -45,7 +44,7 @@ __device__ __forceinline__ bool resolve_tile(const TileSource& src, const int32_
   t.count = min(src.implicit_height, src.implicit_rows - r0);
   t.pad = 0;
 #pragma unroll
-  for (int q = 0; q < kTileTok; ++q) t.tok[q] = q < t.count ? row_token[t.row0 + q] : 0;
+  for (int q = 0; q < kTileTok; ++q) t.tok[q] = q < t.count ? r0 + q : 0;  // token = row - row0
   return true;
 }
 
@@ -354,7 +353,7 @@ template <int FMT, int LPR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_dec_gate_up(ExpertGemmArgs a, int rpw) {
   extern __shared__ __align__(16) uint16_t s_x[];
   Tile tile;
-  if (!resolve_tile(a.src, a.row_token, blockIdx.y, tile)) return;
+  if (!resolve_tile(a.src, blockIdx.y, tile)) return;
   if (blockIdx.x * kDecWaves * rpw >= a.I) return;
   // one step per wave (one pass, one chunk per lane and row): no staging, no pipeline
   const bool one = rpw == kGateRowsPerPass && a.H / DecFmt<FMT>::CPC <= LPR;
@@ -457,7 +456,7 @@ template <int FMT, int LPR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_dec_down(ExpertGemmArgs a, int rpw) {
   extern __shared__ __align__(16) uint16_t s_x[];
   Tile tile;
-  if (!resolve_tile(a.src, a.row_token, blockIdx.y, tile)) return;
+  if (!resolve_tile(a.src, blockIdx.y, tile)) return;
   if (blockIdx.x * kDecWaves * rpw >= a.H) return;
   const bool one = rpw == kDownRowsPerPass && a.I / DecFmt<FMT>::CPC <= LPR;
   if (tile.count == 1) {
@@ -653,7 +652,7 @@ __device__ __forceinline__ void dec_one_body(const ExpertGemmArgs& a, const Tile
 template <int FMT, int LPR, int M, int ROWS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ROWS == 4 ? (FMT == 0 ? 8 : 5) : 4))) void k_dec_one(ExpertGemmArgs a) {
   Tile tile;
-  if (!resolve_tile(a.src, a.row_token, blockIdx.y, tile)) return;
+  if (!resolve_tile(a.src, blockIdx.y, tile)) return;
   dec_one_body<FMT, LPR, M, ROWS>(a, tile);
 }
 

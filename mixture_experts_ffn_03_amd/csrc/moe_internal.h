@@ -32,7 +32,9 @@ struct Tile {
 
 // Where the rows a kernel processes come from: either the device tile list written by
 // the dispatch kernel, or an implicit list of fixed-height tiles over a known row range
-// (the shared expert, whose rows are [0, T) of the row space).
+// (the shared expert, whose rows are [0, T) of the row space). Row r of an implicit list
+// holds token r - implicit_row0, so its kernels read no dispatch output and may run
+// before or beside the dispatch.
 struct TileSource {
   const Tile* tiles;       // device list, or nullptr for the implicit list
   const int32_t* ntiles;   // device count of the list

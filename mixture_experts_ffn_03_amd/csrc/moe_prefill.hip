@@ -355,7 +355,9 @@ void k_pre_gemm(ExpertGemmArgs a) {
   if constexpr (!PERSIST) {
     for (int i = threadIdx.x; i < MT; i += NT) {
       const int ii = i < t.count ? i : 0;
-      s_tok[i] = GATEUP ? a.row_token[t.row0 + ii] : t.row0 + ii;
+      // an implicit list's row r holds token r - implicit_row0 (no dispatch output read)
+      const int tok = a.src.tiles ? a.row_token[t.row0 + ii] : t.row0 + ii - a.src.implicit_row0;
+      s_tok[i] = GATEUP ? tok : t.row0 + ii;
     }
     __syncthreads();
   }

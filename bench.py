@@ -165,17 +165,25 @@ def summarize_trace(d, command):
     trace = [r for r in _rocprof_rows(d, "kernel_trace.csv") if "moe::" in r["Kernel_Name"]]
     trace.sort(key=lambda r: int(r["Start_Timestamp"]))
     dur = {"gate_up": [], "down": []}
-    stage = None
+    stage, stream = None, None
+
+    def us(r):
+        return (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+
     for r in trace:
-        name = r["Kernel_Name"]
-        if "k_dispatch" in name:
-            stage = 0
-        elif stage is not None and stage < 2 and ("k_dec_" in name or "k_pre_gemm" in name):
-            dur["gate_up" if stage == 0 else "down"].append(
-                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        name, sid = r["Kernel_Name"], r.get("Stream_Id")
+        if "k_dispatch" in name:  # (also k_topk_dispatch)
+            stage, stream = 0, sid
+        elif "k_dec_one_topk" in name:  # one token: the dispatch runs inside gate+up
+            dur["gate_up"].append(us(r))
+            stage, stream = 1, sid
+        elif stage is not None and stage < 2 and sid == stream and \
+                ("k_dec_" in name or "k_pre_gemm" in name):
+            dur["gate_up" if stage == 0 else "down"].append(us(r))
             stage += 1
     out += ["", "Routed experts' launches only (the first two expert kernels after each dispatch "
-            "build):", "", "| stage | launches | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
+            "build on the layer's stream; a shared expert runs on a side stream):", "",
+            "| stage | launches | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
     for k, v in dur.items():
         if v:
             out.append(f"| {k} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")

@@ -392,6 +392,19 @@ int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const 
   a.gate = desc(routed->gate);
   a.up = desc(routed->up);
   a.down = desc(routed->down);
+  CombineArgs cb{};
+  cb.y = reinterpret_cast<const float*>(a.y);
+  cb.xe = xe;
+  cb.w = w;
+  cb.inv = d.inv;
+  cb.shared = c.has_shared;
+  cb.residual = residual;
+  cb.out = out;
+  cb.T = c.tokens;
+  cb.K = c.top_k;
+  cb.H = c.hidden;
+  // one token without a shared expert: the blend runs inside the down kernel
+  const bool blend_in_down = !pre && decode_blend_fusable(a, cb);
   if (pre) {
     a.work = d.ntiles + kWorkCtrOffset;
 #if MOE_PRE_MX8
@@ -429,7 +442,11 @@ int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const 
       MOE_HIP(launch_decode_gate_up(a, s));
     }
     MOE_HIP(marks.mark(MOE_STAGE_GATE_UP));
-    MOE_HIP(launch_decode_down(a, s));
+    if (blend_in_down) {
+      MOE_HIP(launch_decode_down_blend(a, cb, s));
+    } else {
+      MOE_HIP(launch_decode_down(a, s));
+    }
   }
   MOE_HIP(marks.mark(MOE_STAGE_DOWN));
   if (side) {
@@ -438,18 +455,7 @@ int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const 
     if ((r = launch_shared(c, L, a, shared, pre, ws, s)) != MOE_OK) return r;
   }
   MOE_HIP(marks.mark(MOE_STAGE_SHARED));
-  CombineArgs cb{};
-  cb.y = reinterpret_cast<const float*>(a.y);
-  cb.xe = xe;
-  cb.w = w;
-  cb.inv = d.inv;
-  cb.shared = c.has_shared;
-  cb.residual = residual;
-  cb.out = out;
-  cb.T = c.tokens;
-  cb.K = c.top_k;
-  cb.H = c.hidden;
-  MOE_HIP(launch_combine(cb, s));
+  if (!blend_in_down) MOE_HIP(launch_combine(cb, s));
   MOE_HIP(marks.mark(MOE_STAGE_COMBINED));
   return MOE_OK;
 }

@@ -553,16 +553,18 @@ struct OneShape {
   static_assert(NV <= LPR, "one reduced value per lane expected");
 };
 
-template <int FMT, int LPR, int M, int ROWS>
-__device__ __forceinline__ void dec_one_body(const ExpertGemmArgs& a, const Tile& tile) {
+// The wave's GR output rows start at nbase; store(q, n, v) receives the result of the
+// tile's q-th row for output row n (only rows n < N, one lane each).
+template <int FMT, int LPR, int M, int ROWS, typename Store>
+__device__ __forceinline__ void dec_one_body(const ExpertGemmArgs& a, const Tile& tile, int nbase,
+                                             Store&& store) {
   using SH = OneShape<LPR, M, ROWS>;
   constexpr int G = SH::G, NI = SH::NI, GR = SH::GR, NV = SH::NV;
   constexpr int XW = DecFmt<FMT>::XW, CPC = DecFmt<FMT>::CPC;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63;
   const int sub = lane % LPR, grp = lane / LPR;
   const int N = M == 2 ? a.I : a.H;  // output rows of each matrix
   const int K = M == 2 ? a.H : a.I;  // reduction length
-  const int nbase = (blockIdx.x * kDecWaves + wave) * GR;
   if (nbase >= N) return;  // whole wave
   const int nchunk = K / CPC;
   const bool live = sub < nchunk;
@@ -641,19 +643,66 @@ __device__ __forceinline__ void dec_one_body(const ExpertGemmArgs& a, const Tile
   if (owner && n < N) {
 #pragma unroll
     for (int q = 0; q < kTileTok; ++q) {
-      if (q < tile.count) {
-        if (M == 2) a.h[(size_t)(tile.row0 + q) * a.h_stride + n] = f32_to_bf16(res[q]);
-        else reinterpret_cast<float*>(a.y)[(size_t)(tile.row0 + q) * N + n] = res[q];
-      }
+      if (q < tile.count) store(q, n, res[q]);
     }
   }
+}
+
+// The tile's rows of h (gate+up) or y (down) in memory.
+template <int M>
+struct StoreRows {
+  const ExpertGemmArgs& a;
+  const Tile& tile;
+  __device__ __forceinline__ void operator()(int q, int n, float v) const {
+    if (M == 2) a.h[(size_t)(tile.row0 + q) * a.h_stride + n] = f32_to_bf16(v);
+    else reinterpret_cast<float*>(a.y)[(size_t)(tile.row0 + q) * a.H + n] = v;
+  }
+};
+
+template <int FMT, int LPR, int M, int ROWS>
+__device__ __forceinline__ int one_nbase() {
+  return (blockIdx.x * kDecWaves + (threadIdx.x >> 6)) * OneShape<LPR, M, ROWS>::GR;
 }
 
 template <int FMT, int LPR, int M, int ROWS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ROWS == 4 ? (FMT == 0 ? 8 : 5) : 4))) void k_dec_one(ExpertGemmArgs a) {
   Tile tile;
   if (!resolve_tile(a.src, blockIdx.y, tile)) return;
-  dec_one_body<FMT, LPR, M, ROWS>(a, tile);
+  dec_one_body<FMT, LPR, M, ROWS>(a, tile, one_nbase<FMT, LPR, M, ROWS>(), StoreRows<M>{a, tile});
+}
+
+// One token without a shared expert: the down projection of every slot and the blend in one
+// kernel (MoE constructor page: the weighted-sum blend into the residual). A block has one
+// wave per tile of the token (at most kBlendMaxTiles), all on the same GR output rows; the
+// waves leave their sums in LDS by row, then the block's first GR threads add the slots in
+// order (w_j * y_j, a zero-computation expert's w_j * x_e, a dropped slot nothing) and the
+// residual, exactly as the separate blend does, and store bf16 out. The fp32 rows of y never
+// reach memory and the blend needs no launch of its own.
+constexpr int kBlendMaxTiles = 16;
+
+template <int FMT, int LPR, int ROWS>
+__global__ __launch_bounds__(kBlendMaxTiles * 64) void k_dec_one_blend(ExpertGemmArgs a, CombineArgs cb) {
+  constexpr int GR = OneShape<LPR, 1, ROWS>::GR;
+  __shared__ float s_y[kBlendMaxTiles * kTileTok][GR];  // [row of the token][output row]
+  const int nbase = blockIdx.x * GR;
+  const int wave = threadIdx.x >> 6;
+  const int rbase = a.rows - cb.T * cb.K;  // first routed row (the token's rows follow)
+  Tile tile;
+  if (resolve_tile(a.src, wave, tile)) {
+    auto store = [&](int q, int n, float v) { s_y[tile.row0 + q - rbase][n - nbase] = v; };
+    dec_one_body<FMT, LPR, 1, ROWS>(a, tile, nbase, store);
+  }
+  __syncthreads();
+  const int i = threadIdx.x, n = nbase + i;
+  if (i >= GR || n >= cb.H) return;
+  float acc = 0.f;
+  for (int j = 0; j < cb.K; ++j) {
+    const int p = cb.inv[j];
+    if (p >= 0) acc = fmaf(cb.w[j], s_y[p - rbase][i], acc);
+    else if (p == -2) acc = fmaf(cb.w[j], bf16_to_f32(cb.xe[n]), acc);
+  }
+  if (cb.residual) acc += bf16_to_f32(cb.residual[n]);
+  cb.out[n] = f32_to_bf16(acc);
 }
 
 // One token with top-K selection: the experts are chosen inside the gate+up kernel. The k
@@ -704,7 +753,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FMT == 0 ? 
   tile.pad = 0;
 #pragma unroll
   for (int q = 0; q < kTileTok; ++q) tile.tok[q] = 0;
-  dec_one_body<FMT, LPR, 2, 4>(a, tile);
+  dec_one_body<FMT, LPR, 2, 4>(a, tile, one_nbase<FMT, LPR, 2, 4>(), StoreRows<2>{a, tile});
 }
 
 // Host side: FP4 weights, rows of at most 64 chunks, tiles of at most kTileTok rows.
@@ -798,6 +847,42 @@ hipError_t launch_decode_gate_up_topk(const ExpertGemmArgs& a, const TopkArgs& t
   if (a.gate.fmt == 0) { MOE_TOPK_LPR(0) }
   MOE_TOPK_LPR(1)
 #undef MOE_TOPK_LPR
+}
+
+// One token, no shared expert, FP4 down rows of at most 64 chunks, at most kBlendMaxTiles
+// tiles: the down projection and the blend in one launch.
+bool decode_blend_fusable(const ExpertGemmArgs& a, const CombineArgs& cb) {
+  return cb.T == 1 && !cb.shared && a.src.tiles && a.tile_bound <= kBlendMaxTiles &&
+         cb.K <= kBlendMaxTiles && one_fits(a.down.fmt, a.I, kDecodeTile);
+}
+
+template <int FMT, int LPR, int ROWS>
+static hipError_t launch_blend_t(const ExpertGemmArgs& a, const CombineArgs& cb, hipStream_t s) {
+  constexpr int GR = OneShape<LPR, 1, ROWS>::GR;
+  hipLaunchKernelGGL((k_dec_one_blend<FMT, LPR, ROWS>), dim3((a.H + GR - 1) / GR),
+                     dim3(a.tile_bound * 64), 0, s, a, cb);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_down_blend(const ExpertGemmArgs& a, const CombineArgs& cb,
+                                    hipStream_t s) {
+  if (!decode_blend_fusable(a, cb) || a.tile_bound <= 0) return hipErrorInvalidValue;
+  const int lpr = one_lanes(a.I / 32);
+  const bool wide = a.H >= kOneWideMinN;
+#define MOE_BLEND_LPR(FMT, ROWS)                                  \
+  switch (lpr) {                                                  \
+    case 8: return launch_blend_t<FMT, 8, ROWS>(a, cb, s);        \
+    case 16: return launch_blend_t<FMT, 16, ROWS>(a, cb, s);      \
+    case 32: return launch_blend_t<FMT, 32, ROWS>(a, cb, s);      \
+    default: return launch_blend_t<FMT, 64, ROWS>(a, cb, s);      \
+  }
+  if (a.down.fmt == 0) {
+    if (wide) { MOE_BLEND_LPR(0, 8) }
+    MOE_BLEND_LPR(0, 4)
+  }
+  if (wide) { MOE_BLEND_LPR(1, 8) }
+  MOE_BLEND_LPR(1, 4)
+#undef MOE_BLEND_LPR
 }
 
 hipError_t launch_decode_down(const ExpertGemmArgs& a, hipStream_t s) {

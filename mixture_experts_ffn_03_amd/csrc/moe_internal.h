@@ -186,6 +186,10 @@ struct CombineArgs {
   int T, K, H;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+// One token without a shared expert on the one-step down GEMV: down and blend in one launch.
+bool decode_blend_fusable(const ExpertGemmArgs& a, const CombineArgs& cb);
+hipError_t launch_decode_down_blend(const ExpertGemmArgs& a, const CombineArgs& cb,
+                                    hipStream_t s);
 
 hipError_t launch_debug_dequant(const WeightDesc& w, int expert, int path, float* out,
                                 hipStream_t s);

@@ -520,6 +520,32 @@ def test_bad_expert_ids_are_dropped_and_flagged():
     assert_layer_close(out.float().cpu().numpy(), want, None, "bad-ids")
 
 
+@pytest.mark.parametrize("fmt", [S.NVFP4, S.MXFP4])
+def test_one_token_blend_inside_down(fmt):
+    """One token without a shared expert: the down kernel blends the slots itself. Slots of
+    routed experts (one repeated), zero-computation experts and an out-of-range id (dropped,
+    flagged), against the oracle; with and without a residual."""
+    E, Z = 16, 4
+    spec = S.LayerSpec(name="t1_blend", tokens=1, hidden=1024, experts=E, top_k=7, inter=512,
+                       fmt=fmt, zero_experts=Z, seed=1300 + fmt)
+    inp = S.make_inputs(spec, device=DEV)
+    ids = torch.tensor([[3, E + 1, 5, 99, 0, E, 3]], dtype=torch.int32, device=DEV)
+    w = torch.tensor([[0.3, 0.2, 0.15, 0.1, 0.1, 0.1, 0.05]], dtype=torch.float32, device=DEV)
+    cfg = config_for(inp, M.PATH_DECODE)
+    ws = M.alloc_workspace(cfg, DEV)
+    oids = ids.cpu().numpy()
+    oids = np.where((oids >= 0) & (oids < E + Z), oids, -1)
+    for residual in (inp.residual, None):
+        _announce("one-token blend", fmt, residual is not None)
+        out = torch.empty_like(inp.x)
+        M.experts_forward(cfg, inp.x, ids, w, M.expert_weights(inp.routed), None, residual, out, ws)
+        assert M.get_device_error(ws) & M.DEVERR_EXPERT_ID
+        res = f32(residual) if residual is not None else np.zeros_like(f32(inp.x))
+        want = O.experts_forward(f32(inp.x), oids, w.cpu().numpy().astype(np.float64),
+                                 oracle_cache(inp.routed), res, num_experts=E)
+        assert_layer_close(out.float().cpu().numpy(), want, None, "one-token blend")
+
+
 def test_bad_expert_ids_many_slots():
     """Out-of-range ids among 9000 slots (multi-block dispatch): dropped, flagged, and the
     other slots still match the oracle."""

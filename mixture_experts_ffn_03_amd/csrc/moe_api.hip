@@ -49,6 +49,15 @@ int tile_bound(int S, int E, int h) {
 // GEMV's tiles of kDecodeTile tokens (its weights streamed once per 4 tokens).
 constexpr int kSharedMfmaMinTokens = 8;
 
+// From this many tokens the shared expert's MFMA launches keep K whole: beside the routed
+// experts on the side stream its few long blocks cost the layer less than split-K's short
+// blocks with their fp32 partial sums (hash layer, 512 tokens: 0.810 against 0.836 ms). Below
+// it, K is split: a DeepSeek-V3-like decode layer's 16 blocks of 112 stages would be on the
+// critical path whenever the two streams do not overlap (graph replays: 0.651 against
+// 0.610 ms). The choice depends on the configuration alone, so every entry and every replay
+// of a configuration rounds the same way.
+constexpr int kSharedNoSplitTokens = 256;
+
 // Tile height of the shared expert: its one group holds every token. (Choosing 32-row tiles
 // whenever taller ones leave the chip's block slots unfilled, and splitting their K, was
 // slower: hash layer shared stage 88.7 us against 71.7 us with 128-row tiles.)
@@ -103,7 +112,7 @@ Layout make_layout(const moe_config& c) {
   L.errpart = take((size_t)dblocks * 4);
   // K-split partial sums of the shared expert's MFMA launches
   L.part_bytes = 0;
-  if (c.has_shared) {
+  if (c.has_shared && c.tokens < kSharedNoSplitTokens) {
     const int nout = 2 * c.shared_inter > H ? 2 * c.shared_inter : H;
     L.part_bytes = (size_t)kMaxKsplit * T * nout * sizeof(float);
     if (L.part_bytes > kSplitPartMax) L.part_bytes = kSplitPartMax;
@@ -338,7 +347,7 @@ int launch_shared(const moe_config& c, const Layout& L, const ExpertGemmArgs& ba
   b.up = desc(shared->up);
   b.down = desc(shared->down);
   b.I = c.shared_inter;
-  b.part = at<float>(ws, L.part);
+  b.part = L.part_bytes ? at<float>(ws, L.part) : nullptr;
   b.part_bytes = L.part_bytes;
   if (sh_pre) {
     MOE_HIP(launch_prefill_gate_up(b, smt, s));

@@ -85,23 +85,28 @@ __device__ __forceinline__ void bf16x8_to_f64(const uint4& v, double (&o)[8]) {
 
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
-// MF 16-token fragments. MFMA operand layout (16x16x4 f64): lane l holds A[l % 16][l / 16]
-// and B[l / 16][l % 16]; the result D[l / 16 + 4 v][l % 16] sits in element v. The
-// K index of (lane quad q, step s) inside a 32-wide chunk is 8q + s for both operands.
-template <int MF>
+// MF 16-token fragments x NE 16-expert groups. MFMA operand layout (16x16x4 f64): lane l
+// holds A[l % 16][l / 16] and B[l / 16][l % 16]; the result D[l / 16 + 4 v][l % 16] sits in
+// element v. The K index of (lane quad q, step s) inside a 32-wide chunk is 8q + s for both
+// operands. Each widened token operand feeds NE MFMAs, each widened expert operand MF.
+template <int MF, int NE>
 __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict__ x,
                                                      const uint16_t* __restrict__ w,
                                                      double* __restrict__ partial, int T, int E,
                                                      int H, int hsplit) {
-  __shared__ f64x4_t s_red[3][MF][64];
+  __shared__ f64x4_t s_red[3][NE][MF][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int idx = lane & 15, q = lane >> 4;
-  const int e0 = blockIdx.x * 16;
+  const int e0 = blockIdx.x * 16 * NE;
   const int tb = blockIdx.y * 16 * MF;  // first token of the tile
   const int kb = blockIdx.z * hsplit;
   const int ke = min(H, kb + hsplit);
-  const int eload = e0 + idx < E ? e0 + idx : 0;  // rows past E: results not stored
-  const uint16_t* wrow = w + (size_t)eload * H + 8 * q;
+  const uint16_t* wrow[NE];
+#pragma unroll
+  for (int g = 0; g < NE; ++g) {
+    const int e = e0 + 16 * g + idx;
+    wrow[g] = w + (size_t)(e < E ? e : 0) * H + 8 * q;  // rows past E: results not stored
+  }
   const uint16_t* xrow[MF];
   bool tv[MF];
 #pragma unroll
@@ -110,19 +115,24 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
     tv[m] = t < T;
     xrow[m] = x + (size_t)(tv[m] ? t : 0) * H + 8 * q;
   }
-  f64x4_t acc[MF];
+  f64x4_t acc[NE][MF];
 #pragma unroll
-  for (int m = 0; m < MF; ++m) acc[m] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  for (int g = 0; g < NE; ++g)
+#pragma unroll
+    for (int m = 0; m < MF; ++m) acc[g][m] = f64x4_t{0.0, 0.0, 0.0, 0.0};
   // the operands of the wave's next two 32-wide chunks are in flight while the current
   // chunk's MFMAs run (one chunk ahead is shorter than a loaded HBM round trip)
   const int kstart = kb + 32 * wave;
-  uint4 wv = make_uint4(0, 0, 0, 0), xv[MF], w1 = wv, x1[MF];
+  uint4 wv[NE], w1[NE], xv[MF], x1[MF];
+#pragma unroll
+  for (int g = 0; g < NE; ++g) wv[g] = w1[g] = make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int m = 0; m < MF; ++m) xv[m] = x1[m] = make_uint4(0, 0, 0, 0);
   // (unconditional loads: rows past T read row 0 and are zeroed after the load; the
   // prefetches past the slice re-read the current chunk)
-  auto load = [&](int k0, uint4& w_, uint4 (&x_)[MF]) {
-    w_ = *reinterpret_cast<const uint4*>(wrow + k0);
+  auto load = [&](int k0, uint4 (&w_)[NE], uint4 (&x_)[MF]) {
+#pragma unroll
+    for (int g = 0; g < NE; ++g) w_[g] = *reinterpret_cast<const uint4*>(wrow[g] + k0);
 #pragma unroll
     for (int m = 0; m < MF; ++m) x_[m] = *reinterpret_cast<const uint4*>(xrow[m] + k0);
   };
@@ -131,10 +141,8 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
     load(kstart + 128 < ke ? kstart + 128 : kstart, w1, x1);
   }
   for (int k0 = kstart; k0 < ke; k0 += 128) {
-    uint4 wn, xn[MF];
+    uint4 wn[NE], xn[MF];
     load(k0 + 256 < ke ? k0 + 256 : k0, wn, xn);
-    double wd[8];
-    bf16x8_to_f64(wv, wd);
     double xd[MF][8];
 #pragma unroll
     for (int m = 0; m < MF; ++m) {
@@ -142,12 +150,20 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
       bf16x8_to_f64(v, xd[m]);
     }
 #pragma unroll
-    for (int st = 0; st < 8; ++st)
+    for (int g = 0; g < NE; ++g) {
+      double wd[8];
+      bf16x8_to_f64(wv[g], wd);
 #pragma unroll
-      for (int m = 0; m < MF; ++m)
-        acc[m] = __builtin_amdgcn_mfma_f64_16x16x4f64(xd[m][st], wd[st], acc[m], 0, 0, 0);
-    wv = w1;
-    w1 = wn;
+      for (int st = 0; st < 8; ++st)
+#pragma unroll
+        for (int m = 0; m < MF; ++m)
+          acc[g][m] = __builtin_amdgcn_mfma_f64_16x16x4f64(xd[m][st], wd[st], acc[g][m], 0, 0, 0);
+    }
+#pragma unroll
+    for (int g = 0; g < NE; ++g) {
+      wv[g] = w1[g];
+      w1[g] = wn[g];
+    }
 #pragma unroll
     for (int m = 0; m < MF; ++m) {
       xv[m] = x1[m];
@@ -156,28 +172,42 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
   }
   if (wave > 0) {
 #pragma unroll
-    for (int m = 0; m < MF; ++m) s_red[wave - 1][m][lane] = acc[m];
+    for (int g = 0; g < NE; ++g)
+#pragma unroll
+      for (int m = 0; m < MF; ++m) s_red[wave - 1][g][m][lane] = acc[g][m];
   }
   __syncthreads();
   if (wave != 0) return;
-  const int e = e0 + idx;
-  if (e >= E) return;
   double* p = partial + (size_t)blockIdx.z * T * E;
 #pragma unroll
-  for (int m = 0; m < MF; ++m) {
-    const f64x4_t sum = ((acc[m] + s_red[0][m][lane]) + s_red[1][m][lane]) + s_red[2][m][lane];
+  for (int g = 0; g < NE; ++g) {
+    const int e = e0 + 16 * g + idx;
+    if (e >= E) continue;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int t = tb + m * 16 + q + 4 * v;
-      if (t < T) p[(size_t)t * E + e] = sum[v];
+    for (int m = 0; m < MF; ++m) {
+      const f64x4_t sum =
+          ((acc[g][m] + s_red[0][g][m][lane]) + s_red[1][g][m][lane]) + s_red[2][g][m][lane];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = tb + m * 16 + q + 4 * v;
+        if (t < T) p[(size_t)t * E + e] = sum[v];
+      }
     }
   }
 }
 
+// 16-expert groups per block: two once a block has four 16-token fragments and the experts
+// fill them (the prefill router), else one.
+#ifndef MOE_ROUTER_NE
+#define MOE_ROUTER_NE 2
+#endif
+static int router_ne(int T, int E) { return (T >= 64 && E >= 32) ? MOE_ROUTER_NE : 1; }
+
 RouterPlan plan_router(int T, int E, int H) {
   RouterPlan r;
   // enough H slices that the grid has about 512 blocks (two per CU)
-  const int blocks = max(1, ((E + 15) / 16) * ((T + 63) / 64));  // T = 0: no launch
+  const int ge = 16 * router_ne(T, E);
+  const int blocks = max(1, ((E + ge - 1) / ge) * ((T + 63) / 64));  // T = 0: no launch
   int ks = min((512 + blocks - 1) / blocks, min(kRouterMaxSplit, H / 32));
   ks = max(ks, 1);
   r.hsplit = ((H + ks - 1) / ks + 31) / 32 * 32;  // whole 32-wide chunks
@@ -189,11 +219,13 @@ hipError_t launch_router_partial(const uint16_t* x, const uint16_t* w, double* p
                                  int E, int H, int ks, int hsplit, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int mf = T >= 64 ? 4 : (T + 15) / 16;  // 16-token fragments per block
-  const dim3 grid((E + 15) / 16, (T + 16 * mf - 1) / (16 * mf), ks);
-  if (mf == 1) hipLaunchKernelGGL(k_router_mfma<1>, grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
-  else if (mf == 2) hipLaunchKernelGGL(k_router_mfma<2>, grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
-  else if (mf == 3) hipLaunchKernelGGL(k_router_mfma<3>, grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
-  else hipLaunchKernelGGL(k_router_mfma<4>, grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
+  const int ne = router_ne(T, E);
+  const dim3 grid((E + 16 * ne - 1) / (16 * ne), (T + 16 * mf - 1) / (16 * mf), ks);
+  if (mf == 1) hipLaunchKernelGGL((k_router_mfma<1, 1>), grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
+  else if (mf == 2) hipLaunchKernelGGL((k_router_mfma<2, 1>), grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
+  else if (mf == 3) hipLaunchKernelGGL((k_router_mfma<3, 1>), grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
+  else if (ne == 2) hipLaunchKernelGGL((k_router_mfma<4, 2>), grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
+  else hipLaunchKernelGGL((k_router_mfma<4, 1>), grid, dim3(256), 0, s, x, w, partial, T, E, H, hsplit);
   return hipGetLastError();
 }
 

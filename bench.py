@@ -201,7 +201,8 @@ def _dispatch_id(r):
 
 def _routed_counter(d, path):
     """Mean counter value (KiB) per dispatch of the routed gate+up and down kernels: the
-    first two expert kernels after each k_dispatch (shared-expert launches come later)."""
+    first two expert kernels after each dispatch build, or the one-token gate+up that builds
+    it and the kernel after it (shared-expert launches are enqueued before the dispatch)."""
     rows = _rocprof_rows(d, "counter_collection.csv")
     per = {}
     for r in rows:  # one row per (dispatch, counter); sum over counter instances
@@ -213,8 +214,11 @@ def _routed_counter(d, path):
     stage = None
     for k in sorted(per):
         name, v = per[k]
-        if "k_dispatch" in name:
+        if "k_dispatch" in name:  # (also k_topk_dispatch)
             stage = 0
+        elif "k_dec_one_topk" in name:  # one token: the dispatch runs inside gate+up
+            got["gate_up"].append(v)
+            stage = 1
         elif stage is not None and stage < 2 and want[stage] in name:
             got["gate_up" if stage == 0 else "down"].append(v)
             stage += 1

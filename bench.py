@@ -616,6 +616,60 @@ def microbench(M, torch):
     print(json.dumps(res), flush=True)
 
 
+def wait_split(M, torch, workload):
+    """Where the routed MXFP4 grouped GEMMs' waves spend their K loop, from a library built with
+    MOE_PRE_WAIT_SPLIT=1 MOE_PRE_PERSIST=0 (passed with --lib): per step, the stage-load wait,
+    the barrier, and the rest (the stage's LDS reads, decode and MFMA issue), summed over every
+    wave of the routed launches of three layer calls."""
+    import numpy as np
+    lib = M.load_library()
+    if not hasattr(lib, "moe_debug_prefill_wait_split"):
+        raise SystemExit("--wait-split needs --lib of a build with MOE_PRE_WAIT_SPLIT=1 "
+                         "MOE_PRE_PERSIST=0")
+    fn = lib.moe_debug_prefill_wait_split
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p]
+    import moe_synth as S
+    spec = S.WORKLOADS[workload]
+    inp = S.make_inputs(spec, device="cuda")
+    cfg = M.make_config(spec.tokens, spec.hidden, spec.experts, spec.top_k, spec.inter,
+                        score_mode=spec.score, select_mode=spec.select,
+                        renormalize=spec.renormalize, has_shared=spec.shared,
+                        shared_inter=spec.shared_inter, pre_norm=spec.pre_norm,
+                        norm_eps=spec.norm_eps, vocab=spec.vocab)
+    ws = M.alloc_workspace(cfg, "cuda")
+    out = torch.empty_like(inp.x)
+    shared = M.expert_weights(inp.shared) if inp.shared is not None else None
+
+    def call():
+        M.layer_forward(cfg, inp.x, inp.router_w, M.expert_weights(inp.routed), out, ws,
+                        norm_gamma=inp.gamma, logit_bias=inp.logit_bias,
+                        correction_bias=inp.correction_bias, token_ids=inp.token_ids,
+                        tid2eid=inp.tid2eid, shared=shared, residual=inp.residual)
+        torch.cuda.synchronize()
+
+    raw = np.zeros((2, 8192, 4, 4), np.uint64)
+    call()
+    fn(raw.ctypes.data)  # (clears the sums of the warm-up call)
+    acc = np.zeros_like(raw, dtype=np.float64)
+    for _ in range(3):
+        call()
+        if fn(raw.ctypes.data) != 0:
+            raise SystemExit("moe_debug_prefill_wait_split failed")
+        acc += raw.astype(np.float64)
+    res = {"metric": "wait_split", "workload": workload, "kernels": {}}
+    for k, name in enumerate(("gate_up", "down")):
+        v = acc[k][acc[k][:, 0, 3] > 0]
+        if not len(v):
+            continue
+        loop, load, bar, n = (v[:, :, i].sum() for i in range(4))
+        res["kernels"][name] = {"blocks": int(len(v)), "steps_per_wave": round(n / len(v) / 4 / 3, 1),
+                                "load_wait": round(load / loop, 3), "barrier": round(bar / loop, 3),
+                                "rest": round(1 - (load + bar) / loop, 3),
+                                "cycles_per_step": round(loop / n)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -647,6 +701,9 @@ def main():
     ap.add_argument("--microbench", action="store_true",
                     help="only measure the achievable rates (streaming read, MFMA probes with "
                          "their sustained clock) and print them as one JSON line")
+    ap.add_argument("--wait-split", action="store_true",
+                    help="with --lib of a MOE_PRE_WAIT_SPLIT=1 MOE_PRE_PERSIST=0 build: where the "
+                         "routed MXFP4 grouped GEMMs' waves spend their K loop (one JSON line)")
     ap.add_argument("--command", action="append", default=[],
                     help="command line recorded in a summary (repeatable)")
     args = ap.parse_args()
@@ -686,6 +743,9 @@ def main():
         M.load_library()
     if args.microbench:
         microbench(M, torch)
+        return
+    if args.wait_split:
+        wait_split(M, torch, args.workload)
         return
     result = run_workload(args.workload, args)
     if args.workload == DEFAULT_WORKLOAD and args.tokens <= 0 and not args.no_others:

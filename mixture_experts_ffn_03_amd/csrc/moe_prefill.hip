@@ -79,6 +79,36 @@ __device__ __forceinline__ void dma2(const void* g, uint32_t lds_base) {
                :: "s"(lds_base), "v"(g) : "memory", "m0");
 }
 
+// Build flag MOE_PRE_WAIT_SPLIT (off in the library; a diagnostic build): the one-block-per-tile
+// grouped GEMM of the routed MXFP4 experts sums per wave the shader-clock cycles of each step
+// spent in the stage-load wait, at the barrier, and in the whole K loop, into g_wait_split
+// [gate+up, down][block][wave][loop, load wait, barrier, steps] (moe_debug_prefill_wait_split).
+#ifndef MOE_PRE_WAIT_SPLIT
+#define MOE_PRE_WAIT_SPLIT 0
+#endif
+#if MOE_PRE_WAIT_SPLIT
+constexpr int kWaitSplitBlocks = 8192;
+__device__ unsigned long long g_wait_split[2][kWaitSplitBlocks][4][4];
+#endif
+
+// The stage-load half of wait_stage: at most N loads of this wave in flight, LDS reads done.
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"(N) : "memory");
+}
+template <int NL, int NSS>
+__device__ __forceinline__ void wait_loads_inflight(int r, bool ss) {
+  if (r <= 0) {
+    wait_loads<0>();
+  } else if (r == 1) {
+    if (ss) wait_loads<NL + NSS>(); else wait_loads<NL>();
+  } else if (r == 2) {
+    if (ss) wait_loads<2 * NL + NSS>(); else wait_loads<2 * NL>();
+  } else {
+    if (ss) wait_loads<3 * NL + NSS>(); else wait_loads<3 * NL>();
+  }
+}
+
 // Wait until at most N vector-memory loads of this wave are in flight and its LDS reads
 // have returned, then synchronise the block: every wave's loads of the stage have
 // landed, and every read of the slot about to be refilled is done.
@@ -645,6 +675,9 @@ void k_pre_gemm(ExpertGemmArgs a) {
 #pragma unroll
   for (int i = 0; i < LEAD; ++i)
     if (i < nch) issue(i, i % NSTG);
+#if MOE_PRE_WAIT_SPLIT
+  unsigned long long ws_load = 0, ws_bar = 0, ws_steps = 0;
+#endif
   auto kloop = [&](auto nr_c) __attribute__((always_inline)) {
 #pragma unroll 1
     for (int c = 0; c < nch; ++c) {
@@ -657,7 +690,18 @@ void k_pre_gemm(ExpertGemmArgs a) {
         const int next = (c / SUPER + 1) * SUPER;  // first super-stage start after c
         ss = next <= c + inflight;
       }
+#if MOE_PRE_WAIT_SPLIT
+      const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+      wait_loads_inflight<Sh::NLOADS, NSS>(inflight, ss);
+      const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+      asm volatile("s_barrier" ::: "memory");
+      const unsigned long long t2 = __builtin_amdgcn_s_memtime();
+      ws_load += t1 - t0;
+      ws_bar += t2 - t1;
+      ws_steps += 1;
+#else
       wait_inflight<Sh::NLOADS, NSS>(inflight, ss);
+#endif
       stage_mma(nr_c, c);
     }
   };
@@ -816,7 +860,21 @@ void k_pre_gemm(ExpertGemmArgs a) {
         for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x16_t{};
     }
   } else {
+#if MOE_PRE_WAIT_SPLIT
+    const unsigned long long ts = __builtin_amdgcn_s_memtime();
+#endif
     run_tile(kloop);
+#if MOE_PRE_WAIT_SPLIT
+    const unsigned long long te = __builtin_amdgcn_s_memtime();
+    const int bid = blockIdx.y * gridDim.x + blockIdx.x;
+    if (FMT == 1 && a.src.tiles && blockIdx.z == 0 && (threadIdx.x & 63) == 0 && bid < kWaitSplitBlocks) {
+      unsigned long long* d = g_wait_split[GATEUP ? 0 : 1][bid][threadIdx.x >> 6];
+      d[0] = te - ts;
+      d[1] = ws_load;
+      d[2] = ws_bar;
+      d[3] = ws_steps;
+    }
+#endif
     epilogue();
   }
 }
@@ -1097,3 +1155,16 @@ hipError_t launch_prefill_down(const ExpertGemmArgs& a, int mt, hipStream_t s) {
 }
 
 }  // namespace moe
+
+#if MOE_PRE_WAIT_SPLIT
+// Diagnostic build only (not declared in the public header): copy g_wait_split to `host`
+// (2 x 8192 x 4 x 4 uint64) and clear it.
+extern "C" int moe_debug_prefill_wait_split(void* host) {
+  if (hipMemcpyFromSymbol(host, HIP_SYMBOL(moe::g_wait_split), sizeof(moe::g_wait_split), 0,
+                          hipMemcpyDeviceToHost) != hipSuccess)
+    return -4;
+  static unsigned long long zero[2][moe::kWaitSplitBlocks][4][4];
+  return hipMemcpyToSymbol(HIP_SYMBOL(moe::g_wait_split), zero, sizeof(zero), 0,
+                           hipMemcpyHostToDevice) == hipSuccess ? 0 : -4;
+}
+#endif

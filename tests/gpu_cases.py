@@ -72,7 +72,7 @@ def run_layer(inp: S.LayerInputs, path=M.PATH_AUTO, residual=True, stream=None):
 
 
 def oracle_workers() -> int:
-    """Host threads for the oracle's expert loop (the GPU machine's CPU share is 16)."""
+    """Host threads for the oracle's expert loop (at most 16: a GPU host's CPU share)."""
     n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     return max(1, min(16, n))
 

@@ -20,7 +20,7 @@ FMT_NVFP4, FMT_MXFP4, FMT_FP8, FMT_BF16 = 0, 1, 2, 3
 SCORE_SOFTMAX, SCORE_SIGMOID, SCORE_SQRT_SOFTPLUS, SCORE_SOFTMAX_BIAS = 0, 1, 2, 3
 SELECT_TOPK, SELECT_HASH = 0, 1
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
-DEVERR_EXPERT_ID, DEVERR_TOKEN_ID, DEVERR_TABLE = 1, 2, 4
+DEVERR_EXPERT_ID, DEVERR_TOKEN_ID, DEVERR_TABLE, DEVERR_Y_RANGE = 1, 2, 4, 8
 MAX_EXPERTS, MAX_TOP_K = 1024, 32
 
 

@@ -347,6 +347,8 @@ int launch_shared(const moe_config& c, const Layout& L, const ExpertGemmArgs& ba
   b.up = desc(shared->up);
   b.down = desc(shared->down);
   b.I = c.shared_inter;
+  b.y_half = 0;  // the shared expert's rows stay fp32
+  b.err_word = nullptr;
   b.part = L.part_bytes ? at<float>(ws, L.part) : nullptr;
   b.part_bytes = L.part_bytes;
   if (sh_pre) {
@@ -403,6 +405,17 @@ int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const 
   a.down = desc(routed->down);
   CombineArgs cb{};
   cb.y = reinterpret_cast<const float*>(a.y);
+  // routed prefill rows of y as fp16, after the shared expert's fp32 rows: row r >=
+  // shared_rows at byte 2 * H * (shared_rows + r) of the y region (past the 4 * H *
+  // shared_rows bytes of fp32 rows; the last row ends within the region's 4 * H * rows bytes)
+  ExpertGemmArgs ad = a;
+  if (pre) {
+    uint16_t* y16 = at<uint16_t>(ws, L.y) + (size_t)d.shared_rows * c.hidden;
+    cb.y16 = y16;
+    ad.y = y16;
+    ad.y_half = 1;
+    ad.err_word = d.err_word;
+  }
   cb.xe = xe;
   cb.w = w;
   cb.inv = d.inv;
@@ -436,7 +449,12 @@ int run_experts(const moe_config& c, const Layout& L, const uint16_t* xe, const 
       a.a8s = at<uint16_t>(ws, L.hs8);
     }
 #endif
-    MOE_HIP(launch_prefill_down(a, mt, s));
+    ad.work = a.work;
+#if MOE_PRE_MX8
+    ad.a8 = a.a8;
+    ad.a8s = a.a8s;
+#endif
+    MOE_HIP(launch_prefill_down(ad, mt, s));
   } else {
     if (fused_topk) {  // one token: selection and dispatch inside the gate+up kernel
       FusedRoute fr{};

@@ -4,8 +4,8 @@
 //   out[t] = bf16_rne(residual[t] + sum_j w[t,j] * y[row(t,j)] + y_shared[t])
 // summed in fp32 in the fixed order j = 0..K-1, then the shared expert, then the residual.
 // A zero-computation expert's y is the expert input x_e[t] itself.
-// y is fp32 [rows, H] on both expert paths. Each thread produces 8 consecutive outputs
-// with 128-bit stores.
+// y is fp32 [rows, H], except the routed rows of a prefill layer, which are fp16 (y16). Each
+// thread produces 8 consecutive outputs with 128-bit stores.
 #include "moe_device.h"
 
 namespace moe {
@@ -27,6 +27,17 @@ __device__ __forceinline__ void load_y8(const float* y, size_t off, float (&v)[8
   const float4 a = p[0], b = p[1];
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// 8 consecutive fp16 values of y16
+__device__ __forceinline__ void load_h8(const uint16_t* y16, size_t off, float (&v)[8]) {
+  const uint4 q = *reinterpret_cast<const uint4*>(y16 + off);
+  const uint32_t d[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = f16_to_f32(d[i] & 0xFFFFu);
+    v[2 * i + 1] = f16_to_f32(d[i] >> 16);
+  }
 }
 
 constexpr int kCombineBatch = 8;  // slots whose rows are loaded together
@@ -51,8 +62,11 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     }
     float v[kCombineBatch][8];
 #pragma unroll
-    for (int jj = 0; jj < kCombineBatch; ++jj)
-      load_y8(a.y, (size_t)(p[jj] >= 0 ? p[jj] : 0) * a.H + h0, v[jj]);
+    for (int jj = 0; jj < kCombineBatch; ++jj) {
+      const size_t off = (size_t)(p[jj] >= 0 ? p[jj] : 0) * a.H + h0;
+      if (a.y16) load_h8(a.y16, off, v[jj]);
+      else load_y8(a.y, off, v[jj]);
+    }
 #pragma unroll
     for (int jj = 0; jj < kCombineBatch; ++jj) {
       if (p[jj] == -2) load_bf16x8(a.xe + (size_t)t * a.H + h0, v[jj]);  // zero expert: x_e[t]

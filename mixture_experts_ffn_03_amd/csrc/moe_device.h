@@ -41,6 +41,21 @@ __device__ __forceinline__ float silu(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
 }
 
+// Two fp32 -> fp16 pair, round to nearest even, saturating at +-65504 (NaN stays NaN).
+__device__ __forceinline__ uint32_t pack_f16x2_sat(float lo, float hi) {
+  lo = fminf(fmaxf(lo, -65504.f), 65504.f);
+  hi = fminf(fmaxf(hi, -65504.f), 65504.f);
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  f16x2_t v;
+  v[0] = (_Float16)lo;
+  v[1] = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t h16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2_t v;
   v[0] = (__bf16)lo;

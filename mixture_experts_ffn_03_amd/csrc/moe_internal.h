@@ -143,6 +143,10 @@ struct ExpertGemmArgs {
   // per-XCD work counters of a persistent launch over the device tile list (zeroed by the
   // dispatch), or nullptr: one block per tile
   int32_t* work;
+  // prefill down over the device tile list: store y as fp16 (uint16_t rows [R, H], row r at
+  // y + r * H), saturating at +-65504 and setting MOE_DEVERR_Y_RANGE in *err_word; else fp32
+  int y_half;
+  int32_t* err_word;
 #if MOE_PRE_MX8
   // block-scaled MFMA variant (build flag, off by default; see moe_prefill.hip): activations
   // as MXFP8 hi + lo pairs ([rows][K/32][32 hi bytes, 32 lo bytes], same row bytes as bf16)
@@ -176,7 +180,8 @@ hipError_t launch_prefill_gate_up(const ExpertGemmArgs& a, int mt, hipStream_t s
 hipError_t launch_prefill_down(const ExpertGemmArgs& a, int mt, hipStream_t s);
 
 struct CombineArgs {
-  const float* y;         // [R, H] fp32
+  const float* y;         // [R, H] fp32 (with y16: the shared expert's rows [0, T) only)
+  const uint16_t* y16;    // routed rows as fp16 (row r at y16 + r * H), or nullptr
   const float* w;         // [T, K]
   const int32_t* inv;     // [T, K] row of slot (t, j), -1 (dropped) or -2 (zero expert)
   const uint16_t* xe;     // [T, H] expert input (the identity of a zero expert)

@@ -47,6 +47,7 @@
 #include <type_traits>
 
 #include "moe_device.h"
+#include "moe_fp4.h"
 
 namespace moe {
 
@@ -819,10 +820,13 @@ void k_pre_gemm(ExpertGemmArgs a) {
         }
       }
     } else {
-      // y stays fp32 (the blend reads it once): rounding it to bf16 would add up to half
-      // a bf16 ulp of every expert output to the layer's error
+      // y is fp32, or fp16 for routed prefill rows (y_half): the blend reads it once, and
+      // fp16's 11-bit significand keeps its rounding an eighth of a bf16 one (bf16 would add
+      // up to half a bf16 ulp of every expert output to the layer's error)
       const float gs = FMT == 0 ? load_uniform_f32(a.down.global, e) : 1.0f;
       float* y = reinterpret_cast<float*>(a.y);
+      uint16_t* y16 = reinterpret_cast<uint16_t*>(a.y);
+      bool range = false;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const int nb = n0 + wn * CB * 32 + cb * 32;
@@ -831,16 +835,27 @@ void k_pre_gemm(ExpertGemmArgs a) {
         for (int rb = 0; rb < RB; ++rb) {
           const int i = wm * 32 * RB + rb * 32 + r;
           if (i >= t.count) continue;
-          float* yrow = y + (size_t)(t.row0 + i) * a.H + nb + 4 * half;
+          const size_t off = (size_t)(t.row0 + i) * a.H + nb + 4 * half;
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const f32x16_t& c = acc[rb][cb];
-            *reinterpret_cast<float4*>(yrow + 8 * g4) =
-                make_float4(c[4 * g4] * gs, c[4 * g4 + 1] * gs, c[4 * g4 + 2] * gs,
-                            c[4 * g4 + 3] * gs);
+            const float v0 = c[4 * g4] * gs, v1 = c[4 * g4 + 1] * gs;
+            const float v2 = c[4 * g4 + 2] * gs, v3 = c[4 * g4 + 3] * gs;
+            if (a.y_half) {
+              range |= !(fabsf(v0) <= 65504.f && fabsf(v1) <= 65504.f &&
+                         fabsf(v2) <= 65504.f && fabsf(v3) <= 65504.f);
+              *reinterpret_cast<uint2*>(y16 + off + 8 * g4) =
+                  make_uint2(pack_f16x2_sat(v0, v1), pack_f16x2_sat(v2, v3));
+            } else {
+              *reinterpret_cast<float4*>(y + off + 8 * g4) = make_float4(v0, v1, v2, v3);
+            }
           }
         }
       }
+      // a value beyond the fp16 range was saturated: flag it (rare; one lane of the wave)
+      if (a.y_half && __builtin_amdgcn_ballot_w64(range) != 0ull && (threadIdx.x & 63) == 0 &&
+          a.err_word)
+        atomicOr(a.err_word, MOE_DEVERR_Y_RANGE);
     }
   };
 

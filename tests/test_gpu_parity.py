@@ -500,6 +500,26 @@ def test_prefill_persistent_down(fmt, shape):
     assert torch.equal(out, out2)
 
 
+def test_prefill_expert_output_range_is_flagged():
+    """Routed prefill expert outputs are stored as fp16 between the down projection and the
+    blend: an output beyond +-65504 saturates there and sets MOE_DEVERR_Y_RANGE (ordinary
+    outputs set nothing)."""
+    spec = S.LayerSpec(name="y_range", tokens=256, hidden=512, experts=8, top_k=2, inter=256,
+                       fmt=S.NVFP4, seed=1400)
+    inp = S.make_inputs(spec, device=DEV)
+    cfg = config_for(inp, M.PATH_PREFILL)
+    ws = M.alloc_workspace(cfg, DEV)
+    out = torch.empty_like(inp.x)
+    M.layer_forward(cfg, inp.x, inp.router_w, M.expert_weights(inp.routed), out, ws,
+                    residual=inp.residual)
+    assert M.get_device_error(ws) == 0
+    inp.routed.down.global_scale.mul_(1e9)  # NVFP4 tensor scale: every expert output huge
+    M.layer_forward(cfg, inp.x, inp.router_w, M.expert_weights(inp.routed), out, ws,
+                    residual=inp.residual)
+    assert M.get_device_error(ws) & M.DEVERR_Y_RANGE
+    assert torch.isfinite(out.float()).all()  # saturated, not inf
+
+
 def spec_e(inp):
     return inp.spec.experts
 

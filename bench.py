@@ -471,14 +471,15 @@ def run_workload(name, args, with_cpu=True, with_graph=True, steps=None, warmup=
     u_mean = sum(uniq[(warmup + i) % period] for i in range(steps)) / steps
     bpe = bytes_per_elem(spec.fmt)
     # algorithmic work of the dominant kernel per launch: each touched expert's weights
-    # once, its input activations and its output rows (y in fp32); flops of the routed rows
+    # once, its input activations and its output rows (y: fp16 routed prefill rows, else
+    # fp32); flops of the routed rows
     if kernel_stage == "gate_up":
         kbytes = u_mean * 2 * I * H * bpe + T * H * 2 + S_rows * I * 2
         kflops = 2 * S_rows * H * 2 * I
         unit_bytes = "2*I*H*b bytes per touched expert (b = 0.5625 NVFP4, 0.53125 MXFP4) + x in + h out"
         unit_flops = "4*H*I flops per routed row"
     else:
-        kbytes = u_mean * I * H * bpe + S_rows * I * 2 + S_rows * H * 4
+        kbytes = u_mean * I * H * bpe + S_rows * I * 2 + S_rows * H * (4 if decode else 2)
         kflops = 2 * S_rows * H * I
         unit_bytes = "I*H*b bytes per touched expert + h in + y out"
         unit_flops = "2*H*I flops per routed row"

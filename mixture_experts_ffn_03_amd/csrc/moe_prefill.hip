@@ -302,13 +302,16 @@ constexpr int kPreWaves = PreShape<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS>::BLOCK
 
 // Persistent form (PERSIST): gridDim.x blocks (a multiple of kXcds, at most the resident
 // slots) walk the work list of (row tile, column tile) items. The items are split into
-// kXcds contiguous ranges, one per XCD; block b (on XCD b % kXcds) starts at item
-// b / kXcds of its range and then takes the next unclaimed item of the range from the
-// XCD's work counter. The stage ring runs on across items: the next item is claimed at
-// step 0 of the current one, its tile read at step 2, and its first LEAD stages issued
-// during the current item's last LEAD steps, so neither the pipeline fill nor the
-// epilogue leaves the CU idle (MoE constructor page: the grouped GEMM runs as a
-// persistent grid over the compacted tile work list).
+// kXcds contiguous ranges, one per XCD; block b (dispatched to XCD b % kXcds) starts at
+// item b / kXcds of its range and then takes the next unclaimed item of the range from
+// that range's work counter. (Correctness does not depend on where a block runs: every
+// item of a range is claimed exactly once by the blocks of that range; only L2 locality
+// does.) The stage ring runs on across items: the next item is claimed at step 0 of the
+// current one and published in LDS at step 1; at step nch - LEAD every wave reads it, the
+// next tile's header and its load sources, and the next tile's first LEAD stages are
+// issued during the current item's last LEAD steps, so neither the pipeline fill nor the
+// epilogue leaves the CU idle (MoE constructor page: the grouped GEMM runs as a persistent
+// grid over the compacted tile work list).
 template <int FMT, int KC, int NSTG, int RB, int WM, int CB, bool GATEUP, bool SS>
 constexpr int kPersistLds = PreShape<FMT, KC, NSTG, RB, WM, CB, GATEUP, SS>::SMEM + 16;
 

@@ -242,10 +242,10 @@ __device__ __forceinline__ void load_step(const WSrc src, size_t row_bytes, int 
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int n = min(n_base + pass * GR + G * i, nmax);
-    st.w[i][0] = *reinterpret_cast<const uint4*>(src.p0 + (size_t)n * row_bytes + c * 16);
+    st.w[i][0] = load_weights16(src.p0 + (size_t)n * row_bytes + c * 16);
     st.s[i][0] = load_chunk_scales<FMT>(src.s0, n, sstride, c);
     if (M > 1) {
-      st.w[i][M - 1] = *reinterpret_cast<const uint4*>(src.p1 + (size_t)n * row_bytes + c * 16);
+      st.w[i][M - 1] = load_weights16(src.p1 + (size_t)n * row_bytes + c * 16);
       st.s[i][M - 1] = load_chunk_scales<FMT>(src.s1, n, sstride, c);
     }
   }
@@ -585,10 +585,10 @@ __device__ __forceinline__ void dec_one_body(const ExpertGemmArgs& a, const Tile
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int n = min(nbase + grp + G * i, N - 1);
-    w[i][0] = *reinterpret_cast<const uint4*>(w0.packed + eoff + (size_t)n * row_bytes + c * 16);
+    w[i][0] = load_weights16(w0.packed + eoff + (size_t)n * row_bytes + c * 16);
     sc[i][0] = load_chunk_scales<FMT>(w0.scales + e * sexp, n, sstride, c);
     if (M == 2) {
-      w[i][M - 1] = *reinterpret_cast<const uint4*>(a.up.packed + eoff + (size_t)n * row_bytes + c * 16);
+      w[i][M - 1] = load_weights16(a.up.packed + eoff + (size_t)n * row_bytes + c * 16);
       sc[i][M - 1] = load_chunk_scales<FMT>(a.up.scales + e * sexp, n, sstride, c);
     }
   }

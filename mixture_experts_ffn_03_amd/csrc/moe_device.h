@@ -18,6 +18,25 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
 
+// Weight streams of the decode GEMVs: each 16-byte piece of an expert's weights is read once
+// per layer call, so these loads carry the non-temporal hint (streaming cache policy). Measured
+// on the Qwen3-like 8-token decode: gate+up 20.6 -> 19.6 us, step 50.0 -> 46.8 us; neutral on
+// the DeepSeek-V3-like and one-token decodes. The block-scale bytes stay plain loads: neighbouring
+// lanes and passes share their lines (non-temporal scales slowed the DeepSeek-V3-like gate+up by
+// 3 %). Build flag MOE_NT_WEIGHTS=0 gives plain weight loads.
+#ifndef MOE_NT_WEIGHTS
+#define MOE_NT_WEIGHTS 1
+#endif
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_weights16(const void* p) {
+#if MOE_NT_WEIGHTS
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *reinterpret_cast<const uint4*>(p);
+#endif
+}
+
 // Tile count of a dispatch, written with the persistent GEMMs' work counters zeroed
 // (one thread; the GEMMs run after the dispatch on the same stream).
 __device__ __forceinline__ void publish_tile_count(int32_t* ntiles, int n) {

@@ -14,9 +14,16 @@ constexpr int kProbeThreads = 256;      // four waves, one per SIMD
 constexpr int kProbeChains = 8;         // independent MFMA accumulators per wave
 
 // Streaming read: block b reads the b-th contiguous chunk of the region, each thread eight
-// 16-byte pieces in flight per round (the fastest of the grid-stride and per-block-chunk
-// shapes measured, 2048 x 256 threads). The pieces' XOR feeds the output, so no load can
-// be dropped; a block writes its sink slot only if its XOR hits one particular value.
+// 16-byte pieces in flight per round, with the non-temporal hint (among the grid-stride and
+// per-block-chunk shapes of 1024-16384 blocks measured, the non-temporal loads were the
+// fastest, about 10 % above plain ones: 6.2 against 5.5 TB/s over 200 MB). The pieces' XOR
+// feeds the output, so no load can be dropped; a block writes its sink slot only if its XOR
+// hits one particular value.
+__device__ __forceinline__ uint4 load_nt16(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __global__ __launch_bounds__(kProbeThreads) void k_probe_read(const uint4* __restrict__ p,
                                                              size_t n, float* sink) {
   constexpr int U = 8;
@@ -28,12 +35,12 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_read(const uint4* __res
   for (; i + (U - 1) * kProbeThreads < b1; i += U * kProbeThreads) {
     uint4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = p[i + u * kProbeThreads];
+    for (int u = 0; u < U; ++u) v[u] = load_nt16(p + i + u * kProbeThreads);
 #pragma unroll
     for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (; i < b1; i += kProbeThreads) {
-    const uint4 a = p[i];
+    const uint4 a = load_nt16(p + i);
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
   if (acc == 0x9E3779B9u) sink[blockIdx.x] = 1.0f;

@@ -10,6 +10,14 @@
 
 namespace moe {
 
+// The expert outputs y are dead after the blend: their loads carry the non-temporal hint
+// (streaming cache policy). Zipf prefill at 4096 tokens: blend 52.2 -> 49.2 us. The output keeps
+// plain stores: the next layer reads it.
+__device__ __forceinline__ uint4 load_y_nt(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // 8 consecutive bf16 values -> fp32
 __device__ __forceinline__ void load_bf16x8(const uint16_t* p, float (&v)[8]) {
   const uint4 q = *reinterpret_cast<const uint4*>(p);
@@ -23,15 +31,14 @@ __device__ __forceinline__ void load_bf16x8(const uint16_t* p, float (&v)[8]) {
 
 // 8 consecutive fp32 values of y
 __device__ __forceinline__ void load_y8(const float* y, size_t off, float (&v)[8]) {
-  const float4* p = reinterpret_cast<const float4*>(y + off);
-  const float4 a = p[0], b = p[1];
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  const uint4 a = load_y_nt(y + off), b = load_y_nt(y + off + 4);
+  v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+  v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
 }
 
 // 8 consecutive fp16 values of y16
 __device__ __forceinline__ void load_h8(const uint16_t* y16, size_t off, float (&v)[8]) {
-  const uint4 q = *reinterpret_cast<const uint4*>(y16 + off);
+  const uint4 q = load_y_nt(y16 + off);
   const uint32_t d[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -50,7 +57,8 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   // batches of kCombineBatch slots: their rows and weights first, then every row's loads
-  // (a dropped slot's load reads row 0 and is discarded), then the sums in slot order
+  // (a dropped slot's load reads row 0 and is discarded; slots past K load nothing), then the
+  // sums in slot order
   for (int j0 = 0; j0 < a.K; j0 += kCombineBatch) {
     int p[kCombineBatch];
     float w[kCombineBatch];
@@ -63,6 +71,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     float v[kCombineBatch][8];
 #pragma unroll
     for (int jj = 0; jj < kCombineBatch; ++jj) {
+      if (j0 + jj >= a.K) break;  // (uniform over the grid)
       const size_t off = (size_t)(p[jj] >= 0 ? p[jj] : 0) * a.H + h0;
       if (a.y16) load_h8(a.y16, off, v[jj]);
       else load_y8(a.y, off, v[jj]);

@@ -98,9 +98,17 @@ __global__ __launch_bounds__(kDispatchThreads) void k_dispatch_scatter(DispatchA
   __shared__ int s_wc[kDispatchWaves][kMaxExperts];
   __shared__ int s_off[kMaxExperts];
   __shared__ int s_tmp[2 * kDispatchWaves + 1];
+  __shared__ int s_err;
   const int tid = threadIdx.x, wave = tid >> 6;
   const int E = a.E, S = a.T * a.K;
   const int nb = gridDim.x;  // a multiple of 4
+  // block 0: the error bits of every block of the count launch, requested up front and
+  // OR-ed over the block (one load per thread, not a loop of dependent loads)
+  int perr = 0;
+  if (blockIdx.x == 0) {
+    if (tid == 0) s_err = 0;
+    for (int b = tid; b < nb; b += kDispatchThreads) perr |= a.err_part[b];
+  }
   // per expert: rows of the blocks before this one, and the group size
   int cnt = 0, before = 0;
   if (tid < E) {
@@ -137,13 +145,13 @@ __global__ __launch_bounds__(kDispatchThreads) void k_dispatch_scatter(DispatchA
   scatter_segment(a, a.ids, sb, se, s_wc[wave], s_off);
   if (blockIdx.x != 0) return;
   for (int p = tid; p < a.shared_rows; p += kDispatchThreads) a.row_token[p] = p;
+  if (perr) atomicOr(&s_err, perr);  // (s_err was zeroed before the block's first barrier)
   int ntot = 0;
   write_tiles<kDispatchWaves>(a, cnt, s_off, s_tmp, &ntot);  // prefill tiles: no tokens read
+  __syncthreads();
   if (tid == 0) {
-    int err = 0;
-    for (int b = 0; b < nb; ++b) err |= a.err_part[b];
     publish_tile_count(a.ntiles, ntot);
-    a.err_word[0] = err;
+    a.err_word[0] = s_err;
   }
 }
 

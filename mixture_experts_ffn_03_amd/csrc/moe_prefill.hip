@@ -12,11 +12,12 @@
 // * A block of 4 waves (one per SIMD) computes an MT-row tile of one expert against
 //   BROWS weight rows. Each wave owns RB 32-row blocks and CB 32-column blocks of
 //   weight rows (gate+up: half of them gate and the same ones of up, so SwiGLU runs in
-//   the epilogue on values held by the same lane), i.e. RB*CB independent accumulators;
-//   each decoded B operand feeds RB MFMAs.
+//   the epilogue on values held by the same lane; with one column block per wave, waves
+//   0-1 hold gate and 2-3 up, paired through LDS in the epilogue), i.e. RB*CB independent
+//   accumulators; each decoded B operand feeds RB MFMAs.
 // * Both operands reach LDS by direct-to-LDS loads (global_load_lds_*: the activation
 //   rows gathered by row_token, the FP4 weight rows and their scale bytes) into a ring
-//   of three 64-wide K stages. Step c waits for stage c, synchronises the block once,
+//   of K stages (three of 64 codes for most shapes; see launch_pre). Step c waits for stage c, synchronises the block once,
 //   reads stage c's operands from LDS, issues stage c+2 into the slot freed by step c-1,
 //   then runs the MFMAs of stage c.
 //   Loads therefore have two steps to land, and no registers are spent on them.
@@ -143,12 +144,13 @@ __device__ __forceinline__ void wait_inflight(int r, bool ss) {
 // bit 3; of 4 pieces (64 bytes) by ((row >> 1) ^ (row >> 3)) & 3.
 template <int PA>
 __device__ __forceinline__ int a_swz(int row) {
-  if (PA == 16) return row & 15;
+  if (PA >= 16) return row & 15;
   if (PA == 8) return ((row >> 1) ^ ((row & 1) << 2)) & 7;
   return ((row >> 1) ^ (row >> 2)) & 3;  // 4 pieces (64-byte rows)
 }
 template <int PB>
 __device__ __forceinline__ int b_swz(int row) {
+  if (PB == 8) return (row >> 1) & 7;
   return PB == 2 ? ((row >> 2) ^ (row >> 3)) & 1 : ((row >> 1) ^ (row >> 3)) & 3;
 }
 
@@ -282,13 +284,16 @@ struct PreShape {
   static constexpr int TAB_BYTES = FMT == 2 ? MATS * NBL * kFp8MaxKb * 4 : 0;
   static constexpr size_t SMEM = (size_t)NSTG * STAGE + SS_BYTES + TAB_BYTES;
   static constexpr int BLOCKS_PER_CU = SMEM <= 80 * 1024 ? 2 : 1;
-  static_assert(FP4 ? (KC == 64 || KC == 128) : KC == 32, "stage width");
+  static_assert(FP4 ? (KC == 64 || KC == 128 || (KC == 256 && FMT == 1 && SS)) : KC == 32,
+                "stage width");
   static_assert(!SS || FP4, "super-staged scales are FP4 only");
   static_assert(PB >= 2 && WPS * 2 * STEPS * 4 == B_ROW, "B row split over the lane halves");
   static_assert(NA * NT == MT * PA && NB * NT == BROWS * PB && NS * NT * 4 == S_BYTES,
                 "a stage must split evenly over the block");
   static_assert(!SS || NSS * SS_WAVES * 64 == BROWS, "one super-stage load per row");
-  static_assert(CB % 2 == 0 || !GATEUP, "gate+up pairs column blocks");
+  // gate+up pairs column blocks inside a wave, or (one column block per wave, FP4) across
+  // waves: waves 0 .. WN/2-1 hold gate columns, the others the same columns of up
+  static_assert(CB % 2 == 0 || !GATEUP || (CB == 1 && WN == 4 && FP4), "gate+up pairs column blocks");
   static_assert(NSTG >= 2 && NSTG <= 5, "ring depth");
   static_assert(LEAD <= SUPER, "a super-stage slot is refilled only after its last read");
   static_assert((LEAD - 1) * NLOADS + NSS <= 63, "the loads in flight must fit the wait counter");
@@ -542,12 +547,16 @@ void k_pre_gemm(ExpertGemmArgs a) {
 
   // B-tile rows of this wave's column blocks
   // (gate+up: column blocks 0..CB/2-1 are gate rows, CB/2.. the same rows of up)
-  constexpr int CH = GATEUP ? CB / 2 : CB;
+  // XW: one column block per wave, gate in waves 0 and 1, up in waves 2 and 3 (paired in
+  // the epilogue through LDS)
+  constexpr bool XW = GATEUP && CB == 1;
+  constexpr int CH = GATEUP ? (XW ? 1 : CB / 2) : CB;
   int brow0[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    brow0[cb] = GATEUP ? (cb / CH) * (BROWS / 2) + wn * CH * 32 + (cb % CH) * 32
-                       : wn * CB * 32 + cb * 32;
+    brow0[cb] = XW ? wn * 32
+                   : GATEUP ? (cb / CH) * (BROWS / 2) + wn * CH * 32 + (cb % CH) * 32
+                            : wn * CB * 32 + cb * 32;
   }
   const int arow = wm * 32 * RB + r;  // + rb * 32
   const int bsw = b_swz<PB>(r);  // = b_swz(brow0[cb] + r): brow0 is a multiple of 32
@@ -780,9 +789,10 @@ void k_pre_gemm(ExpertGemmArgs a) {
       float* prow0 = a.part + (size_t)blockIdx.z * a.src.implicit_rows * NO;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const int col = GATEUP ? n0 + wn * CH * 32 + (cb % CH) * 32 : n0 + wn * CB * 32 + cb * 32;
+        const int col = XW ? n0 + (wn & 1) * 32
+                           : GATEUP ? n0 + wn * CH * 32 + (cb % CH) * 32 : n0 + wn * CB * 32 + cb * 32;
         if (col >= N) continue;
-        const int ocol = GATEUP && cb >= CH ? a.I + col : col;
+        const int ocol = XW ? (wn >= 2 ? a.I + col : col) : (GATEUP && cb >= CH ? a.I + col : col);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const int i = wm * 32 * RB + rb * 32 + r;
@@ -793,6 +803,42 @@ void k_pre_gemm(ExpertGemmArgs a) {
             const f32x16_t& cc = acc[rb][cb];
             *reinterpret_cast<float4*>(prow + 8 * g4) =
                 make_float4(cc[4 * g4], cc[4 * g4 + 1], cc[4 * g4 + 2], cc[4 * g4 + 3]);
+          }
+        }
+      }
+    } else if constexpr (XW) {
+      // up waves hand their sums to the gate waves of the same columns through LDS (the
+      // stage ring is idle once every wave has left the K loop)
+      const float gs_g = FMT == 0 ? a.gate.global[e] : 1.0f;
+      const float gs_u = FMT == 0 ? a.up.global[e] : 1.0f;
+      float* s_u = reinterpret_cast<float*>(s_dyn);
+      __syncthreads();
+      if (wn >= 2) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) s_u[(((wn - 2) * RB + rb) * 16 + v) * 64 + lane] = acc[rb][0][v];
+      }
+      __syncthreads();
+      const int nb = n0 + (wn & 1) * 32;
+      if (wn < 2 && nb < N) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int i = wm * 32 * RB + rb * 32 + r;
+          if (i >= t.count) continue;
+          uint16_t* hrow = a.h + (size_t)(t.row0 + i) * a.h_stride + nb + 4 * half;
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            float hv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int v = 4 * g4 + j;
+              const float g = acc[rb][0][v] * gs_g;
+              const float u = s_u[((wn * RB + rb) * 16 + v) * 64 + lane] * gs_u;
+              hv[j] = silu(g) * u;
+            }
+            *reinterpret_cast<uint2*>(hrow + 8 * g4) =
+                make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
           }
         }
       }
@@ -1041,7 +1087,8 @@ static hipError_t launch_pre_shape(const ExpertGemmArgs& a, hipStream_t s) {
     if (FMT == 1 && KC == 64) return launch_pre_ss<FMT, KC, NSTG, RB, WM, CB, GATEUP, false>(a, s);
 #endif
     if (sbytes % 16 == 0) return launch_pre_ss<FMT, KC, NSTG, RB, WM, CB, GATEUP, true>(a, s);
-    return launch_pre_ss<FMT, KC, NSTG, RB, WM, CB, GATEUP, false>(a, s);
+    if constexpr (KC == 256) return hipErrorInvalidValue;  // (super-staged scales only)
+    else return launch_pre_ss<FMT, KC, NSTG, RB, WM, CB, GATEUP, false>(a, s);
   }
 }
 
@@ -1049,8 +1096,9 @@ static hipError_t launch_pre_shape(const ExpertGemmArgs& a, hipStream_t s) {
 // WM, column blocks per wave CB): FP4 128 = 64-code stages, 4 x 1 x 2 (128 x 256 weight
 // rows; each wave all 128 rows, so a decoded B operand feeds four MFMAs); FP4 64 = 64-code
 // stages, 2 x 1 x 2 (64 x 256); FP4 32 = 128-code stages, 1 x 1 x 2 (32 x 256: twice the
-// blocks of 32 x 512, which balanced worse). K that is not a multiple of 128 takes 64-code
-// stages, 1 x 1 x 4 (32 x 512), at height 32.
+// blocks of 32 x 512, which balanced worse), except MXFP4 with K a multiple of 512:
+// 256-code stages in a two-slot ring, 1 x 1 x 1 (32 x 128). K that is not a multiple of 128
+// takes 64-code stages, 1 x 1 x 4 (32 x 512), at height 32.
 #ifndef MOE_PRE_NSTG
 #define MOE_PRE_NSTG 3
 #endif
@@ -1068,6 +1116,12 @@ static hipError_t launch_pre(const ExpertGemmArgs& a, int mt, hipStream_t s) {
     if (mt == 64) return launch_pre_shape<0, 64, 3, 2, 1, 2, GATEUP>(a, s);
     return launch_pre_shape<0, 64, NS3, 4, 1, 2, GATEUP>(a, s);
   }
+  // MXFP4 at 32-row tiles with K a multiple of 512: 256-code stages, so each stage reads
+  // whole 128-byte lines of the weight rows (with 128-code stages the second half of every
+  // line was fetched again one stage later: 1.42x the weight bytes at the hash layer's
+  // gate+up). Gate+up pairs gate and up columns across waves to keep the block at 68 KB.
+  if (mt == 32 && fmt == 1 && K % 512 == 0)
+    return launch_pre_shape<1, 256, 2, 1, 1, 1, GATEUP>(a, s);
   if (mt == 32 && fmt == 1) {
     return K % 128 == 0 ? launch_pre_shape<1, 128, 3, 1, 1, 2, GATEUP>(a, s)
                         : launch_pre_shape<1, 64, 3, 1, 1, 4, GATEUP>(a, s);

@@ -72,6 +72,14 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(lds_base), "v"(g) : "memory", "m0");
 }
+// the same with the non-temporal hint: weight rows that one block streams once (256-code
+// stages of 32-row tiles, whose experts rarely have a second row tile). Hash layer gate+up
+// 498 -> 476 us; on 128-row tiles, whose weights the expert's other row tiles re-read from the
+// caches, the hint made gate+up 25 % slower.
+__device__ __forceinline__ void dma16_nt(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+               :: "s"(lds_base), "v"(g) : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
                :: "s"(lds_base), "v"(g) : "memory", "m0");
@@ -504,7 +512,10 @@ void k_pre_gemm(ExpertGemmArgs a) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int slot0 = (wave * NB + i) * 64;
-      dma16(bsrc[i] + (size_t)k0 * Sh::B_ROW / KC, __builtin_amdgcn_readfirstlane(bbase + slot0 * 16));
+      if (KC == 256)
+        dma16_nt(bsrc[i] + (size_t)k0 * Sh::B_ROW / KC, __builtin_amdgcn_readfirstlane(bbase + slot0 * 16));
+      else
+        dma16(bsrc[i] + (size_t)k0 * Sh::B_ROW / KC, __builtin_amdgcn_readfirstlane(bbase + slot0 * 16));
     }
     if (Sh::MX8) {
       const uint32_t asbase = sbase + Sh::S_BYTES;

@@ -312,6 +312,12 @@ SMALL = {
                                     experts=64, top_k=6, inter=192, fmt=S.MXFP4,
                                     score=S.SOFTMAX, renormalize=False, shared=True,
                                     shared_inter=192, shared_fmt=S.MXFP4, seed=1089),
+    # MXFP4 at 32-row tiles with K a multiple of 512 (256-code stages, gate and up paired
+    # across waves): routed experts on the dispatch's tile list, and a shared expert of few
+    # tokens whose K is split over blocks (the split sums of the paired columns)
+    "mx_k256_split": S.LayerSpec(name="mx_k256_split", tokens=20, hidden=4096, experts=8,
+                                 top_k=2, inter=128, fmt=S.MXFP4, renormalize=True,
+                                 shared=True, shared_inter=128, shared_fmt=S.MXFP4, seed=1093),
     # the library's limits, 1024 experts and 32 slots per token: 96 slots (the bitmap
     # dispatch, two words per expert) and 1280 slots (the block counting sort)
     "max_e1024_k32_t3": S.LayerSpec(name="max_e1024_k32_t3", tokens=3, hidden=256,

@@ -232,16 +232,17 @@ __device__ __forceinline__ bf16x8_t b_operand(const uint32_t q, const uint32_t s
 
 // Block = 4 waves (one per SIMD) in a WM x WN grid, with a ring of NSTG stage slots. Tile height MT = 32 * RB * WM;
 // BROWS weight rows per block (gate+up: BROWS/2 gate rows and the same BROWS/2 up rows;
-// down: BROWS output columns). A stage holds KC (64 or 128) codes of K: the A tile (MT
+// down: BROWS output columns). A stage holds KC (64, 128 or 256) codes of K: the A tile (MT
 // rows x 2*KC bytes of bf16) and the B tile (BROWS rows x KC/2 bytes of E2M1 codes).
 // Scales come one of two ways:
 // * SS = false: with each stage, per weight row one 4-byte LDS slot per 64 codes holding
 //   their scale bytes (NVFP4 four, MXFP4 two), loaded as one dword or one ushort.
 // * SS = true (scale rows a multiple of 16 bytes): 16 bytes per row at a time, covering
 //   SUPER stages (256 codes NVFP4, 512 MXFP4), into one of two super-stage slots.
-// With KC = 64 a block takes at most 80 KB of LDS, so two blocks share a CU: the waves of
-// one fill the SIMDs while the other waits at its barrier or on LDS. KC = 128 (one block
-// per CU) reads each weight row in 64-byte pieces, which suits the HBM-bound short tiles.
+// Every shape in use keeps a block within 80 KB of LDS, so two blocks share a CU: the waves
+// of one fill the SIMDs while the other waits at its barrier or on LDS. The 32-row tiles
+// of the HBM-bound short groups take longer stages: 128 codes (64-byte pieces of each weight
+// row), or 256 for MXFP4 (whole 128-byte lines, in a two-slot ring).
 template <int FMT, int KC, int NSTG, int RB, int WM, int CB, bool GATEUP, bool SS>
 struct PreShape {
   static constexpr int NW = 4;

@@ -162,11 +162,14 @@ __device__ __forceinline__ int b_swz(int row) {
   return PB == 2 ? ((row >> 2) ^ (row >> 3)) & 1 : ((row >> 1) ^ (row >> 3)) & 3;
 }
 
-// Little-endian load of W (1, 2 or 4) scale bytes from LDS.
+// Scale word of a lane half: W (1, 2, 4 or 8) scale bytes, little-endian.
 template <int W>
-__device__ __forceinline__ uint32_t lds_scale(const uint8_t* p) {
-  if (W == 4) return *reinterpret_cast<const uint32_t*>(p);
-  if (W == 2) return *reinterpret_cast<const uint16_t*>(p);
+using ScaleWord = std::conditional_t<(W > 4), uint64_t, uint32_t>;
+template <int W>
+__device__ __forceinline__ ScaleWord<W> lds_scale(const uint8_t* p) {
+  if constexpr (W == 8) return *reinterpret_cast<const uint64_t*>(p);
+  if constexpr (W == 4) return *reinterpret_cast<const uint32_t*>(p);
+  if constexpr (W == 2) return *reinterpret_cast<const uint16_t*>(p);
   return *p;
 }
 
@@ -221,8 +224,8 @@ __device__ __forceinline__ Tile load_tile_header(const Tile* tiles, int i) {
 }
 
 // Operand for MFMA step s (codes 8s..8s+7 of the lane's codes of the stage).
-template <int FMT>
-__device__ __forceinline__ bf16x8_t b_operand(const uint32_t q, const uint32_t sc_word, int s) {
+template <int FMT, typename W>
+__device__ __forceinline__ bf16x8_t b_operand(const uint32_t q, const W sc_word, int s) {
   const int blk = FMT == 0 ? s / 2 : s / 4;  // 16- or 32-code block inside the lane's codes
   const uint32_t sb = (sc_word >> (8 * blk)) & 0xFFu;
   uint32_t d[4];
@@ -293,8 +296,7 @@ struct PreShape {
   static constexpr int TAB_BYTES = FMT == 2 ? MATS * NBL * kFp8MaxKb * 4 : 0;
   static constexpr size_t SMEM = (size_t)NSTG * STAGE + SS_BYTES + TAB_BYTES;
   static constexpr int BLOCKS_PER_CU = SMEM <= 80 * 1024 ? 2 : 1;
-  static_assert(FP4 ? (KC == 64 || KC == 128 || (KC == 256 && FMT == 1 && SS)) : KC == 32,
-                "stage width");
+  static_assert(FP4 ? (KC == 64 || KC == 128 || (KC == 256 && SS)) : KC == 32, "stage width");
   static_assert(!SS || FP4, "super-staged scales are FP4 only");
   static_assert(PB >= 2 && WPS * 2 * STEPS * 4 == B_ROW, "B row split over the lane halves");
   static_assert(NA * NT == MT * PA && NB * NT == BROWS * PB && NS * NT * 4 == S_BYTES,
@@ -586,7 +588,8 @@ void k_pre_gemm(ExpertGemmArgs a) {
     const uint8_t* sbq = sa + Sh::A_BYTES;
     const uint8_t* ssc = sbq + Sh::B_BYTES;
     constexpr int WPS = Sh::WPS;
-    uint32_t q[CB][STEPS * WPS], sc[CB];
+    uint32_t q[CB][STEPS * WPS];
+    ScaleWord<Sh::SW> sc[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const int srow = brow0[cb] + r;
@@ -1108,8 +1111,8 @@ static hipError_t launch_pre_shape(const ExpertGemmArgs& a, hipStream_t s) {
 // WM, column blocks per wave CB): FP4 128 = 64-code stages, 4 x 1 x 2 (128 x 256 weight
 // rows; each wave all 128 rows, so a decoded B operand feeds four MFMAs); FP4 64 = 64-code
 // stages, 2 x 1 x 2 (64 x 256); FP4 32 = 128-code stages, 1 x 1 x 2 (32 x 256: twice the
-// blocks of 32 x 512, which balanced worse), except MXFP4 with K a multiple of 512:
-// 256-code stages in a two-slot ring, 1 x 1 x 1 (32 x 128). K that is not a multiple of 128
+// blocks of 32 x 512, which balanced worse), except MXFP4 with K a multiple of 512 and
+// NVFP4 with K a multiple of 256: 256-code stages in a two-slot ring, 1 x 1 x 1 (32 x 128). K that is not a multiple of 128
 // takes 64-code stages, 1 x 1 x 4 (32 x 512), at height 32.
 #ifndef MOE_PRE_NSTG
 #define MOE_PRE_NSTG 3
@@ -1122,6 +1125,8 @@ static hipError_t launch_pre(const ExpertGemmArgs& a, int mt, hipStream_t s) {
   constexpr int NS3 = MOE_PRE_NSTG;
   if (fmt == 0) {
     if (mt == 32) {
+      // K a multiple of 256: 256-code stages reading whole weight lines, as for MXFP4 below
+      if (K % 256 == 0) return launch_pre_shape<0, 256, 2, 1, 1, 1, GATEUP>(a, s);
       return K % 128 == 0 ? launch_pre_shape<0, 128, 3, 1, 1, 2, GATEUP>(a, s)
                           : launch_pre_shape<0, 64, 3, 1, 1, 4, GATEUP>(a, s);
     }

@@ -318,6 +318,11 @@ SMALL = {
     "mx_k256_split": S.LayerSpec(name="mx_k256_split", tokens=20, hidden=4096, experts=8,
                                  top_k=2, inter=128, fmt=S.MXFP4, renormalize=True,
                                  shared=True, shared_inter=128, shared_fmt=S.MXFP4, seed=1093),
+    # the same with NVFP4 (eight E4M3 scale bytes per lane half and stage): routed gate+up
+    # over 16 stages, down over a single stage, a split-K shared expert
+    "nv_k256_split": S.LayerSpec(name="nv_k256_split", tokens=20, hidden=4096, experts=8,
+                                 top_k=2, inter=256, fmt=S.NVFP4, renormalize=True,
+                                 shared=True, shared_inter=256, shared_fmt=S.NVFP4, seed=1094),
     # the library's limits, 1024 experts and 32 slots per token: 96 slots (the bitmap
     # dispatch, two words per expert) and 1280 slots (the block counting sort)
     "max_e1024_k32_t3": S.LayerSpec(name="max_e1024_k32_t3", tokens=3, hidden=256,

@@ -900,17 +900,36 @@ void k_pre_gemm(ExpertGemmArgs a) {
           const int i = wm * 32 * RB + rb * 32 + r;
           if (i >= t.count) continue;
           const size_t off = (size_t)(t.row0 + i) * a.H + nb + 4 * half;
+          const f32x16_t& c = acc[rb][cb];
+          if (a.y_half) {
+            // lane half h holds columns 8g + 4h .. 8g + 4h + 3 (g = 0..3). The two halves swap
+            // half of them (lane l <-> l + 32), so that each lane stores 16 contiguous bytes
+            // and each store instruction fills whole 32-byte sectors: half 0 columns 0-7 and
+            // 16-23, half 1 columns 8-15 and 24-31.
+            uint32_t pk[4][2];
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x16_t& c = acc[rb][cb];
-            const float v0 = c[4 * g4] * gs, v1 = c[4 * g4 + 1] * gs;
-            const float v2 = c[4 * g4 + 2] * gs, v3 = c[4 * g4 + 3] * gs;
-            if (a.y_half) {
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const float v0 = c[4 * g4] * gs, v1 = c[4 * g4 + 1] * gs;
+              const float v2 = c[4 * g4 + 2] * gs, v3 = c[4 * g4 + 3] * gs;
               range |= !(fabsf(v0) <= 65504.f && fabsf(v1) <= 65504.f &&
                          fabsf(v2) <= 65504.f && fabsf(v3) <= 65504.f);
-              *reinterpret_cast<uint2*>(y16 + off + 8 * g4) =
-                  make_uint2(pack_f16x2_sat(v0, v1), pack_f16x2_sat(v2, v3));
-            } else {
+              pk[g4][0] = pack_f16x2_sat(v0, v1);
+              pk[g4][1] = pack_f16x2_sat(v2, v3);
+            }
+            const uint32_t s0 = half ? pk[0][0] : pk[1][0], s1 = half ? pk[0][1] : pk[1][1];
+            const uint32_t s2 = half ? pk[2][0] : pk[3][0], s3 = half ? pk[2][1] : pk[3][1];
+            const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 32), r1 = (uint32_t)__shfl_xor((int)s1, 32);
+            const uint32_t r2 = (uint32_t)__shfl_xor((int)s2, 32), r3 = (uint32_t)__shfl_xor((int)s3, 32);
+            uint16_t* yrow = y16 + (size_t)(t.row0 + i) * a.H + nb;
+            *reinterpret_cast<uint4*>(yrow + (half ? 8 : 0)) =
+                half ? make_uint4(r0, r1, pk[1][0], pk[1][1]) : make_uint4(pk[0][0], pk[0][1], r0, r1);
+            *reinterpret_cast<uint4*>(yrow + (half ? 24 : 16)) =
+                half ? make_uint4(r2, r3, pk[3][0], pk[3][1]) : make_uint4(pk[2][0], pk[2][1], r2, r3);
+          } else {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const float v0 = c[4 * g4] * gs, v1 = c[4 * g4 + 1] * gs;
+              const float v2 = c[4 * g4 + 2] * gs, v3 = c[4 * g4 + 3] * gs;
               *reinterpret_cast<float4*>(y + off + 8 * g4) = make_float4(v0, v1, v2, v3);
             }
           }

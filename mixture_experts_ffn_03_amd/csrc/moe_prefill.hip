@@ -61,6 +61,23 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint32_t (&d)[4]) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// One row's 32 columns of an MFMA output block as 16-bit values, lane half h holding
+// columns 8g + 4h .. 8g + 4h + 3 (g = 0..3) packed in pk[g]: the two halves swap half of
+// them (lane l with l + 32), so each lane stores 16 contiguous bytes and each store
+// instruction writes 32 contiguous bytes of each of 32 rows (half 0: columns 0-7 and 16-23,
+// half 1: 8-15 and 24-31). Both lanes of a pair must be active.
+__device__ __forceinline__ void store_cols32_16bit(uint16_t* row, const uint32_t (&pk)[4][2],
+                                                   int half) {
+  const uint32_t s0 = half ? pk[0][0] : pk[1][0], s1 = half ? pk[0][1] : pk[1][1];
+  const uint32_t s2 = half ? pk[2][0] : pk[3][0], s3 = half ? pk[2][1] : pk[3][1];
+  const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 32), r1 = (uint32_t)__shfl_xor((int)s1, 32);
+  const uint32_t r2 = (uint32_t)__shfl_xor((int)s2, 32), r3 = (uint32_t)__shfl_xor((int)s3, 32);
+  *reinterpret_cast<uint4*>(row + (half ? 8 : 0)) =
+      half ? make_uint4(r0, r1, pk[1][0], pk[1][1]) : make_uint4(pk[0][0], pk[0][1], r0, r1);
+  *reinterpret_cast<uint4*>(row + (half ? 24 : 16)) =
+      half ? make_uint4(r2, r3, pk[3][0], pk[3][1]) : make_uint4(pk[2][0], pk[2][1], r2, r3);
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return (uint32_t)(uintptr_t)(const lds_u8*)p;
 }
@@ -793,8 +810,10 @@ void k_pre_gemm(ExpertGemmArgs a) {
   // epilogue. The weights are the MFMA's first operand, so block (rb, cb) holds
   // out[token][n] transposed: lane l owns token row wm*32*RB + rb*32 + l % 32 and, in
   // element v, column 8*(v/4) + 4*half + v%4 of the 32-column block, i.e. four runs of 4
-  // consecutive columns, each stored as one write (8 bytes of h, 16 bytes of y). Column blocks are 32-aligned
-  // and N is a multiple of 32, so a block is wholly inside N or wholly outside.
+  // consecutive columns: fp32 outputs are stored one run per write (16 bytes), 16-bit ones
+  // (h, fp16 y) 8 columns per write after a swap between the lane halves
+  // (store_cols32_16bit). Column blocks are 32-aligned and N is a multiple of 32, so a block
+  // is wholly inside N or wholly outside.
   auto epilogue = [&]() __attribute__((always_inline)) {
     if (!PERSIST && a.ksplit > 1) {  // (the persistent form never splits K)
       // split K: the raw fp32 sums of this split, [split][row][gate cols | up cols] or
@@ -841,7 +860,7 @@ void k_pre_gemm(ExpertGemmArgs a) {
         for (int rb = 0; rb < RB; ++rb) {
           const int i = wm * 32 * RB + rb * 32 + r;
           if (i >= t.count) continue;
-          uint16_t* hrow = a.h + (size_t)(t.row0 + i) * a.h_stride + nb + 4 * half;
+          uint32_t pk[4][2];
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             float hv[4];
@@ -852,9 +871,10 @@ void k_pre_gemm(ExpertGemmArgs a) {
               const float u = s_u[((wn * RB + rb) * 16 + v) * 64 + lane] * gs_u;
               hv[j] = silu(g) * u;
             }
-            *reinterpret_cast<uint2*>(hrow + 8 * g4) =
-                make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+            pk[g4][0] = pack_bf16x2(hv[0], hv[1]);
+            pk[g4][1] = pack_bf16x2(hv[2], hv[3]);
           }
+          store_cols32_16bit(a.h + (size_t)(t.row0 + i) * a.h_stride + nb, pk, half);
         }
       }
     } else if (GATEUP) {
@@ -868,7 +888,7 @@ void k_pre_gemm(ExpertGemmArgs a) {
         for (int rb = 0; rb < RB; ++rb) {
           const int i = wm * 32 * RB + rb * 32 + r;
           if (i >= t.count) continue;
-          uint16_t* hrow = a.h + (size_t)(t.row0 + i) * a.h_stride + nb + 4 * half;
+          uint32_t pk[4][2];
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             float hv[4];
@@ -878,9 +898,10 @@ void k_pre_gemm(ExpertGemmArgs a) {
               const float u = acc[rb][CH + cg][4 * g4 + j] * gs_u;
               hv[j] = silu(g) * u;
             }
-            *reinterpret_cast<uint2*>(hrow + 8 * g4) =
-                make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+            pk[g4][0] = pack_bf16x2(hv[0], hv[1]);
+            pk[g4][1] = pack_bf16x2(hv[2], hv[3]);
           }
+          store_cols32_16bit(a.h + (size_t)(t.row0 + i) * a.h_stride + nb, pk, half);
         }
       }
     } else {
@@ -902,10 +923,6 @@ void k_pre_gemm(ExpertGemmArgs a) {
           const size_t off = (size_t)(t.row0 + i) * a.H + nb + 4 * half;
           const f32x16_t& c = acc[rb][cb];
           if (a.y_half) {
-            // lane half h holds columns 8g + 4h .. 8g + 4h + 3 (g = 0..3). The two halves swap
-            // half of them (lane l <-> l + 32), so that each lane stores 16 contiguous bytes
-            // and each store instruction fills whole 32-byte sectors: half 0 columns 0-7 and
-            // 16-23, half 1 columns 8-15 and 24-31.
             uint32_t pk[4][2];
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
@@ -916,15 +933,7 @@ void k_pre_gemm(ExpertGemmArgs a) {
               pk[g4][0] = pack_f16x2_sat(v0, v1);
               pk[g4][1] = pack_f16x2_sat(v2, v3);
             }
-            const uint32_t s0 = half ? pk[0][0] : pk[1][0], s1 = half ? pk[0][1] : pk[1][1];
-            const uint32_t s2 = half ? pk[2][0] : pk[3][0], s3 = half ? pk[2][1] : pk[3][1];
-            const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 32), r1 = (uint32_t)__shfl_xor((int)s1, 32);
-            const uint32_t r2 = (uint32_t)__shfl_xor((int)s2, 32), r3 = (uint32_t)__shfl_xor((int)s3, 32);
-            uint16_t* yrow = y16 + (size_t)(t.row0 + i) * a.H + nb;
-            *reinterpret_cast<uint4*>(yrow + (half ? 8 : 0)) =
-                half ? make_uint4(r0, r1, pk[1][0], pk[1][1]) : make_uint4(pk[0][0], pk[0][1], r0, r1);
-            *reinterpret_cast<uint4*>(yrow + (half ? 24 : 16)) =
-                half ? make_uint4(r2, r3, pk[3][0], pk[3][1]) : make_uint4(pk[2][0], pk[2][1], r2, r3);
+            store_cols32_16bit(y16 + (size_t)(t.row0 + i) * a.H + nb, pk, half);
           } else {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {

@@ -68,8 +68,9 @@ enum {
   MOE_DEVERR_EXPERT_ID = 1, /* an expert id outside [0, num_experts) reached dispatch */
   MOE_DEVERR_TOKEN_ID = 2,  /* hash routing: a token id outside [0, vocab) */
   MOE_DEVERR_TABLE = 4,     /* hash routing: a tid2eid entry outside [0, num_experts) */
-  MOE_DEVERR_Y_RANGE = 8    /* prefill: a routed expert output beyond the fp16 range of its
-                               intermediate store (+-65504); it was saturated there */
+  MOE_DEVERR_Y_RANGE = 8    /* prefill: a routed expert output whose fp16 intermediate store
+                               (round to nearest even) left the fp16 range (|y| >= 65520) or
+                               was not finite; it was stored saturated to +-65504 */
 };
 
 /* Expert weight storage formats (MoE module page, doc of MoeLayer.experts_scale_kind;

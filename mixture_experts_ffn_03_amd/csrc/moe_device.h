@@ -71,6 +71,21 @@ __device__ __forceinline__ uint32_t pack_f16x2_sat(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Two floats -> fp16 pair, round to nearest even, no saturation (beyond the range: +-inf).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  f16x2_t v;
+  v[0] = (_Float16)lo;
+  v[1] = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Nonzero in bit 15 or 31 where an fp16 of the pair is infinite or NaN (exponent field all
+// ones: adding one to it carries out of the field).
+__device__ __forceinline__ uint32_t f16x2_nonfinite_bits(uint32_t p) {
+  return ((p & 0x7C007C00u) + 0x04000400u) & 0x80008000u;
+}
+
 __device__ __forceinline__ float f16_to_f32(uint32_t h16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
 }

@@ -923,15 +923,22 @@ void k_pre_gemm(ExpertGemmArgs a) {
           const size_t off = (size_t)(t.row0 + i) * a.H + nb + 4 * half;
           const f32x16_t& c = acc[rb][cb];
           if (a.y_half) {
-            uint32_t pk[4][2];
+            // round to fp16; a value that rounds past +-65504 (or is not finite) is rare, so
+            // the saturating conversion runs only for a lane that produced one
+            uint32_t pk[4][2], nf = 0;
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-              const float v0 = c[4 * g4] * gs, v1 = c[4 * g4 + 1] * gs;
-              const float v2 = c[4 * g4 + 2] * gs, v3 = c[4 * g4 + 3] * gs;
-              range |= !(fabsf(v0) <= 65504.f && fabsf(v1) <= 65504.f &&
-                         fabsf(v2) <= 65504.f && fabsf(v3) <= 65504.f);
-              pk[g4][0] = pack_f16x2_sat(v0, v1);
-              pk[g4][1] = pack_f16x2_sat(v2, v3);
+              pk[g4][0] = pack_f16x2(c[4 * g4] * gs, c[4 * g4 + 1] * gs);
+              pk[g4][1] = pack_f16x2(c[4 * g4 + 2] * gs, c[4 * g4 + 3] * gs);
+              nf |= f16x2_nonfinite_bits(pk[g4][0]) | f16x2_nonfinite_bits(pk[g4][1]);
+            }
+            if (nf) {
+              range = true;
+#pragma unroll
+              for (int g4 = 0; g4 < 4; ++g4) {
+                pk[g4][0] = pack_f16x2_sat(c[4 * g4] * gs, c[4 * g4 + 1] * gs);
+                pk[g4][1] = pack_f16x2_sat(c[4 * g4 + 2] * gs, c[4 * g4 + 3] * gs);
+              }
             }
             store_cols32_16bit(y16 + (size_t)(t.row0 + i) * a.H + nb, pk, half);
           } else {

@@ -513,8 +513,8 @@ def test_prefill_persistent_down(fmt, shape):
 
 def test_prefill_expert_output_range_is_flagged():
     """Routed prefill expert outputs are stored as fp16 between the down projection and the
-    blend: an output beyond +-65504 saturates there and sets MOE_DEVERR_Y_RANGE (ordinary
-    outputs set nothing)."""
+    blend: an output that rounds past +-65504 saturates there and sets MOE_DEVERR_Y_RANGE
+    (ordinary outputs set nothing)."""
     spec = S.LayerSpec(name="y_range", tokens=256, hidden=512, experts=8, top_k=2, inter=256,
                        fmt=S.NVFP4, seed=1400)
     inp = S.make_inputs(spec, device=DEV)

@@ -60,7 +60,8 @@ __device__ __forceinline__ float silu(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
 }
 
-// Two fp32 -> fp16 pair, round to nearest even, saturating at +-65504 (NaN stays NaN).
+// Two fp32 -> fp16 pair, round to nearest even, saturating at +-65504 (fmaxf / fminf order:
+// a NaN becomes -65504).
 __device__ __forceinline__ uint32_t pack_f16x2_sat(float lo, float hi) {
   lo = fminf(fmaxf(lo, -65504.f), 65504.f);
   hi = fminf(fmaxf(hi, -65504.f), 65504.f);

@@ -1134,7 +1134,7 @@ static hipError_t launch_pre_shape(const ExpertGemmArgs& a, hipStream_t s) {
   } else {
     const int sbytes = K / (FMT == 0 ? 16 : 32);
 #if MOE_PRE_MX8
-    if (FMT == 1 && KC == 64) return launch_pre_ss<FMT, KC, NSTG, RB, WM, CB, GATEUP, false>(a, s);
+    if constexpr (FMT == 1 && KC == 64) return launch_pre_ss<FMT, KC, NSTG, RB, WM, CB, GATEUP, false>(a, s);
 #endif
     if (sbytes % 16 == 0) return launch_pre_ss<FMT, KC, NSTG, RB, WM, CB, GATEUP, true>(a, s);
     if constexpr (KC == 256) return hipErrorInvalidValue;  // (super-staged scales only)

@@ -332,6 +332,41 @@ def cpu_baseline(spec, inp, name, seconds):
                       f"CPUs, {model})"}
 
 
+def kernel_work(stage, u_mean, T, K, H, I, fmt, decode):
+    """Algorithmic work of one routed launch of `stage` ("gate_up" or "down"): bytes (each
+    touched expert's weights once, its input activations and its output rows; y is fp16 for
+    routed prefill rows, else fp32) and flops of the T * K routed rows, with their per-unit
+    notes. u_mean = mean number of touched experts."""
+    bpe = bytes_per_elem(fmt)
+    rows = T * K
+    if stage == "gate_up":
+        return (u_mean * 2 * I * H * bpe + T * H * 2 + rows * I * 2, 2 * rows * H * 2 * I,
+                "2*I*H*b bytes per touched expert (b = 0.5625 NVFP4, 0.53125 MXFP4) + x in + h out",
+                "4*H*I flops per routed row")
+    return (u_mean * I * H * bpe + rows * I * 2 + rows * H * (4 if decode else 2), 2 * rows * H * I,
+            "I*H*b bytes per touched expert + h in + y out", "2*H*I flops per routed row")
+
+
+def roofline(kbytes, kflops, kernel_ms, unit_bytes="", unit_flops=""):
+    """The bound of a kernel from its arithmetic intensity against the ridge of the published
+    peaks (bf16 MFMA, HBM), and its achieved rate over the measured launch duration."""
+    ridge = BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if kflops / kbytes < ridge:
+        achieved = kbytes / (kernel_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        per_launch, unit_note = kbytes, unit_bytes
+    else:
+        achieved = kflops / (kernel_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4)}
+        per_launch, unit_note = kflops, unit_flops
+    roof["per_launch"] = per_launch
+    roof["per_unit"] = unit_note
+    roof["arith_intensity"] = round(kflops / kbytes, 1)
+    return roof
+
+
 def run_workload(name, args, with_cpu=True, with_graph=True, steps=None, warmup=None):
     """Time `steps` layer calls of one workload; returns the result dict of the JSON line."""
     import torch
@@ -470,37 +505,13 @@ def run_workload(name, args, with_cpu=True, with_graph=True, steps=None, warmup=
 
     u_mean = sum(uniq[(warmup + i) % period] for i in range(steps)) / steps
     bpe = bytes_per_elem(spec.fmt)
-    # algorithmic work of the dominant kernel per launch: each touched expert's weights
-    # once, its input activations and its output rows (y: fp16 routed prefill rows, else
-    # fp32); flops of the routed rows
-    if kernel_stage == "gate_up":
-        kbytes = u_mean * 2 * I * H * bpe + T * H * 2 + S_rows * I * 2
-        kflops = 2 * S_rows * H * 2 * I
-        unit_bytes = "2*I*H*b bytes per touched expert (b = 0.5625 NVFP4, 0.53125 MXFP4) + x in + h out"
-        unit_flops = "4*H*I flops per routed row"
-    else:
-        kbytes = u_mean * I * H * bpe + S_rows * I * 2 + S_rows * H * (4 if decode else 2)
-        kflops = 2 * S_rows * H * I
-        unit_bytes = "I*H*b bytes per touched expert + h in + y out"
-        unit_flops = "2*H*I flops per routed row"
-    ridge = BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if kflops / kbytes < ridge:
-        achieved = kbytes / (kernel_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-        per_launch, unit_note = kbytes, unit_bytes
-    else:
-        achieved = kflops / (kernel_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4)}
-        per_launch, unit_note = kflops, unit_flops
+    kbytes, kflops, unit_bytes, unit_flops = kernel_work(kernel_stage, u_mean, T, K, H, I,
+                                                         spec.fmt, decode)
+    roof = roofline(kbytes, kflops, kernel_ms, unit_bytes, unit_flops)
     kname = f"{'decode' if decode else 'prefill'}_{kernel_stage}"
     roof["traffic"] = load_traffic(name, kname) if args.tokens <= 0 else None
     roof["kernel"] = kname
     roof["kernel_ms"] = round(kernel_ms, 5)
-    roof["per_launch"] = per_launch
-    roof["per_unit"] = unit_note
-    roof["arith_intensity"] = round(kflops / kbytes, 1)
 
     # whole-layer algorithmic work
     shared_bytes = (3 * H * spec.shared_inter * bytes_per_elem(spec.shared_fmt)) if spec.shared else 0

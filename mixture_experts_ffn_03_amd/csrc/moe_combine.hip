@@ -56,6 +56,13 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  // the shared expert's row and the residual do not depend on the slot rows: requested
+  // first, so that their round trip overlaps that of the rows and weights (a few-token
+  // layer otherwise pays it again after the slots)
+  float ysh[8];
+  uint4 res = make_uint4(0, 0, 0, 0);  // (8 bf16, widened after the slots)
+  if (a.shared) load_y8(a.y, (size_t)t * a.H + h0, ysh);
+  if (a.residual) res = *reinterpret_cast<const uint4*>(a.residual + (size_t)t * a.H + h0);
   // batches of kCombineBatch slots: their rows and weights first, then every row's loads
   // (a dropped slot's load reads row 0 and is discarded; slots past K load nothing), then the
   // sums in slot order
@@ -86,16 +93,16 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     }
   }
   if (a.shared) {
-    float v[8];
-    load_y8(a.y, (size_t)t * a.H + h0, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    for (int i = 0; i < 8; ++i) acc[i] += ysh[i];
   }
   if (a.residual) {
-    float v[8];
-    load_bf16x8(a.residual + (size_t)t * a.H + h0, v);
+    const uint32_t d[4] = {res.x, res.y, res.z, res.w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += bf16_to_f32(d[i] & 0xFFFFu);
+      acc[2 * i + 1] += bf16_to_f32(d[i] >> 16);
+    }
   }
   uint4 o;
   o.x = pack_bf16x2(acc[0], acc[1]);

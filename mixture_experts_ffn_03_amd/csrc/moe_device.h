@@ -262,4 +262,35 @@ __device__ __forceinline__ int reduced_index(int lane, int i) {
   return idx;
 }
 
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const lds_u8*)p;
+}
+
+// Direct-to-LDS loads: every active lane reads SIZE bytes at its own global address; the
+// wave writes them to LDS at m0 + lane * SIZE (m0 = the wave-uniform base; the 2-byte form
+// fills 4-byte slots, the value in the low half). The compiler cannot see them: their wait
+// (vmcnt) is issued by hand.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds_base), "v"(g) : "memory", "m0");
+}
+// the same with the non-temporal hint: weight rows that one block streams once (256-code
+// stages of 32-row tiles, whose experts rarely have a second row tile). Hash layer gate+up
+// 498 -> 476 us; on 128-row tiles, whose weights the expert's other row tiles re-read from the
+// caches, the hint made gate+up 25 % slower.
+__device__ __forceinline__ void dma16_nt(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+               :: "s"(lds_base), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(lds_base), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void dma2(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ushort %1, off"
+               :: "s"(lds_base), "v"(g) : "memory", "m0");
+}
+
 }  // namespace moe

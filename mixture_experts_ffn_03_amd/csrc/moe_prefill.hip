@@ -54,8 +54,6 @@ namespace moe {
 
 constexpr int kFp8MaxKb = 128;  // FP8 prefill: K up to 128 * 128 codes (block-scale table)
 
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint32_t (&d)[4]) {
   uint4 v = make_uint4(d[0], d[1], d[2], d[3]);
   return __builtin_bit_cast(bf16x8_t, v);
@@ -76,34 +74,6 @@ __device__ __forceinline__ void store_cols32_16bit(uint16_t* row, const uint32_t
       half ? make_uint4(r0, r1, pk[1][0], pk[1][1]) : make_uint4(pk[0][0], pk[0][1], r0, r1);
   *reinterpret_cast<uint4*>(row + (half ? 24 : 16)) =
       half ? make_uint4(r2, r3, pk[3][0], pk[3][1]) : make_uint4(pk[2][0], pk[2][1], r2, r3);
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-  return (uint32_t)(uintptr_t)(const lds_u8*)p;
-}
-
-// Direct-to-LDS loads: every lane reads SIZE bytes at its own global address; the wave
-// writes them to LDS at m0 + lane * SIZE (m0 = the wave-uniform base). Their wait is
-// issued by hand (wait_stage).
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds_base), "v"(g) : "memory", "m0");
-}
-// the same with the non-temporal hint: weight rows that one block streams once (256-code
-// stages of 32-row tiles, whose experts rarely have a second row tile). Hash layer gate+up
-// 498 -> 476 us; on 128-row tiles, whose weights the expert's other row tiles re-read from the
-// caches, the hint made gate+up 25 % slower.
-__device__ __forceinline__ void dma16_nt(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
-               :: "s"(lds_base), "v"(g) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-               :: "s"(lds_base), "v"(g) : "memory", "m0");
-}
-__device__ __forceinline__ void dma2(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ushort %1, off"
-               :: "s"(lds_base), "v"(g) : "memory", "m0");
 }
 
 // Build flag MOE_PRE_WAIT_SPLIT (off in the library; a diagnostic build): the one-block-per-tile

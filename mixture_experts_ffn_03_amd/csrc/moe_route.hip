@@ -115,11 +115,14 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
     tv[m] = t < T;
     xrow[m] = x + (size_t)(tv[m] ? t : 0) * H + 8 * q;
   }
-  f64x4_t acc[NE][MF];
+  // with at most two accumulators per wave (few tokens), odd chunks add into a second set,
+  // halving the dependent MFMA chain; the two are added once at the end
+  constexpr int NALT = MF * NE <= 2 ? 2 : 1;
+  f64x4_t acc[NE][MF], accb[NE][MF];
 #pragma unroll
   for (int g = 0; g < NE; ++g)
 #pragma unroll
-    for (int m = 0; m < MF; ++m) acc[g][m] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    for (int m = 0; m < MF; ++m) acc[g][m] = accb[g][m] = f64x4_t{0.0, 0.0, 0.0, 0.0};
   // the operands of the wave's next two 32-wide chunks are in flight while the current
   // chunk's MFMAs run (one chunk ahead is shorter than a loaded HBM round trip)
   const int kstart = kb + 32 * wave;
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
     load(kstart, wv, xv);
     load(kstart + 128 < ke ? kstart + 128 : kstart, w1, x1);
   }
-  for (int k0 = kstart; k0 < ke; k0 += 128) {
+  for (int k0 = kstart, odd = 0; k0 < ke; k0 += 128, odd ^= 1) {
     uint4 wn[NE], xn[MF];
     load(k0 + 256 < ke ? k0 + 256 : k0, wn, xn);
     double xd[MF][8];
@@ -153,11 +156,19 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
     for (int g = 0; g < NE; ++g) {
       double wd[8];
       bf16x8_to_f64(wv[g], wd);
+      if (NALT == 2 && odd) {
 #pragma unroll
-      for (int st = 0; st < 8; ++st)
+        for (int st = 0; st < 8; ++st)
 #pragma unroll
-        for (int m = 0; m < MF; ++m)
-          acc[g][m] = __builtin_amdgcn_mfma_f64_16x16x4f64(xd[m][st], wd[st], acc[g][m], 0, 0, 0);
+          for (int m = 0; m < MF; ++m)
+            accb[g][m] = __builtin_amdgcn_mfma_f64_16x16x4f64(xd[m][st], wd[st], accb[g][m], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+#pragma unroll
+          for (int m = 0; m < MF; ++m)
+            acc[g][m] = __builtin_amdgcn_mfma_f64_16x16x4f64(xd[m][st], wd[st], acc[g][m], 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int g = 0; g < NE; ++g) {
@@ -169,6 +180,12 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
       xv[m] = x1[m];
       x1[m] = xn[m];
     }
+  }
+  if (NALT == 2) {
+#pragma unroll
+    for (int g = 0; g < NE; ++g)
+#pragma unroll
+      for (int m = 0; m < MF; ++m) acc[g][m] += accb[g][m];
   }
   if (wave > 0) {
 #pragma unroll

@@ -86,9 +86,13 @@ __device__ __forceinline__ double score_f64(int score, float logit) {
 // ---------------------------------------------------------------------------
 // Returns, in lane j < K, the expert of slot j (-1 for a dropped slot; other lanes -1). The
 // global outputs (ids, w, err_tok, logits_out) are written where their pointers are set.
-template <int NPL>
+// LEAN form (top-K selection only, no outputs, no routing weights): every lane returns the
+// selected expert of rank `rank` in index order (the rank-th lowest index among the k
+// selected), from the same keys and the same selection rounds as the full form; the
+// softmax normaliser is only formed where a key needs it (softmax+bias).
+template <int NPL, bool LEAN = false>
 __device__ __forceinline__ int topk_token(const TopkArgs& a, int t, int32_t* lds_ids,
-                                          int32_t* lds_err) {
+                                          int32_t* lds_err, int rank = 0) {
   const int lane = threadIdx.x & 63;
   const int E = a.E, K = a.K;
 
@@ -133,7 +137,7 @@ __device__ __forceinline__ int topk_token(const TopkArgs& a, int t, int32_t* lds
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + kWave * i;
     if (e < E) {
-      if (a.logits_out) a.logits_out[(size_t)t * E + e] = lg[i];
+      if (!LEAN && a.logits_out) a.logits_out[(size_t)t * E + e] = lg[i];
     } else {
       lg[i] = -__builtin_inff();  // padding: never selectable, no softmax mass
     }
@@ -149,12 +153,12 @@ __device__ __forceinline__ int topk_token(const TopkArgs& a, int t, int32_t* lds
   // softmax+bias key, whose probability is rounded once)
   float m = -__builtin_inff(), S = 0.f;
   double S64 = 0.0;
-  if (a.score == 0 || a.score == 3) {
+  if ((!LEAN && a.score == 0) || a.score == 3) {
 #pragma unroll
     for (int i = 0; i < NPL; ++i) m = fmaxf(m, lg[i]);
     m = wave_max_dpp(m);
   }
-  if (a.score == 0) {
+  if (!LEAN && a.score == 0) {
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
       if (lane + kWave * i < E) S += expf(lg[i] - m);
@@ -194,6 +198,22 @@ __device__ __forceinline__ int topk_token(const TopkArgs& a, int t, int32_t* lds
         if (i == (idx >> 6) && lane == (idx & 63)) kv[i] = 0u;  // taken
       if (lane == j) my_id = idx;
     }
+    if constexpr (LEAN) {
+      // the selected experts are the valid lanes whose key was taken (a valid key is never
+      // 0); walk their index-ordered masks to the rank-th one
+      int r = rank, e = -1;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        uint64_t sel = __ballot(lane + kWave * i < E && kv[i] == 0u);
+        const int c = __popcll(sel);
+        if (e < 0 && r < c) {
+          for (int q = 0; q < r; ++q) sel &= sel - 1;
+          e = kWave * i + __builtin_ctzll(sel);
+        }
+        r -= c;
+      }
+      return e;
+    }
   } else {  // hash routing: ids from the static table, no selection
     const int64_t tok = a.token_ids[t];
     const bool tok_ok = tok >= 0 && tok < a.vocab;
@@ -205,6 +225,7 @@ __device__ __forceinline__ int topk_token(const TopkArgs& a, int t, int32_t* lds
     }
     err = __builtin_amdgcn_readfirstlane(err) | (int)(__ballot(err & 4) ? 4 : 0);
   }
+  if constexpr (LEAN) return -1;  // (the lean form selects; it never takes hash routing)
 
   // the selected experts' logits, fetched from their lanes (every lane takes part)
   float l = 0.f;

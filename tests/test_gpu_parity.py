@@ -297,6 +297,16 @@ SMALL = {
                                 experts=64, inter=256, shared_inter=192),
     "t1_fused_mxfp4": S.LayerSpec(name="t1_fused_mxfp4", tokens=1, hidden=512, experts=128,
                                   top_k=6, inter=256, fmt=S.MXFP4, renormalize=True, seed=1092),
+    # the other scores through the one-token kernel, whose expert blocks select with the lean
+    # form (keys and rounds only) while one wave writes the full routing: sqrt-softplus with
+    # a correction bias over 96 experts (two keys per lane, the last 32 lanes padding), and
+    # softmax+bias over 40 experts (one key per lane), with no zero-computation experts
+    "t1_fused_sqrtsp": S.LayerSpec(name="t1_fused_sqrtsp", tokens=1, hidden=512, experts=96,
+                                   top_k=4, inter=256, fmt=S.NVFP4, score=S.SQRT_SOFTPLUS,
+                                   renormalize=True, correction_bias=True, seed=1095),
+    "t1_fused_softmax_bias": S.LayerSpec(name="t1_fused_softmax_bias", tokens=1, hidden=512,
+                                         experts=40, top_k=5, inter=128, fmt=S.MXFP4,
+                                         score=S.SOFTMAX_BIAS, correction_bias=True, seed=1096),
     # 40 tokens on the decode path: the shared expert's implicit list of ten 4-token tiles
     "dsv3_t40_mini": S.scaled(S.WORKLOADS["dsv3_decode_t32"], tokens=40, hidden=1024,
                               experts=64, inter=256, shared_inter=192),

@@ -17,12 +17,17 @@
  * - Every call is asynchronous on `stream`: it validates on the host, enqueues
  *   kernels and returns. No call waits for the device, except
  *   moe_get_device_error, which synchronises `stream` to read the error word.
- * - With a shared expert, moe_experts_forward and moe_layer_forward fork a side stream of
- *   `stream` (one per caller stream, created on the first such call made while `stream` is
- *   not being captured, non-blocking, default priority, kept until the process ends): the
- *   shared expert runs there beside the dispatch and the routed experts and is joined back
- *   by an event before the blend, so the call is still one ordered unit on `stream` (and
- *   captures into a graph as a fork and a join). moe_layer_forward_noalloc never forks.
+ * - With a shared expert whose launches would leave most of the chip idle (on the decode
+ *   GEMV: below 8 tokens, or sizes the MFMA tiles do not take; on the MFMA kernels from 256
+ *   tokens, whose K is then kept whole),
+ *   moe_experts_forward and moe_layer_forward fork a side stream of `stream` (one per
+ *   caller stream, created on the first such call made while `stream` is not being
+ *   captured, non-blocking, default priority, kept until the process ends): the shared
+ *   expert runs there beside the dispatch and the routed experts and is joined back by an
+ *   event before the blend, so the call is still one ordered unit on `stream` (and captures
+ *   into a graph as a fork and a join). Between the two (MFMA launches with K split over
+ *   blocks, which fill the chip) it runs on `stream` after the routed experts.
+ *   moe_layer_forward_noalloc never forks.
  *   Indices and weights stay on the device (module doc: no device-to-host sync).
  * - bf16 tensors are passed as uint16_t bit patterns; every activation is
  *   row-major [tokens, hidden]. Activations (x, x_experts, out, residual), norm_gamma,

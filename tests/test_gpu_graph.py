@@ -14,9 +14,14 @@ pytestmark = pytest.mark.gpu
 
 CASES = {
     "qwen3_decode_t8": S.WORKLOADS["qwen3_decode_t8"],
-    # shared expert, sigmoid + correction bias, several tiles per expert
+    # shared expert, sigmoid + correction bias, several tiles per expert; at 13 tokens the
+    # shared expert's split-K MFMA launches run on the layer's stream
     "dsv3_mini": S.scaled(S.WORKLOADS["dsv3_decode_t32"], tokens=13, hidden=1024, experts=64,
                           inter=256, shared_inter=192),
+    # at 4 tokens it runs on the GEMV, on a side stream forked from the layer's stream and
+    # joined before the blend (captured as a fork and a join)
+    "dsv3_t4_mini": S.scaled(S.WORKLOADS["dsv3_decode_t32"], tokens=4, hidden=1024, experts=64,
+                             inter=256, shared_inter=192),
 }
 
 

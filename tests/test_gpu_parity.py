@@ -4,6 +4,8 @@ Bars: expert ids bit-exact on identical fp32 logits; router logits bit-exact (fp
 accumulation on both sides, one rounding); layer output within max-abs 2e-2 and
 rel-L2 5e-3 of the fp64 oracle (before its bf16 rounding).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -585,6 +587,42 @@ def test_one_token_blend_inside_down(fmt):
         want = O.experts_forward(f32(inp.x), oids, w.cpu().numpy().astype(np.float64),
                                  oracle_cache(inp.routed), res, num_experts=E)
         assert_layer_close(out.float().cpu().numpy(), want, None, "one-token blend")
+
+
+@pytest.mark.parametrize("score", [S.SOFTMAX, S.SIGMOID])
+def test_one_token_fused_topk_ties(score):
+    """One token through the gate+up kernel that selects its own experts (a writer wave with
+    the full top-K, and in each expert block a lean selection of the expert of its rank),
+    with tied router logits: three experts share one router row and eight have a zero row
+    (logit 0), so the top-k boundary falls inside tied groups. The ids, weights and layer
+    output match the oracle's lowest-index tie-break."""
+    spec = S.LayerSpec(name="t1_ties", tokens=1, hidden=512, experts=64, top_k=6, inter=256,
+                       fmt=S.NVFP4, score=score, renormalize=True, seed=1097)
+    inp = S.make_inputs(spec, device=DEV)
+    rw = inp.router_w.clone()
+    lg = (inp.x.float() @ rw.float().t())[0]
+    best = int(torch.argmax(lg))
+    assert float(lg[best]) > 0.0
+    # the strongest row copied to two more experts; eight zero rows (logit exactly 0); every
+    # other row the negated strongest one (logit exactly minus the top one)
+    top = [best, (best + 17) % 64, (best + 33) % 64]
+    rest = [e for e in range(64) if e not in top]
+    zero = rest[20:28]
+    neg = [e for e in rest if e not in zero]
+    for e in top[1:]:
+        rw[e] = rw[best]
+    rw[zero] = 0
+    rw[neg] = -rw[best]
+    inp = dataclasses.replace(inp, router_w=rw)
+    _announce("one-token ties", score)
+    out, logits, ids, w, ws = run_layer(inp, path=M.PATH_DECODE)
+    _sync()
+    assert M.get_device_error(ws) == 0
+    want, ologits, oids, ow = oracle_layer(inp)
+    assert np.array_equal(logits.cpu().numpy(), ologits)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    assert np.allclose(w.cpu().numpy(), ow, rtol=W_RTOL, atol=1e-7)
+    assert_layer_close(out.float().cpu().numpy(), want, f32(inp.residual), "one-token ties")
 
 
 def test_bad_expert_ids_many_slots():

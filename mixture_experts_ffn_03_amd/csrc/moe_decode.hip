@@ -674,36 +674,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ROWS == 4 ?
   dec_one_body<FMT, LPR, M, ROWS>(a, tile, one_nbase<FMT, LPR, M, ROWS>(), StoreRows<M>{a, tile});
 }
 
-// One token without a shared expert: the down projection of every slot and the blend in one
-// kernel (MoE constructor page: the weighted-sum blend into the residual). A block has one
-// wave per tile of the token (at most kBlendMaxTiles), all on the same GR output rows; the
-// waves leave their sums in LDS by row, then the block's first GR threads add the slots in
-// order (w_j * y_j, a zero-computation expert's w_j * x_e, a dropped slot nothing) and the
-// residual, exactly as the separate blend does, and store bf16 out. The fp32 rows of y never
-// reach memory and the blend needs no launch of its own.
+// A few tokens without a shared expert: the down projection of every slot and the blend in
+// one kernel (MoE constructor page: the weighted-sum blend into the residual). A block has one
+// wave per tile (at most kBlendMaxTiles), all on the same GR output rows; the waves leave their
+// sums in LDS by row, then the block's first T x GR threads (token t, output row i) add that
+// token's slots in order (w_j * y_j, a zero-computation expert's w_j * x_e, a dropped slot
+// nothing) and the residual, exactly as the separate blend does, and store bf16 out. The fp32
+// rows of y never reach memory and the blend needs no launch of its own.
 constexpr int kBlendMaxTiles = 16;
+constexpr int kBlendMaxSlots = kBlendMaxTiles * kTileTok;  // token rows of the block's tiles
 
 template <int FMT, int LPR, int ROWS>
 __global__ __launch_bounds__(kBlendMaxTiles * 64) void k_dec_one_blend(ExpertGemmArgs a, CombineArgs cb) {
   constexpr int GR = OneShape<LPR, 1, ROWS>::GR;
-  __shared__ float s_y[kBlendMaxTiles * kTileTok][GR];  // [row of the token][output row]
+  __shared__ float s_y[kBlendMaxSlots][GR];  // [row of a token][output row]
   // the blend's inputs that do not depend on the sums (each slot's row and weight, the
   // residual of the block's rows, in 4-byte slots) reach LDS by direct-to-LDS loads that
   // wave 0 issues before its part of the down projection: their latency is hidden, and no
   // register waits for them
-  __shared__ int32_t s_inv[kBlendMaxTiles];
-  __shared__ float s_w[kBlendMaxTiles];
-  __shared__ uint32_t s_res[GR];
+  __shared__ int32_t s_inv[kBlendMaxSlots];
+  __shared__ float s_w[kBlendMaxSlots];
+  __shared__ uint32_t s_res[kBlendMaxSlots];
   const int nbase = blockIdx.x * GR;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int rbase = a.rows - cb.T * cb.K;  // first routed row (the token's rows follow)
+  const int rbase = a.rows - cb.T * cb.K;  // first routed row (the tokens' rows follow)
   if (wave == 0) {
-    if (lane < cb.K) {
+    if (lane < cb.T * cb.K) {
       dma4(cb.inv + lane, lds_addr(reinterpret_cast<const uint8_t*>(s_inv)));
       dma4(cb.w + lane, lds_addr(reinterpret_cast<const uint8_t*>(s_w)));
     }
-    if (cb.residual && lane < GR && nbase + lane < cb.H)
-      dma2(cb.residual + nbase + lane, lds_addr(reinterpret_cast<const uint8_t*>(s_res)));
+    const int rt = lane / GR, rn = nbase + lane % GR;  // (token, output row) of a residual
+    if (cb.residual && rt < cb.T && rn < cb.H)
+      dma2(cb.residual + (size_t)rt * cb.H + rn, lds_addr(reinterpret_cast<const uint8_t*>(s_res)));
   }
   Tile tile;
   if (resolve_tile(a.src, wave, tile)) {
@@ -712,16 +714,17 @@ __global__ __launch_bounds__(kBlendMaxTiles * 64) void k_dec_one_blend(ExpertGem
   }
   if (wave == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // (the loads above landed)
   __syncthreads();
-  const int i = threadIdx.x, n = nbase + i;
-  if (i >= GR || n >= cb.H) return;
+  const int t = threadIdx.x / GR, i = threadIdx.x % GR, n = nbase + i;
+  if (t >= cb.T || n >= cb.H) return;
   float acc = 0.f;
   for (int j = 0; j < cb.K; ++j) {
-    const int p = s_inv[j];
-    if (p >= 0) acc = fmaf(s_w[j], s_y[p - rbase][i], acc);
-    else if (p == -2) acc = fmaf(s_w[j], bf16_to_f32(cb.xe[n]), acc);
+    const int p = s_inv[t * cb.K + j];
+    const float wj = s_w[t * cb.K + j];
+    if (p >= 0) acc = fmaf(wj, s_y[p - rbase][i], acc);
+    else if (p == -2) acc = fmaf(wj, bf16_to_f32(cb.xe[(size_t)t * cb.H + n]), acc);
   }
-  if (cb.residual) acc += bf16_to_f32((uint16_t)(s_res[i] & 0xFFFFu));
-  cb.out[n] = f32_to_bf16(acc);
+  if (cb.residual) acc += bf16_to_f32((uint16_t)(s_res[threadIdx.x] & 0xFFFFu));
+  cb.out[(size_t)t * cb.H + n] = f32_to_bf16(acc);
 }
 
 // One token with top-K selection: the experts are chosen inside the gate+up kernel. The k
@@ -875,8 +878,14 @@ hipError_t launch_decode_gate_up_topk(const ExpertGemmArgs& a, const TopkArgs& t
 // One token, no shared expert, FP4 down rows of at most 64 chunks, at most kBlendMaxTiles
 // tiles: the down projection and the blend in one launch.
 bool decode_blend_fusable(const ExpertGemmArgs& a, const CombineArgs& cb) {
-  return cb.T == 1 && !cb.shared && a.src.tiles && a.tile_bound <= kBlendMaxTiles &&
-         cb.K <= kBlendMaxTiles && one_fits(a.down.fmt, a.I, kDecodeTile);
+  if (cb.shared || !a.src.tiles || a.tile_bound > kBlendMaxTiles ||
+      !one_fits(a.down.fmt, a.I, kDecodeTile))
+    return false;
+  // output rows per block of the one-step down GEMV (OneShape<LPR, 1, ROWS>::GR)
+  const int lpr = one_lanes(a.I / 32), rows = a.H >= kOneWideMinN ? 8 : 4;
+  const int gr = (kWave / lpr) * (lpr < rows ? lpr : rows);
+  // every slot's row and weight, and every (token, output row) residual, in one wave's lanes
+  return cb.T * cb.K <= kWave && cb.T * gr <= kWave;
 }
 
 template <int FMT, int LPR, int ROWS>

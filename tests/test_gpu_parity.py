@@ -564,16 +564,20 @@ def test_bad_expert_ids_are_dropped_and_flagged():
 
 
 @pytest.mark.parametrize("fmt", [S.NVFP4, S.MXFP4])
-def test_one_token_blend_inside_down(fmt):
-    """One token without a shared expert: the down kernel blends the slots itself. Slots of
-    routed experts (one repeated), zero-computation experts and an out-of-range id (dropped,
-    flagged), against the oracle; with and without a residual."""
+@pytest.mark.parametrize("tokens", [1, 2])
+def test_one_token_blend_inside_down(fmt, tokens):
+    """One or two tokens without a shared expert: the down kernel blends the slots itself.
+    Slots of routed experts (one repeated within a token and across the two), zero-computation
+    experts and out-of-range ids (dropped, flagged), against the oracle; with and without a
+    residual."""
     E, Z = 16, 4
-    spec = S.LayerSpec(name="t1_blend", tokens=1, hidden=1024, experts=E, top_k=7, inter=512,
-                       fmt=fmt, zero_experts=Z, seed=1300 + fmt)
+    spec = S.LayerSpec(name="t1_blend", tokens=tokens, hidden=1024, experts=E, top_k=7,
+                       inter=512, fmt=fmt, zero_experts=Z, seed=1300 + fmt)
     inp = S.make_inputs(spec, device=DEV)
-    ids = torch.tensor([[3, E + 1, 5, 99, 0, E, 3]], dtype=torch.int32, device=DEV)
-    w = torch.tensor([[0.3, 0.2, 0.15, 0.1, 0.1, 0.1, 0.05]], dtype=torch.float32, device=DEV)
+    rows = [[3, E + 1, 5, 99, 0, E, 3], [7, 3, E + 2, 1, -4, 2, 5]][:tokens]
+    ws_ = [[0.3, 0.2, 0.15, 0.1, 0.1, 0.1, 0.05], [0.25, 0.2, 0.2, 0.15, 0.1, 0.06, 0.04]][:tokens]
+    ids = torch.tensor(rows, dtype=torch.int32, device=DEV)
+    w = torch.tensor(ws_, dtype=torch.float32, device=DEV)
     cfg = config_for(inp, M.PATH_DECODE)
     ws = M.alloc_workspace(cfg, DEV)
     oids = ids.cpu().numpy()

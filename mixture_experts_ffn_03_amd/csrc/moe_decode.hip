@@ -676,7 +676,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ROWS == 4 ?
 
 // A few tokens without a shared expert: the down projection of every slot and the blend in
 // one kernel (MoE constructor page: the weighted-sum blend into the residual). A block has one
-// wave per tile (at most kBlendMaxTiles), all on the same GR output rows; the waves leave their
+// wave per tile (at most kBlendMaxTiles; beyond that, up to two tiles a wave, one after the
+// other), all on the same GR output rows; the waves leave their
 // sums in LDS by row, then the block's first T x GR threads (token t, output row i) add that
 // token's slots in order (w_j * y_j, a zero-computation expert's w_j * x_e, a dropped slot
 // nothing) and the residual, exactly as the separate blend does, and store bf16 out. The fp32
@@ -707,10 +708,12 @@ __global__ __launch_bounds__(kBlendMaxTiles * 64) void k_dec_one_blend(ExpertGem
     if (cb.residual && rt < cb.T && rn < cb.H)
       dma2(cb.residual + (size_t)rt * cb.H + rn, lds_addr(reinterpret_cast<const uint8_t*>(s_res)));
   }
-  Tile tile;
-  if (resolve_tile(a.src, wave, tile)) {
-    auto store = [&](int q, int n, float v) { s_y[tile.row0 + q - rbase][n - nbase] = v; };
-    dec_one_body<FMT, LPR, 1, ROWS>(a, tile, nbase, store);
+  for (int tw = wave; tw < a.tile_bound; tw += (int)(blockDim.x >> 6)) {
+    Tile tile;
+    if (resolve_tile(a.src, tw, tile)) {
+      auto store = [&](int q, int n, float v) { s_y[tile.row0 + q - rbase][n - nbase] = v; };
+      dec_one_body<FMT, LPR, 1, ROWS>(a, tile, nbase, store);
+    }
   }
   if (wave == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // (the loads above landed)
   __syncthreads();
@@ -878,7 +881,7 @@ hipError_t launch_decode_gate_up_topk(const ExpertGemmArgs& a, const TopkArgs& t
 // One token, no shared expert, FP4 down rows of at most 64 chunks, at most kBlendMaxTiles
 // tiles: the down projection and the blend in one launch.
 bool decode_blend_fusable(const ExpertGemmArgs& a, const CombineArgs& cb) {
-  if (cb.shared || !a.src.tiles || a.tile_bound > kBlendMaxTiles ||
+  if (cb.shared || !a.src.tiles || a.tile_bound > 2 * kBlendMaxTiles ||
       !one_fits(a.down.fmt, a.I, kDecodeTile))
     return false;
   // output rows per block of the one-step down GEMV (OneShape<LPR, 1, ROWS>::GR)
@@ -891,8 +894,9 @@ bool decode_blend_fusable(const ExpertGemmArgs& a, const CombineArgs& cb) {
 template <int FMT, int LPR, int ROWS>
 static hipError_t launch_blend_t(const ExpertGemmArgs& a, const CombineArgs& cb, hipStream_t s) {
   constexpr int GR = OneShape<LPR, 1, ROWS>::GR;
+  const int waves = a.tile_bound < kBlendMaxTiles ? a.tile_bound : kBlendMaxTiles;
   hipLaunchKernelGGL((k_dec_one_blend<FMT, LPR, ROWS>), dim3((a.H + GR - 1) / GR),
-                     dim3(a.tile_bound * 64), 0, s, a, cb);
+                     dim3(waves * 64), 0, s, a, cb);
   return hipGetLastError();
 }
 

@@ -381,9 +381,9 @@ def test_layer_without_residual_and_experts_entry(path):
     assert torch.equal(out, out2)
 
 
-@pytest.mark.parametrize("tokens", [1, 2, 16])
+@pytest.mark.parametrize("tokens", [1, 2, 4, 16])
 def test_qwen3_shape_small_batches_and_experts_entry(tokens):
-    """Qwen3-like decode layer at 1, 2 and 16 tokens against the oracle; then
+    """Qwen3-like decode layer at 1, 2, 4 and 16 tokens against the oracle; then
     moe_experts_forward builds its own dispatch from the ids in memory (the standalone
     dispatch kernel) where the layer's fused top-K built it from ids in LDS: same rows,
     same tiles, bit-identical outputs."""
@@ -564,18 +564,20 @@ def test_bad_expert_ids_are_dropped_and_flagged():
 
 
 @pytest.mark.parametrize("fmt", [S.NVFP4, S.MXFP4])
-@pytest.mark.parametrize("tokens", [1, 2])
+@pytest.mark.parametrize("tokens", [1, 2, 3])
 def test_one_token_blend_inside_down(fmt, tokens):
-    """One or two tokens without a shared expert: the down kernel blends the slots itself.
-    Slots of routed experts (one repeated within a token and across the two), zero-computation
-    experts and out-of-range ids (dropped, flagged), against the oracle; with and without a
-    residual."""
+    """A few tokens without a shared expert: the down kernel blends the slots itself (at three
+    tokens some of its waves take two tiles). Slots of routed experts (one repeated within a
+    token and across tokens), zero-computation experts and out-of-range ids (dropped,
+    flagged), against the oracle; with and without a residual."""
     E, Z = 16, 4
     spec = S.LayerSpec(name="t1_blend", tokens=tokens, hidden=1024, experts=E, top_k=7,
                        inter=512, fmt=fmt, zero_experts=Z, seed=1300 + fmt)
     inp = S.make_inputs(spec, device=DEV)
-    rows = [[3, E + 1, 5, 99, 0, E, 3], [7, 3, E + 2, 1, -4, 2, 5]][:tokens]
-    ws_ = [[0.3, 0.2, 0.15, 0.1, 0.1, 0.1, 0.05], [0.25, 0.2, 0.2, 0.15, 0.1, 0.06, 0.04]][:tokens]
+    rows = [[3, E + 1, 5, 99, 0, E, 3], [7, 3, E + 2, 1, -4, 2, 5],
+            [9, 11, 13, 3, E + 3, 15, 8]][:tokens]
+    ws_ = [[0.3, 0.2, 0.15, 0.1, 0.1, 0.1, 0.05], [0.25, 0.2, 0.2, 0.15, 0.1, 0.06, 0.04],
+           [0.2, 0.2, 0.15, 0.15, 0.1, 0.1, 0.1]][:tokens]
     ids = torch.tensor(rows, dtype=torch.int32, device=DEV)
     w = torch.tensor(ws_, dtype=torch.float32, device=DEV)
     cfg = config_for(inp, M.PATH_DECODE)

@@ -685,7 +685,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ROWS == 4 ?
 constexpr int kBlendMaxTiles = 16;
 constexpr int kBlendMaxSlots = kBlendMaxTiles * kTileTok;  // token rows of the block's tiles
 
-template <int FMT, int LPR, int ROWS>
+template <int FMT, int LPR, int ROWS, bool MULTI>
 __global__ __launch_bounds__(kBlendMaxTiles * 64) void k_dec_one_blend(ExpertGemmArgs a, CombineArgs cb) {
   constexpr int GR = OneShape<LPR, 1, ROWS>::GR;
   __shared__ float s_y[kBlendMaxSlots][GR];  // [row of a token][output row]
@@ -708,9 +708,17 @@ __global__ __launch_bounds__(kBlendMaxTiles * 64) void k_dec_one_blend(ExpertGem
     if (cb.residual && rt < cb.T && rn < cb.H)
       dma2(cb.residual + (size_t)rt * cb.H + rn, lds_addr(reinterpret_cast<const uint8_t*>(s_res)));
   }
-  for (int tw = wave; tw < a.tile_bound; tw += (int)(blockDim.x >> 6)) {
+  if constexpr (MULTI) {  // several tiles a wave, one after the other
+    for (int tw = wave; tw < a.tile_bound; tw += (int)(blockDim.x >> 6)) {
+      Tile tile;
+      if (resolve_tile(a.src, tw, tile)) {
+        auto store = [&](int q, int n, float v) { s_y[tile.row0 + q - rbase][n - nbase] = v; };
+        dec_one_body<FMT, LPR, 1, ROWS>(a, tile, nbase, store);
+      }
+    }
+  } else {  // one tile a wave (the loop would cost the 8 KB waves registers)
     Tile tile;
-    if (resolve_tile(a.src, tw, tile)) {
+    if (resolve_tile(a.src, wave, tile)) {
       auto store = [&](int q, int n, float v) { s_y[tile.row0 + q - rbase][n - nbase] = v; };
       dec_one_body<FMT, LPR, 1, ROWS>(a, tile, nbase, store);
     }
@@ -891,6 +899,8 @@ bool decode_blend_fusable(const ExpertGemmArgs& a, const CombineArgs& cb) {
   if (cb.shared || !a.src.tiles || a.tile_bound > MOE_BLEND_TILES_PER_WAVE * kBlendMaxTiles ||
       !one_fits(a.down.fmt, a.I, kDecodeTile))
     return false;
+  // several tiles a wave only with the 4 KB waves (the 8 KB waves' loop would spill)
+  if (a.tile_bound > kBlendMaxTiles && a.H >= kOneWideMinN) return false;
   // output rows per block of the one-step down GEMV (OneShape<LPR, 1, ROWS>::GR)
   const int lpr = one_lanes(a.I / 32), rows = a.H >= kOneWideMinN ? 8 : 4;
   const int gr = (kWave / lpr) * (lpr < rows ? lpr : rows);
@@ -902,8 +912,12 @@ template <int FMT, int LPR, int ROWS>
 static hipError_t launch_blend_t(const ExpertGemmArgs& a, const CombineArgs& cb, hipStream_t s) {
   constexpr int GR = OneShape<LPR, 1, ROWS>::GR;
   const int waves = a.tile_bound < kBlendMaxTiles ? a.tile_bound : kBlendMaxTiles;
-  hipLaunchKernelGGL((k_dec_one_blend<FMT, LPR, ROWS>), dim3((a.H + GR - 1) / GR),
-                     dim3(waves * 64), 0, s, a, cb);
+  if (ROWS == 4 && a.tile_bound > kBlendMaxTiles)
+    hipLaunchKernelGGL((k_dec_one_blend<FMT, LPR, ROWS, ROWS == 4>), dim3((a.H + GR - 1) / GR),
+                       dim3(waves * 64), 0, s, a, cb);
+  else
+    hipLaunchKernelGGL((k_dec_one_blend<FMT, LPR, ROWS, false>), dim3((a.H + GR - 1) / GR),
+                       dim3(waves * 64), 0, s, a, cb);
   return hipGetLastError();
 }
 

@@ -536,10 +536,18 @@ int launch_route(const moe_config& c, const Layout& L, const uint16_t* x,
   const int NE = c.num_experts + c.zero_experts;
   const TopkArgs t = make_topk_args(c, L, logit_bias, corr, token_ids, tid2eid, logits_in,
                                     logits_out, ids, w, ws);
+  // hash routing whose weights need only the selected experts' logits, none asked for: no
+  // router GEMM (unless the top-K runs fused with the dispatch)
+  const bool fuse_dispatch = dispatched && fused_topk_dispatch_fits(c.tokens, NE, c.top_k);
+  if (!fuse_dispatch && hash_gather_fits(t, c.hidden)) {
+    MOE_HIP(launch_hash_gather(t, x, router_w, c.hidden, s));
+    if (marks) MOE_HIP(marks->mark(MOE_STAGE_ROUTED));
+    return MOE_OK;
+  }
   if (!logits_in)
     MOE_HIP(launch_router_partial(x, router_w, at<double>(ws, L.partial), c.tokens, NE,
                                   c.hidden, L.ks, L.hsplit, s));
-  if (dispatched && fused_topk_dispatch_fits(c.tokens, NE, c.top_k)) {
+  if (fuse_dispatch) {
     if (marks) MOE_HIP(marks->mark(MOE_STAGE_ROUTED));
     const DispatchArgs d = make_dispatch_args(c, L, ids, t.err_tok, ws);
     MOE_HIP(launch_topk_dispatch(t, d, s));

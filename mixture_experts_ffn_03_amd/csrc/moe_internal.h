@@ -90,6 +90,11 @@ struct TopkArgs {
   float scaling;
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+// Hash routing from the selected experts' logits only (no router GEMM), where the scores
+// allow it and no logits are asked for.
+bool hash_gather_fits(const TopkArgs& a, int H);
+hipError_t launch_hash_gather(const TopkArgs& a, const uint16_t* x, const uint16_t* w, int H,
+                              hipStream_t s);
 
 struct DispatchArgs {
   const int32_t* ids;     // [T, K]

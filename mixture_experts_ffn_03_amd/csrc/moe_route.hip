@@ -271,4 +271,113 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Hash routing whose weights need only the selected experts' logits (sigmoid or
+// sqrt-softplus scores, or a renormalised softmax, where the normaliser over all experts
+// cancels), when no logits are asked for: one block per token reads its k experts from the
+// table and forms just those k router dot products, one wave per slot (fp64 over H, each
+// lane 8 columns per step, then a wave reduction; rounded to fp32 once with the logit bias, as the full
+// router's logits are), instead of the router GEMM over every expert (hidden a multiple of
+// 512, at most 4096). The weights follow the
+// hash branch of topk_token, the softmax taken over the selected experts (the renormalised
+// weights are the same). Error bits as topk_token's.
+// ---------------------------------------------------------------------------
+constexpr int kGatherSteps = 8;  // steps of 512 columns: hidden sizes up to 4096
+constexpr int kGatherWaves = 8;  // one block per token; wave w takes slots w, w + 8, ...
+
+__global__ __launch_bounds__(kGatherWaves * 64) void k_hash_gather(TopkArgs a,
+                                                                  const uint16_t* __restrict__ x,
+                                                                  const uint16_t* __restrict__ wr,
+                                                                  int H) {
+  __shared__ int s_id[kMaxTopK];
+  __shared__ float s_l[kMaxTopK];
+  __shared__ int s_err;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x;
+  const int E = a.E, K = a.K;
+  // the token's row in registers (8 columns per lane and step of 512), requested first
+  const int ns = H / (kWave * 8);
+  const uint16_t* xr = x + (size_t)t * H + lane * 8;
+  uint4 xv[kGatherSteps];
+#pragma unroll
+  for (int q = 0; q < kGatherSteps; ++q)
+    if (q < ns) xv[q] = *reinterpret_cast<const uint4*>(xr + q * kWave * 8);
+  if (wave == 0) {  // the slots' experts from the table
+    const int64_t tok = a.token_ids[t];
+    const bool tok_ok = tok >= 0 && tok < a.vocab;
+    int err = tok_ok ? 0 : 2;
+    int my_id = -1;
+    if (lane < K && tok_ok) {
+      const int64_t e = a.tid2eid[tok * K + lane];
+      if (e >= 0 && e < E) my_id = (int)e;
+      else err |= 4;
+    }
+    if (lane < K) s_id[lane] = my_id;
+    if (lane == 0) s_err = __builtin_amdgcn_readfirstlane(err) | (int)(__ballot(err & 4) ? 4 : 0);
+  }
+  __syncthreads();
+  // slot j's dot product: every step's weight piece requested at once, fp64 sums, a wave
+  // reduction, one rounding to fp32 with the logit bias
+  for (int j = wave; j < K; j += kGatherWaves) {
+    const int e = s_id[j];
+    if (e < 0) continue;  // (wave-uniform) a dropped slot has no logit
+    const uint16_t* er = wr + (size_t)e * H + lane * 8;
+    uint4 wv[kGatherSteps];
+#pragma unroll
+    for (int q = 0; q < kGatherSteps; ++q)
+      if (q < ns) wv[q] = *reinterpret_cast<const uint4*>(er + q * kWave * 8);
+    double acc = 0.0;
+#pragma unroll
+    for (int q = 0; q < kGatherSteps; ++q) {
+      if (q >= ns) break;
+      double xd[8], wd[8];
+      bf16x8_to_f64(xv[q], xd);
+      bf16x8_to_f64(wv[q], wd);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc = fma(xd[i], wd[i], acc);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kWave);
+    if (a.logit_bias) acc += (double)a.logit_bias[e];
+    if (lane == 0) s_l[j] = (float)acc;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int my_id = lane < K ? s_id[lane] : -1;
+  const bool sel = my_id >= 0;
+  const float l = sel ? s_l[lane] : 0.f;
+  float wj = 0.f;
+  if (a.score == 0) {  // softmax over the selected experts (renormalised: as over all)
+    float m = sel ? l : -__builtin_inff();
+    m = wave_max_dpp(m);
+    const float p = sel ? expf(l - m) : 0.f;
+    const float S = wave_sum_dpp(p);
+    wj = sel ? p / S : 0.f;
+  } else if (sel) {
+    wj = (float)score_f64(a.score, l);
+  }
+  if (a.renorm) {
+    const float sum = wave_sum_dpp(wj);
+    wj = sum > 0.f ? wj / sum : 0.f;
+  }
+  if (lane < K) {
+    a.w[(size_t)t * K + lane] = wj * a.scaling;
+    a.ids[(size_t)t * K + lane] = my_id;
+  }
+  if (lane == 0 && a.err_tok) a.err_tok[t] = s_err;
+}
+
+bool hash_gather_fits(const TopkArgs& a, int H) {
+  return a.select == 1 && !a.logits_out && !a.logits_in && H % (kWave * 8) == 0 &&
+         H <= kGatherSteps * kWave * 8 &&
+         (a.score == 1 || a.score == 2 || (a.score == 0 && a.renorm));
+}
+
+hipError_t launch_hash_gather(const TopkArgs& a, const uint16_t* x, const uint16_t* w, int H,
+                              hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_hash_gather, dim3(a.T), dim3(kGatherWaves * 64), 0, s, a, x, w, H);
+  return hipGetLastError();
+}
+
 }  // namespace moe

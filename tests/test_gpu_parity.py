@@ -595,6 +595,45 @@ def test_one_token_blend_inside_down(fmt, tokens):
         assert_layer_close(out.float().cpu().numpy(), want, None, "one-token blend")
 
 
+HASH_GATHER = {
+    "hash_mini": SMALL["hash_mini"],
+    "hash_sqrtsp_mini": SMALL["hash_sqrtsp_mini"],
+    "hash_sigmoid_mini": S.scaled(S.WORKLOADS["hash_mxfp4_t512"], tokens=50, hidden=512,
+                                  experts=32, inter=256, shared_inter=128, vocab=1000,
+                                  score=S.SIGMOID, renormalize=False, seed=1098),
+    "hash_mxfp4_t512": S.WORKLOADS["hash_mxfp4_t512"],
+}
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", sorted(HASH_GATHER))
+def test_hash_layer_without_logits(name):
+    """A hash-routed layer called without a logits output: its weights need only the k
+    selected experts' logits (renormalised softmax, sigmoid, sqrt-softplus), so no router GEMM
+    runs and the routing kernel forms just those dot products. Ids bit-exact, weights within
+    the weight tolerance and the layer output within the bar, against the oracle."""
+    _announce("hash without logits", name)
+    inp = S.make_inputs(HASH_GATHER[name], device=DEV)
+    cfg = config_for(inp)
+    T, K, H = inp.spec.tokens, inp.spec.top_k, inp.spec.hidden
+    ws = M.alloc_workspace(cfg, DEV)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    ids = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, K), dtype=torch.float32, device=DEV)
+    M.layer_forward(cfg, inp.x, inp.router_w, M.expert_weights(inp.routed), out, ws,
+                    norm_gamma=inp.gamma, logit_bias=inp.logit_bias,
+                    correction_bias=inp.correction_bias, token_ids=inp.token_ids,
+                    tid2eid=inp.tid2eid,
+                    shared=M.expert_weights(inp.shared) if inp.shared is not None else None,
+                    residual=inp.residual, dbg_ids=ids, dbg_w=w)
+    _sync()
+    assert M.get_device_error(ws) == 0
+    want, _, oids, ow = oracle_layer(inp, workers=oracle_workers())
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    assert np.allclose(w.cpu().numpy(), ow, rtol=W_RTOL, atol=1e-7)
+    assert_layer_close(out.float().cpu().numpy(), want, f32(inp.residual), name)
+
+
 @pytest.mark.parametrize("score", [S.SOFTMAX, S.SIGMOID])
 def test_one_token_fused_topk_ties(score):
     """One token through the gate+up kernel that selects its own experts (a writer wave with

@@ -313,7 +313,9 @@ __global__ __launch_bounds__(kGatherWaves * 64) void k_hash_gather(TopkArgs a,
       else err |= 4;
     }
     if (lane < K) s_id[lane] = my_id;
-    if (lane == 0) s_err = __builtin_amdgcn_readfirstlane(err) | (int)(__ballot(err & 4) ? 4 : 0);
+    // (the ballot over the whole wave: a table error sits in the lane of its slot)
+    const int werr = __builtin_amdgcn_readfirstlane(err) | (int)(__ballot(err & 4) ? 4 : 0);
+    if (lane == 0) s_err = werr;
   }
   __syncthreads();
   // slot j's dot product: every step's weight piece requested at once, fp64 sums, a wave

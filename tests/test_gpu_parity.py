@@ -634,6 +634,38 @@ def test_hash_layer_without_logits(name):
     assert_layer_close(out.float().cpu().numpy(), want, f32(inp.residual), name)
 
 
+def test_hash_layer_without_logits_bad_ids():
+    """The gathered-logit hash routing with an out-of-range token id and an out-of-range table
+    entry: the token's slots and the bad entry's slot are dropped (id -1, weight 0), both error
+    bits are set, and the other slots and the output match the oracle."""
+    spec = SMALL["hash_mini"]
+    inp = S.make_inputs(spec, device=DEV)
+    inp.token_ids[5] = spec.vocab + 9
+    row = int(inp.token_ids[11])
+    inp.tid2eid[row, 2] = spec.experts + 40
+    _announce("hash without logits, bad ids")
+    cfg = config_for(inp)
+    T, K, H = spec.tokens, spec.top_k, spec.hidden
+    ws = M.alloc_workspace(cfg, DEV)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    ids = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, K), dtype=torch.float32, device=DEV)
+    M.layer_forward(cfg, inp.x, inp.router_w, M.expert_weights(inp.routed), out, ws,
+                    norm_gamma=inp.gamma, correction_bias=inp.correction_bias,
+                    token_ids=inp.token_ids, tid2eid=inp.tid2eid,
+                    shared=M.expert_weights(inp.shared), residual=inp.residual, dbg_ids=ids,
+                    dbg_w=w)
+    _sync()
+    err = M.get_device_error(ws)
+    assert err & M.DEVERR_TOKEN_ID and err & M.DEVERR_TABLE
+    got = ids.cpu().numpy()
+    assert (got[5] == -1).all() and got[11, 2] == -1
+    want, _, oids, ow = oracle_layer(inp)
+    assert np.array_equal(got, oids)
+    assert np.allclose(w.cpu().numpy(), ow, rtol=W_RTOL, atol=1e-7)
+    assert_layer_close(out.float().cpu().numpy(), want, f32(inp.residual), "hash bad ids")
+
+
 @pytest.mark.parametrize("score", [S.SOFTMAX, S.SIGMOID])
 def test_one_token_fused_topk_ties(score):
     """One token through the gate+up kernel that selects its own experts (a writer wave with

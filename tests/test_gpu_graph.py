@@ -13,6 +13,9 @@ from gpu_cases import config_for
 pytestmark = pytest.mark.gpu
 
 CASES = {
+    # one token: top-K inside the gate+up kernel (a writer row and per-block lean selection),
+    # the blend inside the down kernel
+    "qwen3_decode_t1": S.WORKLOADS["qwen3_decode_t1"],
     "qwen3_decode_t8": S.WORKLOADS["qwen3_decode_t8"],
     # shared expert, sigmoid + correction bias, several tiles per expert; at 13 tokens the
     # shared expert's split-K MFMA launches run on the layer's stream
@@ -22,6 +25,9 @@ CASES = {
     # joined before the blend (captured as a fork and a join)
     "dsv3_t4_mini": S.scaled(S.WORKLOADS["dsv3_decode_t32"], tokens=4, hidden=1024, experts=64,
                              inter=256, shared_inter=192),
+    # hash routing from the selected experts' logits (no logits output), RMSNorm input
+    "hash_mini": S.scaled(S.WORKLOADS["hash_mxfp4_t512"], tokens=40, hidden=512, experts=32,
+                          inter=256, shared_inter=128, vocab=1000),
 }
 
 
